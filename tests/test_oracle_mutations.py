@@ -1,0 +1,56 @@
+"""Each plausible slip in the oracle must make a pin fail.
+
+The test copies the oracle's C source, plants one mistake by text
+substitution (a dropped term, a wrong sign, a wrong index, a flipped
+comparison), builds that copy into a temporary library and runs the pin suite
+against it in a child process. A mutant that passes every pin would mean the
+pins cannot see that kind of mistake. Runs on the CPU only.
+"""
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "moe_oracle.c")
+
+MUTANTS = {
+    "tie_break_high_index": ("if (best < 0 || l[e] > l[best]) best = e;",
+                             "if (best < 0 || l[e] >= l[best]) best = e;"),
+    "drop_b1": ("a[(size_t)r * h + n] = silu(s + b);", "a[(size_t)r * h + n] = silu(s);"),
+    "drop_b2": ("y[(size_t)r * d + m] = s + b;", "y[(size_t)r * d + m] = s;"),
+    "silu_sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
+    "w2_transposed": ("w[n] = widen(w2e, wdt, (size_t)m * h + n);",
+                      "w[n] = widen(w2e, wdt, (size_t)n * d + m);"),
+    "always_renorm": ("renorm ? pj / sel : pj", "pj / sel"),
+    "capacity_zero_unlimited": ("if (capacity >= 0 && kept > capacity)",
+                                "if (capacity > 0 && kept > capacity)"),
+    "aux_missing_E": ("*loss = (double)E * s;", "*loss = s;"),
+    "residual_dropped": ("double s = residual ? widen(residual, rdt, (size_t)tok[i] * d + m) : 0.0;",
+                         "double s = 0.0;"),
+    "router_bias_dropped": ("if (gate_bias) s += (double)gate_bias[e];", ""),
+    "bf16_shift": ("uint32_t u = (uint32_t)((const uint16_t *)p)[i] << 16;",
+                   "uint32_t u = (uint32_t)((const uint16_t *)p)[i] << 15;"),
+    "softmax_no_shift_in_num": ("p[e] = exp(l[e] - m) / z;", "p[e] = exp(l[e]) / z;"),
+    "combine_gate_ignored": ("s += gate[(size_t)i * k + j] * y_slots", "s += y_slots"),
+    "drop_keeps_last": ("if (rank < kept) {", "if (rank >= counts[e] - kept) {"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    mut = tmp_path / "mut.c"
+    mut.write_text(src.replace(old, new))
+    lib = tmp_path / "libmut.so"
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-o", str(lib),
+                    str(mut), "-lm"], check=True)
+    env = dict(os.environ, MOE_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"

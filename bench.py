@@ -1,0 +1,213 @@
+"""Benchmark: one MoE layer forward on one MI355X, routed tokens per second.
+
+A step is one pass of the whole layer over one batch of synthetic, seeded
+inputs already resident in HBM: router -> permute -> grouped FFN -> combine
+-> aux loss, five library calls enqueued on one stream. W untimed warm-up
+steps, then K timed steps bracketed by device synchronisation. Per-call
+durations come from HIP events recorded on the same stream around every
+call of every timed step.
+
+The default workload is the Mixtral-shaped prefill layer (T=4096, d=4096,
+expert hidden 14336, 8 experts, top-2, bf16). Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "routed tokens/sec per MoE layer fwd (bf16, 1 GPU) + % of MFMA/HBM roofline"
+CALLS = ("router", "permute", "ffn", "combine", "aux")
+# tokens whose expert FFN the CPU baseline evaluates (routing always covers all T)
+CPU_SAMPLE = {"tiny_fp32": 256, "mixtral_prefill": 256, "switch_top1_cap": 2048, "decode": 32,
+              "deepseek_v3": 64}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="mixtral_prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file with HBM bytes per dominant-kernel launch from counters")
+    return ap.parse_args()
+
+
+def cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(cfg, inp, sample_n):
+    """The oracle timed on this host: routing/permute/aux on all T tokens, expert FFN +
+    combine on a seeded token sample; the rate is extrapolated to the full batch."""
+    import moe_inputs as mi
+    from oracle import oracle as orc
+    x = mi.to_host_array(inp["x"])
+    wg = mi.to_host_array(inp["w_gate"])
+    gb = None if inp["gate_bias"] is None else inp["gate_bias"].cpu().numpy()
+    rng = np.random.default_rng(7)
+    toks = np.sort(rng.choice(cfg.T, size=min(sample_n, cfg.T), replace=False)).astype(np.int32)
+    host_w = {}
+
+    def fetch(e):  # host copies are made before the clock starts
+        return host_w[e]
+    # which experts the sample needs: route once untimed to know what to copy to the host
+    lg0 = orc.logits(x[toks], wg, gb)
+    need = set(orc.route(lg0, cfg.k, cfg.renorm)[0].ravel().tolist())
+    lg_all = orc.logits(x, wg, gb)
+    need |= set(orc.route(lg_all, cfg.k, cfg.renorm)[0][toks].ravel().tolist())
+    for e in sorted(need):
+        host_w[e] = tuple(None if inp[n] is None else mi.to_host_array(inp[n][e])
+                          for n in ("w1", "b1", "w2", "b2"))
+    t0 = time.perf_counter()
+    lg = orc.logits(x, wg, gb)
+    t1 = time.perf_counter()
+    idx, gate, ps = orc.route(lg, cfg.k, cfg.renorm)
+    counts, offsets, dest, st = orc.permute(idx, cfg.E, cfg.capacity)
+    orc.aux(ps, counts, cfg.T)
+    t2 = time.perf_counter()
+    # moe_forward re-runs route/permute/aux on all tokens, then FFN + combine on the sample
+    orc.moe_forward(x, wg, None, None, None, None, cfg.k, cfg.renorm, cfg.capacity, gate_bias=gb,
+                    residual=cfg.residual, lg=lg, tokens=toks, expert_weights=fetch)
+    t3 = time.perf_counter()
+    t_route = (t1 - t0) + (t2 - t1)
+    t_ffn = max((t3 - t2) - (t2 - t1), 1e-9)
+    full = t_route + t_ffn * cfg.T / toks.size
+    threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    return {"value": cfg.T / full, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"routing, permute and aux on all {cfg.T} tokens ({t_route:.2f} s); expert "
+                       f"FFN + combine on {toks.size} seeded tokens ({t_ffn:.2f} s), extrapolated "
+                       f"to {cfg.T}; double precision, {threads} threads on {cpu_model()}"),
+            "extrapolated": toks.size < cfg.T, "seconds": t3 - t0}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this layer forward runs on a single MI355X "
+              "(no expert or data parallelism across GPUs); run it with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import moe_inputs as mi
+    import top_routing_expert_topk_amd as moe
+    from top_routing_expert_topk_amd import native as N
+
+    cfg = mi.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = mi.make_inputs(cfg, dev)
+    torch.cuda.synchronize()
+    T, d, h, E, k = cfg.T, cfg.d, cfg.h, cfg.E, cfg.k
+    bufs = moe.MoEBuffers(T, d, h, E, k, cfg.torch_dtype, dev)
+    stream = torch.cuda.Stream(dev)  # default priority
+    x = inp["x"]
+    resid = x if cfg.residual else None
+
+    def step(ev=None):
+        b = bufs
+        if ev is not None:
+            ev[0].record(stream)
+        N.moe_router_topk(x, inp["w_gate"], inp["gate_bias"], E, k, cfg.renorm, None, b.topk_idx,
+                          b.topk_gate, b.prob_sum, b.ws_router, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        N.moe_permute(b.topk_idx, T, k, E, cfg.capacity, b.counts, b.offsets, b.dest_row,
+                      b.sorted_token, b.ws_permute, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        N.moe_grouped_ffn(x, T, d, h, E, k, b.offsets, b.sorted_token, inp["w1"], inp["b1"],
+                          inp["w2"], inp["b2"], b.y_perm, b.ws_ffn, stream)
+        if ev is not None:
+            ev[3].record(stream)
+        N.moe_combine(b.y_perm, b.dest_row, b.topk_gate, T, k, d, resid, b.out, stream)
+        if ev is not None:
+            ev[4].record(stream)
+        N.moe_aux_loss(b.prob_sum, b.counts, T, E, b.f, b.P, b.loss, stream)
+        if ev is not None:
+            ev[5].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call = {c: [] for c in CALLS}
+    step_ms = []
+    for ev in events:
+        for j, c in enumerate(CALLS):
+            per_call[c].append(ev[j].elapsed_time(ev[j + 1]))
+        step_ms.append(ev[0].elapsed_time(ev[5]))
+    ms = {c: float(np.mean(v)) for c, v in per_call.items()}
+    # whole timed region (gaps between steps included) over K steps
+    ms_step = events[0][0].elapsed_time(events[-1][5]) / args.steps
+
+    R = int(bufs.offsets[-1])
+    counts = bufs.counts.cpu().numpy()
+    touched = int((np.minimum(counts, cfg.capacity if cfg.capacity >= 0 else counts) > 0).sum())
+    ebytes = 2 if cfg.dtype == "bf16" else 4
+    ffn_flop = 4.0 * R * d * h
+    expert_bytes = touched * (2 * d * h + d + h) * ebytes
+    t_ffn = ms["ffn"] * 1e-3
+    mfma_bound = cfg.dtype == "bf16" and ffn_flop / max(expert_bytes, 1) > \
+        PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        traffic = json.load(open(args.traffic)).get(cfg.name)
+    if cfg.dtype != "bf16":
+        roof = {"bound": "alu", "achieved": ffn_flop / t_ffn / 1e12, "peak": PEAK_F32_TFLOPS,
+                "unit": "TFLOP/s"}
+    elif mfma_bound:
+        roof = {"bound": "mfma", "achieved": ffn_flop / t_ffn / 1e12, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": expert_bytes / t_ffn / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic
+    roof["kernel"] = "moe_grouped_ffn (expert GEMM1+SiLU and GEMM2, both grouped MFMA launches)"
+    roof["per_launch"] = {"flop": ffn_flop, "expert_weight_bytes": expert_bytes, "rows": R,
+                          "touched_experts": touched}
+
+    out = {
+        "metric": METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "T": T, "d": d, "h": h, "E": E, "k": k,
+                   "renorm": bool(cfg.renorm), "capacity": cfg.capacity,
+                   "residual": bool(cfg.residual), "parallelism": "single GPU"},
+        "roofline": roof,
+        "kept_rows_per_s": R / (ms_step * 1e-3),
+        "ms_per_call": ms,
+        "wall_ms_per_step": wall * 1e3 / args.steps,
+        "device": torch.cuda.get_device_name(dev),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, CPU_SAMPLE.get(cfg.name, 64))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

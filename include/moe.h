@@ -1,0 +1,162 @@
+/*
+ * moe.h -- C ABI of libmoe.so: the forward pass of one Mixture-of-Experts
+ * layer on one AMD Instinct MI355X (gfx950), in five calls.
+ *
+ * Sources for what each call computes:
+ *   [Routing page] "MoE混合专家模型路由机制原理与稀疏激活实现" (yunthe.com):
+ *     section "MoE混合专家模型架构与门控路由原理" -- gate equation
+ *       G(x) = softmax(TopK(x . W_g)) and output y = sum_i G(x)_i E_i(x);
+ *     section "Top-K门控路由的PyTorch实现" -- TopKRouter (bias-free linear
+ *       gate, softmax, top-k, renormalise), Expert (w2(silu(w1 x)) with
+ *       biases), MoELayer (slot-by-slot gate-weighted accumulation) and
+ *       load_balancing_loss (E * sum f * P);
+ *     section "Expert Choice路由策略与容量因子调优" -- capacity
+ *       = tokens / experts * factor; rejected tokens pass on the residual.
+ *   [Trilemma page] "MoE三难困境破解：按需加载+路由解耦+显存精控"
+ *     (0539edu.com), sections 3.2-3.3 -- the router returns (weights,
+ *     indices); the executor counts tokens per expert and runs one grouped
+ *     FFN per expert group.
+ *   [Guide page] "MoE 架构完整指南：路由、负载均衡、EP、训练稳定性、Serving"
+ *     (walkerchi.com), section 5.2 -- a per-expert router bias on the logits.
+ *
+ * Conventions shared by every call:
+ *   - Every pointer argument is a DEVICE pointer unless stated otherwise.
+ *     Tensors are dense, row-major, and 16-byte aligned.
+ *   - The caller owns every buffer, workspace included. The library never
+ *     allocates, frees or synchronises, and holds no state between calls.
+ *   - Each call enqueues its kernels on `stream` (a hipStream_t; NULL means
+ *     the null stream) and returns at once with a status code. Arguments are
+ *     validated on the host before anything is launched; on a non-zero status
+ *     nothing was enqueued, except for MOE_ERR_LAUNCH.
+ *   - dtype is MOE_F32 or MOE_BF16 and applies to x, the weights, the expert
+ *     biases, y_perm, residual and out. Logits, gates, probability sums, f, P
+ *     and the loss are always fp32; indices and offsets are int32.
+ *   - Inputs must be finite: NaN or Inf in x or the weights is outside the
+ *     contract.
+ *   - Results are deterministic: every sum has a fixed order and no kernel
+ *     uses floating-point atomics.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *moe_stream_t; /* a hipStream_t */
+
+enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID = 1,     /* bad pointer, size or flag */
+    MOE_ERR_UNSUPPORTED = 2, /* shape or dtype this build has no kernel for */
+    MOE_ERR_LAUNCH = 3,      /* the HIP runtime rejected a launch */
+    MOE_ERR_WORKSPACE = 4    /* ws_bytes smaller than moe_workspace_size() */
+};
+
+enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
+
+enum moe_op { MOE_OP_ROUTER = 0, MOE_OP_PERMUTE = 1, MOE_OP_FFN = 2 };
+
+/* Static text for a status code (host memory, never freed). */
+const char *moe_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int moe_version(void);
+
+/*
+ * Workspace bytes that call `op` needs for these sizes (dtype-independent
+ * upper bound; d, h unused by some ops). Returns 0 for a bad op or size.
+ */
+size_t moe_workspace_size(int op, int T, int d, int h, int E, int k);
+
+/*
+ * Router: logits, softmax, top-k selection and gates   [Routing page, gate
+ * equation and TopKRouter; Guide page 5.2 for gate_bias].
+ *   logits[t,e] = sum_i x[t,i] * w_gate[e,i] (+ gate_bias[e]), fp32 accumulate
+ *   topk_idx[t,j]: the k experts with the largest logits, in descending
+ *                  order; equal logits go to the lower expert index (+0 and -0
+ *                  compare equal)
+ *   p[t,e]       = softmax over all E logits of token t
+ *   topk_gate[t,j] = renorm ? p[t,idx_j] / sum_j' p[t,idx_j'] : p[t,idx_j]
+ *   prob_sum[e]  = sum_t p[t,e]   (feeds f of the aux loss)
+ * x [T][d] dtype; w_gate [E][d] dtype; gate_bias [E] fp32 or NULL;
+ * logits_out [T][E] fp32 or NULL; topk_idx [T][k] int32; topk_gate [T][k]
+ * fp32; prob_sum [E] fp32 or NULL. 1 <= k <= E <= 512, k <= 16, T >= 0.
+ * Workspace: moe_workspace_size(MOE_OP_ROUTER, ...).
+ */
+int moe_router_topk(const void *x, int dtype, int T, int d, const void *w_gate,
+                    const float *gate_bias, int E, int k, int renorm, float *logits_out,
+                    int32_t *topk_idx, float *topk_gate, float *prob_sum, void *ws,
+                    size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * Permute: per-expert counting sort with capacity   [Trilemma page 3.3
+ * (count tokens per expert, group them); Routing page capacity section].
+ * The T*k assignments are taken in flat order f = t*k + j.
+ *   counts[e]  = #{f : topk_idx[f] == e}   (before any drop)
+ *   kept[e]    = capacity < 0 ? counts[e] : min(counts[e], capacity)
+ *   offsets[e] = sum_{e'<e} kept[e'],  offsets[E] = R (rows kept)
+ *   dest_row[f] = offsets[e] + rank of f among expert e's assignments in
+ *                 ascending f, if that rank < kept[e]; otherwise -1 (dropped)
+ *   sorted_token[dest_row[f]] = f / k   (entries R..T*k-1 are not written)
+ * counts [E], offsets [E+1], dest_row [T*k], sorted_token [T*k]: int32.
+ * Indices outside [0, E) are outside the contract. E <= 512.
+ * Workspace: moe_workspace_size(MOE_OP_PERMUTE, ...).
+ */
+int moe_permute(const int32_t *topk_idx, int T, int k, int E, int capacity, int32_t *counts,
+                int32_t *offsets, int32_t *dest_row, int32_t *sorted_token, void *ws,
+                size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * Grouped expert FFN over the permuted rows   [Routing page, Expert;
+ * Trilemma page 3.3, one grouped FFN per expert]:
+ *   for each expert e and row r in [offsets[e], offsets[e+1]):
+ *     H[r]      = SiLU(W1[e] . x[sorted_token[r]] + b1[e]),  SiLU(z) = z/(1+e^-z)
+ *     y_perm[r] = W2[e] . H[r] + b2[e]
+ * x [T][d]; w1 [E][h][d]; b1 [E][h] or NULL; w2 [E][d][h]; b2 [E][d] or
+ * NULL; y_perm [T*k][d] (rows 0..R-1 written, R = offsets[E] read on the
+ * device). fp32 accumulation; with MOE_BF16, H and y_perm are rounded to
+ * bf16. offsets and sorted_token must come from moe_permute with the same
+ * T, k, E. The kernel choice depends only on T*k (no device-to-host read).
+ * bf16 needs d and h to be multiples of 64. Workspace holds H:
+ * moe_workspace_size(MOE_OP_FFN, ...).
+ */
+int moe_grouped_ffn(const void *x, int dtype, int T, int d, int h, int E, int k,
+                    const int32_t *offsets, const int32_t *sorted_token, const void *w1,
+                    const void *b1, const void *w2, const void *b2, void *y_perm, void *ws,
+                    size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * Combine: gate-weighted sum of each token's expert outputs   [Routing page,
+ * output equation and MoELayer accumulation; capacity section for the
+ * residual pass-through of dropped tokens]:
+ *   out[t] = (residual ? residual[t] : 0)
+ *            + sum_{j=0..k-1, dest_row[t,j] >= 0} topk_gate[t,j] * y_perm[dest_row[t,j]]
+ * summed in fp32 in ascending j, then stored as out_dtype. A token with every
+ * slot dropped gets residual[t] (or 0). y_perm [T*k][d] and residual [T][d]
+ * (or NULL) are `dtype`; dest_row [T][k]; topk_gate [T][k] fp32; out [T][d]
+ * is `out_dtype`: MOE_F32 (always allowed; keeps the fp32 sum unrounded) or
+ * MOE_BF16 (only with dtype MOE_BF16).
+ */
+int moe_combine(const void *y_perm, int dtype, const int32_t *dest_row, const float *topk_gate,
+                int T, int k, int d, const void *residual, void *out, int out_dtype,
+                moe_stream_t stream);
+
+/*
+ * Load-balancing auxiliary loss   [Routing page, load_balancing_loss]:
+ *   f[e] = prob_sum[e] / T,  P[e] = counts[e] / T,  loss = E * sum_e f[e]*P[e]
+ * counts are before capacity drops, so sum_e P[e] = k. prob_sum [E] fp32,
+ * counts [E] int32; f [E], P [E], loss [1] fp32 (any may be NULL except
+ * loss). T >= 1, E <= 512.
+ */
+int moe_aux_loss(const float *prob_sum, const int32_t *counts, int T, int E, float *f, float *P,
+                 float *loss, moe_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -70,16 +70,21 @@ void orc_silu(const double *z, int n, double *out) {
  */
 void orc_logits(const void *x, int xdt, int T, int d, const void *wg, int wdt,
                 const float *gate_bias, int E, double *logits) {
+    double *w = (double *)malloc(sizeof(double) * (size_t)E * d);
+    for (size_t i = 0; i < (size_t)E * d; ++i) w[i] = widen(wg, wdt, i);
 #pragma omp parallel for schedule(static)
     for (int t = 0; t < T; ++t) {
+        double *xr = (double *)malloc(sizeof(double) * (size_t)d);
+        for (int i = 0; i < d; ++i) xr[i] = widen(x, xdt, (size_t)t * d + i);
         for (int e = 0; e < E; ++e) {
             double s = 0.0;
-            for (int i = 0; i < d; ++i)
-                s += widen(x, xdt, (size_t)t * d + i) * widen(wg, wdt, (size_t)e * d + i);
+            for (int i = 0; i < d; ++i) s += xr[i] * w[(size_t)e * d + i];
             if (gate_bias) s += (double)gate_bias[e];
             logits[(size_t)t * E + e] = s;
         }
+        free(xr);
     }
+    free(w);
 }
 
 /*

@@ -1,0 +1,112 @@
+"""The C-ABI boundary on the host: the library loads, exports what the header
+declares, and rejects bad arguments with status codes before any launch.
+No call here reaches a kernel launch, so these run without a GPU."""
+import ctypes
+import subprocess
+
+import pytest
+
+from top_routing_expert_topk_amd import native as N
+
+BAD = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def test_library_exports_every_declared_symbol():
+    lib = N.lib()
+    declared = N.declared_functions()
+    assert {"moe_router_topk", "moe_permute", "moe_grouped_ffn", "moe_combine",
+            "moe_aux_loss", "moe_workspace_size", "moe_status_string", "moe_version"} <= set(declared)
+    for name in declared:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", N.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert set(declared) <= exported
+
+
+def test_status_strings_and_version():
+    assert N.status_string(0) == "ok"
+    assert "workspace" in N.status_string(4)
+    assert N.status_string(99) == "unknown status"
+    assert N.version() >= 100
+
+
+def test_workspace_sizes():
+    assert N.moe_workspace_size(N.MOE_OP_ROUTER, 4096, 4096, 14336, 8, 2) >= 128 * 8 * 4
+    assert N.moe_workspace_size(N.MOE_OP_PERMUTE, 8192, 7168, 2048, 256, 8) >= 2 * 256 * 64 * 4
+    ffn = N.moe_workspace_size(N.MOE_OP_FFN, 4096, 4096, 14336, 8, 2)
+    assert ffn >= 4096 * 2 * 14336 * 2
+    assert N.moe_workspace_size(7, 10, 10, 10, 4, 2) == 0
+    assert N.moe_workspace_size(N.MOE_OP_FFN, 10, 0, 10, 4, 2) == 0
+
+
+def _router(**kw):
+    a = dict(x=BAD, dtype=1, T=64, d=64, w=BAD, gb=None, E=8, k=2, renorm=1, lg=None, idx=BAD,
+             gate=BAD, ps=None, ws=BAD, wsb=1 << 20, s=None)
+    a.update(kw)
+    return N.lib().moe_router_topk(a["x"], a["dtype"], a["T"], a["d"], a["w"], a["gb"], a["E"],
+                                   a["k"], a["renorm"], a["lg"], a["idx"], a["gate"], a["ps"],
+                                   a["ws"], a["wsb"], a["s"])
+
+
+def test_router_rejects_bad_arguments():
+    assert _router(T=-1) == N.MOE_ERR_INVALID
+    assert _router(k=0) == N.MOE_ERR_INVALID
+    assert _router(k=9) == N.MOE_ERR_INVALID
+    assert _router(dtype=5) == N.MOE_ERR_INVALID
+    assert _router(renorm=2) == N.MOE_ERR_INVALID
+    assert _router(E=600, k=2) == N.MOE_ERR_UNSUPPORTED
+    assert _router(E=64, k=17) == N.MOE_ERR_UNSUPPORTED
+    assert _router(d=60) == N.MOE_ERR_UNSUPPORTED
+    assert _router(x=None) == N.MOE_ERR_INVALID
+    assert _router(idx=None) == N.MOE_ERR_INVALID
+    assert _router(wsb=16) == N.MOE_ERR_WORKSPACE
+    assert _router(ws=None) == N.MOE_ERR_WORKSPACE
+
+
+def test_permute_rejects_bad_arguments():
+    L = N.lib()
+    assert L.moe_permute(BAD, -1, 2, 8, -1, BAD, BAD, BAD, BAD, BAD, 1 << 20, None) == 1
+    assert L.moe_permute(BAD, 10, 9, 8, -1, BAD, BAD, BAD, BAD, BAD, 1 << 20, None) == 1
+    assert L.moe_permute(BAD, 10, 2, 513, -1, BAD, BAD, BAD, BAD, BAD, 1 << 20, None) == 2
+    assert L.moe_permute(BAD, 10, 2, 8, -1, None, BAD, BAD, BAD, BAD, 1 << 20, None) == 1
+    assert L.moe_permute(BAD, 10, 2, 8, -1, BAD, BAD, None, BAD, BAD, 1 << 20, None) == 1
+    assert L.moe_permute(BAD, 10, 2, 8, -1, BAD, BAD, BAD, BAD, BAD, 4, None) == 4
+
+
+def test_ffn_rejects_bad_arguments():
+    L = N.lib()
+
+    def ffn(dtype=1, T=10, d=128, h=256, E=8, k=2, wsb=1 << 30, w1=BAD, ws=BAD):
+        return L.moe_grouped_ffn(BAD, dtype, T, d, h, E, k, BAD, BAD, w1, None, BAD, None, BAD,
+                                 ws, wsb, None)
+    assert ffn(T=-1) == 1
+    assert ffn(dtype=3) == 1
+    assert ffn(k=9) == 1
+    assert ffn(d=100) == 2   # bf16 needs multiples of 64
+    assert ffn(h=96) == 2
+    assert ffn(E=1000, k=2) == 2
+    assert ffn(w1=None) == 1
+    assert ffn(wsb=100) == 4
+    assert ffn(ws=None) == 4
+
+
+def test_combine_and_aux_reject_bad_arguments():
+    L = N.lib()
+    assert L.moe_combine(BAD, 1, BAD, BAD, -1, 2, 64, None, BAD, 0, None) == 1
+    assert L.moe_combine(BAD, 2, BAD, BAD, 4, 2, 64, None, BAD, 0, None) == 1
+    assert L.moe_combine(BAD, 1, BAD, BAD, 4, 2, 64, None, BAD, 5, None) == 1
+    assert L.moe_combine(BAD, 0, BAD, BAD, 4, 2, 64, None, BAD, 1, None) == 2
+    assert L.moe_combine(BAD, 1, BAD, BAD, 4, 17, 64, None, BAD, 0, None) == 2
+    assert L.moe_combine(BAD, 1, BAD, BAD, 4, 2, 60, None, BAD, 0, None) == 2
+    assert L.moe_combine(None, 1, BAD, BAD, 4, 2, 64, None, BAD, 0, None) == 1
+    assert L.moe_aux_loss(BAD, BAD, 0, 8, None, None, BAD, None) == 1
+    assert L.moe_aux_loss(BAD, BAD, 4, 600, None, None, BAD, None) == 2
+    assert L.moe_aux_loss(BAD, BAD, 4, 8, None, None, None, None) == 1
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        N.moe_combine(x, x, x, 4, 1, 64, None, x)

@@ -1,0 +1,159 @@
+// Combine and aux loss.
+//
+// Combine: out[t] = residual[t] + sum_j gate[t,j] * y_perm[dest_row[t,j]], the
+// output equation y = sum_i G(x)_i E_i(x) of page "MoE混合专家模型路由机制原理与稀疏激活实现"
+// (section "门控路由原理") with the MoELayer's slot-by-slot accumulation
+// (section "Top-K门控路由的PyTorch实现"); dropped slots (dest_row = -1)
+// contribute nothing and the token keeps its residual (capacity section).
+// The "weighted scatter" is done as a per-token gather: each output element
+// is owned by one lane, which sums its k terms in fp32 in ascending j, so
+// the result is deterministic and needs no atomics.
+//
+// Aux loss: load_balancing_loss of the same page: f = mean probability per
+// expert, P = assignments per token per expert (before drops), loss = E *
+// sum f*P, summed in a fixed-order tree.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kCombineWaves = 4;  // tokens per block, one wave each
+
+template <typename OutT>
+__device__ __forceinline__ void store8(OutT* p, const float* v);
+template <>
+__device__ __forceinline__ void store8<uint16_t>(uint16_t* p, const float* v) {
+  u32x4 o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
+  *(u32x4*)p = o;
+}
+template <>
+__device__ __forceinline__ void store8<float>(float* p, const float* v) {
+  *(f32x4*)p = f32x4{v[0], v[1], v[2], v[3]};
+  *(f32x4*)(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+}
+
+template <typename OutT>
+__global__ __launch_bounds__(256) void combine_bf16(
+    const uint16_t* __restrict__ y, const int32_t* __restrict__ dest,
+    const float* __restrict__ gate, int T, int k, int d, const uint16_t* __restrict__ resid,
+    OutT* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kCombineWaves + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int dj[kMaxK];
+  float gj[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j < k) {
+      dj[j] = dest[(size_t)t * k + j];
+      gj[j] = gate[(size_t)t * k + j];
+    }
+  }
+  for (int c = lane * 8; c < d; c += 64 * 8) {
+    float acc[8];
+    if (resid) {
+      const u32x4 r = *(const u32x4*)(resid + (size_t)t * d + c);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] = bf16lo(r[q]);
+        acc[2 * q + 1] = bf16hi(r[q]);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j < k && dj[j] >= 0) {
+        const u32x4 v = *(const u32x4*)(y + (size_t)dj[j] * d + c);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] = fmaf(gj[j], bf16lo(v[q]), acc[2 * q]);
+          acc[2 * q + 1] = fmaf(gj[j], bf16hi(v[q]), acc[2 * q + 1]);
+        }
+      }
+    }
+    store8<OutT>(out + (size_t)t * d + c, acc);
+  }
+}
+
+__global__ __launch_bounds__(256) void combine_f32(
+    const float* __restrict__ y, const int32_t* __restrict__ dest, const float* __restrict__ gate,
+    int T, int k, int d, const float* __restrict__ resid, float* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kCombineWaves + (threadIdx.x >> 6);
+  if (t >= T) return;
+  for (int c = lane; c < d; c += 64) {
+    float acc = resid ? resid[(size_t)t * d + c] : 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const int r = dest[(size_t)t * k + j];
+      if (r >= 0) acc = fmaf(gate[(size_t)t * k + j], y[(size_t)r * d + c], acc);
+    }
+    out[(size_t)t * d + c] = acc;
+  }
+}
+
+__global__ __launch_bounds__(512) void aux_kernel(const float* __restrict__ prob_sum,
+                                                  const int32_t* __restrict__ counts, int T, int E,
+                                                  float* __restrict__ f, float* __restrict__ P,
+                                                  float* __restrict__ loss) {
+  __shared__ double s[512];
+  const int e = threadIdx.x;
+  double term = 0.0;
+  if (e < E) {
+    const double fe = (double)prob_sum[e] / (double)T;
+    const double pe = (double)counts[e] / (double)T;
+    if (f) f[e] = (float)fe;
+    if (P) P[e] = (float)pe;
+    term = fe * pe;
+  }
+  s[e] = term;
+  __syncthreads();
+  for (int w = 256; w >= 1; w >>= 1) {
+    if (e < w) s[e] += s[e + w];
+    __syncthreads();
+  }
+  if (e == 0) *loss = (float)((double)E * s[0]);
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int moe_combine(const void* y_perm, int dtype, const int32_t* dest_row,
+                           const float* topk_gate, int T, int k, int d, const void* residual,
+                           void* out, int out_dtype, moe_stream_t stream) {
+  if (T < 0 || k < 1 || d < 1) return MOE_ERR_INVALID;
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_INVALID;
+  if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return MOE_ERR_INVALID;
+  if (dtype == MOE_F32 && out_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
+  if (k > kMaxK) return MOE_ERR_UNSUPPORTED;
+  if (dtype == MOE_BF16 && (d % 8) != 0) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!y_perm || !dest_row || !topk_gate || !out) return MOE_ERR_INVALID;
+  hipStream_t s = (hipStream_t)stream;
+  const int nb = ceil_div(T, kCombineWaves);
+  if (dtype == MOE_BF16 && out_dtype == MOE_BF16)
+    hipLaunchKernelGGL(combine_bf16<uint16_t>, dim3(nb), dim3(256), 0, s, (const uint16_t*)y_perm,
+                       dest_row, topk_gate, T, k, d, (const uint16_t*)residual, (uint16_t*)out);
+  else if (dtype == MOE_BF16)
+    hipLaunchKernelGGL(combine_bf16<float>, dim3(nb), dim3(256), 0, s, (const uint16_t*)y_perm,
+                       dest_row, topk_gate, T, k, d, (const uint16_t*)residual, (float*)out);
+  else
+    hipLaunchKernelGGL(combine_f32, dim3(nb), dim3(256), 0, s, (const float*)y_perm, dest_row,
+                       topk_gate, T, k, d, (const float*)residual, (float*)out);
+  return launch_status();
+}
+
+extern "C" int moe_aux_loss(const float* prob_sum, const int32_t* counts, int T, int E, float* f,
+                            float* P, float* loss, moe_stream_t stream) {
+  if (T < 1 || E < 1) return MOE_ERR_INVALID;
+  if (E > kMaxE) return MOE_ERR_UNSUPPORTED;
+  if (!prob_sum || !counts || !loss) return MOE_ERR_INVALID;
+  hipLaunchKernelGGL(aux_kernel, dim3(1), dim3(512), 0, (hipStream_t)stream, prob_sum, counts, T,
+                     E, f, P, loss);
+  return launch_status();
+}

@@ -1,0 +1,442 @@
+// Grouped expert FFN: for each expert e, over its rows of the permutation,
+//   H = SiLU(W1[e] . x[sorted_token] + b1[e]),   Y = W2[e] . H + b2[e]
+// (the Expert module of page "MoE混合专家模型路由机制原理与稀疏激活实现", section
+// "Top-K门控路由的PyTorch实现"; one grouped kernel per layer of the FFN
+// rather than a loop over experts, as section 3.3 of
+// "MoE三难困境破解：按需加载+路由解耦+显存精控" asks of its _grouped_ffn).
+//
+// Kernels:
+//   build_tile_map  prefix sum of ceil(kept_e / BM) -> tile_start[E+1], so a
+//                   GEMM block finds its (expert, row block) with no host read
+//   gemm_bf16       MFMA grouped GEMM, LDS double-buffered 64-deep K steps;
+//                   the gather of x rows is fused into the B-tile load and
+//                   bias (+SiLU) into the epilogue
+//   decode_bf16     weight-streaming path for few rows per expert: each
+//                   touched expert's weights are read once per 4 rows, rows
+//                   of untouched experts cost one offsets read
+//   gemm_f32        FMA tiles for fp32 layers
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int KC = 64;  // bf16 K elements per LDS stage (128 bytes per row)
+
+// ---------------------------------------------------------------- tile map --
+__global__ __launch_bounds__(512) void build_tile_map(const int32_t* __restrict__ offsets, int E,
+                                                      int BM, int32_t* __restrict__ tile_start) {
+  __shared__ int sc[2][kMaxE];
+  const int e = threadIdx.x;
+  int v = 0;
+  if (e < E) v = (offsets[e + 1] - offsets[e] + BM - 1) / BM;
+  int cur = 0;
+  sc[0][e] = v;
+  __syncthreads();
+  for (int off = 1; off < kMaxE; off <<= 1) {
+    const int s = sc[cur][e] + (e >= off ? sc[cur][e - off] : 0);
+    sc[cur ^ 1][e] = s;
+    cur ^= 1;
+    __syncthreads();
+  }
+  if (e < E) tile_start[e + 1] = sc[cur][e];
+  if (e == 0) tile_start[0] = 0;
+}
+
+// Expert e with tile_start[e] <= ms < tile_start[e+1] (ms < tile_start[E]).
+__device__ __forceinline__ int find_expert(const int32_t* __restrict__ tile_start, int E, int ms) {
+  int lo = 0, hi = E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (tile_start[mid] <= ms) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// ------------------------------------------------------------- MFMA GEMM --
+// Block tile: BN weight rows (output features) x BM permuted rows. Four waves
+// in a 2 x 2 grid, each (BN/2) x (BM/2) of 16x16 MFMA tiles.
+// v_mfma_f32_16x16x32_bf16 operands: A = weight rows (16 n x 32 k), B =
+// activation rows (32 k x 16 rows); lane l gives row (l%16), k-octet (l/16)
+// and receives D[n = 4*(l/16)+v][row = l%16], i.e. 4 consecutive output
+// features of one row -> one 8-byte store.
+// LDS rows are 64 bf16 (8 chunks of 16 B); chunk c of row r sits at c^(r&7)
+// so the 16 lanes reading 16 rows at one chunk spread over all banks.
+template <int BN, int BM, bool GATHER, bool SILU>
+__global__ __launch_bounds__(256) void gemm_bf16(
+    const uint16_t* __restrict__ act, const int32_t* __restrict__ sorted_token,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_start,
+    const uint16_t* __restrict__ w, const uint16_t* __restrict__ bias,
+    uint16_t* __restrict__ out, int E, int N, int K, int mslots) {
+  constexpr int TN = BN / 32, TM = BM / 32;  // 16-wide tiles per wave
+  constexpr int AL = BN * 8 / 256, BL = BM * 8 / 256;  // 16-byte chunks per thread
+  __shared__ __align__(16) uint16_t sA[2][BN * KC];
+  __shared__ __align__(16) uint16_t sB[2][BM * KC];
+
+  const int ms = blockIdx.x % mslots, nt = blockIdx.x / mslots;
+  const int total = tile_start[E];
+  if (ms >= total) return;
+  const int e = find_expert(tile_start, E, ms);
+  const int row0 = offsets[e] + (ms - tile_start[e]) * BM;
+  const int rows = min(BM, offsets[e + 1] - row0);
+  const int n0 = nt * BN;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wn = wave >> 1, wm = wave & 1;
+
+  const uint16_t* asrc[AL];
+  const uint16_t* bsrc[BL];
+  int aoff[AL], boff[BL];
+#pragma unroll
+  for (int i = 0; i < AL; ++i) {
+    const int c = tid + 256 * i, r = c >> 3, ch = c & 7;
+    asrc[i] = w + ((size_t)e * N + n0 + r) * K + ch * 8;
+    aoff[i] = r * KC + ((ch ^ (r & 7)) * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < BL; ++i) {
+    const int c = tid + 256 * i, r = c >> 3, ch = c & 7;
+    const int rr = row0 + (r < rows ? r : rows - 1);
+    const size_t src = GATHER ? (size_t)sorted_token[rr] : (size_t)rr;
+    bsrc[i] = act + src * K + ch * 8;
+    boff[i] = r * KC + ((ch ^ (r & 7)) * 8);
+  }
+
+  f32x4 acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 ra[AL], rb[BL];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < AL; ++i) ra[i] = *(const u32x4*)(asrc[i] + k0);
+#pragma unroll
+    for (int i = 0; i < BL; ++i) rb[i] = *(const u32x4*)(bsrc[i] + k0);
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < AL; ++i) *(u32x4*)(&sA[buf][aoff[i]]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < BL; ++i) *(u32x4*)(&sB[buf][boff[i]]) = rb[i];
+  };
+
+  const int nk = K / KC;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * KC);
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const int ch = kh * 4 + (lane >> 4);
+      bf16x8 a[TN], b[TM];
+#pragma unroll
+      for (int i = 0; i < TN; ++i) {
+        const int r = wn * (BN / 2) + i * 16 + (lane & 15);
+        a[i] = *(const bf16x8*)(&sA[cur][r * KC + ((ch ^ (r & 7)) * 8)]);
+      }
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        const int r = wm * (BM / 2) + j * 16 + (lane & 15);
+        b[j] = *(const bf16x8*)(&sB[cur][r * KC + ((ch ^ (r & 7)) * 8)]);
+      }
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < TN; ++i) {
+    const int n = n0 + wn * (BN / 2) + i * 16 + 4 * (lane >> 4);
+    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (bias) {
+      const u32x2 bb = *(const u32x2*)(bias + (size_t)e * N + n);
+      bv[0] = bf16lo(bb[0]);
+      bv[1] = bf16hi(bb[0]);
+      bv[2] = bf16lo(bb[1]);
+      bv[3] = bf16hi(bb[1]);
+    }
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      const int m = wm * (BM / 2) + j * 16 + (lane & 15);
+      if (m < rows) {
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[q] = acc[i][j][q] + bv[q];
+          if (SILU) v[q] = silu(v[q]);
+        }
+        u32x2 o;
+        o[0] = pack_bf16x2(v[0], v[1]);
+        o[1] = pack_bf16x2(v[2], v[3]);
+        *(u32x2*)(out + (size_t)(row0 + m) * N + n) = o;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------ decode streaming --
+// Grid (ceil(N / 16), E). Each wave owns 4 consecutive output features and
+// computes them for up to G rows of expert e at a time; the rows' activations
+// sit in LDS, the weights stream straight from HBM with 16-byte loads (8
+// loads per row in flight per lane for K = 4096), and each dot product ends
+// in a wave butterfly sum.
+constexpr int DG = 4;    // rows per pass
+constexpr int DRPW = 4;  // output features per wave
+constexpr int DRPB = 4 * DRPW;
+
+__device__ __forceinline__ float dot8(const u32x4 a, const u32x4 b) {
+  float s = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    s = fmaf(bf16lo(a[q]), bf16lo(b[q]), s);
+    s = fmaf(bf16hi(a[q]), bf16hi(b[q]), s);
+  }
+  return s;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+template <bool GATHER, bool SILU>
+__global__ __launch_bounds__(256) void decode_bf16(
+    const uint16_t* __restrict__ act, const int32_t* __restrict__ sorted_token,
+    const int32_t* __restrict__ offsets, const uint16_t* __restrict__ w,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int E, int N, int K) {
+  extern __shared__ __align__(16) uint16_t sx[];  // [DG][K]
+  const int e = blockIdx.y;
+  const int r0 = offsets[e];
+  const int cnt = offsets[e + 1] - r0;
+  if (cnt <= 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nw = blockIdx.x * DRPB + wave * DRPW;
+  const int kchunks = K / 8;
+
+  for (int g0 = 0; g0 < cnt; g0 += DG) {
+    const int ng = min(DG, cnt - g0);
+    for (int c = tid; c < ng * kchunks; c += 256) {
+      const int g = c / kchunks, kc = c - g * kchunks;
+      const int rr = r0 + g0 + g;
+      const size_t src = GATHER ? (size_t)sorted_token[rr] : (size_t)rr;
+      *(u32x4*)(sx + g * K + kc * 8) = *(const u32x4*)(act + src * K + kc * 8);
+    }
+    __syncthreads();
+    for (int rp = 0; rp < DRPW; rp += 2) {
+      const int n = nw + rp;
+      float acc[2][DG];
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int g = 0; g < DG; ++g) acc[a][g] = 0.0f;
+      const uint16_t* w0 = w + ((size_t)e * N + (n < N ? n : N - 1)) * K;
+      const uint16_t* w1 = w + ((size_t)e * N + (n + 1 < N ? n + 1 : N - 1)) * K;
+      for (int kb = 0; kb < K; kb += 8 * 512) {
+        u32x4 wa[8], wb[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int kk = kb + u * 512 + lane * 8;
+          if (kk < K) {
+            wa[u] = *(const u32x4*)(w0 + kk);
+            wb[u] = *(const u32x4*)(w1 + kk);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int kk = kb + u * 512 + lane * 8;
+          if (kk < K) {
+#pragma unroll
+            for (int g = 0; g < DG; ++g) {
+              if (g < ng) {
+                const u32x4 xv = *(const u32x4*)(sx + g * K + kk);
+                acc[0][g] += dot8(wa[u], xv);
+                acc[1][g] += dot8(wb[u], xv);
+              }
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const int na = n + a;
+        const float b = (bias && na < N) ? bf16_to_f32(bias[(size_t)e * N + na]) : 0.0f;
+#pragma unroll
+        for (int g = 0; g < DG; ++g) {
+          if (g < ng) {
+            float v = wave_sum(acc[a][g]) + b;
+            if (SILU) v = silu(v);
+            if (lane == 0 && na < N) out[(size_t)(r0 + g0 + g) * N + na] = (uint16_t)f32_to_bf16(v);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- fp32 ----
+constexpr int FB = 64;   // tile edge
+constexpr int FKC = 16;  // K step
+
+template <bool GATHER, bool SILU>
+__global__ __launch_bounds__(256) void gemm_f32(
+    const float* __restrict__ act, const int32_t* __restrict__ sorted_token,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_start,
+    const float* __restrict__ w, const float* __restrict__ bias, float* __restrict__ out, int E,
+    int N, int K, int mslots) {
+  __shared__ float sW[FKC][FB + 4];
+  __shared__ float sX[FKC][FB + 4];
+  const int ms = blockIdx.x % mslots, nt = blockIdx.x / mslots;
+  const int total = tile_start[E];
+  if (ms >= total) return;
+  const int e = find_expert(tile_start, E, ms);
+  const int row0 = offsets[e] + (ms - tile_start[e]) * FB;
+  const int rows = min(FB, offsets[e + 1] - row0);
+  const int n0 = nt * FB;
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+
+  size_t xsrc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (tid + 256 * i) / FKC;
+    const int rr = row0 + (r < rows ? r : rows - 1);
+    xsrc[i] = GATHER ? (size_t)sorted_token[rr] : (size_t)rr;
+  }
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+
+  for (int k0 = 0; k0 < K; k0 += FKC) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i, r = c / FKC, kk = c % FKC;
+      const int n = n0 + r, kg = k0 + kk;
+      sW[kk][r] = (n < N && kg < K) ? w[((size_t)e * N + n) * K + kg] : 0.0f;
+      sX[kk][r] = (r < rows && kg < K) ? act[xsrc[i] * K + kg] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < FKC; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = sW[kk][tx * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = sX[kk][ty * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = n0 + tx * 4 + i;
+    if (n >= N) continue;
+    const float b = bias ? bias[(size_t)e * N + n] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = ty * 4 + j;
+      if (m < rows) {
+        float v = acc[i][j] + b;
+        if (SILU) v = silu(v);
+        out[(size_t)(row0 + m) * N + n] = v;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ dispatch ----
+constexpr int kBM = 128;
+
+template <int BN>
+int launch_gemms_bf16(const uint16_t* x, const int32_t* sorted_token, const int32_t* offsets,
+                      const int32_t* tile_start, const uint16_t* w1, const uint16_t* b1,
+                      const uint16_t* w2, const uint16_t* b2, uint16_t* H, uint16_t* y, int E,
+                      int d, int h, int mslots, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_bf16<BN, kBM, true, true>), dim3(mslots * (h / BN)), dim3(256), 0, s, x,
+                     sorted_token, offsets, tile_start, w1, b1, H, E, h, d, mslots);
+  hipLaunchKernelGGL((gemm_bf16<BN, kBM, false, false>), dim3(mslots * (d / BN)), dim3(256), 0, s,
+                     H, sorted_token, offsets, tile_start, w2, b2, y, E, d, h, mslots);
+  return launch_status();
+}
+
+bool use_decode(long rows, int E) { return rows <= 4L * E && rows <= 1024; }
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int moe_grouped_ffn(const void* x, int dtype, int T, int d, int h, int E, int k,
+                               const int32_t* offsets, const int32_t* sorted_token, const void* w1,
+                               const void* b1, const void* w2, const void* b2, void* y_perm,
+                               void* ws, size_t ws_bytes, moe_stream_t stream) {
+  if (T < 0 || d < 1 || h < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID;
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_INVALID;
+  if (E > kMaxE) return MOE_ERR_UNSUPPORTED;
+  const long rows = (long)T * k;
+  if (rows > 0x7FFFFFFFL) return MOE_ERR_UNSUPPORTED;
+  if (dtype == MOE_BF16 && ((d % 64) != 0 || (h % 64) != 0)) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!x || !offsets || !sorted_token || !w1 || !w2 || !y_perm) return MOE_ERR_INVALID;
+  if (!ws || ws_bytes < ffn_ws(T, h, E, k)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* tile_start = (int32_t*)ws;
+  void* H = (unsigned char*)ws + ffn_tilemap_bytes(E);
+  const int nonempty = (int)(rows < E ? rows : E);
+
+  if (dtype == MOE_F32) {
+    const int mslots = ceil_div(rows, FB) + nonempty;
+    hipLaunchKernelGGL(build_tile_map, dim3(1), dim3(512), 0, s, offsets, E, FB, tile_start);
+    hipLaunchKernelGGL((gemm_f32<true, true>), dim3(mslots * ceil_div(h, FB)), dim3(256), 0, s,
+                       (const float*)x, sorted_token, offsets, tile_start, (const float*)w1,
+                       (const float*)b1, (float*)H, E, h, d, mslots);
+    hipLaunchKernelGGL((gemm_f32<false, false>), dim3(mslots * ceil_div(d, FB)), dim3(256), 0, s,
+                       (const float*)H, sorted_token, offsets, tile_start, (const float*)w2,
+                       (const float*)b2, (float*)y_perm, E, d, h, mslots);
+    return launch_status();
+  }
+
+  const uint16_t* xb = (const uint16_t*)x;
+  if (use_decode(rows, E)) {
+    const size_t lds1 = (size_t)DG * d * 2, lds2 = (size_t)DG * h * 2;
+    if (lds1 > 160 * 1024 || lds2 > 160 * 1024) return MOE_ERR_UNSUPPORTED;
+    if (lds1 > 65536 &&
+        hipFuncSetAttribute((const void*)decode_bf16<true, true>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1) != hipSuccess)
+      return MOE_ERR_LAUNCH;
+    if (lds2 > 65536 &&
+        hipFuncSetAttribute((const void*)decode_bf16<false, false>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2) != hipSuccess)
+      return MOE_ERR_LAUNCH;
+    hipLaunchKernelGGL((decode_bf16<true, true>), dim3(ceil_div(h, DRPB), E), dim3(256), lds1, s,
+                       xb, sorted_token, offsets, (const uint16_t*)w1, (const uint16_t*)b1,
+                       (uint16_t*)H, E, h, d);
+    hipLaunchKernelGGL((decode_bf16<false, false>), dim3(ceil_div(d, DRPB), E), dim3(256), lds2, s,
+                       (const uint16_t*)H, sorted_token, offsets, (const uint16_t*)w2,
+                       (const uint16_t*)b2, (uint16_t*)y_perm, E, d, h);
+    return launch_status();
+  }
+
+  const int mslots = ceil_div(rows, kBM) + nonempty;
+  hipLaunchKernelGGL(build_tile_map, dim3(1), dim3(512), 0, s, offsets, E, kBM, tile_start);
+  if ((d % 128) == 0 && (h % 128) == 0)
+    return launch_gemms_bf16<128>(xb, sorted_token, offsets, tile_start, (const uint16_t*)w1,
+                                  (const uint16_t*)b1, (const uint16_t*)w2, (const uint16_t*)b2,
+                                  (uint16_t*)H, (uint16_t*)y_perm, E, d, h, mslots, s);
+  return launch_gemms_bf16<64>(xb, sorted_token, offsets, tile_start, (const uint16_t*)w1,
+                               (const uint16_t*)b1, (const uint16_t*)w2, (const uint16_t*)b2,
+                               (uint16_t*)H, (uint16_t*)y_perm, E, d, h, mslots, s);
+}

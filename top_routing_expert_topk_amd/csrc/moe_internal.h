@@ -1,0 +1,73 @@
+// Internal helpers shared by the libmoe.so translation units (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// ---- limits of this build --------------------------------------------------
+constexpr int kMaxE = 512;  // experts per layer
+constexpr int kMaxK = 16;   // top-k
+
+// ---- vector types ----------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));  // MFMA bf16 operand
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+// Low and high bf16 of a packed pair.
+__device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+// fp32 -> bf16, round to nearest even (inputs are finite by contract).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  return (1ull << __lane_id()) - 1ull;
+}
+
+// ---- host helpers ----------------------------------------------------------
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+
+inline int launch_status() {
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+// Workspace layouts; each op's size function is the single source of truth
+// for both moe_workspace_size() and the call that consumes the workspace.
+constexpr int kRouterTokens = 32;  // tokens per router block
+constexpr int kPermuteChunk = 1024;  // assignments per permute block
+
+inline int router_blocks(int T) { return ceil_div(T, kRouterTokens); }
+inline size_t router_ws(int T, int E) {
+  return align_up((size_t)router_blocks(T) * E * sizeof(float), 256);
+}
+inline int permute_blocks(long n) { return n > 0 ? ceil_div(n, kPermuteChunk) : 0; }
+inline size_t permute_ws(int T, int k, int E) {
+  long n = (long)T * k;
+  return align_up((size_t)2 * E * permute_blocks(n) * sizeof(int32_t), 256);
+}
+// FFN: [tile map: 2*(E+1) int32][hidden H: T*k*h elements of 4 bytes max]
+inline size_t ffn_tilemap_bytes(int E) { return align_up((size_t)2 * (E + 1) * sizeof(int32_t), 256); }
+inline size_t ffn_ws(int T, int h, int E, int k) {
+  return ffn_tilemap_bytes(E) + align_up((size_t)T * k * h * 4, 256);
+}
+
+}  // namespace moe

@@ -57,6 +57,11 @@ SMALL = {
                                                    renorm=False),
     "no_bias": CFG["deepseek_v3"].with_(name="no_bias", T=100, d=256, h=128, E=32, k=4,
                                         expert_bias=False),
+    # 256-row MFMA tiles: every tile is a tail tile split along K
+    "big_tail_only": CFG["mixtral_prefill"].with_(name="big_tail_only", T=1024, d=512, h=1024,
+                                                   E=4),
+    # 256-row MFMA tiles: whole rounds of tiles plus a split tail
+    "big_full_tail": CFG["mixtral_prefill"].with_(name="big_full_tail", T=4096, d=512, h=2048),
 }
 
 

@@ -182,6 +182,319 @@ __global__ __launch_bounds__(256) void gemm_bf16(
   }
 }
 
+// --------------------------------------------- MFMA GEMM, 256-row tiles --
+// For experts with a few hundred rows or more. Block tile 256 weight rows x
+// 256 permuted rows, four waves in a 2 x 2 grid, each 128 x 128 as 4 x 4
+// v_mfma_f32_32x32x16_bf16 tiles (256 accumulator floats per lane, in AGPRs).
+//
+// Data path: direct global->LDS DMA (16 bytes per lane, no VGPR round trip)
+// into a ring of kStages slots of 32 K-columns; up to two slots are in flight
+// while one is consumed. LDS rows are 64 bytes (4 chunks of 16 B); chunk c of
+// row r sits at slot c ^ ((r >> 1) & 3), so 8 lanes reading 8 rows at one
+// chunk hit 8 distinct 16-byte bank groups. One DMA instruction fills 1 KB =
+// 16 rows, lane l writing slot l%4 of row l/4, so lane l fetches chunk
+// (l%4) ^ swizzle(row).
+//
+// Each 32-column slot is consumed in two k16 sub-steps; the fragment reads of
+// one sub-step overlap the 16 MFMAs of the other, and the ring barrier (which
+// both publishes slot kt+1 and retires slot kt-1 for refilling) sits between
+// the two sub-steps, so it never waits on an empty MFMA pipe. The barrier is
+// an s_barrier with a compiler memory clobber: it keeps LDS accesses on their
+// side without draining the DMA queue, which a workgroup fence would do.
+//
+// v_mfma_f32_32x32x16_bf16: lane l supplies row l%32 and k-octet l/32 of each
+// operand (A = 32 weight rows x 16 k, B = 16 k x 32 permuted rows) and
+// receives D[n = 8*(v/4) + 4*(l/32) + v%4][row = l%32], v = 0..15, i.e. four
+// runs of 4 consecutive output features of one row -> 8-byte stores.
+//
+// Tile order: expert-major; inside an expert, groups of 8 weight-row tiles,
+// inside a group the expert's row blocks. Consecutive logical tiles then
+// share a weight panel (across row blocks) or a row panel (across the group),
+// and the hardware block id is remapped so each XCD (blocks are dealt to the
+// 8 XCDs round-robin) walks one contiguous range of that order through its L2.
+constexpr int kBigBM = 256;
+constexpr int kBigBN = 256;
+constexpr int kKS = 32;
+constexpr int kStages = 4;
+constexpr int kMaxSplit = 8;  // K-ranges per tail tile
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Workgroup barrier that the compiler may not move memory accesses across.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// One 16-byte direct global->LDS load per lane; the LDS address is the
+// wave-uniform base plus 16 * lane.
+__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ int swz64(int r, int c) { return c ^ ((r >> 1) & 3); }
+
+// Largest e with tile_start[e] * ntiles <= L.
+__device__ __forceinline__ int find_expert_scaled(const int32_t* __restrict__ tile_start, int E,
+                                                  int L, int ntiles) {
+  int lo = 0, hi = E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (tile_start[mid] * ntiles <= L) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Tile t of the expert-major order -> (expert, first row, rows, first output feature).
+struct BigTile {
+  int e, row0, rows, n0;
+};
+__device__ __forceinline__ BigTile big_tile(const int32_t* __restrict__ tile_start,
+                                            const int32_t* __restrict__ offsets, int E,
+                                            int ntiles, int t) {
+  BigTile r;
+  r.e = find_expert_scaled(tile_start, E, t, ntiles);
+  const int mt = tile_start[r.e + 1] - tile_start[r.e];
+  const int l = t - tile_start[r.e] * ntiles;
+  const int g = l / (mt * 8);
+  const int gs = min(8, ntiles - g * 8);
+  const int l2 = l - g * mt * 8;
+  const int mi = l2 / gs, nt = g * 8 + l2 % gs;
+  r.row0 = offsets[r.e] + mi * kBigBM;
+  r.rows = min(kBigBM, offsets[r.e + 1] - r.row0);
+  r.n0 = nt * kBigBN;
+  return r;
+}
+
+// Work split: the first `full` tiles (a whole number of rounds over the
+// kTailSlots-block machine) run whole; the remaining `tail` tiles are each
+// cut into `split` K-ranges so that the last round fills every CU.
+struct BigSplit {
+  int tiles, full, tail, split;
+};
+__device__ __forceinline__ BigSplit big_split(const int32_t* __restrict__ tile_start, int E,
+                                              int ntiles, int nk) {
+  BigSplit s;
+  s.tiles = tile_start[E] * ntiles;
+  s.tail = s.tiles % kTailSlots;
+  s.full = s.tiles - s.tail;
+  s.split = 1;
+  if (s.tail > 0) {
+    s.split = kTailSlots / s.tail;
+    if (s.split > kMaxSplit) s.split = kMaxSplit;
+    if (s.split > nk) s.split = nk;
+    if (s.split < 1) s.split = 1;
+  }
+  return s;
+}
+
+template <bool GATHER, bool SILU>
+__global__ __launch_bounds__(256) void gemm_bf16_big(
+    const uint16_t* __restrict__ act, const int32_t* __restrict__ sorted_token,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_start,
+    const uint16_t* __restrict__ w, const uint16_t* __restrict__ bias,
+    uint16_t* __restrict__ out, float* __restrict__ part, int E, int N, int K, int ntiles) {
+  constexpr int BN = kBigBN, BM = kBigBM;
+  constexpr int TN = 4, TM = 4;              // 32-row MFMA tiles per wave
+  constexpr int AI = BN / 64, BI = BM / 64;  // DMA instructions per thread per slot
+  constexpr int SA = BN * kKS, SB = BM * kKS;
+  constexpr int PER_SLOT = AI + BI;
+  __shared__ __align__(1024) uint16_t lds[kStages][SA + SB];
+
+  // Live tiles are known only on the device. Whole tiles are dealt to the XCDs
+  // in contiguous ranges (full is a multiple of 8); tail units follow.
+  const int nk_all = K / kKS;
+  const BigSplit sp = big_split(tile_start, E, ntiles, nk_all);
+  const int b = blockIdx.x;
+  int t, p = 0, split = 1;
+  if (b < sp.full) {
+    const int per = sp.full >> 3;
+    t = (b & 7) * per + (b >> 3);
+  } else {
+    const int u = b - sp.full;
+    if (u >= sp.tail * sp.split) return;
+    split = sp.split;
+    t = sp.full + u / split;
+    p = u % split;
+  }
+  const BigTile tile = big_tile(tile_start, offsets, E, ntiles, t);
+  const int e = tile.e, row0 = tile.row0, rows = tile.rows, n0 = tile.n0;
+  const int kbeg = p * nk_all / split, kend = (p + 1) * nk_all / split;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wn = wave >> 1, wm = wave & 1;
+
+  const uint16_t* aptr[AI];
+  const uint16_t* bptr[BI];
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    const int r = (i * 4 + wave) * 16 + (lane >> 2);
+    aptr[i] = w + ((size_t)e * N + n0 + r) * K + swz64(r, lane & 3) * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < BI; ++i) {
+    const int r = (i * 4 + wave) * 16 + (lane >> 2);
+    const int rr = row0 + (r < rows ? r : rows - 1);
+    const size_t src = GATHER ? (size_t)sorted_token[rr] : (size_t)rr;
+    bptr[i] = act + src * K + swz64(r, lane & 3) * 8;
+  }
+
+  auto issue = [&](int st, int kt) {
+    const int koff = (kbeg + kt) * kKS;
+#pragma unroll
+    for (int i = 0; i < AI; ++i) dma16(aptr[i] + koff, &lds[st][(i * 4 + wave) * 16 * kKS]);
+#pragma unroll
+    for (int i = 0; i < BI; ++i) dma16(bptr[i] + koff, &lds[st][SA + (i * 4 + wave) * 16 * kKS]);
+  };
+
+  f32x16 acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) acc[i][j] = f32x16{};
+
+  const int nk = kend - kbeg;
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s)
+    if (s < nk) issue(s, s);
+
+  const int ch = lane >> 5;
+  bf16x8 f0a[TN], f0b[TM], f1a[TN], f1b[TM];
+#define MOE_RD(st, sub, FA, FB)                                                         \
+  do {                                                                                  \
+    const uint16_t* sa_ = &lds[st][0];                                                  \
+    const uint16_t* sb_ = sa_ + SA;                                                     \
+    _Pragma("unroll") for (int i = 0; i < TN; ++i) {                                    \
+      const int r = wn * 128 + i * 32 + (lane & 31);                                    \
+      FA[i] = *(const bf16x8*)(sa_ + r * kKS + swz64(r, 2 * (sub) + ch) * 8);           \
+    }                                                                                   \
+    _Pragma("unroll") for (int j = 0; j < TM; ++j) {                                    \
+      const int r = wm * 128 + j * 32 + (lane & 31);                                    \
+      FB[j] = *(const bf16x8*)(sb_ + r * kKS + swz64(r, 2 * (sub) + ch) * 8);           \
+    }                                                                                   \
+  } while (0)
+#define MOE_MM(FA, FB)                                                                  \
+  do {                                                                                  \
+    _Pragma("unroll") for (int i = 0; i < TN; ++i)                                      \
+    _Pragma("unroll") for (int j = 0; j < TM; ++j)                                      \
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[i], FB[j], acc[i][j], 0, 0, 0); \
+  } while (0)
+
+  if (nk > kStages - 2) wait_vmcnt<(kStages - 2) * PER_SLOT>(); else wait_vmcnt<0>();
+  lds_barrier();
+  MOE_RD(0, 0, f0a, f0b);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt % kStages;
+    MOE_RD(st, 1, f1a, f1b);
+    MOE_MM(f0a, f0b);
+    if (kt + 1 < nk) {
+      // slot kt+1 must have landed; slot kt-1 (refilled below) was last read
+      // by MFMAs this wave has already issued
+      if (kt + kStages - 1 < nk) wait_vmcnt<(kStages - 3) * PER_SLOT>(); else wait_vmcnt<0>();
+      lds_barrier();
+      if (kt + kStages - 1 < nk) issue((kt + kStages - 1) % kStages, kt + kStages - 1);
+      MOE_RD((kt + 1) % kStages, 0, f0a, f0b);
+    }
+    MOE_MM(f1a, f1b);
+  }
+#undef MOE_RD
+#undef MOE_MM
+
+  if (split > 1) {
+    // fp32 partial of a tail tile: [256 rows][256 features], summed by big_tail_reduce
+    float* pp = part + ((size_t)(t - sp.full) * split + p) * (BM * BN);
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int nl = wn * 128 + i * 32 + 8 * q + 4 * ch;
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+          const int m = wm * 128 + j * 32 + (lane & 31);
+          *(f32x4*)(pp + m * BN + nl) =
+              f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        }
+      }
+    return;
+  }
+
+#pragma unroll
+  for (int i = 0; i < TN; ++i) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int n = n0 + wn * 128 + i * 32 + 8 * q + 4 * ch;
+      float bv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (bias) {
+        const u32x2 bb = *(const u32x2*)(bias + (size_t)e * N + n);
+        bv[0] = bf16lo(bb[0]);
+        bv[1] = bf16hi(bb[0]);
+        bv[2] = bf16lo(bb[1]);
+        bv[3] = bf16hi(bb[1]);
+      }
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        const int m = wm * 128 + j * 32 + (lane & 31);
+        if (m < rows) {
+          float v[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            v[u] = acc[i][j][4 * q + u] + bv[u];
+            if (SILU) v[u] = silu(v[u]);
+          }
+          u32x2 o;
+          o[0] = pack_bf16x2(v[0], v[1]);
+          o[1] = pack_bf16x2(v[2], v[3]);
+          *(u32x2*)(out + (size_t)(row0 + m) * N + n) = o;
+        }
+      }
+    }
+  }
+}
+
+// Tail tiles: out = act(sum_p partial[p] + bias), partials summed in order of
+// their K-range, so the result does not depend on timing. One block per tail
+// tile; each thread owns 8 consecutive features of 32 rows.
+template <bool SILU>
+__global__ __launch_bounds__(256) void big_tail_reduce(
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_start,
+    const uint16_t* __restrict__ bias, const float* __restrict__ part, uint16_t* __restrict__ out,
+    int E, int N, int K, int ntiles) {
+  const BigSplit sp = big_split(tile_start, E, ntiles, K / kKS);
+  if ((int)blockIdx.x >= sp.tail || sp.split < 2) return;
+  const int t = sp.full + blockIdx.x;
+  const BigTile tile = big_tile(tile_start, offsets, E, ntiles, t);
+  const int nl = (threadIdx.x & 31) * 8;
+  float bv[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+    bv[u] = bias ? bf16_to_f32(bias[(size_t)tile.e * N + tile.n0 + nl + u]) : 0.0f;
+  const float* base = part + (size_t)blockIdx.x * sp.split * (kBigBM * kBigBN);
+  for (int m = threadIdx.x >> 5; m < tile.rows; m += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = 0.0f;
+    for (int p = 0; p < sp.split; ++p) {
+      const float* src = base + (size_t)p * (kBigBM * kBigBN) + m * kBigBN + nl;
+      const f32x4 lo = *(const f32x4*)src, hi = *(const f32x4*)(src + 4);
+      v[0] += lo[0]; v[1] += lo[1]; v[2] += lo[2]; v[3] += lo[3];
+      v[4] += hi[0]; v[5] += hi[1]; v[6] += hi[2]; v[7] += hi[3];
+    }
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float a = v[2 * q] + bv[2 * q], c = v[2 * q + 1] + bv[2 * q + 1];
+      if (SILU) {
+        a = silu(a);
+        c = silu(c);
+      }
+      o[q] = pack_bf16x2(a, c);
+    }
+    *(u32x4*)(out + (size_t)(tile.row0 + m) * N + tile.n0 + nl) = o;
+  }
+}
+
 // ------------------------------------------------------ decode streaming --
 // Grid (ceil(N / 16), E). Each wave owns 4 consecutive output features and
 // computes them for up to G rows of expert e at a time; the rows' activations
@@ -374,6 +687,13 @@ int launch_gemms_bf16(const uint16_t* x, const int32_t* sorted_token, const int3
 
 bool use_decode(long rows, int E) { return rows <= 4L * E && rows <= 1024; }
 
+// 256-row tiles when experts average at least 192 rows and both widths tile by 256.
+bool use_big(long rows, int E, int T, int k, int d, int h) {
+  (void)T;
+  (void)k;
+  return rows >= 192L * E && (d % kBigBN) == 0 && (h % kBigBN) == 0;
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -430,6 +750,26 @@ extern "C" int moe_grouped_ffn(const void* x, int dtype, int T, int d, int h, in
     return launch_status();
   }
 
+  if (use_big(rows, E, T, k, d, h)) {
+    const int mslots = ceil_div(rows, kBigBM) + nonempty;
+    float* part = (float*)((unsigned char*)H + ffn_hidden_bytes(T, h, k));
+    hipLaunchKernelGGL(build_tile_map, dim3(1), dim3(512), 0, s, offsets, E, kBigBM, tile_start);
+    const int nt1 = h / kBigBN, nt2 = d / kBigBN;
+    // blocks: every tile once, plus at most kTailSlots tail units
+    const int g1 = ceil_div((long)mslots * nt1 + kTailSlots, 8) * 8;
+    const int g2 = ceil_div((long)mslots * nt2 + kTailSlots, 8) * 8;
+    hipLaunchKernelGGL((gemm_bf16_big<true, true>), dim3(g1), dim3(256), 0, s, xb, sorted_token,
+                       offsets, tile_start, (const uint16_t*)w1, (const uint16_t*)b1, (uint16_t*)H,
+                       part, E, h, d, nt1);
+    hipLaunchKernelGGL((big_tail_reduce<true>), dim3(kTailSlots), dim3(256), 0, s, offsets,
+                       tile_start, (const uint16_t*)b1, part, (uint16_t*)H, E, h, d, nt1);
+    hipLaunchKernelGGL((gemm_bf16_big<false, false>), dim3(g2), dim3(256), 0, s,
+                       (const uint16_t*)H, sorted_token, offsets, tile_start, (const uint16_t*)w2,
+                       (const uint16_t*)b2, (uint16_t*)y_perm, part, E, d, h, nt2);
+    hipLaunchKernelGGL((big_tail_reduce<false>), dim3(kTailSlots), dim3(256), 0, s, offsets,
+                       tile_start, (const uint16_t*)b2, part, (uint16_t*)y_perm, E, d, h, nt2);
+    return launch_status();
+  }
   const int mslots = ceil_div(rows, kBM) + nonempty;
   hipLaunchKernelGGL(build_tile_map, dim3(1), dim3(512), 0, s, offsets, E, kBM, tile_start);
   if ((d % 128) == 0 && (h % 128) == 0)

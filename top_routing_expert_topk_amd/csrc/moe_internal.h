@@ -65,9 +65,13 @@ inline size_t permute_ws(int T, int k, int E) {
   return align_up((size_t)2 * E * permute_blocks(n) * sizeof(int32_t), 256);
 }
 // FFN: [tile map: 2*(E+1) int32][hidden H: T*k*h elements of 4 bytes max]
+//      [tail partials: kTailSlots tiles of 256 x 256 fp32]
+constexpr int kTailSlots = 256;
 inline size_t ffn_tilemap_bytes(int E) { return align_up((size_t)2 * (E + 1) * sizeof(int32_t), 256); }
+inline size_t ffn_hidden_bytes(int T, int h, int k) { return align_up((size_t)T * k * h * 4, 256); }
+inline size_t ffn_partial_bytes() { return (size_t)kTailSlots * 256 * 256 * sizeof(float); }
 inline size_t ffn_ws(int T, int h, int E, int k) {
-  return ffn_tilemap_bytes(E) + align_up((size_t)T * k * h * 4, 256);
+  return ffn_tilemap_bytes(E) + ffn_hidden_bytes(T, h, k) + ffn_partial_bytes();
 }
 
 }  // namespace moe

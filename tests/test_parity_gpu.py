@@ -166,3 +166,11 @@ def test_bf16_output_within_rounding_bound():
     got = b.out.float().cpu().numpy().astype(np.float64)
     rms = float(np.sqrt(np.mean(ref ** 2)))
     assert np.all(np.abs(got - ref) <= 2e-2 * rms + 2.0 ** -8 * np.abs(ref))
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (100, 3), (130, 1), (200, 4), (300, 2), (400, 6),
+                                 (450, 2), (512, 8)])
+def test_router_expert_counts(E, k):
+    """Every expert-tile shape of the bf16 router (E padded to 64, 128, ..., 512)."""
+    cfg = CFG["deepseek_v3"].with_(T=300, d=320, h=64, E=E, k=k)
+    _run_and_check(cfg, label=f"router_E{E}_k{k}")

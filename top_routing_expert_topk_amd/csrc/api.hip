@@ -19,7 +19,7 @@ extern "C" int moe_version(void) { return 100; }
 extern "C" size_t moe_workspace_size(int op, int T, int d, int h, int E, int k) {
   if (T < 0 || E < 1 || k < 1) return 0;
   switch (op) {
-    case MOE_OP_ROUTER: return router_ws(T, E);
+    case MOE_OP_ROUTER: return d < 1 ? 0 : router_ws(T, d, E);
     case MOE_OP_PERMUTE: return permute_ws(T, k, E);
     case MOE_OP_FFN: return (h < 1 || d < 1) ? 0 : ffn_ws(T, h, E, k);
     default: return 0;

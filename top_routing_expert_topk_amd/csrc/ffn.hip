@@ -217,6 +217,7 @@ constexpr int kBigBN = 256;
 constexpr int kKS = 32;
 constexpr int kStages = 4;
 constexpr int kMaxSplit = 8;  // K-ranges per tail tile
+constexpr int kReduceSlices = 8;  // row slices per tail tile in the reduction
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -454,24 +455,27 @@ __global__ __launch_bounds__(256) void gemm_bf16_big(
 }
 
 // Tail tiles: out = act(sum_p partial[p] + bias), partials summed in order of
-// their K-range, so the result does not depend on timing. One block per tail
-// tile; each thread owns 8 consecutive features of 32 rows.
+// their K-range, so the result does not depend on timing. kReduceSlices
+// blocks per tail tile, each over 32 rows; a thread owns 8 consecutive
+// features of 4 rows.
 template <bool SILU>
 __global__ __launch_bounds__(256) void big_tail_reduce(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_start,
     const uint16_t* __restrict__ bias, const float* __restrict__ part, uint16_t* __restrict__ out,
     int E, int N, int K, int ntiles) {
   const BigSplit sp = big_split(tile_start, E, ntiles, K / kKS);
-  if ((int)blockIdx.x >= sp.tail || sp.split < 2) return;
-  const int t = sp.full + blockIdx.x;
+  const int tt = blockIdx.x / kReduceSlices, slice = blockIdx.x % kReduceSlices;
+  if (tt >= sp.tail || sp.split < 2) return;
+  const int t = sp.full + tt;
   const BigTile tile = big_tile(tile_start, offsets, E, ntiles, t);
   const int nl = (threadIdx.x & 31) * 8;
   float bv[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u)
     bv[u] = bias ? bf16_to_f32(bias[(size_t)tile.e * N + tile.n0 + nl + u]) : 0.0f;
-  const float* base = part + (size_t)blockIdx.x * sp.split * (kBigBM * kBigBN);
-  for (int m = threadIdx.x >> 5; m < tile.rows; m += 8) {
+  const float* base = part + (size_t)tt * sp.split * (kBigBM * kBigBN);
+  const int mend = min(tile.rows, (slice + 1) * (kBigBM / kReduceSlices));
+  for (int m = slice * (kBigBM / kReduceSlices) + (threadIdx.x >> 5); m < mend; m += 8) {
     float v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) v[u] = 0.0f;
@@ -761,12 +765,14 @@ extern "C" int moe_grouped_ffn(const void* x, int dtype, int T, int d, int h, in
     hipLaunchKernelGGL((gemm_bf16_big<true, true>), dim3(g1), dim3(256), 0, s, xb, sorted_token,
                        offsets, tile_start, (const uint16_t*)w1, (const uint16_t*)b1, (uint16_t*)H,
                        part, E, h, d, nt1);
-    hipLaunchKernelGGL((big_tail_reduce<true>), dim3(kTailSlots), dim3(256), 0, s, offsets,
+    hipLaunchKernelGGL((big_tail_reduce<true>), dim3(kTailSlots * kReduceSlices), dim3(256), 0, s,
+                       offsets,
                        tile_start, (const uint16_t*)b1, part, (uint16_t*)H, E, h, d, nt1);
     hipLaunchKernelGGL((gemm_bf16_big<false, false>), dim3(g2), dim3(256), 0, s,
                        (const uint16_t*)H, sorted_token, offsets, tile_start, (const uint16_t*)w2,
                        (const uint16_t*)b2, (uint16_t*)y_perm, part, E, d, h, nt2);
-    hipLaunchKernelGGL((big_tail_reduce<false>), dim3(kTailSlots), dim3(256), 0, s, offsets,
+    hipLaunchKernelGGL((big_tail_reduce<false>), dim3(kTailSlots * kReduceSlices), dim3(256), 0, s,
+                       offsets,
                        tile_start, (const uint16_t*)b2, part, (uint16_t*)y_perm, E, d, h, nt2);
     return launch_status();
   }

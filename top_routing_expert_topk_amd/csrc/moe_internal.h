@@ -52,12 +52,35 @@ inline int launch_status() {
 
 // Workspace layouts; each op's size function is the single source of truth
 // for both moe_workspace_size() and the call that consumes the workspace.
-constexpr int kRouterTokens = 32;  // tokens per router block
+constexpr int kRouterTokens = 4;  // tokens per selection block (one per wave)
 constexpr int kPermuteChunk = 1024;  // assignments per permute block
 
+// bf16 router logits: blocks of tt tokens x ep (E padded to 64) experts, each
+// over one of `split` ranges of the 32-wide K chunks; fp32 partial logits
+// [split][T][E] are summed in order by the selection kernel.
+struct RouterPlan {
+  int ep, tt, ntt, nch, split;
+};
+inline RouterPlan router_plan(int T, int d, int E) {
+  RouterPlan p;
+  p.ep = (E + 63) / 64 * 64;
+  int tt = 32768 / p.ep / 64 * 64;
+  if (tt > 256) tt = 256;
+  p.tt = tt;  // 256, 128 or 64 for E <= 512
+  p.ntt = ceil_div(T > 0 ? T : 1, tt);
+  p.nch = ceil_div(d, 32);
+  int s = 512 / p.ntt;
+  if (s > p.nch) s = p.nch;
+  if (s < 1) s = 1;
+  p.split = s;
+  return p;
+}
 inline int router_blocks(int T) { return ceil_div(T, kRouterTokens); }
-inline size_t router_ws(int T, int E) {
-  return align_up((size_t)router_blocks(T) * E * sizeof(float), 256);
+inline size_t router_partial_bytes(int T, int d, int E) {
+  return align_up((size_t)router_plan(T, d, E).split * T * E * sizeof(float), 256);
+}
+inline size_t router_ws(int T, int d, int E) {
+  return router_partial_bytes(T, d, E) + align_up((size_t)router_blocks(T) * E * sizeof(float), 256);
 }
 inline int permute_blocks(long n) { return n > 0 ? ceil_div(n, kPermuteChunk) : 0; }
 inline size_t permute_ws(int T, int k, int E) {

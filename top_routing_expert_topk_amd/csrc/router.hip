@@ -1,6 +1,5 @@
-// Router: skinny GEMM x . W_g^T on bf16 MFMA (or fp32 FMA), fused with the
-// full softmax, a wavefront top-k with lowest-index tie-break, the gates and
-// per-block probability partial sums.
+// Router: logits x . W_g^T (+ router bias), full softmax, a wavefront top-k
+// with lowest-index tie-break, gates and per-block probability partial sums.
 //
 // What it computes: the gate equation G(x) = softmax(TopK(x . W_g)) and the
 // TopKRouter of page "MoE混合专家模型路由机制原理与稀疏激活实现" (sections
@@ -9,15 +8,26 @@
 // optional per-expert router bias of "MoE 架构完整指南" section 5.2.
 // The selection is made on the fp32 logits (the same order as selecting on
 // the probabilities) so that no tie is created by rounding in exp.
+//
+// bf16 layers run two kernels:
+//   router_logits_bf16  a skinny MFMA GEMM split over (token tile, K range)
+//                       blocks so that even a handful of tokens (decode) or
+//                       a long K (d = 7168) spreads over every CU; operands
+//                       reach LDS by direct global->LDS DMA, double-buffered;
+//                       each block writes fp32 partial logits [split][T][E].
+//   router_select       one wave per token: partial logits summed in split
+//                       order (+ bias), then softmax / top-k / gates.
+// fp32 layers (small) use one fused kernel with FMA dot products.
+// router_reduce sums the per-block probability partials in a fixed order.
 #include "moe_internal.h"
 
 namespace moe {
-
 namespace {
 
-constexpr int RT = kRouterTokens;  // tokens per block
-constexpr int KC = 64;             // bf16 elements of K staged per step
+constexpr int RT = kRouterTokens;  // tokens per selection block
 constexpr int kWaves = 4;
+constexpr int RT32 = 32;  // tokens per fp32 fused block (a multiple of RT)
+constexpr int RKS = 32;  // K columns per LDS stage (64-byte rows)
 
 // Total order for selection: larger value first, then lower expert index.
 // +0 and -0 map to the same key.
@@ -44,184 +54,68 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   return v;
 }
 
-// LDS byte layout of one block: [GEMM staging | logits tile] (aliased) then
-// the per-wave probability partials.
-__host__ __device__ inline int pad16(int E) { return (E + 15) & ~15; }
-__host__ __device__ inline size_t stage_bytes(int E) { return (size_t)(RT + pad16(E)) * KC * 2; }
-__host__ __device__ inline size_t logit_bytes(int E) { return (size_t)RT * pad16(E) * 4; }
-__host__ __device__ inline size_t union_bytes(int E) {
-  size_t a = stage_bytes(E), b = logit_bytes(E);
-  return a > b ? a : b;
-}
-__host__ __device__ inline size_t router_lds(int E) {
-  return union_bytes(E) + (size_t)kWaves * E * 4;
-}
-
-// Logits of the block's RT tokens into lg[RT][Ep] (bias added), bf16 MFMA.
-// v_mfma_f32_16x16x32_bf16: A = 16 tokens x 32 k, B = 32 k x 16 experts;
-// lane l supplies row (l%16) and k-octet (l/16) of each operand and receives
-// D[4*(l/16)+v][l%16], v = 0..3.
-__device__ void logits_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
-                            const float* __restrict__ gbias, int T, int d, int E, int t0,
-                            unsigned char* smem, float* lg) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int Ep = pad16(E);
-  const int NT = Ep / 16;
-  const int P = 2 * NT;  // (token tile, expert tile) pairs
-  uint16_t* sX = (uint16_t*)smem;
-  uint16_t* sW = sX + RT * KC;
-  f32x4 acc[16];
+// One token, one wave. Lane l holds v[i] = logit of expert l + 64 i (i < 8).
+// Writes the k selected experts (descending, lower index first on ties) and
+// their gates, and adds this token's softmax probabilities to pacc.
+__device__ __forceinline__ void select_token(const float (&v)[8], int E, int k, int renorm,
+                                             int lane, int32_t* __restrict__ idx_row,
+                                             float* __restrict__ gate_row, float (&pacc)[8]) {
+  const int EPL = (E + 63) >> 6;
+  uint32_t taken = 0;
+  float selv[kMaxK];
+  int sele[kMaxK];
 #pragma unroll
-  for (int q = 0; q < 16; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int k0 = 0; k0 < d; k0 += KC) {
-    {  // x tile: RT rows x 8 chunks of 16 B, one chunk per thread
-      int row = tid >> 3, ch = tid & 7;
-      int t = t0 + row, kk = k0 + ch * 8;
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (t < T && kk < d) v = *(const u32x4*)(x + (size_t)t * d + kk);
-      *(u32x4*)(sX + row * KC + ((ch ^ (row & 7)) * 8)) = v;
-    }
-    for (int c = tid; c < Ep * 8; c += 256) {
-      int row = c >> 3, ch = c & 7;
-      int kk = k0 + ch * 8;
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (row < E && kk < d) v = *(const u32x4*)(w + (size_t)row * d + kk);
-      *(u32x4*)(sW + row * KC + ((ch ^ (row & 7)) * 8)) = v;
-    }
-    __syncthreads();
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j < k) {
+      uint64_t best = 0;
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      const int ch = kh * 4 + (lane >> 4);
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int p = wave + kWaves * q;
-        if (p < P) {
-          const int mt = p / NT, nt = p % NT;
-          const int ra = mt * 16 + (lane & 15), rb = nt * 16 + (lane & 15);
-          bf16x8 a = *(const bf16x8*)(sX + ra * KC + ((ch ^ (ra & 7)) * 8));
-          bf16x8 b = *(const bf16x8*)(sW + rb * KC + ((ch ^ (rb & 7)) * 8));
-          acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[q], 0, 0, 0);
+      for (int i = 0; i < 8; ++i) {
+        const int e = lane + 64 * i;
+        if (i < EPL && e < E && !((taken >> i) & 1u)) {
+          const uint64_t key =
+              ((uint64_t)ordered_bits(v[i]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+          best = key > best ? key : best;
         }
       }
-    }
-    __syncthreads();
-  }
-  // staging is dead now; lg aliases it
-#pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const int p = wave + kWaves * q;
-    if (p < P) {
-      const int mt = p / NT, nt = p % NT;
-      const int e = nt * 16 + (lane & 15);
-      const float b = (gbias && e < E) ? gbias[e] : 0.0f;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int tl = mt * 16 + 4 * (lane >> 4) + v;
-        lg[tl * Ep + e] = acc[q][v] + b;
-      }
+      best = wave_max_u64(best);
+      const int ej = (int)(0xFFFFFFFFu - (uint32_t)best);
+      if ((ej & 63) == lane) taken |= 1u << (ej >> 6);
+      sele[j] = ej;
+      selv[j] = from_ordered_bits((uint32_t)(best >> 32));
     }
   }
-}
-
-// fp32 logits by plain FMA dot products (the small fp32 workloads).
-__device__ void logits_f32(const float* __restrict__ x, const float* __restrict__ w,
-                           const float* __restrict__ gbias, int T, int d, int E, int t0,
-                           float* lg) {
-  const int Ep = pad16(E);
-  for (int pi = threadIdx.x; pi < RT * E; pi += 256) {
-    const int tl = pi / E, e = pi % E, t = t0 + tl;
-    float s = 0.0f;
-    if (t < T) {
-      const float* xr = x + (size_t)t * d;
-      const float* wr = w + (size_t)e * d;
-      for (int i = 0; i < d; ++i) s = fmaf(xr[i], wr[i], s);
-    }
-    lg[tl * Ep + e] = s + (gbias ? gbias[e] : 0.0f);
+  const float m = selv[0];
+  float ex[8], zl = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int e = lane + 64 * i;
+    ex[i] = (i < EPL && e < E) ? expf(v[i] - m) : 0.0f;
+    zl += ex[i];
   }
-}
-
-template <bool BF16>
-__global__ __launch_bounds__(256) void router_kernel(
-    const void* __restrict__ x, const void* __restrict__ w, const float* __restrict__ gbias,
-    int T, int d, int E, int k, int renorm, float* __restrict__ logits_out,
-    int32_t* __restrict__ idx_out, float* __restrict__ gate_out, float* __restrict__ partial) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  const int t0 = blockIdx.x * RT;
-  const int Ep = pad16(E);
-  float* lg = (float*)smem;
-  float* part = (float*)(smem + union_bytes(E));  // [kWaves][E]
-
-  if (BF16)
-    logits_bf16((const uint16_t*)x, (const uint16_t*)w, gbias, T, d, E, t0, smem, lg);
-  else
-    logits_f32((const float*)x, (const float*)w, gbias, T, d, E, t0, lg);
-  __syncthreads();
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int EPL = (E + 63) >> 6;  // experts per lane (<= 8)
-  float pacc[8];
+  const float z = wave_sum_f32(zl);
+  float zs = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) pacc[i] = 0.0f;
-
-  for (int tl = wave; tl < RT; tl += kWaves) {
-    const int t = t0 + tl;
-    if (t >= T) break;
-    float v[8], ex[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int e = lane + 64 * i;
-      v[i] = (i < EPL && e < E) ? lg[tl * Ep + e] : 0.0f;
-      if (logits_out && i < EPL && e < E) logits_out[(size_t)t * E + e] = v[i];
-    }
-    uint32_t taken = 0;
-    float selv[kMaxK];
-    int sele[kMaxK];
+  for (int j = 0; j < kMaxK; ++j)
+    if (j < k) zs += expf(selv[j] - m);
+  const float denom = renorm ? zs : z;
+  if (lane == 0) {
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) {
       if (j < k) {
-        uint64_t best = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int e = lane + 64 * i;
-          if (i < EPL && e < E && !((taken >> i) & 1u)) {
-            uint64_t key = ((uint64_t)ordered_bits(v[i]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
-            best = key > best ? key : best;
-          }
-        }
-        best = wave_max_u64(best);
-        const int ej = (int)(0xFFFFFFFFu - (uint32_t)best);
-        if ((ej & 63) == lane) taken |= 1u << (ej >> 6);
-        sele[j] = ej;
-        selv[j] = from_ordered_bits((uint32_t)(best >> 32));
+        idx_row[j] = sele[j];
+        gate_row[j] = expf(selv[j] - m) / denom;
       }
     }
-    const float m = selv[0];
-    float zl = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int e = lane + 64 * i;
-      ex[i] = (i < EPL && e < E) ? expf(v[i] - m) : 0.0f;
-      zl += ex[i];
-    }
-    const float z = wave_sum_f32(zl);
-    float zs = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j)
-      if (j < k) zs += expf(selv[j] - m);
-    const float denom = renorm ? zs : z;
-    if (lane == 0) {
-#pragma unroll
-      for (int j = 0; j < kMaxK; ++j) {
-        if (j < k) {
-          idx_out[(size_t)t * k + j] = sele[j];
-          gate_out[(size_t)t * k + j] = expf(selv[j] - m) / denom;
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) pacc[i] += ex[i] / z;
   }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) pacc[i] += ex[i] / z;
+}
+
+// Per-block probability partials: the four waves' sums added in wave order.
+__device__ __forceinline__ void write_prob_partial(const float (&pacc)[8], int E, float* part,
+                                                   float* __restrict__ out) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int EPL = (E + 63) >> 6;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int e = lane + 64 * i;
@@ -229,16 +123,192 @@ __global__ __launch_bounds__(256) void router_kernel(
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += 256)
-    partial[(size_t)blockIdx.x * E + e] = ((part[e] + part[E + e]) + part[2 * E + e]) + part[3 * E + e];
+    out[(size_t)blockIdx.x * E + e] =
+        ((part[e] + part[E + e]) + part[2 * E + e]) + part[3 * E + e];
 }
 
-// prob_sum[e] = sum over blocks of partial[b][e]: fixed-order tree in double.
-__global__ __launch_bounds__(256) void router_reduce(const float* __restrict__ partial, int nb,
+// ---------------------------------------------------- bf16 partial logits --
+__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+__device__ __forceinline__ int rswz(int r, int c) { return c ^ ((r >> 1) & 3); }
+
+// Block: TT tokens (64 * MTW) x EP experts (16 * NTE) over the 32-wide K
+// chunks [c0, c1) of its split. LDS stage = TT token rows then EP expert rows,
+// 64 bytes each, chunk c of row r at slot c ^ ((r >> 1) & 3); each DMA
+// instruction fills 16 rows, lane l writing slot l%4 of row l/4. Wave w owns
+// token tiles w, w+4, ... and every expert tile, so a token fragment is read
+// once per chunk and reused across all expert tiles.
+// v_mfma_f32_16x16x32_bf16: A = 16 tokens x 32 k, B = 32 k x 16 experts; lane
+// l supplies row l%16, k-octet l/16 and receives D[4*(l/16)+v][l%16].
+template <int MTW, int NTE>
+__global__ __launch_bounds__(256) void router_logits_bf16(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int T, int d, int E, int nch,
+    int split, float* __restrict__ part) {
+  constexpr int TT = 64 * MTW, EP = 16 * NTE;
+  constexpr int ROWS = TT + EP;
+  constexpr int STAGE = ROWS * RKS;
+  constexpr int NI = ROWS / 16;  // DMA instructions per stage (multiple of 4)
+  extern __shared__ __align__(1024) uint16_t rs[];
+  const int tile = blockIdx.x / split, p = blockIdx.x % split;
+  const int t0 = tile * TT;
+  const int c0 = p * nch / split, c1 = (p + 1) * nch / split;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+  const uint16_t* src[NI / 4];
+#pragma unroll
+  for (int q = 0; q < NI / 4; ++q) {
+    const int r = (q * 4 + wave) * 16 + (lane >> 2);
+    const uint16_t* base;
+    if (r < TT) {
+      const int t = min(t0 + r, T - 1);
+      base = x + (size_t)t * d;
+    } else {
+      const int e = min(r - TT, E - 1);
+      base = w + (size_t)e * d;
+    }
+    src[q] = base + rswz(r, lane & 3) * 8;
+  }
+  auto issue = [&](int buf, int c) {
+#pragma unroll
+    for (int q = 0; q < NI / 4; ++q)
+      dma16(src[q] + c * RKS, &rs[buf * STAGE + (q * 4 + wave) * 16 * RKS]);
+  };
+
+  f32x4 acc[MTW][NTE];
+#pragma unroll
+  for (int j = 0; j < MTW; ++j)
+#pragma unroll
+    for (int n = 0; n < NTE; ++n) acc[j][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int ch = lane >> 4;
+  if (c0 < c1) issue(0, c0);
+  for (int c = c0; c < c1; ++c) {
+    const int buf = (c - c0) & 1;
+    // this wave's DMA of chunk c has landed; after the barrier every wave's
+    // has, and every wave is done reading the other buffer
+    wait_vmcnt0();
+    lds_barrier();
+    if (c + 1 < c1) issue(buf ^ 1, c + 1);
+    const uint16_t* sx = rs + buf * STAGE;
+    const uint16_t* sw = sx + TT * RKS;
+    bf16x8 a[MTW];
+#pragma unroll
+    for (int j = 0; j < MTW; ++j) {
+      const int r = (wave + 4 * j) * 16 + (lane & 15);
+      a[j] = *(const bf16x8*)(sx + r * RKS + rswz(r, ch) * 8);
+    }
+#pragma unroll
+    for (int n = 0; n < NTE; ++n) {
+      const int r = n * 16 + (lane & 15);
+      const bf16x8 b = *(const bf16x8*)(sw + r * RKS + rswz(r, ch) * 8);
+#pragma unroll
+      for (int j = 0; j < MTW; ++j)
+        acc[j][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], b, acc[j][n], 0, 0, 0);
+    }
+  }
+  float* pp = part + (size_t)p * T * E;
+#pragma unroll
+  for (int j = 0; j < MTW; ++j)
+#pragma unroll
+    for (int n = 0; n < NTE; ++n) {
+      const int e = n * 16 + (lane & 15);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int t = t0 + (wave + 4 * j) * 16 + 4 * (lane >> 4) + v;
+        if (t < T && e < E) pp[(size_t)t * E + e] = acc[j][n][v];
+      }
+    }
+}
+
+__global__ __launch_bounds__(256) void router_select(
+    const float* __restrict__ part, int split, const float* __restrict__ gbias, int T, int E,
+    int k, int renorm, float* __restrict__ logits_out, int32_t* __restrict__ idx_out,
+    float* __restrict__ gate_out, float* __restrict__ probpart) {
+  __shared__ float wpart[kWaves * kMaxE];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int EPL = (E + 63) >> 6;
+  float pacc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) pacc[i] = 0.0f;
+  const int t = blockIdx.x * RT + wave;
+  if (t < T) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = lane + 64 * i;
+      float s = 0.0f;
+      if (i < EPL && e < E) {
+        // partials in split order; loads issued 8 at a time
+        const float* src = part + (size_t)t * E + e;
+        const size_t stride = (size_t)T * E;
+        int p = 0;
+        for (; p + 8 <= split; p += 8) {
+          float q[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) q[u] = src[(size_t)(p + u) * stride];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) s += q[u];
+        }
+        for (; p < split; ++p) s += src[(size_t)p * stride];
+        if (gbias) s += gbias[e];
+        if (logits_out) logits_out[(size_t)t * E + e] = s;
+      }
+      v[i] = s;
+    }
+    select_token(v, E, k, renorm, lane, idx_out + (size_t)t * k, gate_out + (size_t)t * k, pacc);
+  }
+  write_prob_partial(pacc, E, wpart, probpart);
+}
+
+// ----------------------------------------------------------- fp32 fused --
+// RT tokens per block: logits by FMA dot products into LDS, then selection.
+__global__ __launch_bounds__(256) void router_f32(
+    const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ gbias,
+    int T, int d, int E, int k, int renorm, float* __restrict__ logits_out,
+    int32_t* __restrict__ idx_out, float* __restrict__ gate_out, float* __restrict__ probpart) {
+  extern __shared__ float lg[];  // [RT32][E] then [kWaves][E]
+  const int t0 = blockIdx.x * RT32;
+  for (int pi = threadIdx.x; pi < RT32 * E; pi += 256) {
+    const int tl = pi / E, e = pi % E, t = t0 + tl;
+    float s = 0.0f;
+    if (t < T) {
+      const float* xr = x + (size_t)t * d;
+      const float* wr = w + (size_t)e * d;
+      for (int i = 0; i < d; ++i) s = fmaf(xr[i], wr[i], s);
+    }
+    lg[pi] = s + (gbias ? gbias[e] : 0.0f);
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int EPL = (E + 63) >> 6;
+  float pacc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) pacc[i] = 0.0f;
+  for (int tl = wave; tl < RT32; tl += kWaves) {
+    const int t = t0 + tl;
+    if (t >= T) break;
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = lane + 64 * i;
+      v[i] = (i < EPL && e < E) ? lg[tl * E + e] : 0.0f;
+      if (logits_out && i < EPL && e < E) logits_out[(size_t)t * E + e] = v[i];
+    }
+    select_token(v, E, k, renorm, lane, idx_out + (size_t)t * k, gate_out + (size_t)t * k, pacc);
+  }
+  write_prob_partial(pacc, E, lg + RT32 * E, probpart);
+}
+
+// prob_sum[e] = sum over blocks of probpart[b][e]: fixed-order tree in double.
+__global__ __launch_bounds__(256) void router_reduce(const float* __restrict__ probpart, int nb,
                                                       int E, float* __restrict__ prob_sum) {
   __shared__ double s[256];
   const int e = blockIdx.x;
   double a = 0.0;
-  for (int b = threadIdx.x; b < nb; b += 256) a += (double)partial[(size_t)b * E + e];
+  for (int b = threadIdx.x; b < nb; b += 256) a += (double)probpart[(size_t)b * E + e];
   s[threadIdx.x] = a;
   __syncthreads();
   for (int w = 128; w >= 1; w >>= 1) {
@@ -251,6 +321,36 @@ __global__ __launch_bounds__(256) void router_reduce(const float* __restrict__ p
 __global__ void fill_zero_f32(float* __restrict__ p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0.0f;
+}
+
+template <int MTW, int NTE>
+bool launch_logits(const RouterPlan& pl, const void* x, const void* w, int T, int d, int E,
+                   float* part, hipStream_t s) {
+  const size_t lds = (size_t)2 * (64 * MTW + 16 * NTE) * RKS * 2;
+  if (lds > 65536 &&
+      hipFuncSetAttribute((const void*)router_logits_bf16<MTW, NTE>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+    return false;
+  hipLaunchKernelGGL((router_logits_bf16<MTW, NTE>), dim3(pl.ntt * pl.split), dim3(256), lds, s,
+                     (const uint16_t*)x, (const uint16_t*)w, T, d, E, pl.nch, pl.split, part);
+  return true;
+}
+
+bool dispatch_logits(const RouterPlan& pl, const void* x, const void* w, int T, int d, int E,
+                     float* part, hipStream_t s) {
+  const int mtw = pl.tt / 64, nte = pl.ep / 16;
+#define MOE_CASE(A, B)                               \
+  if (mtw == A && nte == B) return launch_logits<A, B>(pl, x, w, T, d, E, part, s);
+  MOE_CASE(4, 4)
+  MOE_CASE(4, 8)
+  MOE_CASE(2, 12)
+  MOE_CASE(2, 16)
+  MOE_CASE(1, 20)
+  MOE_CASE(1, 24)
+  MOE_CASE(1, 28)
+  MOE_CASE(1, 32)
+#undef MOE_CASE
+  return false;
 }
 
 }  // namespace
@@ -267,33 +367,37 @@ extern "C" int moe_router_topk(const void* x, int dtype, int T, int d, const voi
   if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_INVALID;
   if (renorm != 0 && renorm != 1) return MOE_ERR_INVALID;
   if (E > kMaxE || k > kMaxK) return MOE_ERR_UNSUPPORTED;
-  if (dtype == MOE_BF16 && (d % 8) != 0) return MOE_ERR_UNSUPPORTED;
+  if (dtype == MOE_BF16 && (d % RKS) != 0) return MOE_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
   if (T == 0) {
     if (prob_sum) {
-      hipLaunchKernelGGL(fill_zero_f32, dim3(ceil_div(E, 256)), dim3(256), 0,
-                         (hipStream_t)stream, prob_sum, E);
+      hipLaunchKernelGGL(fill_zero_f32, dim3(ceil_div(E, 256)), dim3(256), 0, s, prob_sum, E);
       return launch_status();
     }
     return MOE_OK;
   }
   if (!x || !w_gate || !topk_idx || !topk_gate) return MOE_ERR_INVALID;
-  if (!ws || ws_bytes < router_ws(T, E)) return MOE_ERR_WORKSPACE;
-  const int nb = router_blocks(T);
-  const size_t lds = router_lds(E);
-  hipStream_t s = (hipStream_t)stream;
-  float* partial = (float*)ws;
-  if (lds > 65536 &&
-      hipFuncSetAttribute(
-          (const void*)(dtype == MOE_BF16 ? router_kernel<true> : router_kernel<false>),
-          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-    return MOE_ERR_LAUNCH;
-  if (dtype == MOE_BF16)
-    hipLaunchKernelGGL(router_kernel<true>, dim3(nb), dim3(256), lds, s, x, w_gate, gate_bias, T,
-                       d, E, k, renorm, logits_out, topk_idx, topk_gate, partial);
-  else
-    hipLaunchKernelGGL(router_kernel<false>, dim3(nb), dim3(256), lds, s, x, w_gate, gate_bias,
-                       T, d, E, k, renorm, logits_out, topk_idx, topk_gate, partial);
+  if (!ws || ws_bytes < router_ws(T, d, E)) return MOE_ERR_WORKSPACE;
+  int nb = router_blocks(T);
+  float* logit_part = (float*)ws;
+  float* probpart = (float*)((unsigned char*)ws + router_partial_bytes(T, d, E));
+  if (dtype == MOE_BF16) {
+    const RouterPlan pl = router_plan(T, d, E);
+    if (!dispatch_logits(pl, x, w_gate, T, d, E, logit_part, s)) return MOE_ERR_LAUNCH;
+    hipLaunchKernelGGL(router_select, dim3(nb), dim3(256), 0, s, logit_part, pl.split, gate_bias,
+                       T, E, k, renorm, logits_out, topk_idx, topk_gate, probpart);
+  } else {
+    const size_t lds = (size_t)(RT32 + kWaves) * E * sizeof(float);
+    if (lds > 65536 &&
+        hipFuncSetAttribute((const void*)router_f32, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds) != hipSuccess)
+      return MOE_ERR_LAUNCH;
+    nb = ceil_div(T, RT32);
+    hipLaunchKernelGGL(router_f32, dim3(nb), dim3(256), lds, s, (const float*)x,
+                       (const float*)w_gate, gate_bias, T, d, E, k, renorm, logits_out, topk_idx,
+                       topk_gate, probpart);
+  }
   if (prob_sum)
-    hipLaunchKernelGGL(router_reduce, dim3(E), dim3(256), 0, s, partial, nb, E, prob_sum);
+    hipLaunchKernelGGL(router_reduce, dim3(E), dim3(256), 0, s, probpart, nb, E, prob_sum);
   return launch_status();
 }

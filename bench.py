@@ -26,10 +26,11 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "routed tokens/sec per MoE layer fwd (bf16, 1 GPU) + % of MFMA/HBM roofline"
+ROOT = os.path.dirname(os.path.abspath(__file__))
 CALLS = ("router", "permute", "ffn", "combine", "aux")
 # tokens whose expert FFN the CPU baseline evaluates (routing always covers all T)
-CPU_SAMPLE = {"tiny_fp32": 256, "mixtral_prefill": 256, "switch_top1_cap": 2048, "decode": 32,
-              "deepseek_v3": 64}
+CPU_SAMPLE = {"tiny_fp32": 256, "mixtral_prefill": 2048, "switch_top1_cap": 8192, "decode": 32,
+              "deepseek_v3": 512}
 
 
 def parse():
@@ -39,9 +40,39 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="mixtral_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--traffic", default=None,
-                    help="JSON file with HBM bytes per dominant-kernel launch from counters")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="JSON with HBM bytes per dominant-call launch from rocprofv3 counters")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a device-to-device copy of BYTES bytes (counter calibration)")
     return ap.parse_args()
+
+
+def ffn_source_hash() -> str:
+    """Hash of the grouped-FFN kernel source; counter data for another source is stale."""
+    import hashlib
+    path = os.path.join(ROOT, "top_routing_expert_topk_amd", "csrc", "ffn.hip")
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(path, workload):
+    """HBM bytes per moe_grouped_ffn call, if measured for this kernel source, else None."""
+    if not path or not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(workload)
+    if not rec or rec.get("ffn_source") != ffn_source_hash():
+        return None
+    return rec["fetch_bytes"] + rec["write_bytes"]
+
+
+def copy_calibration(nbytes, steps):
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "steps": steps}), flush=True)
 
 
 def cpu_model():
@@ -105,6 +136,9 @@ def main():
               "(no expert or data parallelism across GPUs); run it with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, args.steps)
+        return
     import torch
     import moe_inputs as mi
     import top_routing_expert_topk_amd as moe
@@ -172,9 +206,7 @@ def main():
     t_ffn = ms["ffn"] * 1e-3
     mfma_bound = cfg.dtype == "bf16" and ffn_flop / max(expert_bytes, 1) > \
         PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        traffic = json.load(open(args.traffic)).get(cfg.name)
+    traffic = measured_traffic(args.traffic, cfg.name)
     if cfg.dtype != "bf16":
         roof = {"bound": "alu", "achieved": ffn_flop / t_ffn / 1e12, "peak": PEAK_F32_TFLOPS,
                 "unit": "TFLOP/s"}

@@ -59,8 +59,9 @@ __device__ __forceinline__ int find_expert(const int32_t* __restrict__ tile_star
 // activation rows (32 k x 16 rows); lane l gives row (l%16), k-octet (l/16)
 // and receives D[n = 4*(l/16)+v][row = l%16], i.e. 4 consecutive output
 // features of one row -> one 8-byte store.
-// LDS rows are 64 bf16 (8 chunks of 16 B); chunk c of row r sits at c^(r&7)
-// so the 16 lanes reading 16 rows at one chunk spread over all banks.
+// LDS rows are 64 bf16 (8 chunks of 16 B); chunk c of row r sits at
+// c ^ ((r >> 1) & 7), so the 16 lanes of one ds_read_b128 pass, reading 16
+// rows at one chunk, spread over all 16 bank groups of 16 bytes.
 template <int BN, int BM, bool GATHER, bool SILU>
 __global__ __launch_bounds__(256) void gemm_bf16(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ sorted_token,
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(256) void gemm_bf16(
   for (int i = 0; i < AL; ++i) {
     const int c = tid + 256 * i, r = c >> 3, ch = c & 7;
     asrc[i] = w + ((size_t)e * N + n0 + r) * K + ch * 8;
-    aoff[i] = r * KC + ((ch ^ (r & 7)) * 8);
+    aoff[i] = r * KC + ((ch ^ ((r >> 1) & 7)) * 8);
   }
 #pragma unroll
   for (int i = 0; i < BL; ++i) {
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(256) void gemm_bf16(
     const int rr = row0 + (r < rows ? r : rows - 1);
     const size_t src = GATHER ? (size_t)sorted_token[rr] : (size_t)rr;
     bsrc[i] = act + src * K + ch * 8;
-    boff[i] = r * KC + ((ch ^ (r & 7)) * 8);
+    boff[i] = r * KC + ((ch ^ ((r >> 1) & 7)) * 8);
   }
 
   f32x4 acc[TN][TM];
@@ -135,12 +136,12 @@ __global__ __launch_bounds__(256) void gemm_bf16(
 #pragma unroll
       for (int i = 0; i < TN; ++i) {
         const int r = wn * (BN / 2) + i * 16 + (lane & 15);
-        a[i] = *(const bf16x8*)(&sA[cur][r * KC + ((ch ^ (r & 7)) * 8)]);
+        a[i] = *(const bf16x8*)(&sA[cur][r * KC + ((ch ^ ((r >> 1) & 7)) * 8)]);
       }
 #pragma unroll
       for (int j = 0; j < TM; ++j) {
         const int r = wm * (BM / 2) + j * 16 + (lane & 15);
-        b[j] = *(const bf16x8*)(&sB[cur][r * KC + ((ch ^ (r & 7)) * 8)]);
+        b[j] = *(const bf16x8*)(&sB[cur][r * KC + ((ch ^ ((r >> 1) & 7)) * 8)]);
       }
 #pragma unroll
       for (int i = 0; i < TN; ++i)
@@ -184,14 +185,15 @@ __global__ __launch_bounds__(256) void gemm_bf16(
 
 // --------------------------------------------- MFMA GEMM, 256-row tiles --
 // For experts with a few hundred rows or more. Block tile 256 weight rows x
-// 256 permuted rows, four waves in a 2 x 2 grid, each 128 x 128 as 4 x 4
-// v_mfma_f32_32x32x16_bf16 tiles (256 accumulator floats per lane, in AGPRs).
+// 256 permuted rows, eight waves (two per SIMD, so one wave's MFMAs cover the
+// other's waits) in a 2 x 4 grid, each 128 x 64 as 4 x 2
+// v_mfma_f32_32x32x16_bf16 tiles (128 accumulator floats per lane).
 //
 // Data path: direct global->LDS DMA (16 bytes per lane, no VGPR round trip)
 // into a ring of kStages slots of 32 K-columns; up to two slots are in flight
 // while one is consumed. LDS rows are 64 bytes (4 chunks of 16 B); chunk c of
-// row r sits at slot c ^ ((r >> 1) & 3), so 8 lanes reading 8 rows at one
-// chunk hit 8 distinct 16-byte bank groups. One DMA instruction fills 1 KB =
+// row r sits at slot c ^ ((r >> 2) & 3), so the 16 lanes of one ds_read_b128
+// pass (16 rows, one chunk) hit 16 distinct 16-byte bank groups. One DMA instruction fills 1 KB =
 // 16 rows, lane l writing slot l%4 of row l/4, so lane l fetches chunk
 // (l%4) ^ swizzle(row).
 //
@@ -215,7 +217,8 @@ __global__ __launch_bounds__(256) void gemm_bf16(
 constexpr int kBigBM = 256;
 constexpr int kBigBN = 256;
 constexpr int kKS = 32;
-constexpr int kStages = 4;
+constexpr int kStages = 5;  // 5 x 32 KB = all 160 KB of LDS
+constexpr int kBigThreads = 512;
 constexpr int kMaxSplit = 8;  // K-ranges per tail tile
 constexpr int kReduceSlices = 8;  // row slices per tail tile in the reduction
 
@@ -235,7 +238,10 @@ __device__ __forceinline__ void dma16(const void* g, void* lds_base) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
 
-__device__ __forceinline__ int swz64(int r, int c) { return c ^ ((r >> 1) & 3); }
+// 64-byte rows: chunk c of row r at slot c ^ ((r >> 2) & 3). A ds_read_b128
+// is served 16 lanes (256 bytes) at a time; 16 consecutive rows at one chunk
+// then cover all 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz64(int r, int c) { return c ^ ((r >> 2) & 3); }
 
 // Largest e with tile_start[e] * ntiles <= L.
 __device__ __forceinline__ int find_expert_scaled(const int32_t* __restrict__ tile_start, int E,
@@ -292,14 +298,15 @@ __device__ __forceinline__ BigSplit big_split(const int32_t* __restrict__ tile_s
 }
 
 template <bool GATHER, bool SILU>
-__global__ __launch_bounds__(256) void gemm_bf16_big(
+__global__ __launch_bounds__(kBigThreads) void gemm_bf16_big(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ sorted_token,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_start,
     const uint16_t* __restrict__ w, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ out, float* __restrict__ part, int E, int N, int K, int ntiles) {
   constexpr int BN = kBigBN, BM = kBigBM;
-  constexpr int TN = 4, TM = 4;              // 32-row MFMA tiles per wave
-  constexpr int AI = BN / 64, BI = BM / 64;  // DMA instructions per thread per slot
+  constexpr int TN = 4, TM = 2;                // 32-row MFMA tiles per wave
+  constexpr int NW = kBigThreads / 64;         // waves
+  constexpr int AI = BN / 16 / NW, BI = BM / 16 / NW;  // DMA instructions per wave per slot
   constexpr int SA = BN * kKS, SB = BM * kKS;
   constexpr int PER_SLOT = AI + BI;
   __shared__ __align__(1024) uint16_t lds[kStages][SA + SB];
@@ -325,18 +332,18 @@ __global__ __launch_bounds__(256) void gemm_bf16_big(
   const int kbeg = p * nk_all / split, kend = (p + 1) * nk_all / split;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wn = wave >> 1, wm = wave & 1;
+  const int wn = wave >> 2, wm = wave & 3;
 
   const uint16_t* aptr[AI];
   const uint16_t* bptr[BI];
 #pragma unroll
   for (int i = 0; i < AI; ++i) {
-    const int r = (i * 4 + wave) * 16 + (lane >> 2);
+    const int r = (i * NW + wave) * 16 + (lane >> 2);
     aptr[i] = w + ((size_t)e * N + n0 + r) * K + swz64(r, lane & 3) * 8;
   }
 #pragma unroll
   for (int i = 0; i < BI; ++i) {
-    const int r = (i * 4 + wave) * 16 + (lane >> 2);
+    const int r = (i * NW + wave) * 16 + (lane >> 2);
     const int rr = row0 + (r < rows ? r : rows - 1);
     const size_t src = GATHER ? (size_t)sorted_token[rr] : (size_t)rr;
     bptr[i] = act + src * K + swz64(r, lane & 3) * 8;
@@ -345,9 +352,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_big(
   auto issue = [&](int st, int kt) {
     const int koff = (kbeg + kt) * kKS;
 #pragma unroll
-    for (int i = 0; i < AI; ++i) dma16(aptr[i] + koff, &lds[st][(i * 4 + wave) * 16 * kKS]);
+    for (int i = 0; i < AI; ++i) dma16(aptr[i] + koff, &lds[st][(i * NW + wave) * 16 * kKS]);
 #pragma unroll
-    for (int i = 0; i < BI; ++i) dma16(bptr[i] + koff, &lds[st][SA + (i * 4 + wave) * 16 * kKS]);
+    for (int i = 0; i < BI; ++i) dma16(bptr[i] + koff, &lds[st][SA + (i * NW + wave) * 16 * kKS]);
   };
 
   f32x16 acc[TN][TM];
@@ -372,7 +379,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_big(
       FA[i] = *(const bf16x8*)(sa_ + r * kKS + swz64(r, 2 * (sub) + ch) * 8);           \
     }                                                                                   \
     _Pragma("unroll") for (int j = 0; j < TM; ++j) {                                    \
-      const int r = wm * 128 + j * 32 + (lane & 31);                                    \
+      const int r = wm * 64 + j * 32 + (lane & 31);                                     \
       FB[j] = *(const bf16x8*)(sb_ + r * kKS + swz64(r, 2 * (sub) + ch) * 8);           \
     }                                                                                   \
   } while (0)
@@ -413,7 +420,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_big(
         const int nl = wn * 128 + i * 32 + 8 * q + 4 * ch;
 #pragma unroll
         for (int j = 0; j < TM; ++j) {
-          const int m = wm * 128 + j * 32 + (lane & 31);
+          const int m = wm * 64 + j * 32 + (lane & 31);
           *(f32x4*)(pp + m * BN + nl) =
               f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
         }
@@ -436,7 +443,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_big(
       }
 #pragma unroll
       for (int j = 0; j < TM; ++j) {
-        const int m = wm * 128 + j * 32 + (lane & 31);
+        const int m = wm * 64 + j * 32 + (lane & 31);
         if (m < rows) {
           float v[4];
 #pragma unroll
@@ -762,13 +769,14 @@ extern "C" int moe_grouped_ffn(const void* x, int dtype, int T, int d, int h, in
     // blocks: every tile once, plus at most kTailSlots tail units
     const int g1 = ceil_div((long)mslots * nt1 + kTailSlots, 8) * 8;
     const int g2 = ceil_div((long)mslots * nt2 + kTailSlots, 8) * 8;
-    hipLaunchKernelGGL((gemm_bf16_big<true, true>), dim3(g1), dim3(256), 0, s, xb, sorted_token,
+    hipLaunchKernelGGL((gemm_bf16_big<true, true>), dim3(g1), dim3(kBigThreads), 0, s, xb,
+                       sorted_token,
                        offsets, tile_start, (const uint16_t*)w1, (const uint16_t*)b1, (uint16_t*)H,
                        part, E, h, d, nt1);
     hipLaunchKernelGGL((big_tail_reduce<true>), dim3(kTailSlots * kReduceSlices), dim3(256), 0, s,
                        offsets,
                        tile_start, (const uint16_t*)b1, part, (uint16_t*)H, E, h, d, nt1);
-    hipLaunchKernelGGL((gemm_bf16_big<false, false>), dim3(g2), dim3(256), 0, s,
+    hipLaunchKernelGGL((gemm_bf16_big<false, false>), dim3(g2), dim3(kBigThreads), 0, s,
                        (const uint16_t*)H, sorted_token, offsets, tile_start, (const uint16_t*)w2,
                        (const uint16_t*)b2, (uint16_t*)y_perm, part, E, d, h, nt2);
     hipLaunchKernelGGL((big_tail_reduce<false>), dim3(kTailSlots * kReduceSlices), dim3(256), 0, s,

@@ -133,11 +133,12 @@ __device__ __forceinline__ void dma16(const void* g, void* lds_base) {
 }
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
-__device__ __forceinline__ int rswz(int r, int c) { return c ^ ((r >> 1) & 3); }
+// 16 consecutive 64-byte rows at one chunk land in 16 distinct bank groups.
+__device__ __forceinline__ int rswz(int r, int c) { return c ^ ((r >> 2) & 3); }
 
 // Block: TT tokens (64 * MTW) x EP experts (16 * NTE) over the 32-wide K
 // chunks [c0, c1) of its split. LDS stage = TT token rows then EP expert rows,
-// 64 bytes each, chunk c of row r at slot c ^ ((r >> 1) & 3); each DMA
+// 64 bytes each, chunk c of row r at slot c ^ ((r >> 2) & 3); each DMA
 // instruction fills 16 rows, lane l writing slot l%4 of row l/4. Wave w owns
 // token tiles w, w+4, ... and every expert tile, so a token fragment is read
 // once per chunk and reused across all expert tiles.

@@ -428,14 +428,22 @@ __global__ __launch_bounds__(kBigThreads) void gemm_bf16_big(
     return;
   }
 
+  // Finished tile -> bf16 in LDS (the ring is idle now), then whole rows out
+  // with 16-byte stores: 32 lanes write one 512-byte row. LDS rows are padded
+  // by 16 bytes so the 32 rows a wave writes at one feature offset spread
+  // over the banks.
+  constexpr int OSTR = BN + 8;  // LDS row stride in bf16 elements
+  static_assert((size_t)BM * OSTR * 2 <= sizeof(lds), "output tile must fit the ring");
+  uint16_t* ot = &lds[0][0];
+  lds_barrier();  // every wave is done reading the ring
 #pragma unroll
   for (int i = 0; i < TN; ++i) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int n = n0 + wn * 128 + i * 32 + 8 * q + 4 * ch;
+      const int nl = wn * 128 + i * 32 + 8 * q + 4 * ch;
       float bv[4] = {0.f, 0.f, 0.f, 0.f};
       if (bias) {
-        const u32x2 bb = *(const u32x2*)(bias + (size_t)e * N + n);
+        const u32x2 bb = *(const u32x2*)(bias + (size_t)e * N + n0 + nl);
         bv[0] = bf16lo(bb[0]);
         bv[1] = bf16hi(bb[0]);
         bv[2] = bf16lo(bb[1]);
@@ -444,20 +452,26 @@ __global__ __launch_bounds__(kBigThreads) void gemm_bf16_big(
 #pragma unroll
       for (int j = 0; j < TM; ++j) {
         const int m = wm * 64 + j * 32 + (lane & 31);
-        if (m < rows) {
-          float v[4];
+        float v[4];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            v[u] = acc[i][j][4 * q + u] + bv[u];
-            if (SILU) v[u] = silu(v[u]);
-          }
-          u32x2 o;
-          o[0] = pack_bf16x2(v[0], v[1]);
-          o[1] = pack_bf16x2(v[2], v[3]);
-          *(u32x2*)(out + (size_t)(row0 + m) * N + n) = o;
+        for (int u = 0; u < 4; ++u) {
+          v[u] = acc[i][j][4 * q + u] + bv[u];
+          if (SILU) v[u] = silu(v[u]);
         }
+        u32x2 o;
+        o[0] = pack_bf16x2(v[0], v[1]);
+        o[1] = pack_bf16x2(v[2], v[3]);
+        *(u32x2*)(ot + m * OSTR + nl) = o;
       }
     }
+  }
+  __syncthreads();
+  constexpr int CPR = BN / 8;  // 16-byte chunks per row
+#pragma unroll 4
+  for (int c = tid; c < BM * CPR; c += kBigThreads) {
+    const int m = c / CPR, cc = c % CPR;
+    if (m < rows)
+      *(u32x4*)(out + (size_t)(row0 + m) * N + n0 + cc * 8) = *(const u32x4*)(ot + m * OSTR + cc * 8);
   }
 }
 

@@ -57,11 +57,16 @@ SMALL = {
                                                    renorm=False),
     "no_bias": CFG["deepseek_v3"].with_(name="no_bias", T=100, d=256, h=128, E=32, k=4,
                                         expert_bias=False),
-    # 256-row MFMA tiles: every tile is a tail tile split along K
+    # 256 x 256 tiles: every tile is a tail tile split along K
     "big_tail_only": CFG["mixtral_prefill"].with_(name="big_tail_only", T=1024, d=512, h=1024,
                                                    E=4),
-    # 256-row MFMA tiles: whole rounds of tiles plus a split tail
+    # 256 x 256 tiles: whole rounds of tiles plus a split tail
     "big_full_tail": CFG["mixtral_prefill"].with_(name="big_full_tail", T=4096, d=512, h=2048),
+    # experts of ~150 rows: 128 x 128 tiles, two row tiles per expert
+    "mid_rows_multi": CFG["mixtral_prefill"].with_(name="mid_rows_multi", T=600, d=512, h=1536),
+    # 64 experts under a capacity of 80 rows: 128 x 128 tiles, capacity drops
+    "mid_rows_capacity": CFG["switch_top1_cap"].with_(name="mid_rows_capacity", T=6000, d=512,
+                                                       h=1536, E=64),
 }
 
 

@@ -21,7 +21,7 @@ extern "C" size_t moe_workspace_size(int op, int T, int d, int h, int E, int k) 
   switch (op) {
     case MOE_OP_ROUTER: return d < 1 ? 0 : router_ws(T, d, E);
     case MOE_OP_PERMUTE: return permute_ws(T, k, E);
-    case MOE_OP_FFN: return (h < 1 || d < 1) ? 0 : ffn_ws(T, h, E, k);
+    case MOE_OP_FFN: return (h < 1 || d < 1) ? 0 : ffn_ws(T, d, h, E, k);
     default: return 0;
   }
 }

@@ -7,14 +7,23 @@
 //
 // Kernels:
 //   build_tile_map  prefix sum of ceil(kept_e / BM) -> tile_start[E+1], so a
-//                   GEMM block finds its (expert, row block) with no host read
-//   gemm_bf16       MFMA grouped GEMM, LDS double-buffered 64-deep K steps;
-//                   the gather of x rows is fused into the B-tile load and
-//                   bias (+SiLU) into the epilogue
+//                   gemm_bf16 / gemm_f32 block finds its (expert, row block)
+//                   with no host read
+//   big_plan        per-block work lists (tile, K range) of both GEMMs for
+//                   the 256 x 256 tile path, built from offsets on the device
+//   gemm_bf16_ring  256 x 256 MFMA tiles fed by a global->LDS DMA ring of
+//                   64-column steps; tail tiles split along K
+//   big_tail_reduce sums the K-range partials of split tail tiles in order
+//   gemm_bf16       128 x 128 MFMA tiles, LDS double-buffered 64-deep K
+//                   steps, for experts with fewer rows
 //   decode_bf16     weight-streaming path for few rows per expert: each
 //                   touched expert's weights are read once per 4 rows, rows
 //                   of untouched experts cost one offsets read
 //   gemm_f32        FMA tiles for fp32 layers
+// In every kernel the gather of x rows is fused into the activation load and
+// bias (+SiLU) into the epilogue.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -172,7 +181,7 @@ __global__ __launch_bounds__(256) void gemm_bf16(
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           v[q] = acc[i][j][q] + bv[q];
-          if (SILU) v[q] = silu(v[q]);
+          if (SILU) v[q] = silu_bf16(v[q]);
         }
         u32x2 o;
         o[0] = pack_bf16x2(v[0], v[1]);
@@ -183,44 +192,45 @@ __global__ __launch_bounds__(256) void gemm_bf16(
   }
 }
 
-// --------------------------------------------- MFMA GEMM, 256-row tiles --
+// ---------------------------------- MFMA GEMM, 256 x 256 tiles, DMA ring --
 // For experts with a few hundred rows or more. Block tile 256 weight rows x
 // 256 permuted rows, eight waves (two per SIMD, so one wave's MFMAs cover the
-// other's waits) in a 2 x 4 grid, each 128 x 64 as 4 x 2
+// other's waits) in a 2 x 4 grid, each owning 128 x 64 of the tile as 4 x 2
 // v_mfma_f32_32x32x16_bf16 tiles (128 accumulator floats per lane).
-//
-// Data path: direct global->LDS DMA (16 bytes per lane, no VGPR round trip)
-// into a ring of kStages slots of 32 K-columns; up to two slots are in flight
-// while one is consumed. LDS rows are 64 bytes (4 chunks of 16 B); chunk c of
-// row r sits at slot c ^ ((r >> 2) & 3), so the 16 lanes of one ds_read_b128
-// pass (16 rows, one chunk) hit 16 distinct 16-byte bank groups. One DMA instruction fills 1 KB =
-// 16 rows, lane l writing slot l%4 of row l/4, so lane l fetches chunk
-// (l%4) ^ swizzle(row).
-//
-// Each 32-column slot is consumed in two k16 sub-steps; the fragment reads of
-// one sub-step overlap the 16 MFMAs of the other, and the ring barrier (which
-// both publishes slot kt+1 and retires slot kt-1 for refilling) sits between
-// the two sub-steps, so it never waits on an empty MFMA pipe. The barrier is
-// an s_barrier with a compiler memory clobber: it keeps LDS accesses on their
-// side without draining the DMA queue, which a workgroup fence would do.
 //
 // v_mfma_f32_32x32x16_bf16: lane l supplies row l%32 and k-octet l/32 of each
 // operand (A = 32 weight rows x 16 k, B = 16 k x 32 permuted rows) and
 // receives D[n = 8*(v/4) + 4*(l/32) + v%4][row = l%32], v = 0..15, i.e. four
-// runs of 4 consecutive output features of one row -> 8-byte stores.
+// runs of 4 consecutive output features of one row.
 //
-// Tile order: expert-major; inside an expert, groups of 8 weight-row tiles,
-// inside a group the expert's row blocks. Consecutive logical tiles then
-// share a weight panel (across row blocks) or a row panel (across the group),
-// and the hardware block id is remapped so each XCD (blocks are dealt to the
-// 8 XCDs round-robin) walks one contiguous range of that order through its L2.
-constexpr int kBigBM = 256;
-constexpr int kBigBN = 256;
-constexpr int kKS = 32;
-constexpr int kStages = 5;  // 5 x 32 KB = all 160 KB of LDS
-constexpr int kBigThreads = 512;
-constexpr int kMaxSplit = 8;  // K-ranges per tail tile
-constexpr int kReduceSlices = 8;  // row slices per tail tile in the reduction
+// Data path: direct global->LDS DMA (16 bytes per lane, no VGPR round trip)
+// of full 128-byte row segments: one DMA instruction moves 8 rows x 64
+// columns, touching 8 cache lines (32-column segments would touch 16 half
+// lines for the same bytes, and the L1/L2 path serves requests, not bytes).
+// A 64-column step of a tile needs four 16 KB blocks (weight rows 0-127 and
+// 128-255, permuted rows 0-127 and 128-255), held in a ring of ten block slots
+// (all 160 KB of LDS): block b of the tile's sequence (step b/4, part b%4)
+// lives in slot b % 10. While step j is computed, step j+1 is landing and
+// half of step j+2 is in flight; at the end of step j, once every wave's
+// fragment reads of it have completed, its four slots take the second half
+// of step j+2 and the first half of step j+3 (1.5 steps, 96 KB, in flight).
+// The ring barrier is an s_barrier with a compiler memory clobber: it keeps
+// LDS accesses on their side without draining the DMA queue, which a
+// workgroup fence would do.
+//
+// LDS rows are 128 bytes (8 chunks of 16 B); chunk c of row r sits at
+// c ^ ((r >> 1) & 7). A ds_read_b128 is served 16 lanes (256 bytes) at a
+// time, and 16 consecutive rows at one chunk then hit 16 distinct 16-byte
+// bank groups. Lane l of a DMA instruction writes chunk slot l%8 of row l/8,
+// so it fetches chunk (l%8) ^ swizzle(row).
+constexpr int kBigBM = 256;          // permuted rows per tile
+constexpr int kBigBN = kBigBNTile;   // weight rows (output features) per tile
+constexpr int kRS = 64;              // K columns per step
+constexpr int kRBlk = 128 * kRS;     // bf16 elements per block (16 KB)
+constexpr int kRSlots = 10;
+constexpr int kMaxSplit = 8;         // K ranges per tail tile
+constexpr int kReduceSlices = 8;     // row slices per tail tile in the reduction
+static_assert(kBigBN == 256, "tile");
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -229,6 +239,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 // Workgroup barrier that the compiler may not move memory accesses across.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
@@ -238,212 +249,154 @@ __device__ __forceinline__ void dma16(const void* g, void* lds_base) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
 
-// 64-byte rows: chunk c of row r at slot c ^ ((r >> 2) & 3). A ds_read_b128
-// is served 16 lanes (256 bytes) at a time; 16 consecutive rows at one chunk
-// then cover all 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int swz64(int r, int c) { return c ^ ((r >> 2) & 3); }
+__device__ __forceinline__ int swz128(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-// Largest e with tile_start[e] * ntiles <= L.
-__device__ __forceinline__ int find_expert_scaled(const int32_t* __restrict__ tile_start, int E,
-                                                  int L, int ntiles) {
+// One entry of a launch's work list: the block's tile and K range. The
+// lists are built on the device by big_plan, so a GEMM block starts with one
+// uniform load instead of searching the tile map.
+struct alignas(16) BigWork {
+  int e;           // expert, -1: no work for this block
+  int row0, rows;  // permuted rows of the tile
+  int n0;          // first output feature
+  int kbeg, kend;  // K range in kRS-column steps
+  int unit;        // fp32 partial slot of a split tail tile, -1 for a whole tile
+  int pad;
+};
+static_assert(sizeof(BigWork) == kWorkBytes, "work entry size");
+// Per launch: tiles = whole tiles + tail tiles; the `full` first tiles (a
+// whole number of rounds over the kTailSlots resident blocks) run whole, the
+// `tail` remaining ones are each cut into `split` K ranges so that the last
+// round fills every CU.
+struct BigHdr {
+  int full, tail, split, tiles;
+};
+
+// Largest e with ts[e] <= v (ts in LDS, ts[0] = 0 <= v).
+__device__ __forceinline__ int find_le(const int* ts, int E, int v) {
   int lo = 0, hi = E;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (tile_start[mid] * ntiles <= L) lo = mid; else hi = mid;
+    if (ts[mid] <= v) lo = mid; else hi = mid;
   }
   return lo;
 }
 
-// Tile t of the expert-major order -> (expert, first row, rows, first output feature).
-struct BigTile {
-  int e, row0, rows, n0;
-};
-__device__ __forceinline__ BigTile big_tile(const int32_t* __restrict__ tile_start,
-                                            const int32_t* __restrict__ offsets, int E,
-                                            int ntiles, int t) {
-  BigTile r;
-  r.e = find_expert_scaled(tile_start, E, t, ntiles);
-  const int mt = tile_start[r.e + 1] - tile_start[r.e];
-  const int l = t - tile_start[r.e] * ntiles;
-  const int g = l / (mt * 8);
-  const int gs = min(8, ntiles - g * 8);
-  const int l2 = l - g * mt * 8;
-  const int mi = l2 / gs, nt = g * 8 + l2 % gs;
-  r.row0 = offsets[r.e] + mi * kBigBM;
-  r.rows = min(kBigBM, offsets[r.e + 1] - r.row0);
-  r.n0 = nt * kBigBN;
-  return r;
-}
-
-// Work split: the first `full` tiles (a whole number of rounds over the
-// kTailSlots-block machine) run whole; the remaining `tail` tiles are each
-// cut into `split` K-ranges so that the last round fills every CU.
-struct BigSplit {
-  int tiles, full, tail, split;
-};
-__device__ __forceinline__ BigSplit big_split(const int32_t* __restrict__ tile_start, int E,
-                                              int ntiles, int nk) {
-  BigSplit s;
-  s.tiles = tile_start[E] * ntiles;
-  s.tail = s.tiles % kTailSlots;
-  s.full = s.tiles - s.tail;
-  s.split = 1;
-  if (s.tail > 0) {
-    s.split = kTailSlots / s.tail;
-    if (s.split > kMaxSplit) s.split = kMaxSplit;
-    if (s.split > nk) s.split = nk;
-    if (s.split < 1) s.split = 1;
+// Work lists of both GEMMs of the FFN (N = nt * kBigBN features, nk K steps).
+// Tile order: expert-major; inside an expert, groups of 8 weight-row tiles,
+// inside a group the expert's row blocks. Whole tiles are dealt to the XCDs
+// in contiguous ranges of that order (hardware block b runs on XCD b % 8), so
+// each XCD's L2 sees a few weight and row panels at a time.
+__global__ __launch_bounds__(512) void big_plan(const int32_t* __restrict__ offsets, int E,
+                                                int nt1, int nk1, int g1, int nt2, int nk2,
+                                                int g2, BigHdr* __restrict__ hdr,
+                                                BigWork* __restrict__ list1,
+                                                BigWork* __restrict__ list2) {
+  __shared__ int sc[2][kMaxE];
+  __shared__ int ts[kMaxE + 1];
+  const int x = threadIdx.x;  // blockDim == kMaxE
+  int cur = 0;
+  sc[0][x] = x < E ? (offsets[x + 1] - offsets[x] + kBigBM - 1) / kBigBM : 0;
+  __syncthreads();
+  for (int off = 1; off < kMaxE; off <<= 1) {
+    const int v = sc[cur][x] + (x >= off ? sc[cur][x - off] : 0);
+    sc[cur ^ 1][x] = v;
+    cur ^= 1;
+    __syncthreads();
   }
-  return s;
-}
+  ts[x + 1] = sc[cur][x];
+  if (x == 0) ts[0] = 0;
+  __syncthreads();
 
-template <bool GATHER, bool SILU>
-__global__ __launch_bounds__(kBigThreads) void gemm_bf16_big(
-    const uint16_t* __restrict__ act, const int32_t* __restrict__ sorted_token,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_start,
-    const uint16_t* __restrict__ w, const uint16_t* __restrict__ bias,
-    uint16_t* __restrict__ out, float* __restrict__ part, int E, int N, int K, int ntiles) {
-  constexpr int BN = kBigBN, BM = kBigBM;
-  constexpr int TN = 4, TM = 2;                // 32-row MFMA tiles per wave
-  constexpr int NW = kBigThreads / 64;         // waves
-  constexpr int AI = BN / 16 / NW, BI = BM / 16 / NW;  // DMA instructions per wave per slot
-  constexpr int SA = BN * kKS, SB = BM * kKS;
-  constexpr int PER_SLOT = AI + BI;
-  __shared__ __align__(1024) uint16_t lds[kStages][SA + SB];
+  const int i = blockIdx.x * kMaxE + x;
+  const bool second = i >= g1;
+  const int b = second ? i - g1 : i;
+  if (second && b >= g2) return;
+  const int nt = second ? nt2 : nt1, nk = second ? nk2 : nk1;
+  BigWork* list = second ? list2 : list1;
 
-  // Live tiles are known only on the device. Whole tiles are dealt to the XCDs
-  // in contiguous ranges (full is a multiple of 8); tail units follow.
-  const int nk_all = K / kKS;
-  const BigSplit sp = big_split(tile_start, E, ntiles, nk_all);
-  const int b = blockIdx.x;
-  int t, p = 0, split = 1;
+  BigHdr sp;
+  sp.tiles = ts[E] * nt;
+  sp.tail = sp.tiles % kTailSlots;
+  sp.full = sp.tiles - sp.tail;
+  sp.split = 1;
+  if (sp.tail > 0) sp.split = max(1, min(min(kTailSlots / sp.tail, kMaxSplit), nk));
+  if (b == 0) hdr[second ? 1 : 0] = sp;
+
+  BigWork w;
+  w.e = -1;
+  w.row0 = w.rows = w.n0 = w.kbeg = w.kend = 0;
+  w.unit = -1;
+  w.pad = 0;
+  int t = -1, p = 0, split = 1;
   if (b < sp.full) {
     const int per = sp.full >> 3;
     t = (b & 7) * per + (b >> 3);
-  } else {
+  } else if (b - sp.full < sp.tail * sp.split) {
     const int u = b - sp.full;
-    if (u >= sp.tail * sp.split) return;
     split = sp.split;
     t = sp.full + u / split;
     p = u % split;
   }
-  const BigTile tile = big_tile(tile_start, offsets, E, ntiles, t);
-  const int e = tile.e, row0 = tile.row0, rows = tile.rows, n0 = tile.n0;
-  const int kbeg = p * nk_all / split, kend = (p + 1) * nk_all / split;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wn = wave >> 2, wm = wave & 3;
-
-  const uint16_t* aptr[AI];
-  const uint16_t* bptr[BI];
-#pragma unroll
-  for (int i = 0; i < AI; ++i) {
-    const int r = (i * NW + wave) * 16 + (lane >> 2);
-    aptr[i] = w + ((size_t)e * N + n0 + r) * K + swz64(r, lane & 3) * 8;
+  if (t >= 0) {
+    const int e = find_le(ts, E, t / nt);  // experts own nt * (ts[e+1] - ts[e]) tiles
+    const int mt = ts[e + 1] - ts[e];
+    const int l = t - ts[e] * nt;
+    const int g = l / (mt * 8);
+    const int gs = min(8, nt - g * 8);
+    const int l2 = l - g * mt * 8;
+    const int mi = l2 / gs, ni = g * 8 + l2 % gs;
+    w.e = e;
+    w.row0 = offsets[e] + mi * kBigBM;
+    w.rows = min(kBigBM, offsets[e + 1] - w.row0);
+    w.n0 = ni * kBigBN;
+    w.kbeg = p * nk / split;
+    w.kend = (p + 1) * nk / split;
+    w.unit = split > 1 ? (t - sp.full) * split + p : -1;
   }
-#pragma unroll
-  for (int i = 0; i < BI; ++i) {
-    const int r = (i * NW + wave) * 16 + (lane >> 2);
-    const int rr = row0 + (r < rows ? r : rows - 1);
-    const size_t src = GATHER ? (size_t)sorted_token[rr] : (size_t)rr;
-    bptr[i] = act + src * K + swz64(r, lane & 3) * 8;
-  }
+  list[b] = w;
+}
 
-  auto issue = [&](int st, int kt) {
-    const int koff = (kbeg + kt) * kKS;
-#pragma unroll
-    for (int i = 0; i < AI; ++i) dma16(aptr[i] + koff, &lds[st][(i * NW + wave) * 16 * kKS]);
-#pragma unroll
-    for (int i = 0; i < BI; ++i) dma16(bptr[i] + koff, &lds[st][SA + (i * NW + wave) * 16 * kKS]);
-  };
-
-  f32x16 acc[TN][TM];
-#pragma unroll
-  for (int i = 0; i < TN; ++i)
-#pragma unroll
-    for (int j = 0; j < TM; ++j) acc[i][j] = f32x16{};
-
-  const int nk = kend - kbeg;
-#pragma unroll
-  for (int s = 0; s < kStages - 1; ++s)
-    if (s < nk) issue(s, s);
-
+// Epilogue of a 256 x 256 tile, each wave holding 128 x 64 of it as 4 x 2
+// 32x32 MFMA accumulators. A split tail tile stores its fp32 partial
+// [256 rows][256 features] for big_tail_reduce; a whole tile adds the bias,
+// applies SiLU if asked, rounds to bf16 into LDS (ot, the idle ring), and
+// leaves with 16-byte stores of whole rows: 32 lanes write one 512-byte row.
+// LDS rows are padded by 16 bytes so the 32 rows a wave writes at one feature
+// offset spread over the banks.
+template <bool SILU>
+__device__ __forceinline__ void big_store(f32x16 (&acc)[4][2], uint16_t* ot, size_t ot_bytes,
+                                          const BigWork& wk, const uint16_t* __restrict__ bias,
+                                          uint16_t* __restrict__ out, float* __restrict__ part,
+                                          int N, int wn, int wm, int lane, int tid) {
+  constexpr int BM = kBigBM, BN = kBigBN, NW = 8, TN = 4, TM = 2, WTN = 128, WTM = 64;
   const int ch = lane >> 5;
-  bf16x8 f0a[TN], f0b[TM], f1a[TN], f1b[TM];
-#define MOE_RD(st, sub, FA, FB)                                                         \
-  do {                                                                                  \
-    const uint16_t* sa_ = &lds[st][0];                                                  \
-    const uint16_t* sb_ = sa_ + SA;                                                     \
-    _Pragma("unroll") for (int i = 0; i < TN; ++i) {                                    \
-      const int r = wn * 128 + i * 32 + (lane & 31);                                    \
-      FA[i] = *(const bf16x8*)(sa_ + r * kKS + swz64(r, 2 * (sub) + ch) * 8);           \
-    }                                                                                   \
-    _Pragma("unroll") for (int j = 0; j < TM; ++j) {                                    \
-      const int r = wm * 64 + j * 32 + (lane & 31);                                     \
-      FB[j] = *(const bf16x8*)(sb_ + r * kKS + swz64(r, 2 * (sub) + ch) * 8);           \
-    }                                                                                   \
-  } while (0)
-#define MOE_MM(FA, FB)                                                                  \
-  do {                                                                                  \
-    _Pragma("unroll") for (int i = 0; i < TN; ++i)                                      \
-    _Pragma("unroll") for (int j = 0; j < TM; ++j)                                      \
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[i], FB[j], acc[i][j], 0, 0, 0); \
-  } while (0)
-
-  if (nk > kStages - 2) wait_vmcnt<(kStages - 2) * PER_SLOT>(); else wait_vmcnt<0>();
-  lds_barrier();
-  MOE_RD(0, 0, f0a, f0b);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt % kStages;
-    MOE_RD(st, 1, f1a, f1b);
-    MOE_MM(f0a, f0b);
-    if (kt + 1 < nk) {
-      // slot kt+1 must have landed; slot kt-1 (refilled below) was last read
-      // by MFMAs this wave has already issued
-      if (kt + kStages - 1 < nk) wait_vmcnt<(kStages - 3) * PER_SLOT>(); else wait_vmcnt<0>();
-      lds_barrier();
-      if (kt + kStages - 1 < nk) issue((kt + kStages - 1) % kStages, kt + kStages - 1);
-      MOE_RD((kt + 1) % kStages, 0, f0a, f0b);
-    }
-    MOE_MM(f1a, f1b);
-  }
-#undef MOE_RD
-#undef MOE_MM
-
-  if (split > 1) {
-    // fp32 partial of a tail tile: [256 rows][256 features], summed by big_tail_reduce
-    float* pp = part + ((size_t)(t - sp.full) * split + p) * (BM * BN);
+  if (wk.unit >= 0) {
+    float* pp = part + (size_t)wk.unit * (BM * BN);
 #pragma unroll
     for (int i = 0; i < TN; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int nl = wn * 128 + i * 32 + 8 * q + 4 * ch;
+        const int nl = wn * WTN + i * 32 + 8 * q + 4 * ch;
 #pragma unroll
         for (int j = 0; j < TM; ++j) {
-          const int m = wm * 64 + j * 32 + (lane & 31);
+          const int m = wm * WTM + j * 32 + (lane & 31);
           *(f32x4*)(pp + m * BN + nl) =
               f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
         }
       }
     return;
   }
-
-  // Finished tile -> bf16 in LDS (the ring is idle now), then whole rows out
-  // with 16-byte stores: 32 lanes write one 512-byte row. LDS rows are padded
-  // by 16 bytes so the 32 rows a wave writes at one feature offset spread
-  // over the banks.
   constexpr int OSTR = BN + 8;  // LDS row stride in bf16 elements
-  static_assert((size_t)BM * OSTR * 2 <= sizeof(lds), "output tile must fit the ring");
-  uint16_t* ot = &lds[0][0];
+  (void)ot_bytes;  // callers static_assert BM * OSTR * 2 <= ot_bytes
   lds_barrier();  // every wave is done reading the ring
 #pragma unroll
   for (int i = 0; i < TN; ++i) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int nl = wn * 128 + i * 32 + 8 * q + 4 * ch;
+      const int nl = wn * WTN + i * 32 + 8 * q + 4 * ch;
       float bv[4] = {0.f, 0.f, 0.f, 0.f};
       if (bias) {
-        const u32x2 bb = *(const u32x2*)(bias + (size_t)e * N + n0 + nl);
+        const u32x2 bb = *(const u32x2*)(bias + (size_t)wk.e * N + wk.n0 + nl);
         bv[0] = bf16lo(bb[0]);
         bv[1] = bf16hi(bb[0]);
         bv[2] = bf16lo(bb[1]);
@@ -451,12 +404,12 @@ __global__ __launch_bounds__(kBigThreads) void gemm_bf16_big(
       }
 #pragma unroll
       for (int j = 0; j < TM; ++j) {
-        const int m = wm * 64 + j * 32 + (lane & 31);
+        const int m = wm * WTM + j * 32 + (lane & 31);
         float v[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           v[u] = acc[i][j][4 * q + u] + bv[u];
-          if (SILU) v[u] = silu(v[u]);
+          if (SILU) v[u] = silu_bf16(v[u]);
         }
         u32x2 o;
         o[0] = pack_bf16x2(v[0], v[1]);
@@ -468,40 +421,181 @@ __global__ __launch_bounds__(kBigThreads) void gemm_bf16_big(
   __syncthreads();
   constexpr int CPR = BN / 8;  // 16-byte chunks per row
 #pragma unroll 4
-  for (int c = tid; c < BM * CPR; c += kBigThreads) {
+  for (int c = tid; c < BM * CPR; c += NW * 64) {
     const int m = c / CPR, cc = c % CPR;
-    if (m < rows)
-      *(u32x4*)(out + (size_t)(row0 + m) * N + n0 + cc * 8) = *(const u32x4*)(ot + m * OSTR + cc * 8);
+    if (m < wk.rows)
+      *(u32x4*)(out + (size_t)(wk.row0 + m) * N + wk.n0 + cc * 8) =
+          *(const u32x4*)(ot + m * OSTR + cc * 8);
   }
+}
+
+template <bool GATHER, bool SILU>
+__global__ __launch_bounds__(512) void gemm_bf16_ring(
+    const uint16_t* __restrict__ act, const int32_t* __restrict__ sorted_token,
+    const BigWork* __restrict__ work, const uint16_t* __restrict__ w,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, float* __restrict__ part, int N,
+    int K) {
+  constexpr int BM = kBigBM, BN = kBigBN, TN = 4, TM = 2, WM = 4;
+  __shared__ __align__(1024) uint16_t ring[kRSlots * kRBlk];
+  static_assert((size_t)BM * (BN + 8) * 2 <= sizeof(ring), "output tile must fit the ring");
+
+  const BigWork wk = work[blockIdx.x];
+  if (wk.e < 0) return;
+  const int e = wk.e, row0 = wk.row0, rows = wk.rows, n0 = wk.n0, kbeg = wk.kbeg;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wn = wave / WM, wm = wave % WM;
+
+  // part q of a step: 0/1 weight rows 0-127 / 128-255, 2/3 permuted rows 0-127 /
+  // 128-255; each wave moves row groups (i * 8 + wave) * 8 .. +7, i = 0, 1
+  const uint16_t* src[4][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = (i * 8 + wave) * 8 + (lane >> 3);
+    const int c = swz128(r, lane & 7) * 8;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) src[q][i] = w + ((size_t)e * N + n0 + q * 128 + r) * K + c;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int pr = q * 128 + r;
+      const int rr = row0 + (pr < rows ? pr : rows - 1);
+      const size_t tok = GATHER ? (size_t)sorted_token[rr] : (size_t)rr;
+      src[2 + q][i] = act + tok * K + c;
+    }
+  }
+  auto issue = [&](auto qc, int step, int slot) {
+    constexpr int q = decltype(qc)::value;
+    const int koff = (kbeg + step) * kRS;
+    uint16_t* dst = ring + slot * kRBlk;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16(src[q][i] + koff, dst + (i * 8 + wave) * 8 * kRS);
+  };
+  using Q0 = std::integral_constant<int, 0>;
+  using Q1 = std::integral_constant<int, 1>;
+  using Q2 = std::integral_constant<int, 2>;
+  using Q3 = std::integral_constant<int, 3>;
+
+  f32x16 acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) acc[i][j] = f32x16{};
+
+  const int ns = wk.kend - kbeg;
+  // blocks 0..9: steps 0 and 1, and the weight half of step 2
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+    if (st < ns) {
+      issue(Q0{}, st, 4 * st);
+      issue(Q1{}, st, 4 * st + 1);
+      issue(Q2{}, st, 4 * st + 2);
+      issue(Q3{}, st, 4 * st + 3);
+    }
+  if (2 < ns) {
+    issue(Q0{}, 2, 8);
+    issue(Q1{}, 2, 9);
+  }
+
+  const int ch = lane >> 5;
+  bf16x8 f0a[TN], f0b[TM], f1a[TN], f1b[TM];
+  int sa0, sa1, sb;  // slots of the current step's weight halves and permuted half
+#define MOE_SLOTS(step)                                   \
+  do {                                                    \
+    const int b_ = (4 * (step)) % kRSlots;                \
+    sa0 = b_;                                             \
+    sa1 = b_ + 1 < kRSlots ? b_ + 1 : b_ + 1 - kRSlots;   \
+    const int q_ = b_ + 2 + (wm >> 1);                    \
+    sb = q_ < kRSlots ? q_ : q_ - kRSlots;                \
+  } while (0)
+#define MOE_RD(sub, FA, FB)                                                            \
+  do {                                                                                 \
+    const uint16_t* sa_ = ring + (wn ? sa1 : sa0) * kRBlk;                             \
+    const uint16_t* sb_ = ring + sb * kRBlk;                                           \
+    _Pragma("unroll") for (int i = 0; i < TN; ++i) {                                   \
+      const int r = i * 32 + (lane & 31);                                              \
+      FA[i] = *(const bf16x8*)(sa_ + r * kRS + swz128(r, 2 * (sub) + ch) * 8);         \
+    }                                                                                  \
+    _Pragma("unroll") for (int j = 0; j < TM; ++j) {                                   \
+      const int r = (wm & 1) * 64 + j * 32 + (lane & 31);                              \
+      FB[j] = *(const bf16x8*)(sb_ + r * kRS + swz128(r, 2 * (sub) + ch) * 8);         \
+    }                                                                                  \
+  } while (0)
+#define MOE_MM(FA, FB)                                                                 \
+  do {                                                                                 \
+    _Pragma("unroll") for (int i = 0; i < TN; ++i)                                     \
+    _Pragma("unroll") for (int j = 0; j < TM; ++j)                                     \
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[i], FB[j], acc[i][j], 0, 0, 0); \
+  } while (0)
+
+  // step 0 landed: the blocks of steps 1 and 2 may still be in flight
+  if (ns > 2) wait_vmcnt<12>(); else if (ns > 1) wait_vmcnt<8>(); else wait_vmcnt<0>();
+  lds_barrier();
+  MOE_SLOTS(0);
+  MOE_RD(0, f0a, f0b);
+  for (int j = 0; j < ns; ++j) {
+    MOE_RD(1, f1a, f1b);
+    MOE_MM(f0a, f0b);
+    MOE_RD(2, f0a, f0b);
+    MOE_MM(f1a, f1b);
+    MOE_RD(3, f1a, f1b);
+    MOE_MM(f0a, f0b);
+    if (j + 1 < ns) {
+      // step j+1 landed (only the weight half of step j+2 may be in flight),
+      // and this wave's reads of step j are done before its slots are refilled
+      if (j + 2 < ns) wait_vmcnt<4>(); else wait_vmcnt<0>();
+      wait_lgkmcnt0();
+      lds_barrier();
+      const int b0 = (4 * j) % kRSlots;
+      const int b1 = b0 + 1 < kRSlots ? b0 + 1 : b0 + 1 - kRSlots;
+      const int b2 = b0 + 2 < kRSlots ? b0 + 2 : b0 + 2 - kRSlots;
+      const int b3 = b0 + 3 < kRSlots ? b0 + 3 : b0 + 3 - kRSlots;
+      if (j + 2 < ns) {
+        issue(Q2{}, j + 2, b0);
+        issue(Q3{}, j + 2, b1);
+      }
+      if (j + 3 < ns) {
+        issue(Q0{}, j + 3, b2);
+        issue(Q1{}, j + 3, b3);
+      }
+      MOE_SLOTS(j + 1);
+      MOE_RD(0, f0a, f0b);
+    }
+    MOE_MM(f1a, f1b);
+  }
+#undef MOE_SLOTS
+#undef MOE_RD
+#undef MOE_MM
+
+  big_store<SILU>(acc, ring, sizeof(ring), wk, bias, out, part, N, wn, wm, lane, tid);
 }
 
 // Tail tiles: out = act(sum_p partial[p] + bias), partials summed in order of
 // their K-range, so the result does not depend on timing. kReduceSlices
 // blocks per tail tile, each over 32 rows; a thread owns 8 consecutive
-// features of 4 rows.
+// features of every 8th row of its slice.
 template <bool SILU>
-__global__ __launch_bounds__(256) void big_tail_reduce(
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_start,
-    const uint16_t* __restrict__ bias, const float* __restrict__ part, uint16_t* __restrict__ out,
-    int E, int N, int K, int ntiles) {
-  const BigSplit sp = big_split(tile_start, E, ntiles, K / kKS);
+__global__ __launch_bounds__(256) void big_tail_reduce(const BigHdr* __restrict__ hdr,
+                                                       const BigWork* __restrict__ work,
+                                                       const uint16_t* __restrict__ bias,
+                                                       const float* __restrict__ part,
+                                                       uint16_t* __restrict__ out, int N) {
+  const BigHdr sp = *hdr;
   const int tt = blockIdx.x / kReduceSlices, slice = blockIdx.x % kReduceSlices;
   if (tt >= sp.tail || sp.split < 2) return;
-  const int t = sp.full + tt;
-  const BigTile tile = big_tile(tile_start, offsets, E, ntiles, t);
+  const BigWork tile = work[sp.full + tt * sp.split];  // the tile's first K range
   const int nl = (threadIdx.x & 31) * 8;
   float bv[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u)
     bv[u] = bias ? bf16_to_f32(bias[(size_t)tile.e * N + tile.n0 + nl + u]) : 0.0f;
-  const float* base = part + (size_t)tt * sp.split * (kBigBM * kBigBN);
-  const int mend = min(tile.rows, (slice + 1) * (kBigBM / kReduceSlices));
-  for (int m = slice * (kBigBM / kReduceSlices) + (threadIdx.x >> 5); m < mend; m += 8) {
+  constexpr int BM = kBigBM, RS = BM / kReduceSlices;
+  const float* base = part + (size_t)tt * sp.split * (BM * kBigBN);
+  const int mend = min(tile.rows, (slice + 1) * RS);
+  for (int m = slice * RS + (threadIdx.x >> 5); m < mend; m += 8) {
     float v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) v[u] = 0.0f;
     for (int p = 0; p < sp.split; ++p) {
-      const float* src = base + (size_t)p * (kBigBM * kBigBN) + m * kBigBN + nl;
+      const float* src = base + (size_t)p * (BM * kBigBN) + m * kBigBN + nl;
       const f32x4 lo = *(const f32x4*)src, hi = *(const f32x4*)(src + 4);
       v[0] += lo[0]; v[1] += lo[1]; v[2] += lo[2]; v[3] += lo[3];
       v[4] += hi[0]; v[5] += hi[1]; v[6] += hi[2]; v[7] += hi[3];
@@ -511,8 +605,8 @@ __global__ __launch_bounds__(256) void big_tail_reduce(
     for (int q = 0; q < 4; ++q) {
       float a = v[2 * q] + bv[2 * q], c = v[2 * q + 1] + bv[2 * q + 1];
       if (SILU) {
-        a = silu(a);
-        c = silu(c);
+        a = silu_bf16(a);
+        c = silu_bf16(c);
       }
       o[q] = pack_bf16x2(a, c);
     }
@@ -611,7 +705,7 @@ __global__ __launch_bounds__(256) void decode_bf16(
         for (int g = 0; g < DG; ++g) {
           if (g < ng) {
             float v = wave_sum(acc[a][g]) + b;
-            if (SILU) v = silu(v);
+            if (SILU) v = silu_bf16(v);
             if (lane == 0 && na < N) out[(size_t)(r0 + g0 + g) * N + na] = (uint16_t)f32_to_bf16(v);
           }
         }
@@ -712,11 +806,31 @@ int launch_gemms_bf16(const uint16_t* x, const int32_t* sorted_token, const int3
 
 bool use_decode(long rows, int E) { return rows <= 4L * E && rows <= 1024; }
 
-// 256-row tiles when experts average at least 192 rows and both widths tile by 256.
-bool use_big(long rows, int E, int T, int k, int d, int h) {
-  (void)T;
-  (void)k;
+// 256 x 256 DMA-ring tiles when experts average at least 192 rows and both
+// widths tile by 256.
+bool use_ring(long rows, int E, int d, int h) {
   return rows >= 192L * E && (d % kBigBN) == 0 && (h % kBigBN) == 0;
+}
+
+int launch_ring(const uint16_t* x, const int32_t* sorted_token, const int32_t* offsets, void* plan,
+                const uint16_t* w1, const uint16_t* b1, const uint16_t* w2, const uint16_t* b2,
+                uint16_t* H, uint16_t* y, int E, int d, int h, int T, int k, long rows,
+                hipStream_t s) {
+  float* part = (float*)((unsigned char*)H + ffn_hidden_bytes(T, h, k));
+  const int g1 = ffn_big_grid(rows, E, h), g2 = ffn_big_grid(rows, E, d);
+  BigHdr* hdr = (BigHdr*)plan;
+  BigWork* list1 = (BigWork*)((unsigned char*)plan + 256);
+  BigWork* list2 = list1 + g1;
+  const dim3 gr(kTailSlots * kReduceSlices);
+  hipLaunchKernelGGL(big_plan, dim3(ceil_div(g1 + g2, kMaxE)), dim3(kMaxE), 0, s, offsets, E,
+                     h / kBigBN, d / kRS, g1, d / kBigBN, h / kRS, g2, hdr, list1, list2);
+  hipLaunchKernelGGL((gemm_bf16_ring<true, true>), dim3(g1), dim3(512), 0, s, x, sorted_token,
+                     list1, w1, b1, H, part, h, d);
+  hipLaunchKernelGGL((big_tail_reduce<true>), gr, dim3(256), 0, s, hdr, list1, b1, part, H, h);
+  hipLaunchKernelGGL((gemm_bf16_ring<false, false>), dim3(g2), dim3(512), 0, s, H, sorted_token,
+                     list2, w2, b2, y, part, d, h);
+  hipLaunchKernelGGL((big_tail_reduce<false>), gr, dim3(256), 0, s, hdr + 1, list2, b2, part, y, d);
+  return launch_status();
 }
 
 }  // namespace
@@ -736,10 +850,10 @@ extern "C" int moe_grouped_ffn(const void* x, int dtype, int T, int d, int h, in
   if (dtype == MOE_BF16 && ((d % 64) != 0 || (h % 64) != 0)) return MOE_ERR_UNSUPPORTED;
   if (rows == 0) return MOE_OK;
   if (!x || !offsets || !sorted_token || !w1 || !w2 || !y_perm) return MOE_ERR_INVALID;
-  if (!ws || ws_bytes < ffn_ws(T, h, E, k)) return MOE_ERR_WORKSPACE;
+  if (!ws || ws_bytes < ffn_ws(T, d, h, E, k)) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   int32_t* tile_start = (int32_t*)ws;
-  void* H = (unsigned char*)ws + ffn_tilemap_bytes(E);
+  void* H = (unsigned char*)ws + ffn_plan_bytes(T, d, h, E, k);
   const int nonempty = (int)(rows < E ? rows : E);
 
   if (dtype == MOE_F32) {
@@ -775,29 +889,10 @@ extern "C" int moe_grouped_ffn(const void* x, int dtype, int T, int d, int h, in
     return launch_status();
   }
 
-  if (use_big(rows, E, T, k, d, h)) {
-    const int mslots = ceil_div(rows, kBigBM) + nonempty;
-    float* part = (float*)((unsigned char*)H + ffn_hidden_bytes(T, h, k));
-    hipLaunchKernelGGL(build_tile_map, dim3(1), dim3(512), 0, s, offsets, E, kBigBM, tile_start);
-    const int nt1 = h / kBigBN, nt2 = d / kBigBN;
-    // blocks: every tile once, plus at most kTailSlots tail units
-    const int g1 = ceil_div((long)mslots * nt1 + kTailSlots, 8) * 8;
-    const int g2 = ceil_div((long)mslots * nt2 + kTailSlots, 8) * 8;
-    hipLaunchKernelGGL((gemm_bf16_big<true, true>), dim3(g1), dim3(kBigThreads), 0, s, xb,
-                       sorted_token,
-                       offsets, tile_start, (const uint16_t*)w1, (const uint16_t*)b1, (uint16_t*)H,
-                       part, E, h, d, nt1);
-    hipLaunchKernelGGL((big_tail_reduce<true>), dim3(kTailSlots * kReduceSlices), dim3(256), 0, s,
-                       offsets,
-                       tile_start, (const uint16_t*)b1, part, (uint16_t*)H, E, h, d, nt1);
-    hipLaunchKernelGGL((gemm_bf16_big<false, false>), dim3(g2), dim3(kBigThreads), 0, s,
-                       (const uint16_t*)H, sorted_token, offsets, tile_start, (const uint16_t*)w2,
-                       (const uint16_t*)b2, (uint16_t*)y_perm, part, E, d, h, nt2);
-    hipLaunchKernelGGL((big_tail_reduce<false>), dim3(kTailSlots * kReduceSlices), dim3(256), 0, s,
-                       offsets,
-                       tile_start, (const uint16_t*)b2, part, (uint16_t*)y_perm, E, d, h, nt2);
-    return launch_status();
-  }
+  if (use_ring(rows, E, d, h))
+    return launch_ring(xb, sorted_token, offsets, ws, (const uint16_t*)w1, (const uint16_t*)b1,
+                       (const uint16_t*)w2, (const uint16_t*)b2, (uint16_t*)H, (uint16_t*)y_perm,
+                       E, d, h, T, k, rows, s);
   const int mslots = ceil_div(rows, kBM) + nonempty;
   hipLaunchKernelGGL(build_tile_map, dim3(1), dim3(512), 0, s, offsets, E, kBM, tile_start);
   if ((d % 128) == 0 && (h % 128) == 0)

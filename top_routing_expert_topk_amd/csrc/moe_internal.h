@@ -37,6 +37,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// SiLU from the hardware exp2 and reciprocal (about 1e-7 relative error), for
+// results that are rounded to bf16 right after.
+__device__ __forceinline__ float silu_bf16(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
+}
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
   return (1ull << __lane_id()) - 1ull;
@@ -87,14 +92,30 @@ inline size_t permute_ws(int T, int k, int E) {
   long n = (long)T * k;
   return align_up((size_t)2 * E * permute_blocks(n) * sizeof(int32_t), 256);
 }
-// FFN: [tile map: 2*(E+1) int32][hidden H: T*k*h elements of 4 bytes max]
+// FFN: [plan: tile map (2*(E+1) int32) or the DMA-ring kernels' work lists]
+//      [hidden H: T*k*h elements of 4 bytes max]
 //      [tail partials: kTailSlots tiles of 256 x 256 fp32]
-constexpr int kTailSlots = 256;
-inline size_t ffn_tilemap_bytes(int E) { return align_up((size_t)2 * (E + 1) * sizeof(int32_t), 256); }
+constexpr int kBigBNTile = 256;  // weight rows per DMA-ring tile
+constexpr int kTailSlots = 256;  // DMA-ring blocks resident at once (one per CU)
+// Blocks of one DMA-ring GEMM launch (256 x 256 tiles over N output
+// features): every tile once plus at most kTailSlots split units, rounded to
+// the 8 XCDs.
+inline int ffn_big_grid(long rows, int E, int N) {
+  const long nonempty = rows < E ? rows : E;
+  const long mslots = (rows + 255) / 256 + nonempty;
+  return ceil_div(mslots * (N / kBigBNTile) + kTailSlots, 8) * 8;
+}
+constexpr int kWorkBytes = 32;  // one work-list entry
+inline size_t ffn_plan_bytes(int T, int d, int h, int E, int k) {
+  const long rows = (long)T * k;
+  const size_t tmap = align_up((size_t)2 * (E + 1) * sizeof(int32_t), 256);
+  const size_t lists = 256 + (size_t)(ffn_big_grid(rows, E, h) + ffn_big_grid(rows, E, d)) * kWorkBytes;
+  return align_up(tmap > lists ? tmap : lists, 256);
+}
 inline size_t ffn_hidden_bytes(int T, int h, int k) { return align_up((size_t)T * k * h * 4, 256); }
 inline size_t ffn_partial_bytes() { return (size_t)kTailSlots * 256 * 256 * sizeof(float); }
-inline size_t ffn_ws(int T, int h, int E, int k) {
-  return ffn_tilemap_bytes(E) + ffn_hidden_bytes(T, h, k) + ffn_partial_bytes();
+inline size_t ffn_ws(int T, int d, int h, int E, int k) {
+  return ffn_plan_bytes(T, d, h, E, k) + ffn_hidden_bytes(T, h, k) + ffn_partial_bytes();
 }
 
 }  // namespace moe

@@ -230,6 +230,8 @@ constexpr int kRBlk = 128 * kRS;     // bf16 elements per block (16 KB)
 constexpr int kRSlots = 10;
 constexpr int kMaxSplit = 8;         // K ranges per tail tile
 constexpr int kReduceSlices = 8;     // row slices per tail tile in the reduction
+constexpr int kGroupN = 4;           // weight-row tiles per group of the tile order
+constexpr int kRingWaves = 8;        // waves per 256 x 256 tile
 static_assert(kBigBN == 256, "tile");
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -282,7 +284,7 @@ __device__ __forceinline__ int find_le(const int* ts, int E, int v) {
 }
 
 // Work lists of both GEMMs of the FFN (N = nt * kBigBN features, nk K steps).
-// Tile order: expert-major; inside an expert, groups of 8 weight-row tiles,
+// Tile order: expert-major; inside an expert, groups of kGroupN weight-row tiles,
 // inside a group the expert's row blocks. Whole tiles are dealt to the XCDs
 // in contiguous ranges of that order (hardware block b runs on XCD b % 8), so
 // each XCD's L2 sees a few weight and row panels at a time.
@@ -341,10 +343,10 @@ __global__ __launch_bounds__(512) void big_plan(const int32_t* __restrict__ offs
     const int e = find_le(ts, E, t / nt);  // experts own nt * (ts[e+1] - ts[e]) tiles
     const int mt = ts[e + 1] - ts[e];
     const int l = t - ts[e] * nt;
-    const int g = l / (mt * 8);
-    const int gs = min(8, nt - g * 8);
-    const int l2 = l - g * mt * 8;
-    const int mi = l2 / gs, ni = g * 8 + l2 % gs;
+    const int g = l / (mt * kGroupN);
+    const int gs = min(kGroupN, nt - g * kGroupN);
+    const int l2 = l - g * mt * kGroupN;
+    const int mi = l2 / gs, ni = g * kGroupN + l2 % gs;
     w.e = e;
     w.row0 = offsets[e] + mi * kBigBM;
     w.rows = min(kBigBM, offsets[e + 1] - w.row0);
@@ -356,19 +358,19 @@ __global__ __launch_bounds__(512) void big_plan(const int32_t* __restrict__ offs
   list[b] = w;
 }
 
-// Epilogue of a 256 x 256 tile, each wave holding 128 x 64 of it as 4 x 2
-// 32x32 MFMA accumulators. A split tail tile stores its fp32 partial
+// Epilogue of a 256 x 256 tile, each of NW waves holding 128 x (32 TM) of it
+// as 4 x TM 32x32 MFMA accumulators. A split tail tile stores its fp32 partial
 // [256 rows][256 features] for big_tail_reduce; a whole tile adds the bias,
 // applies SiLU if asked, rounds to bf16 into LDS (ot, the idle ring), and
 // leaves with 16-byte stores of whole rows: 32 lanes write one 512-byte row.
 // LDS rows are padded by 16 bytes so the 32 rows a wave writes at one feature
 // offset spread over the banks.
-template <bool SILU>
-__device__ __forceinline__ void big_store(f32x16 (&acc)[4][2], uint16_t* ot, size_t ot_bytes,
+template <int NW, int TM, bool SILU>
+__device__ __forceinline__ void big_store(f32x16 (&acc)[4][TM], uint16_t* ot, size_t ot_bytes,
                                           const BigWork& wk, const uint16_t* __restrict__ bias,
                                           uint16_t* __restrict__ out, float* __restrict__ part,
                                           int N, int wn, int wm, int lane, int tid) {
-  constexpr int BM = kBigBM, BN = kBigBN, NW = 8, TN = 4, TM = 2, WTN = 128, WTM = 64;
+  constexpr int BM = kBigBM, BN = kBigBN, TN = 4, WTN = 128, WTM = 32 * TM;
   const int ch = lane >> 5;
   if (wk.unit >= 0) {
     float* pp = part + (size_t)wk.unit * (BM * BN);
@@ -429,13 +431,18 @@ __device__ __forceinline__ void big_store(f32x16 (&acc)[4][2], uint16_t* ot, siz
   }
 }
 
-template <bool GATHER, bool SILU>
-__global__ __launch_bounds__(512) void gemm_bf16_ring(
+template <int NW, bool GATHER, bool SILU>
+__global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ sorted_token,
     const BigWork* __restrict__ work, const uint16_t* __restrict__ w,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, float* __restrict__ part, int N,
     int K) {
-  constexpr int BM = kBigBM, BN = kBigBN, TN = 4, TM = 2, WM = 4;
+  constexpr int BM = kBigBM, BN = kBigBN;
+  constexpr int WM = NW / 2;          // waves along the permuted rows (2 along the weight rows)
+  constexpr int TN = 4, TM = 8 / WM;  // 32x32 MFMA tiles per wave
+  constexpr int WTM = 32 * TM;        // permuted rows per wave
+  constexpr int IPB = 16 / NW;        // DMA instructions per wave per 16 KB block
+  static_assert(NW == 4 || NW == 8, "waves");
   __shared__ __align__(1024) uint16_t ring[kRSlots * kRBlk];
   static_assert((size_t)BM * (BN + 8) * 2 <= sizeof(ring), "output tile must fit the ring");
 
@@ -446,28 +453,34 @@ __global__ __launch_bounds__(512) void gemm_bf16_ring(
   const int wn = wave / WM, wm = wave % WM;
 
   // part q of a step: 0/1 weight rows 0-127 / 128-255, 2/3 permuted rows 0-127 /
-  // 128-255; each wave moves row groups (i * 8 + wave) * 8 .. +7, i = 0, 1
-  const uint16_t* src[4][2];
+  // 128-255; each wave moves row groups (i * NW + wave) * 8 .. +7, i < IPB.
+  // Weight rows are one per-lane base plus a uniform row offset; activation
+  // rows are gathered, kept as 32-bit element offsets (R * K < 2^31 is
+  // checked on the host). The swizzle depends on r only through (r >> 1) & 7,
+  // which the uniform offsets (multiples of 8 rows) leave unchanged.
+  const int r0 = wave * 8 + (lane >> 3);
+  const int c0 = swz128(r0, lane & 7) * 8;
+  const uint16_t* wbase = w + ((size_t)e * N + n0 + r0) * K + c0;
+  uint32_t boff[2][IPB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = (i * 8 + wave) * 8 + (lane >> 3);
-    const int c = swz128(r, lane & 7) * 8;
+  for (int q = 0; q < 2; ++q)
 #pragma unroll
-    for (int q = 0; q < 2; ++q) src[q][i] = w + ((size_t)e * N + n0 + q * 128 + r) * K + c;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int pr = q * 128 + r;
+    for (int i = 0; i < IPB; ++i) {
+      const int pr = q * 128 + i * NW * 8 + r0;
       const int rr = row0 + (pr < rows ? pr : rows - 1);
-      const size_t tok = GATHER ? (size_t)sorted_token[rr] : (size_t)rr;
-      src[2 + q][i] = act + tok * K + c;
+      const uint32_t tok = GATHER ? (uint32_t)sorted_token[rr] : (uint32_t)rr;
+      boff[q][i] = tok * (uint32_t)K + c0;
     }
-  }
   auto issue = [&](auto qc, int step, int slot) {
     constexpr int q = decltype(qc)::value;
     const int koff = (kbeg + step) * kRS;
     uint16_t* dst = ring + slot * kRBlk;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(src[q][i] + koff, dst + (i * 8 + wave) * 8 * kRS);
+    for (int i = 0; i < IPB; ++i) {
+      const uint16_t* g = q < 2 ? wbase + (size_t)(q * 128 + i * NW * 8) * K + koff
+                                : act + boff[q & 1][i] + koff;
+      dma16(g, dst + (i * NW + wave) * 8 * kRS);
+    }
   };
   using Q0 = std::integral_constant<int, 0>;
   using Q1 = std::integral_constant<int, 1>;
@@ -496,26 +509,27 @@ __global__ __launch_bounds__(512) void gemm_bf16_ring(
   }
 
   const int ch = lane >> 5;
+  const int bq = (wm * WTM) >> 7;      // the permuted-row block this wave reads
+  const int br = (wm * WTM) & 127;     // its first row inside that block
   bf16x8 f0a[TN], f0b[TM], f1a[TN], f1b[TM];
-  int sa0, sa1, sb;  // slots of the current step's weight halves and permuted half
-#define MOE_SLOTS(step)                                   \
-  do {                                                    \
-    const int b_ = (4 * (step)) % kRSlots;                \
-    sa0 = b_;                                             \
-    sa1 = b_ + 1 < kRSlots ? b_ + 1 : b_ + 1 - kRSlots;   \
-    const int q_ = b_ + 2 + (wm >> 1);                    \
-    sb = q_ < kRSlots ? q_ : q_ - kRSlots;                \
+  int sa, sb;  // slots of this wave's weight block and permuted-row block in the current step
+#define MOE_SLOTS(step)                                    \
+  do {                                                     \
+    const int b_ = (4 * (step)) % kRSlots;                 \
+    const int a_ = b_ + wn, c_ = b_ + 2 + bq;              \
+    sa = a_ < kRSlots ? a_ : a_ - kRSlots;                 \
+    sb = c_ < kRSlots ? c_ : c_ - kRSlots;                 \
   } while (0)
 #define MOE_RD(sub, FA, FB)                                                            \
   do {                                                                                 \
-    const uint16_t* sa_ = ring + (wn ? sa1 : sa0) * kRBlk;                             \
+    const uint16_t* sa_ = ring + sa * kRBlk;                                           \
     const uint16_t* sb_ = ring + sb * kRBlk;                                           \
     _Pragma("unroll") for (int i = 0; i < TN; ++i) {                                   \
       const int r = i * 32 + (lane & 31);                                              \
       FA[i] = *(const bf16x8*)(sa_ + r * kRS + swz128(r, 2 * (sub) + ch) * 8);         \
     }                                                                                  \
     _Pragma("unroll") for (int j = 0; j < TM; ++j) {                                   \
-      const int r = (wm & 1) * 64 + j * 32 + (lane & 31);                              \
+      const int r = br + j * 32 + (lane & 31);                                         \
       FB[j] = *(const bf16x8*)(sb_ + r * kRS + swz128(r, 2 * (sub) + ch) * 8);         \
     }                                                                                  \
   } while (0)
@@ -527,7 +541,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_ring(
   } while (0)
 
   // step 0 landed: the blocks of steps 1 and 2 may still be in flight
-  if (ns > 2) wait_vmcnt<12>(); else if (ns > 1) wait_vmcnt<8>(); else wait_vmcnt<0>();
+  if (ns > 2) wait_vmcnt<6 * IPB>(); else if (ns > 1) wait_vmcnt<4 * IPB>(); else wait_vmcnt<0>();
   lds_barrier();
   MOE_SLOTS(0);
   MOE_RD(0, f0a, f0b);
@@ -541,7 +555,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_ring(
     if (j + 1 < ns) {
       // step j+1 landed (only the weight half of step j+2 may be in flight),
       // and this wave's reads of step j are done before its slots are refilled
-      if (j + 2 < ns) wait_vmcnt<4>(); else wait_vmcnt<0>();
+      if (j + 2 < ns) wait_vmcnt<2 * IPB>(); else wait_vmcnt<0>();
       wait_lgkmcnt0();
       lds_barrier();
       const int b0 = (4 * j) % kRSlots;
@@ -565,7 +579,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_ring(
 #undef MOE_RD
 #undef MOE_MM
 
-  big_store<SILU>(acc, ring, sizeof(ring), wk, bias, out, part, N, wn, wm, lane, tid);
+  big_store<NW, TM, SILU>(acc, ring, sizeof(ring), wk, bias, out, part, N, wn, wm, lane, tid);
 }
 
 // Tail tiles: out = act(sum_p partial[p] + bias), partials summed in order of
@@ -806,10 +820,11 @@ int launch_gemms_bf16(const uint16_t* x, const int32_t* sorted_token, const int3
 
 bool use_decode(long rows, int E) { return rows <= 4L * E && rows <= 1024; }
 
-// 256 x 256 DMA-ring tiles when experts average at least 192 rows and both
-// widths tile by 256.
-bool use_ring(long rows, int E, int d, int h) {
-  return rows >= 192L * E && (d % kBigBN) == 0 && (h % kBigBN) == 0;
+// 256 x 256 DMA-ring tiles when experts average at least 192 rows, both
+// widths tile by 256 and activation element offsets fit 31 bits.
+bool use_ring(long rows, int E, int T, int d, int h) {
+  return rows >= 192L * E && (d % kBigBN) == 0 && (h % kBigBN) == 0 &&
+         (long)T * d < (1L << 31) && rows * h < (1L << 31);
 }
 
 int launch_ring(const uint16_t* x, const int32_t* sorted_token, const int32_t* offsets, void* plan,
@@ -824,11 +839,11 @@ int launch_ring(const uint16_t* x, const int32_t* sorted_token, const int32_t* o
   const dim3 gr(kTailSlots * kReduceSlices);
   hipLaunchKernelGGL(big_plan, dim3(ceil_div(g1 + g2, kMaxE)), dim3(kMaxE), 0, s, offsets, E,
                      h / kBigBN, d / kRS, g1, d / kBigBN, h / kRS, g2, hdr, list1, list2);
-  hipLaunchKernelGGL((gemm_bf16_ring<true, true>), dim3(g1), dim3(512), 0, s, x, sorted_token,
-                     list1, w1, b1, H, part, h, d);
+  hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, true, true>), dim3(g1), dim3(kRingWaves * 64), 0, s,
+                     x, sorted_token, list1, w1, b1, H, part, h, d);
   hipLaunchKernelGGL((big_tail_reduce<true>), gr, dim3(256), 0, s, hdr, list1, b1, part, H, h);
-  hipLaunchKernelGGL((gemm_bf16_ring<false, false>), dim3(g2), dim3(512), 0, s, H, sorted_token,
-                     list2, w2, b2, y, part, d, h);
+  hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, false, false>), dim3(g2), dim3(kRingWaves * 64),
+                     0, s, H, sorted_token, list2, w2, b2, y, part, d, h);
   hipLaunchKernelGGL((big_tail_reduce<false>), gr, dim3(256), 0, s, hdr + 1, list2, b2, part, y, d);
   return launch_status();
 }
@@ -889,7 +904,7 @@ extern "C" int moe_grouped_ffn(const void* x, int dtype, int T, int d, int h, in
     return launch_status();
   }
 
-  if (use_ring(rows, E, d, h))
+  if (use_ring(rows, E, T, d, h))
     return launch_ring(xb, sorted_token, offsets, ws, (const uint16_t*)w1, (const uint16_t*)b1,
                        (const uint16_t*)w2, (const uint16_t*)b2, (uint16_t*)H, (uint16_t*)y_perm,
                        E, d, h, T, k, rows, s);

@@ -40,6 +40,31 @@ def test_workspace_sizes():
     assert N.moe_workspace_size(N.MOE_OP_FFN, 10, 0, 10, 4, 2) == 0
 
 
+def _ceil(a, b):
+    return -(-a // b)
+
+
+@pytest.mark.parametrize("T,d,h,E,k", [(4096, 4096, 14336, 8, 2), (8192, 7168, 2048, 256, 8),
+                                       (8192, 768, 3072, 128, 1), (32, 4096, 4096, 64, 2),
+                                       (256, 128, 256, 8, 2), (300, 512, 1024, 8, 2),
+                                       (1, 256, 256, 512, 16), (6000, 512, 1536, 64, 1)])
+def test_ffn_workspace_holds_the_tile_path_layout(T, d, h, E, k):
+    """The FFN workspace must hold, for 128- and 256-row tiles alike: two
+    32-byte work entries per tile and per split unit of both GEMMs, a token
+    table of every row block (padded to the tile height), the hidden
+    activations (4 bytes per element at most) and 256 fp32 256x256 partial
+    tiles. Restated here from the layout, independently of the C++ sizing."""
+    rows = T * k
+    need_plan = 0
+    for bm in (128, 256):
+        mslots = _ceil(rows, bm) + min(rows, E)
+        lists = 256 + sum(_ceil(mslots * (n // 256) + 256, 8) * 8 for n in (h, d)) * 32
+        table = mslots * bm * 4
+        need_plan = max(need_plan, _ceil(lists, 256) * 256 + _ceil(table, 256) * 256)
+    need = need_plan + rows * h * 4 + 256 * 256 * 256 * 4
+    assert N.moe_workspace_size(N.MOE_OP_FFN, T, d, h, E, k) >= need
+
+
 def _router(**kw):
     a = dict(x=BAD, dtype=1, T=64, d=64, w=BAD, gb=None, E=8, k=2, renorm=1, lg=None, idx=BAD,
              gate=BAD, ps=None, ws=BAD, wsb=1 << 20, s=None)

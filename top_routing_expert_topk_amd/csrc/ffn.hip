@@ -9,13 +9,16 @@
 //   build_tile_map  prefix sum of ceil(kept_e / BM) -> tile_start[E+1], so a
 //                   gemm_bf16 / gemm_f32 block finds its (expert, row block)
 //                   with no host read
-//   big_plan        per-block work lists (tile, K range) of both GEMMs for
-//                   the 256 x 256 tile path, built from offsets on the device
+//   big_plan        work lists (tile, K range) of both GEMMs of the DMA-ring
+//                   paths and the token table of their row blocks, built
+//                   from offsets on the device
 //   gemm_bf16_ring  256 x 256 MFMA tiles fed by a global->LDS DMA ring of
 //                   64-column steps; tail tiles split along K
+//   gemm_bf16_pring persistent 256 x 128 variant for experts of fewer rows:
+//                   one block per CU, the ring running across its tiles
 //   big_tail_reduce sums the K-range partials of split tail tiles in order
 //   gemm_bf16       128 x 128 MFMA tiles, LDS double-buffered 64-deep K
-//                   steps, for experts with fewer rows
+//                   steps, for widths that are not multiples of 256
 //   decode_bf16     weight-streaming path for few rows per expert: each
 //                   touched expert's weights are read once per 4 rows, rows
 //                   of untouched experts cost one offsets read
@@ -262,7 +265,7 @@ struct alignas(16) BigWork {
   int n0;          // first output feature
   int kbeg, kend;  // K range in kRS-column steps
   int unit;        // fp32 partial slot of a split tail tile, -1 for a whole tile
-  int pad;
+  int ms;          // row block (index into the token table of the tile's rows)
 };
 static_assert(sizeof(BigWork) == kWorkBytes, "work entry size");
 // Per launch: tiles = whole tiles + tail tiles; the `full` first tiles (a
@@ -283,21 +286,27 @@ __device__ __forceinline__ int find_le(const int* ts, int E, int v) {
   return lo;
 }
 
-// Work lists of both GEMMs of the FFN (N = nt * kBigBN features, nk K steps).
-// Tile order: expert-major; inside an expert, groups of kGroupN weight-row tiles,
-// inside a group the expert's row blocks. Whole tiles are dealt to the XCDs
-// in contiguous ranges of that order (hardware block b runs on XCD b % 8), so
-// each XCD's L2 sees a few weight and row panels at a time.
+// Work lists of both GEMMs of the FFN (N = nt * kBigBN features, nk K steps,
+// BM permuted rows per tile). Tile order: expert-major; inside an expert,
+// groups of kGroupN weight-row tiles, inside a group the expert's row blocks.
+// REMAP: entry b is the work of hardware block b, whole tiles dealt to the
+// XCDs in contiguous ranges of that order (block b runs on XCD b % 8), so each
+// XCD's L2 sees a few weight and row panels at a time. Otherwise entries are
+// in that order (whole tiles, then the K ranges of the tail tiles) and the
+// persistent kernel deals them out itself.
+template <int BM, bool REMAP>
 __global__ __launch_bounds__(512) void big_plan(const int32_t* __restrict__ offsets, int E,
                                                 int nt1, int nk1, int g1, int nt2, int nk2,
                                                 int g2, BigHdr* __restrict__ hdr,
                                                 BigWork* __restrict__ list1,
-                                                BigWork* __restrict__ list2) {
+                                                BigWork* __restrict__ list2,
+                                                const int32_t* __restrict__ sorted_token,
+                                                int32_t* __restrict__ tok_tab) {
   __shared__ int sc[2][kMaxE];
   __shared__ int ts[kMaxE + 1];
   const int x = threadIdx.x;  // blockDim == kMaxE
   int cur = 0;
-  sc[0][x] = x < E ? (offsets[x + 1] - offsets[x] + kBigBM - 1) / kBigBM : 0;
+  sc[0][x] = x < E ? (offsets[x + 1] - offsets[x] + BM - 1) / BM : 0;
   __syncthreads();
   for (int off = 1; off < kMaxE; off <<= 1) {
     const int v = sc[cur][x] + (x >= off ? sc[cur][x - off] : 0);
@@ -310,6 +319,18 @@ __global__ __launch_bounds__(512) void big_plan(const int32_t* __restrict__ offs
   __syncthreads();
 
   const int i = blockIdx.x * kMaxE + x;
+  if (i >= g1 + g2) {
+    // token table: entry ms * BM + r = the token of row r of row block ms,
+    // rows past the block's last one repeating it
+    if (!tok_tab) return;
+    const int j = i - g1 - g2, ms = j / BM, r = j % BM;
+    if (ms >= ts[E]) return;
+    const int e = find_le(ts, E, ms);
+    const int row0 = offsets[e] + (ms - ts[e]) * BM;
+    const int rows = min(BM, offsets[e + 1] - row0);
+    tok_tab[j] = sorted_token[row0 + (r < rows ? r : rows - 1)];
+    return;
+  }
   const bool second = i >= g1;
   const int b = second ? i - g1 : i;
   if (second && b >= g2) return;
@@ -328,11 +349,11 @@ __global__ __launch_bounds__(512) void big_plan(const int32_t* __restrict__ offs
   w.e = -1;
   w.row0 = w.rows = w.n0 = w.kbeg = w.kend = 0;
   w.unit = -1;
-  w.pad = 0;
+  w.ms = 0;
   int t = -1, p = 0, split = 1;
   if (b < sp.full) {
     const int per = sp.full >> 3;
-    t = (b & 7) * per + (b >> 3);
+    t = REMAP ? (b & 7) * per + (b >> 3) : b;
   } else if (b - sp.full < sp.tail * sp.split) {
     const int u = b - sp.full;
     split = sp.split;
@@ -348,12 +369,13 @@ __global__ __launch_bounds__(512) void big_plan(const int32_t* __restrict__ offs
     const int l2 = l - g * mt * kGroupN;
     const int mi = l2 / gs, ni = g * kGroupN + l2 % gs;
     w.e = e;
-    w.row0 = offsets[e] + mi * kBigBM;
-    w.rows = min(kBigBM, offsets[e + 1] - w.row0);
+    w.row0 = offsets[e] + mi * BM;
+    w.rows = min(BM, offsets[e + 1] - w.row0);
     w.n0 = ni * kBigBN;
     w.kbeg = p * nk / split;
     w.kend = (p + 1) * nk / split;
     w.unit = split > 1 ? (t - sp.full) * split + p : -1;
+    w.ms = ts[e] + mi;
   }
   list[b] = w;
 }
@@ -582,11 +604,289 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
   big_store<NW, TM, SILU>(acc, ring, sizeof(ring), wk, bias, out, part, N, wn, wm, lane, tid);
 }
 
+// ------------------------------------------------ persistent DMA-ring GEMM --
+// One block per CU walks its share of the launch's tiles with a single DMA
+// ring that runs across tile boundaries: the first steps of the next tile are
+// already in flight while the current one finishes, and each finished tile
+// leaves straight from the accumulators (8-byte stores of 4 features of one
+// row; the ring holds the next tile's data), so no tile pays a pipeline fill
+// or drain. Whole tiles are dealt in the tile order, each XCD's 32 blocks
+// taking one contiguous range 32 tiles at a time; the K ranges of split tail
+// tiles follow, one per block.
+// Used for BM = 128 (experts of fewer rows, where the weight stream from HBM
+// is the bound): 3 blocks per step (two weight halves, one row block), 9
+// slots, so two more steps are in flight; waves 4 x 2 of 64 x 64. The BM =
+// 256 shape (gemm_bf16_ring's tile and waves, 4 blocks per step, 10 slots)
+// measures slower than gemm_bf16_ring, whose LDS-staged epilogue writes
+// whole rows: there the MFMA work per tile dwarfs the pipeline fill.
+template <int BM>
+struct PRing {
+  static constexpr int P = 2 + BM / 128;        // 16 KB blocks per 64-column step
+  static constexpr int S = BM == 256 ? 10 : 9;  // ring slots
+  static constexpr int AHEAD = S - 2 * P;       // blocks past step j+1 in flight at the end of step j
+  static constexpr int WN = BM == 256 ? 2 : 4;  // waves along the weight rows
+  static constexpr int WM = 8 / WN;
+  static constexpr int WTN = kBigBN / WN, WTM = BM / WM;
+  static constexpr int TN = WTN / 32, TM = WTM / 32;
+  static constexpr int NBQ = BM / 128;          // permuted-row blocks per step
+};
+
+typedef const __attribute__((address_space(4))) uint32_t cu32;  // scalar-cache reads
+
+// A work-list entry read through the scalar cache (its index is uniform).
+struct WorkS {
+  int e, row0, rows, n0, kbeg, kend, unit, ms;
+};
+__device__ __forceinline__ WorkS load_work(const BigWork* __restrict__ units, int idx) {
+  cu32* p = (cu32*)(units + idx);
+  WorkS u;
+  u.e = __builtin_amdgcn_readfirstlane((int)p[0]);
+  u.row0 = __builtin_amdgcn_readfirstlane((int)p[1]);
+  u.rows = __builtin_amdgcn_readfirstlane((int)p[2]);
+  u.n0 = __builtin_amdgcn_readfirstlane((int)p[3]);
+  u.kbeg = __builtin_amdgcn_readfirstlane((int)p[4]);
+  u.kend = __builtin_amdgcn_readfirstlane((int)p[5]);
+  u.unit = __builtin_amdgcn_readfirstlane((int)p[6]);
+  u.ms = __builtin_amdgcn_readfirstlane((int)p[7]);
+  return u;
+}
+
+template <int BM, bool GATHER, bool SILU>
+__global__ __launch_bounds__(512) void gemm_bf16_pring(
+    const uint16_t* __restrict__ act, const int32_t* __restrict__ tok_tab,
+    const BigHdr* __restrict__ hdr, const BigWork* __restrict__ units,
+    const uint16_t* __restrict__ w, const uint16_t* __restrict__ bias,
+    uint16_t* __restrict__ out, float* __restrict__ part, int N, int K) {
+  using C = PRing<BM>;
+  constexpr int P = C::P, S = C::S, AHEAD = C::AHEAD, NBQ = C::NBQ;
+  constexpr int TN = C::TN, TM = C::TM, WM = C::WM, WTN = C::WTN, WTM = C::WTM;
+  constexpr int NW = 8, IPB = 2;
+  __shared__ __align__(1024) uint16_t ring[S * kRBlk];
+
+  cu32* hp = (cu32*)hdr;
+  const int full = __builtin_amdgcn_readfirstlane((int)hp[0]);
+  const int tail = __builtin_amdgcn_readfirstlane((int)hp[1]);
+  const int split = __builtin_amdgcn_readfirstlane((int)hp[2]);
+  const int b = blockIdx.x;  // gridDim.x == kTailSlots, one block per CU
+  const int nf = full / kTailSlots;
+  const bool has_tail = b < tail * split;
+  const int nu = nf + (has_tail ? 1 : 0);
+  if (nu == 0) return;
+  const int per_xcd = full >> 3;
+  // unit i of this block: whole tiles walk the XCD's contiguous range 32 at a
+  // time, then this block's K range of a split tail tile
+  auto unit_of = [&](int i) { return i < nf ? (b & 7) * per_xcd + (b >> 3) + 32 * i : full + b; };
+  const int nsf = K / kRS;
+  int tlen = 0;
+  if (has_tail) {
+    const WorkS t = load_work(units, full + b);
+    tlen = t.kend - t.kbeg;
+  }
+  const int total = nf * nsf + tlen;  // 64-column steps of this block
+  const int nblk = total * P;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave / WM, wm = wave % WM;
+  const int r0 = wave * 8 + (lane >> 3);
+  const int c0 = swz128(r0, lane & 7) * 8;
+
+  // ---- issue side: the unit whose blocks are being issued.
+  // Activation rows are 32-bit element offsets. Gathered rows take their
+  // token from the token table with scalar loads (8 consecutive rows per
+  // wave and DMA instruction, lane l using row l/8), so no vector load sits
+  // in the DMA queue that the ring's vmcnt waits count.
+  uint32_t bo[NBQ][IPB];
+  auto row_offsets = [&](int row0, int rows, int ms) {
+#pragma unroll
+    for (int q = 0; q < NBQ; ++q)
+#pragma unroll
+      for (int i = 0; i < IPB; ++i) {
+        uint32_t tok;
+        if (GATHER) {
+          cu32* tp = (cu32*)(tok_tab + (size_t)ms * BM + q * 128 + i * 64 + wave * 8);
+          uint32_t t8[8];
+#pragma unroll
+          for (int v = 0; v < 8; ++v) t8[v] = tp[v];
+          const int sel = lane >> 3;
+          tok = t8[0];
+#pragma unroll
+          for (int v = 1; v < 8; ++v) tok = sel == v ? t8[v] : tok;
+        } else {
+          const int pr = q * 128 + i * 64 + r0;
+          tok = (uint32_t)(row0 + (pr < rows ? pr : rows - 1));
+        }
+        bo[q][i] = tok * (uint32_t)K + c0;
+      }
+  };
+  int iu = 0, ig0 = 0, ilen, ikbeg;
+  const uint16_t* wb;
+  auto enter_unit = [&](int i) {
+    const WorkS u = load_work(units, unit_of(i));
+    ilen = u.kend - u.kbeg;
+    ikbeg = u.kbeg;
+    wb = w + ((size_t)u.e * N + u.n0 + r0) * K + c0;
+    row_offsets(u.row0, u.rows, u.ms);
+  };
+  enter_unit(0);
+  auto issue_block = [&](int bi) {
+    const int g = bi / P, q = bi - g * P;
+    if (g == ig0 + ilen) {  // first block of the next unit
+      ++iu;
+      ig0 += ilen;
+      enter_unit(iu);
+    }
+    const int koff = (ikbeg + g - ig0) * kRS;
+    uint16_t* dst = ring + (bi % S) * kRBlk;
+#pragma unroll
+    for (int i = 0; i < IPB; ++i) {
+      const uint16_t* src;
+      if (q < 2) src = wb + (size_t)(q * 128 + i * 64) * K + koff;
+      else src = act + (q == 2 ? bo[0][i] : bo[NBQ - 1][i]) + koff;
+      dma16(src, dst + (i * NW + wave) * 8 * kRS);
+    }
+  };
+
+  // ---- compute side
+  f32x16 acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) acc[i][j] = f32x16{};
+
+#pragma unroll
+  for (int bi = 0; bi < S; ++bi)
+    if (bi < nblk) issue_block(bi);
+
+  const int ch = lane >> 5;
+  const int aq = (wn * WTN) >> 7, ar = (wn * WTN) & 127;  // this wave's weight block, first row
+  const int bq = (wm * WTM) >> 7, br = (wm * WTM) & 127;  // its permuted-row block, first row
+  bf16x8 f0a[TN], f0b[TM], f1a[TN], f1b[TM];
+  int sa, sb;
+#define MOE_SLOTS(step)                                    \
+  do {                                                     \
+    const int b_ = (P * (step)) % S;                       \
+    const int a_ = b_ + aq, c_ = b_ + 2 + bq;              \
+    sa = a_ < S ? a_ : a_ - S;                             \
+    sb = c_ < S ? c_ : c_ - S;                             \
+  } while (0)
+#define MOE_RD(sub, FA, FB)                                                            \
+  do {                                                                                 \
+    const uint16_t* sa_ = ring + sa * kRBlk;                                           \
+    const uint16_t* sb_ = ring + sb * kRBlk;                                           \
+    _Pragma("unroll") for (int i = 0; i < TN; ++i) {                                   \
+      const int r = ar + i * 32 + (lane & 31);                                         \
+      FA[i] = *(const bf16x8*)(sa_ + r * kRS + swz128(r, 2 * (sub) + ch) * 8);         \
+    }                                                                                  \
+    _Pragma("unroll") for (int j = 0; j < TM; ++j) {                                   \
+      const int r = br + j * 32 + (lane & 31);                                         \
+      FB[j] = *(const bf16x8*)(sb_ + r * kRS + swz128(r, 2 * (sub) + ch) * 8);         \
+    }                                                                                  \
+  } while (0)
+#define MOE_MM(FA, FB)                                                                 \
+  do {                                                                                 \
+    _Pragma("unroll") for (int i = 0; i < TN; ++i)                                     \
+    _Pragma("unroll") for (int j = 0; j < TM; ++j)                                     \
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[i], FB[j], acc[i][j], 0, 0, 0); \
+  } while (0)
+
+  // step 0 landed: the blocks of the next steps may still be in flight
+  if (nblk >= S) wait_vmcnt<(S - P) * IPB>(); else wait_vmcnt<0>();
+  lds_barrier();
+  MOE_SLOTS(0);
+  MOE_RD(0, f0a, f0b);
+  int cu = 0, cend = nf > 0 ? nsf : tlen;  // compute unit, its end step
+  for (int g = 0; g < total; ++g) {
+    MOE_RD(1, f1a, f1b);
+    MOE_MM(f0a, f0b);
+    MOE_RD(2, f0a, f0b);
+    MOE_MM(f1a, f1b);
+    MOE_RD(3, f1a, f1b);
+    MOE_MM(f0a, f0b);
+    if (g + 1 < total) {
+      // step g+1 landed (only later blocks may be in flight), and this wave's
+      // reads of step g are done before its slots are refilled
+      const int newest = min(S + P * g, nblk) - 1, need = P * (g + 2) - 1;
+      if (newest - need >= AHEAD) wait_vmcnt<AHEAD * IPB>(); else wait_vmcnt<0>();
+      wait_lgkmcnt0();
+      lds_barrier();
+#pragma unroll
+      for (int u = 0; u < P; ++u)
+        if (S + P * g + u < nblk) issue_block(S + P * g + u);
+      MOE_SLOTS(g + 1);
+      MOE_RD(0, f0a, f0b);
+    }
+    MOE_MM(f1a, f1b);
+    if (g + 1 == cend) {
+      // the unit is done: partial or finished tile straight from the accumulators
+      const WorkS uc = load_work(units, unit_of(cu));
+      if (uc.unit >= 0) {
+        float* pp = part + (size_t)uc.unit * (BM * kBigBN);
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int nl = wn * WTN + i * 32 + 8 * q + 4 * ch;
+#pragma unroll
+            for (int j = 0; j < TM; ++j) {
+              const int m = wm * WTM + j * 32 + (lane & 31);
+              *(f32x4*)(pp + m * kBigBN + nl) = f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                                      acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            }
+          }
+      } else {
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int nb = wn * WTN + i * 32 + 8 * q;  // uniform: 8 features, 4 per half-wave
+            float bv[4] = {0.f, 0.f, 0.f, 0.f};
+            if (bias) {
+              cu32* bp = (cu32*)(bias + (size_t)uc.e * N + uc.n0 + nb);
+              const uint32_t p0 = bp[0], p1 = bp[1], p2 = bp[2], p3 = bp[3];
+              const uint32_t lo = ch ? p2 : p0, hi = ch ? p3 : p1;
+              bv[0] = bf16lo(lo);
+              bv[1] = bf16hi(lo);
+              bv[2] = bf16lo(hi);
+              bv[3] = bf16hi(hi);
+            }
+            const int nl = nb + 4 * ch;
+#pragma unroll
+            for (int j = 0; j < TM; ++j) {
+              const int m = wm * WTM + j * 32 + (lane & 31);
+              float v[4];
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                v[t] = acc[i][j][4 * q + t] + bv[t];
+                if (SILU) v[t] = silu_bf16(v[t]);
+              }
+              if (m < uc.rows) {
+                u32x2 o;
+                o[0] = pack_bf16x2(v[0], v[1]);
+                o[1] = pack_bf16x2(v[2], v[3]);
+                *(u32x2*)(out + (size_t)(uc.row0 + m) * N + uc.n0 + nl) = o;
+              }
+            }
+          }
+      }
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j) acc[i][j] = f32x16{};
+      ++cu;
+      cend += cu < nf ? nsf : tlen;
+    }
+  }
+#undef MOE_SLOTS
+#undef MOE_RD
+#undef MOE_MM
+}
+
 // Tail tiles: out = act(sum_p partial[p] + bias), partials summed in order of
 // their K-range, so the result does not depend on timing. kReduceSlices
-// blocks per tail tile, each over 32 rows; a thread owns 8 consecutive
+// blocks per tail tile, each over BM/8 rows; a thread owns 8 consecutive
 // features of every 8th row of its slice.
-template <bool SILU>
+template <int BM, bool SILU>
 __global__ __launch_bounds__(256) void big_tail_reduce(const BigHdr* __restrict__ hdr,
                                                        const BigWork* __restrict__ work,
                                                        const uint16_t* __restrict__ bias,
@@ -601,7 +901,7 @@ __global__ __launch_bounds__(256) void big_tail_reduce(const BigHdr* __restrict_
 #pragma unroll
   for (int u = 0; u < 8; ++u)
     bv[u] = bias ? bf16_to_f32(bias[(size_t)tile.e * N + tile.n0 + nl + u]) : 0.0f;
-  constexpr int BM = kBigBM, RS = BM / kReduceSlices;
+  constexpr int RS = BM / kReduceSlices;
   const float* base = part + (size_t)tt * sp.split * (BM * kBigBN);
   const int mend = min(tile.rows, (slice + 1) * RS);
   for (int m = slice * RS + (threadIdx.x >> 5); m < mend; m += 8) {
@@ -822,9 +1122,16 @@ bool use_decode(long rows, int E) { return rows <= 4L * E && rows <= 1024; }
 
 // 256 x 256 DMA-ring tiles when experts average at least 192 rows, both
 // widths tile by 256 and activation element offsets fit 31 bits.
+bool ring_shapes(long rows, int T, int d, int h) {
+  return (d % kBigBN) == 0 && (h % kBigBN) == 0 && (long)T * d < (1L << 31) &&
+         rows * h < (1L << 31);
+}
 bool use_ring(long rows, int E, int T, int d, int h) {
-  return rows >= 192L * E && (d % kBigBN) == 0 && (h % kBigBN) == 0 &&
-         (long)T * d < (1L << 31) && rows * h < (1L << 31);
+  return rows >= 192L * E && ring_shapes(rows, T, d, h);
+}
+// 128-row persistent tiles for experts of fewer rows (above the decode range).
+bool use_ring128(long rows, int E, int T, int d, int h) {
+  return rows < 192L * E && ring_shapes(rows, T, d, h);
 }
 
 int launch_ring(const uint16_t* x, const int32_t* sorted_token, const int32_t* offsets, void* plan,
@@ -832,19 +1139,54 @@ int launch_ring(const uint16_t* x, const int32_t* sorted_token, const int32_t* o
                 uint16_t* H, uint16_t* y, int E, int d, int h, int T, int k, long rows,
                 hipStream_t s) {
   float* part = (float*)((unsigned char*)H + ffn_hidden_bytes(T, h, k));
-  const int g1 = ffn_big_grid(rows, E, h), g2 = ffn_big_grid(rows, E, d);
+  const int g1 = ffn_big_grid(rows, E, h, kBigBM), g2 = ffn_big_grid(rows, E, d, kBigBM);
   BigHdr* hdr = (BigHdr*)plan;
   BigWork* list1 = (BigWork*)((unsigned char*)plan + 256);
   BigWork* list2 = list1 + g1;
   const dim3 gr(kTailSlots * kReduceSlices);
-  hipLaunchKernelGGL(big_plan, dim3(ceil_div(g1 + g2, kMaxE)), dim3(kMaxE), 0, s, offsets, E,
-                     h / kBigBN, d / kRS, g1, d / kBigBN, h / kRS, g2, hdr, list1, list2);
+  hipLaunchKernelGGL((big_plan<kBigBM, true>), dim3(ceil_div(g1 + g2, kMaxE)), dim3(kMaxE), 0, s,
+                     offsets, E, h / kBigBN, d / kRS, g1, d / kBigBN, h / kRS, g2, hdr, list1, list2,
+                     sorted_token, (int32_t*)nullptr);
   hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, true, true>), dim3(g1), dim3(kRingWaves * 64), 0, s,
                      x, sorted_token, list1, w1, b1, H, part, h, d);
-  hipLaunchKernelGGL((big_tail_reduce<true>), gr, dim3(256), 0, s, hdr, list1, b1, part, H, h);
+  hipLaunchKernelGGL((big_tail_reduce<kBigBM, true>), gr, dim3(256), 0, s, hdr, list1, b1, part, H,
+                     h);
   hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, false, false>), dim3(g2), dim3(kRingWaves * 64),
                      0, s, H, sorted_token, list2, w2, b2, y, part, d, h);
-  hipLaunchKernelGGL((big_tail_reduce<false>), gr, dim3(256), 0, s, hdr + 1, list2, b2, part, y, d);
+  hipLaunchKernelGGL((big_tail_reduce<kBigBM, false>), gr, dim3(256), 0, s, hdr + 1, list2, b2, part,
+                     y, d);
+  return launch_status();
+}
+
+// Persistent DMA-ring GEMMs with BM-row tiles: one block per CU.
+template <int BM>
+int launch_pring(const uint16_t* x, const int32_t* sorted_token, const int32_t* offsets,
+                 void* plan, const uint16_t* w1, const uint16_t* b1, const uint16_t* w2,
+                 const uint16_t* b2, uint16_t* H, uint16_t* y, int E, int d, int h, int T, int k,
+                 long rows, hipStream_t s) {
+  float* part = (float*)((unsigned char*)H + ffn_hidden_bytes(T, h, k));
+  const int g1 = ffn_big_grid(rows, E, h, BM), g2 = ffn_big_grid(rows, E, d, BM);
+  BigHdr* hdr = (BigHdr*)plan;
+  BigWork* list1 = (BigWork*)((unsigned char*)plan + 256);
+  BigWork* list2 = list1 + g1;
+  const size_t tok_off = align_up(ffn_lists_bytes(rows, E, d, h), 256);
+  int32_t* tok = (int32_t*)((unsigned char*)plan + tok_off);
+  const long ntok = ffn_tok_entries(rows, E, BM);
+  // the plan region must hold the lists and the table (H follows it)
+  if ((size_t)(g1 + g2) * kWorkBytes + 256 > tok_off ||
+      tok_off + (size_t)ntok * sizeof(int32_t) > ffn_plan_bytes(T, d, h, E, k))
+    return MOE_ERR_WORKSPACE;
+  const dim3 gr(kTailSlots * kReduceSlices);
+  hipLaunchKernelGGL((big_plan<BM, false>), dim3(ceil_div(g1 + g2 + ntok, kMaxE)), dim3(kMaxE), 0,
+                     s, offsets, E, h / kBigBN, d / kRS, g1, d / kBigBN, h / kRS, g2, hdr, list1,
+                     list2, sorted_token, tok);
+  hipLaunchKernelGGL((gemm_bf16_pring<BM, true, true>), dim3(kTailSlots), dim3(512), 0, s, x, tok,
+                     hdr, list1, w1, b1, H, part, h, d);
+  hipLaunchKernelGGL((big_tail_reduce<BM, true>), gr, dim3(256), 0, s, hdr, list1, b1, part, H, h);
+  hipLaunchKernelGGL((gemm_bf16_pring<BM, false, false>), dim3(kTailSlots), dim3(512), 0, s, H,
+                     (const int32_t*)nullptr, hdr + 1, list2, w2, b2, y, part, d, h);
+  hipLaunchKernelGGL((big_tail_reduce<BM, false>), gr, dim3(256), 0, s, hdr + 1, list2, b2, part, y,
+                     d);
   return launch_status();
 }
 
@@ -908,6 +1250,10 @@ extern "C" int moe_grouped_ffn(const void* x, int dtype, int T, int d, int h, in
     return launch_ring(xb, sorted_token, offsets, ws, (const uint16_t*)w1, (const uint16_t*)b1,
                        (const uint16_t*)w2, (const uint16_t*)b2, (uint16_t*)H, (uint16_t*)y_perm,
                        E, d, h, T, k, rows, s);
+  if (use_ring128(rows, E, T, d, h))
+    return launch_pring<128>(xb, sorted_token, offsets, ws, (const uint16_t*)w1,
+                             (const uint16_t*)b1, (const uint16_t*)w2, (const uint16_t*)b2,
+                             (uint16_t*)H, (uint16_t*)y_perm, E, d, h, T, k, rows, s);
   const int mslots = ceil_div(rows, kBM) + nonempty;
   hipLaunchKernelGGL(build_tile_map, dim3(1), dim3(512), 0, s, offsets, E, kBM, tile_start);
   if ((d % 128) == 0 && (h % 128) == 0)

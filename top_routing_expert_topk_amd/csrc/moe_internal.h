@@ -97,20 +97,35 @@ inline size_t permute_ws(int T, int k, int E) {
 //      [tail partials: kTailSlots tiles of 256 x 256 fp32]
 constexpr int kBigBNTile = 256;  // weight rows per DMA-ring tile
 constexpr int kTailSlots = 256;  // DMA-ring blocks resident at once (one per CU)
-// Blocks of one DMA-ring GEMM launch (256 x 256 tiles over N output
+// Work-list entries of one DMA-ring GEMM launch (256 x BM tiles over N output
 // features): every tile once plus at most kTailSlots split units, rounded to
 // the 8 XCDs.
-inline int ffn_big_grid(long rows, int E, int N) {
+inline int ffn_big_grid(long rows, int E, int N, int BM) {
   const long nonempty = rows < E ? rows : E;
-  const long mslots = (rows + 255) / 256 + nonempty;
+  const long mslots = (rows + BM - 1) / BM + nonempty;
   return ceil_div(mslots * (N / kBigBNTile) + kTailSlots, 8) * 8;
 }
 constexpr int kWorkBytes = 32;  // one work-list entry
+// Plan region of the DMA-ring path: [2 headers][work lists of both GEMMs]
+// [token table: the token of each row of each BM-row block, padded rows
+// repeating the block's last]. The lists are longest for 128-row tiles; the
+// table's padding grows with BM, so it is sized for the larger of the two.
+inline long ffn_tok_entries(long rows, int E, int BM) {
+  const long nonempty = rows < E ? rows : E;
+  return ((rows + BM - 1) / BM + nonempty) * BM;
+}
+inline size_t ffn_lists_bytes(long rows, int E, int d, int h) {
+  return 256 + (size_t)(ffn_big_grid(rows, E, h, 128) + ffn_big_grid(rows, E, d, 128)) * kWorkBytes;
+}
+inline size_t ffn_tok_bytes(long rows, int E) {
+  const long a = ffn_tok_entries(rows, E, 128), b = ffn_tok_entries(rows, E, 256);
+  return align_up((size_t)(a > b ? a : b) * sizeof(int32_t), 256);
+}
 inline size_t ffn_plan_bytes(int T, int d, int h, int E, int k) {
   const long rows = (long)T * k;
   const size_t tmap = align_up((size_t)2 * (E + 1) * sizeof(int32_t), 256);
-  const size_t lists = 256 + (size_t)(ffn_big_grid(rows, E, h) + ffn_big_grid(rows, E, d)) * kWorkBytes;
-  return align_up(tmap > lists ? tmap : lists, 256);
+  const size_t ring = align_up(ffn_lists_bytes(rows, E, d, h), 256) + ffn_tok_bytes(rows, E);
+  return align_up(tmap > ring ? tmap : ring, 256);
 }
 inline size_t ffn_hidden_bytes(int T, int h, int k) { return align_up((size_t)T * k * h * 4, 256); }
 inline size_t ffn_partial_bytes() { return (size_t)kTailSlots * 256 * 256 * sizeof(float); }

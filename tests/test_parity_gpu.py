@@ -62,9 +62,13 @@ SMALL = {
                                                    E=4),
     # 256 x 256 tiles: whole rounds of tiles plus a split tail
     "big_full_tail": CFG["mixtral_prefill"].with_(name="big_full_tail", T=4096, d=512, h=2048),
-    # experts of ~150 rows: 128 x 128 tiles, two row tiles per expert
+    # 256 x 256 tiles over experts of ~256 rows: many last row blocks hold a
+    # few rows, whose idle waves and activation DMAs are skipped
+    "big_ragged": CFG["deepseek_v3"].with_(name="big_ragged", T=2048, d=512, h=512, E=64),
+    # experts of ~150 rows: persistent 256 x 128 tiles, two row blocks per expert
     "mid_rows_multi": CFG["mixtral_prefill"].with_(name="mid_rows_multi", T=600, d=512, h=1536),
-    # 64 experts under a capacity of 80 rows: 128 x 128 tiles, capacity drops
+    # 64 experts under a capacity of 80 rows: persistent 256 x 128 tiles, a
+    # split tail, capacity drops
     "mid_rows_capacity": CFG["switch_top1_cap"].with_(name="mid_rows_capacity", T=6000, d=512,
                                                        h=1536, E=64),
 }

@@ -245,6 +245,21 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// At most BASE + n vector memory operations outstanding, n in 0..8 (uniform).
+template <int BASE>
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<BASE>(); break;
+    case 1: wait_vmcnt<BASE + 1>(); break;
+    case 2: wait_vmcnt<BASE + 2>(); break;
+    case 3: wait_vmcnt<BASE + 3>(); break;
+    case 4: wait_vmcnt<BASE + 4>(); break;
+    case 5: wait_vmcnt<BASE + 5>(); break;
+    case 6: wait_vmcnt<BASE + 6>(); break;
+    case 7: wait_vmcnt<BASE + 7>(); break;
+    default: wait_vmcnt<BASE + 8>(); break;
+  }
+}
 // Workgroup barrier that the compiler may not move memory accesses across.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
@@ -471,8 +486,21 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
   const BigWork wk = work[blockIdx.x];
   if (wk.e < 0) return;
   const int e = wk.e, row0 = wk.row0, rows = wk.rows, n0 = wk.n0, kbeg = wk.kbeg;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wn = wave / WM, wm = wave % WM;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Waves alternate along the weight rows, so the waves holding the first
+  // permuted rows sit on different SIMDs (wave w runs on SIMD w % 4).
+  const int wn = wave % 2, wm = wave / 2;
+  // Tiles with few rows (an expert's last row block) skip the work of rows
+  // past the last: a wave whose permuted rows are all past it issues no
+  // MFMAs, and DMA instructions whose 8 rows are all past it are not issued.
+  const bool active = wm * WTM < rows;
+  auto b_live = [&](int q, int i) { return (q - 2) * 128 + i * NW * 8 + wave * 8 < rows; };
+  int nbi = 0;  // activation DMA instructions this wave issues per step
+#pragma unroll
+  for (int q = 2; q < 4; ++q)
+#pragma unroll
+    for (int i = 0; i < IPB; ++i) nbi += b_live(q, i) ? 1 : 0;
 
   // part q of a step: 0/1 weight rows 0-127 / 128-255, 2/3 permuted rows 0-127 /
   // 128-255; each wave moves row groups (i * NW + wave) * 8 .. +7, i < IPB.
@@ -499,6 +527,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
     uint16_t* dst = ring + slot * kRBlk;
 #pragma unroll
     for (int i = 0; i < IPB; ++i) {
+      if (q >= 2 && !b_live(q, i)) continue;
       const uint16_t* g = q < 2 ? wbase + (size_t)(q * 128 + i * NW * 8) * K + koff
                                 : act + boff[q & 1][i] + koff;
       dma16(g, dst + (i * NW + wave) * 8 * kRS);
@@ -543,7 +572,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
     sb = c_ < kRSlots ? c_ : c_ - kRSlots;                 \
   } while (0)
 #define MOE_RD(sub, FA, FB)                                                            \
-  do {                                                                                 \
+  if constexpr (ACT) {                                                                 \
     const uint16_t* sa_ = ring + sa * kRBlk;                                           \
     const uint16_t* sb_ = ring + sb * kRBlk;                                           \
     _Pragma("unroll") for (int i = 0; i < TN; ++i) {                                   \
@@ -554,17 +583,24 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
       const int r = br + j * 32 + (lane & 31);                                         \
       FB[j] = *(const bf16x8*)(sb_ + r * kRS + swz128(r, 2 * (sub) + ch) * 8);         \
     }                                                                                  \
-  } while (0)
+  }
 #define MOE_MM(FA, FB)                                                                 \
   do {                                                                                 \
+    if constexpr (ACT)                                                                 \
     _Pragma("unroll") for (int i = 0; i < TN; ++i)                                     \
     _Pragma("unroll") for (int j = 0; j < TM; ++j)                                     \
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[i], FB[j], acc[i][j], 0, 0, 0); \
   } while (0)
 
-  // step 0 landed: the blocks of steps 1 and 2 may still be in flight
-  if (ns > 2) wait_vmcnt<6 * IPB>(); else if (ns > 1) wait_vmcnt<4 * IPB>(); else wait_vmcnt<0>();
+  // step 0 landed: the blocks of steps 1 and 2 may still be in flight, i.e.
+  // this wave's DMAs of step 1 (both weight halves and its nbi activation
+  // instructions) and of the weight half of step 2
+  if (ns > 2) wait_vmcnt_le<4 * IPB>(nbi); else if (ns > 1) wait_vmcnt_le<2 * IPB>(nbi); else wait_vmcnt<0>();
   lds_barrier();
+  // the loop twice over: with MFMAs for waves that own live rows, without
+  // for the others (barriers and DMA issue are the same)
+  auto main_loop = [&](auto act_c) {
+  constexpr bool ACT = decltype(act_c)::value;
   MOE_SLOTS(0);
   MOE_RD(0, f0a, f0b);
   for (int j = 0; j < ns; ++j) {
@@ -597,6 +633,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
     }
     MOE_MM(f1a, f1b);
   }
+  };
+  if (active) main_loop(std::true_type{});
+  else main_loop(std::false_type{});
 #undef MOE_SLOTS
 #undef MOE_RD
 #undef MOE_MM

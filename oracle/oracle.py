@@ -208,3 +208,95 @@ def moe_forward(x, w_gate, w1, b1, w2, b2, k: int, renorm: bool, capacity: int =
     return dict(logits=lg, idx=idx, gate=gate, prob_sum=prob_sum, counts=counts,
                 offsets=offsets, dest_row=dest, sorted_token=sorted_token, f=f, P=P,
                 loss=loss, out=out, tokens=tokens)
+
+
+# ------------------------------------------------------- Expert Choice ----
+# The capacity-factor section of the routing-principles page
+# ("Expert Choice路由策略与容量因子调优") reverses the direction of selection:
+# each expert takes a fixed number of tokens, capacity = tokens / E * factor,
+# and tokens no expert takes pass through the residual. Readings taken where
+# the page is silent: an expert ranks tokens by the router probability
+# p[t,e] = softmax over experts of token t's logits (the gate equation's
+# softmax without the top-k mask); ties go to the lower token index; the
+# gate of a chosen (token, expert) pair is p[t,e] itself; a token's output
+# sums its experts' contributions in ascending expert order.
+
+def ec_scores(lg) -> np.ndarray:
+    """p[t,e] = exp(l[t,e] - max_e l[t,:]) / sum_e exp(l[t,e] - max_e l[t,:]), in double."""
+    lg = np.asarray(lg, dtype=np.float64)
+    z = np.exp(lg - lg.max(axis=1, keepdims=True))
+    return z / z.sum(axis=1, keepdims=True)
+
+
+def expert_choice(score, C: int):
+    """Each expert takes the min(C, T) tokens of highest score[t, e] (ties: lower t).
+
+    Returns (offsets [E+1], sorted_token [E*Cc] with each expert's tokens in
+    ascending order, dest_row [T, E] = row of (t, e) or -1, gate [T, E] =
+    score of a chosen pair or 0), Cc = min(C, T).
+    """
+    score = np.asarray(score)
+    T, E = score.shape
+    Cc = max(0, min(int(C), T))
+    offsets = np.arange(E + 1, dtype=np.int32) * Cc
+    sorted_token = np.empty(E * Cc, np.int32)
+    dest = np.full((T, E), -1, np.int32)
+    gate = np.zeros((T, E), np.float64)
+    t_idx = np.arange(T)
+    for e in range(E):
+        # primary key: score descending; secondary: token index ascending
+        order = np.lexsort((t_idx, -score[:, e].astype(np.float64)))
+        chosen = np.sort(order[:Cc])
+        sorted_token[e * Cc:(e + 1) * Cc] = chosen
+        dest[chosen, e] = e * Cc + np.arange(Cc)
+        gate[chosen, e] = score[chosen, e]
+    return offsets, sorted_token, dest, gate
+
+
+def moe_forward_ec(x, w_gate, w1, b1, w2, b2, C: int, gate_bias=None, residual: bool = False,
+                   lg=None, score=None, tokens=None, expert_weights=None):
+    """Whole Expert Choice layer: logits -> scores -> per-expert selection ->
+    experts (expert-major) -> combine.
+
+    ``lg``: logits (same-logits mode); computed in double when None.
+    ``score``: selection scores and gates to use verbatim (same-score mode);
+    the double-precision softmax of ``lg`` when None.
+    ``tokens``: evaluate the expert FFN and combine for these tokens only.
+    ``expert_weights``: optional callable e -> (w1e, b1e, w2e, b2e).
+    """
+    T, d = x.shape
+    E = w_gate.shape[0]
+    if lg is None:
+        lg = logits(x, w_gate, gate_bias)
+    p = ec_scores(lg)
+    sel = p if score is None else np.asarray(score, dtype=np.float64)
+    offsets, sorted_token, dest, gate = expert_choice(sel, C)
+    tokens = np.arange(T, dtype=np.int32) if tokens is None else np.asarray(tokens, np.int32)
+    pos = np.full(T, -1, np.int64)
+    pos[tokens] = np.arange(tokens.size)
+    if residual:
+        xr = x.astype(np.float64) if x.dtype == np.float32 else _bf16_to_f64(x)
+        out = xr[tokens].copy()
+    else:
+        out = np.zeros((tokens.size, d), np.float64)
+    for e in range(E):  # ascending expert order for every token
+        rows = sorted_token[offsets[e]:offsets[e + 1]]
+        mine = rows[pos[rows] >= 0]
+        if mine.size == 0:
+            continue
+        if expert_weights is not None:
+            w1e, b1e, w2e, b2e = expert_weights(e)
+        else:
+            w1e, w2e = w1[e], w2[e]
+            b1e = None if b1 is None else b1[e]
+            b2e = None if b2 is None else b2[e]
+        y = expert_rows(x, mine, w1e, b1e, w2e, b2e)
+        out[pos[mine]] += gate[mine, e][:, None] * y
+    return dict(logits=lg, p=p, score=sel, offsets=offsets, sorted_token=sorted_token,
+                dest_row=dest, gate=gate, out=out, tokens=tokens)
+
+
+def _bf16_to_f64(a) -> np.ndarray:
+    """Exact widening of bf16 bit patterns (uint16) to double."""
+    a = np.ascontiguousarray(a, dtype=np.uint16)
+    return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)

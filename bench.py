@@ -28,9 +28,10 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "routed tokens/sec per MoE layer fwd (bf16, 1 GPU) + % of MFMA/HBM roofline"
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CALLS = ("router", "permute", "ffn", "combine", "aux")
+EC_CALLS = ("router", "choice", "ffn", "combine")  # Expert Choice layer
 # tokens whose expert FFN the CPU baseline evaluates (routing always covers all T)
 CPU_SAMPLE = {"tiny_fp32": 256, "mixtral_prefill": 2048, "switch_top1_cap": 8192, "decode": 32,
-              "deepseek_v3": 512}
+              "deepseek_v3": 512, "switch_expert_choice": 2048}
 
 
 def parse():
@@ -100,13 +101,19 @@ def cpu_baseline(cfg, inp, sample_n):
     def fetch(e):  # host copies are made before the clock starts
         return host_w[e]
     # which experts the sample needs: route once untimed to know what to copy to the host
-    lg0 = orc.logits(x[toks], wg, gb)
-    need = set(orc.route(lg0, cfg.k, cfg.renorm)[0].ravel().tolist())
     lg_all = orc.logits(x, wg, gb)
-    need |= set(orc.route(lg_all, cfg.k, cfg.renorm)[0][toks].ravel().tolist())
+    if cfg.routing == "expert_choice":
+        _, _, dest, _ = orc.expert_choice(orc.ec_scores(lg_all), cfg.capacity)
+        need = set(np.nonzero((dest[toks] >= 0).any(axis=0))[0].tolist())
+    else:
+        lg0 = orc.logits(x[toks], wg, gb)
+        need = set(orc.route(lg0, cfg.k, cfg.renorm)[0].ravel().tolist())
+        need |= set(orc.route(lg_all, cfg.k, cfg.renorm)[0][toks].ravel().tolist())
     for e in sorted(need):
         host_w[e] = tuple(None if inp[n] is None else mi.to_host_array(inp[n][e])
                           for n in ("w1", "b1", "w2", "b2"))
+    if cfg.routing == "expert_choice":
+        return _cpu_baseline_ec(cfg, inp, x, wg, gb, toks, host_w, fetch)
     t0 = time.perf_counter()
     lg = orc.logits(x, wg, gb)
     t1 = time.perf_counter()
@@ -127,6 +134,30 @@ def cpu_baseline(cfg, inp, sample_n):
                        f"FFN + combine on {toks.size} seeded tokens ({t_ffn:.2f} s), extrapolated "
                        f"to {cfg.T}; double precision, {threads} threads on {cpu_model()}"),
             "extrapolated": toks.size < cfg.T, "seconds": t3 - t0}
+
+
+def _cpu_baseline_ec(cfg, inp, x, wg, gb, toks, host_w, fetch):
+    """Expert Choice layer on the oracle: logits, scores and every expert's
+    selection on all T tokens; expert FFN + combine on the token sample."""
+    from oracle import oracle as orc
+    t0 = time.perf_counter()
+    lg = orc.logits(x, wg, gb)
+    ta = time.perf_counter()
+    orc.expert_choice(orc.ec_scores(lg), cfg.capacity)
+    t1 = time.perf_counter()
+    orc.moe_forward_ec(x, wg, None, None, None, None, cfg.capacity, gate_bias=gb,
+                       residual=cfg.residual, lg=lg, tokens=toks, expert_weights=fetch)
+    t2 = time.perf_counter()
+    t_route = t1 - t0
+    t_ffn = max((t2 - t1) - (t1 - ta), 1e-9)  # moe_forward_ec redoes scores and selection
+    full = t_route + t_ffn * cfg.T / toks.size
+    threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    return {"value": cfg.T / full, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"logits, scores and Expert Choice selection on all {cfg.T} tokens "
+                       f"({t_route:.2f} s); expert FFN + combine on {toks.size} seeded tokens "
+                       f"({t_ffn:.2f} s), extrapolated to {cfg.T}; double precision, {threads} "
+                       f"threads on {cpu_model()}"),
+            "extrapolated": toks.size < cfg.T, "seconds": t2 - t0}
 
 
 def main():
@@ -150,12 +181,39 @@ def main():
     inp = mi.make_inputs(cfg, dev)
     torch.cuda.synchronize()
     T, d, h, E, k = cfg.T, cfg.d, cfg.h, cfg.E, cfg.k
-    bufs = moe.MoEBuffers(T, d, h, E, k, cfg.torch_dtype, dev)
+    ec = cfg.routing == "expert_choice"
+    calls = EC_CALLS if ec else CALLS
+    if ec:
+        bufs = moe.ECBuffers(T, d, h, E, cfg.capacity, cfg.torch_dtype, dev)
+    else:
+        bufs = moe.MoEBuffers(T, d, h, E, k, cfg.torch_dtype, dev)
     stream = torch.cuda.Stream(dev)  # default priority
     x = inp["x"]
     resid = x if cfg.residual else None
 
+    def step_ec(ev=None):
+        b = bufs
+        if ev is not None:
+            ev[0].record(stream)
+        N.moe_router_topk(x, inp["w_gate"], inp["gate_bias"], E, 1, True, b.logits, b.topk_idx,
+                          b.topk_gate, None, b.ws_router, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        N.moe_expert_choice(b.logits, T, E, cfg.capacity, b.scores, b.offsets, b.sorted_token,
+                            b.dest_row, b.gate, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        N.moe_grouped_ffn(x, T, d, h, E, b.k_ffn, b.offsets, b.sorted_token, inp["w1"],
+                          inp["b1"], inp["w2"], inp["b2"], b.y_perm, b.ws_ffn, stream)
+        if ev is not None:
+            ev[3].record(stream)
+        N.moe_combine(b.y_perm, b.dest_row, b.gate, T, E, d, resid, b.out, stream)
+        if ev is not None:
+            ev[4].record(stream)
+
     def step(ev=None):
+        if ec:
+            return step_ec(ev)
         b = bufs
         if ev is not None:
             ev[0].record(stream)
@@ -181,25 +239,28 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+              for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_call = {c: [] for c in CALLS}
-    step_ms = []
+    nc = len(calls)
+    per_call = {c: [] for c in calls}
     for ev in events:
-        for j, c in enumerate(CALLS):
+        for j, c in enumerate(calls):
             per_call[c].append(ev[j].elapsed_time(ev[j + 1]))
-        step_ms.append(ev[0].elapsed_time(ev[5]))
     ms = {c: float(np.mean(v)) for c, v in per_call.items()}
     # whole timed region (gaps between steps included) over K steps
-    ms_step = events[0][0].elapsed_time(events[-1][5]) / args.steps
+    ms_step = events[0][0].elapsed_time(events[-1][nc]) / args.steps
 
     R = int(bufs.offsets[-1])
-    counts = bufs.counts.cpu().numpy()
-    touched = int((np.minimum(counts, cfg.capacity if cfg.capacity >= 0 else counts) > 0).sum())
+    if ec:
+        touched = E if R > 0 else 0
+    else:
+        counts = bufs.counts.cpu().numpy()
+        touched = int((np.minimum(counts, cfg.capacity if cfg.capacity >= 0 else counts) > 0).sum())
     ebytes = 2 if cfg.dtype == "bf16" else 4
     ffn_flop = 4.0 * R * d * h
     expert_bytes = touched * (2 * d * h + d + h) * ebytes
@@ -229,7 +290,8 @@ def main():
         "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": cfg.name, "T": T, "d": d, "h": h, "E": E, "k": k,
                    "renorm": bool(cfg.renorm), "capacity": cfg.capacity,
-                   "residual": bool(cfg.residual), "parallelism": "single GPU"},
+                   "residual": bool(cfg.residual), "routing": cfg.routing,
+                   "parallelism": "single GPU"},
         "roofline": roof,
         "kept_rows_per_s": R / (ms_step * 1e-3),
         "ms_per_call": ms,

@@ -119,8 +119,9 @@ int moe_permute(const int32_t *topk_idx, int T, int k, int E, int capacity, int3
  * x [T][d]; w1 [E][h][d]; b1 [E][h] or NULL; w2 [E][d][h]; b2 [E][d] or
  * NULL; y_perm [T*k][d] (rows 0..R-1 written, R = offsets[E] read on the
  * device). fp32 accumulation; with MOE_BF16, H and y_perm are rounded to
- * bf16. offsets and sorted_token must come from moe_permute with the same
- * T, k, E. The kernel choice depends only on T*k (no device-to-host read).
+ * bf16. offsets and sorted_token come from moe_permute with the same T, k, E,
+ * or from moe_expert_choice with k = ceil(E * min(C, T) / T) (any k with
+ * R <= T*k). The kernel choice depends only on T*k (no device-to-host read).
  * bf16 needs d and h to be multiples of 64. Workspace holds H:
  * moe_workspace_size(MOE_OP_FFN, ...).
  */
@@ -139,11 +140,34 @@ int moe_grouped_ffn(const void *x, int dtype, int T, int d, int h, int E, int k,
  * slot dropped gets residual[t] (or 0). y_perm [T*k][d] and residual [T][d]
  * (or NULL) are `dtype`; dest_row [T][k]; topk_gate [T][k] fp32; out [T][d]
  * is `out_dtype`: MOE_F32 (always allowed; keeps the fp32 sum unrounded) or
- * MOE_BF16 (only with dtype MOE_BF16).
+ * MOE_BF16 (only with dtype MOE_BF16). 1 <= k <= 512: with the slots of
+ * moe_expert_choice (k = E) a token sums its choosing experts in ascending
+ * expert order.
  */
 int moe_combine(const void *y_perm, int dtype, const int32_t *dest_row, const float *topk_gate,
                 int T, int k, int d, const void *residual, void *out, int out_dtype,
                 moe_stream_t stream);
+
+/*
+ * Expert Choice routing   [Routing page, "Expert Choice路由策略与容量因子调优":
+ * experts choose tokens, each expert takes the same number of them,
+ * capacity = tokens / E * capacity_factor, tokens no expert takes keep only
+ * the residual]:
+ *   scores[e][t] = softmax over e' of logits[t][e']   (fp32, written)
+ *   expert e takes the Cc = min(C, T) tokens with the largest scores[e][t]
+ *   (ties: lower t), in ascending token order as rows [e*Cc, (e+1)*Cc):
+ *     offsets[e] = e*Cc,  sorted_token[e*Cc + i] = i-th chosen token,
+ *     dest_row[t][e] = its row or -1,  gate[t][e] = scores[e][t] or 0.
+ * logits [T][E] fp32 (e.g. moe_router_topk's logits_out); scores [E][T]
+ * fp32; offsets [E+1]; sorted_token [E*Cc]; dest_row [T][E] int32; gate
+ * [T][E] fp32. The outputs feed moe_grouped_ffn (k = ceil(E*Cc/T)) and
+ * moe_combine (k = E). C >= 0 is the caller's capacity (the page's
+ * tokens/E*factor, rounded by the caller). Status 1 for negative sizes or
+ * missing buffers, 2 for E > 512 or T*E >= 2^31. No workspace.
+ */
+int moe_expert_choice(const float *logits, int T, int E, int C, float *scores, int32_t *offsets,
+                      int32_t *sorted_token, int32_t *dest_row, float *gate,
+                      moe_stream_t stream);
 
 /*
  * Load-balancing auxiliary loss   [Routing page, load_balancing_loss]:

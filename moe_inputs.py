@@ -43,6 +43,7 @@ class MoEConfig:
     residual: bool = False      # combine adds x (dropped tokens pass through)
     zipf_gate_bias: bool = False
     expert_bias: bool = True
+    routing: str = "topk"       # "topk" (tokens choose k experts) or "expert_choice"
 
     @property
     def torch_dtype(self):
@@ -66,6 +67,11 @@ CONFIGS = {
     "decode": MoEConfig("decode", 3, T=32, d=4096, h=4096, E=64, k=2),
     # DeepSeek-V3-shaped routed experts: 256 experts, top-8, d=7168, hidden 2048
     "deepseek_v3": MoEConfig("deepseek_v3", 4, T=8192, d=7168, h=2048, E=256, k=8),
+    # Expert Choice on the Switch-shaped layer (same inputs, same Zipf-skewed
+    # router): each of the 128 experts takes its 80 highest-probability tokens
+    "switch_expert_choice": MoEConfig("switch_expert_choice", 2, T=8192, d=768, h=3072, E=128,
+                                      k=1, renorm=False, capacity=80, residual=True,
+                                      zipf_gate_bias=True, routing="expert_choice"),
 }
 
 CONFIG_ORDER = ["tiny_fp32", "mixtral_prefill", "switch_top1_cap", "decode", "deepseek_v3"]

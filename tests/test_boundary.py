@@ -122,12 +122,29 @@ def test_combine_and_aux_reject_bad_arguments():
     assert L.moe_combine(BAD, 2, BAD, BAD, 4, 2, 64, None, BAD, 0, None) == 1
     assert L.moe_combine(BAD, 1, BAD, BAD, 4, 2, 64, None, BAD, 5, None) == 1
     assert L.moe_combine(BAD, 0, BAD, BAD, 4, 2, 64, None, BAD, 1, None) == 2
-    assert L.moe_combine(BAD, 1, BAD, BAD, 4, 17, 64, None, BAD, 0, None) == 2
+    assert L.moe_combine(BAD, 1, BAD, BAD, 4, 513, 64, None, BAD, 0, None) == 2
     assert L.moe_combine(BAD, 1, BAD, BAD, 4, 2, 60, None, BAD, 0, None) == 2
     assert L.moe_combine(None, 1, BAD, BAD, 4, 2, 64, None, BAD, 0, None) == 1
     assert L.moe_aux_loss(BAD, BAD, 0, 8, None, None, BAD, None) == 1
     assert L.moe_aux_loss(BAD, BAD, 4, 600, None, None, BAD, None) == 2
     assert L.moe_aux_loss(BAD, BAD, 4, 8, None, None, None, None) == 1
+
+
+def test_expert_choice_rejects_bad_arguments():
+    L = N.lib()
+
+    def call(T=64, E=8, C=4, logits=BAD, scores=BAD, offsets=BAD, st=BAD, dest=BAD, gate=BAD):
+        return L.moe_expert_choice(logits, T, E, C, scores, offsets, st, dest, gate, None)
+    assert call(T=-1) == N.MOE_ERR_INVALID
+    assert call(E=0) == N.MOE_ERR_INVALID
+    assert call(C=-1) == N.MOE_ERR_INVALID
+    assert call(E=513) == N.MOE_ERR_UNSUPPORTED
+    assert call(T=1 << 23, E=512) == N.MOE_ERR_UNSUPPORTED  # T*E >= 2^31
+    assert call(offsets=None) == N.MOE_ERR_INVALID
+    assert call(logits=None) == N.MOE_ERR_INVALID
+    assert call(dest=None) == N.MOE_ERR_INVALID
+    assert call(st=None) == N.MOE_ERR_INVALID
+    assert call(scores=None) == N.MOE_ERR_INVALID
 
 
 def test_binding_refuses_host_tensors():

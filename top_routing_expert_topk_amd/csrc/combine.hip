@@ -7,7 +7,9 @@
 // contribute nothing and the token keeps its residual (capacity section).
 // The "weighted scatter" is done as a per-token gather: each output element
 // is owned by one lane, which sums its k terms in fp32 in ascending j, so
-// the result is deterministic and needs no atomics.
+// the result is deterministic and needs no atomics. Expert Choice gives a
+// token one slot per expert (k = E, dest_row -1 where the expert did not
+// take it); the same sum then runs over its choosing experts in order.
 //
 // Aux loss: load_balancing_loss of the same page: f = mean probability per
 // expert, P = assignments per token per expert (before drops), loss = E *
@@ -79,6 +81,56 @@ __global__ __launch_bounds__(256) void combine_bf16(
   }
 }
 
+// Any number of slots (Expert Choice gives a token one slot per expert): per
+// 16-byte column chunk, the wave reads 64 slots at a time, ballots the live
+// ones and adds them in ascending slot order.
+template <typename OutT>
+__global__ __launch_bounds__(256) void combine_bf16_many(
+    const uint16_t* __restrict__ y, const int32_t* __restrict__ dest,
+    const float* __restrict__ gate, int T, int k, int d, const uint16_t* __restrict__ resid,
+    OutT* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kCombineWaves + (threadIdx.x >> 6);
+  if (t >= T) return;
+  for (int c0 = 0; c0 < d; c0 += 64 * 8) {
+    const int c = c0 + lane * 8;
+    const bool mine = c < d;
+    float acc[8];
+    if (resid && mine) {
+      const u32x4 r = *(const u32x4*)(resid + (size_t)t * d + c);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] = bf16lo(r[q]);
+        acc[2 * q + 1] = bf16hi(r[q]);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+    }
+    for (int j0 = 0; j0 < k; j0 += 64) {
+      const int j = j0 + lane;
+      const int dj = j < k ? dest[(size_t)t * k + j] : -1;
+      const float gj = j < k ? gate[(size_t)t * k + j] : 0.0f;
+      uint64_t live = __ballot(dj >= 0);
+      while (live) {
+        const int b = __ffsll((long long)live) - 1;
+        live &= live - 1;
+        const int r = __builtin_amdgcn_readlane(dj, b);
+        const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gj), b));
+        if (mine) {
+          const u32x4 v = *(const u32x4*)(y + (size_t)r * d + c);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[2 * q] = fmaf(g, bf16lo(v[q]), acc[2 * q]);
+            acc[2 * q + 1] = fmaf(g, bf16hi(v[q]), acc[2 * q + 1]);
+          }
+        }
+      }
+    }
+    if (mine) store8<OutT>(out + (size_t)t * d + c, acc);
+  }
+}
+
 __global__ __launch_bounds__(256) void combine_f32(
     const float* __restrict__ y, const int32_t* __restrict__ dest, const float* __restrict__ gate,
     int T, int k, int d, const float* __restrict__ resid, float* __restrict__ out) {
@@ -130,13 +182,22 @@ extern "C" int moe_combine(const void* y_perm, int dtype, const int32_t* dest_ro
   if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_INVALID;
   if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return MOE_ERR_INVALID;
   if (dtype == MOE_F32 && out_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
-  if (k > kMaxK) return MOE_ERR_UNSUPPORTED;
+  if (k > kMaxE) return MOE_ERR_UNSUPPORTED;
   if (dtype == MOE_BF16 && (d % 8) != 0) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!y_perm || !dest_row || !topk_gate || !out) return MOE_ERR_INVALID;
   hipStream_t s = (hipStream_t)stream;
   const int nb = ceil_div(T, kCombineWaves);
-  if (dtype == MOE_BF16 && out_dtype == MOE_BF16)
+  if (dtype == MOE_BF16 && k > kMaxK) {
+    if (out_dtype == MOE_BF16)
+      hipLaunchKernelGGL(combine_bf16_many<uint16_t>, dim3(nb), dim3(256), 0, s,
+                         (const uint16_t*)y_perm, dest_row, topk_gate, T, k, d,
+                         (const uint16_t*)residual, (uint16_t*)out);
+    else
+      hipLaunchKernelGGL(combine_bf16_many<float>, dim3(nb), dim3(256), 0, s,
+                         (const uint16_t*)y_perm, dest_row, topk_gate, T, k, d,
+                         (const uint16_t*)residual, (float*)out);
+  } else if (dtype == MOE_BF16 && out_dtype == MOE_BF16)
     hipLaunchKernelGGL(combine_bf16<uint16_t>, dim3(nb), dim3(256), 0, s, (const uint16_t*)y_perm,
                        dest_row, topk_gate, T, k, d, (const uint16_t*)residual, (uint16_t*)out);
   else if (dtype == MOE_BF16)

@@ -53,7 +53,9 @@ def lib():
         L.moe_grouped_ffn.argtypes = [P, I, I, I, I, I, I, P, P, P, P, P, P, P, P, Z, P]
         L.moe_combine.argtypes = [P, I, P, P, I, I, I, P, P, I, P]
         L.moe_aux_loss.argtypes = [P, P, I, I, P, P, P, P]
-        for f in ("moe_router_topk", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_aux_loss"):
+        L.moe_expert_choice.argtypes = [P, I, I, I, P, P, P, P, P, P]
+        for f in ("moe_router_topk", "moe_permute", "moe_grouped_ffn", "moe_combine",
+                  "moe_aux_loss", "moe_expert_choice"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -142,3 +144,10 @@ def moe_combine(y_perm, dest_row, topk_gate, T, k, d, residual, out, stream=None
 def moe_aux_loss(prob_sum, counts, T, E, f, P, loss, stream=None):
     _check("moe_aux_loss", lib().moe_aux_loss(
         _p(prob_sum), _p(counts), T, E, _p(f), _p(P), _p(loss), _stream(stream)))
+
+
+def moe_expert_choice(logits, T, E, C, scores, offsets, sorted_token, dest_row, gate,
+                      stream=None):
+    _check("moe_expert_choice", lib().moe_expert_choice(
+        _p(logits), T, E, int(C), _p(scores), _p(offsets), _p(sorted_token), _p(dest_row),
+        _p(gate), _stream(stream)))

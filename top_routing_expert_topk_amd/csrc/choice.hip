@@ -18,10 +18,11 @@
 //              fixed-order sum), written transposed through LDS as scores
 //              [E][T] so each expert's column is contiguous; also clears the
 //              token's dest_row / gate slots
-//   ec_select  one block per expert: radix select of the C-th largest score
-//              (four 8-bit digit passes over the column, histograms in LDS),
-//              then an ordered block scan that keeps every score above it and
-//              the lowest-index ties at it, writing rows in token order
+//   ec_select  one block per expert: the column staged in LDS, radix select
+//              of the C-th largest score (four 8-bit digit passes, histograms
+//              in LDS), then one ordered block scan over per-thread token
+//              segments that keeps every score above it and the lowest-index
+//              ties at it, writing rows in token order
 #include "moe_internal.h"
 
 namespace moe {
@@ -89,23 +90,29 @@ __global__ __launch_bounds__(256) void ec_scores(const float* __restrict__ logit
 }
 
 constexpr int kSelThreads = 512;
+constexpr int kSelLds = 16384;  // columns up to this many tokens are staged in LDS
 
-// Exclusive prefix count of `flag` over the block (threads in order), and the
-// block total; ws holds one int per wave.
-__device__ __forceinline__ int block_excl_count(bool flag, int* ws, int& total) {
+// Inclusive prefix sum over the block (threads in order) of one int per
+// thread; `total` gets the block sum. ws holds one int per wave.
+__device__ __forceinline__ int block_incl_sum(int v, int* ws, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint64_t m = __ballot(flag);
-  const int in_wave = __popcll(m & lanemask_lt());
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o);
+    if (lane >= o) v += u;
+  }
   __syncthreads();
-  if (lane == 0) ws[wave] = __popcll(m);
+  if (lane == 63) ws[wave] = v;
   __syncthreads();
   int before = 0;
   total = 0;
+#pragma unroll
   for (int w = 0; w < kSelThreads / 64; ++w) {
-    if (w < wave) before += ws[w];
-    total += ws[w];
+    const int x = ws[w];
+    if (w < wave) before += x;
+    total += x;
   }
-  return before + in_wave;
+  return before + v;
 }
 
 __global__ __launch_bounds__(kSelThreads) void ec_select(const float* __restrict__ scores, int T,
@@ -114,67 +121,87 @@ __global__ __launch_bounds__(kSelThreads) void ec_select(const float* __restrict
                                                          int32_t* __restrict__ sorted_token,
                                                          int32_t* __restrict__ dest,
                                                          float* __restrict__ gate) {
+  __shared__ uint32_t skeys[kSelLds];
   __shared__ int hist[256];
   __shared__ int wsum[kSelThreads / 64];
   __shared__ int sh_digit, sh_need;
-  const int e = blockIdx.x;
+  const int e = blockIdx.x, tid = threadIdx.x;
   const uint32_t* key = (const uint32_t*)(scores + (size_t)e * T);  // p >= 0: bits order as values
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     offsets[e] = e * C;
     if (e == 0) offsets[E] = E * C;
   }
   if (C == 0) return;
+  // stage the column (all loads in flight at once) so the passes below read LDS
+  const bool in_lds = T <= kSelLds;
+  if (in_lds) {
+#pragma unroll 4
+    for (int t = tid; t < T; t += kSelThreads) skeys[t] = key[t];
+    __syncthreads();
+  }
+  auto K = [&](int t) { return in_lds ? skeys[t] : key[t]; };
 
   // radix select: the C-th largest key, prefix/mask over the digits fixed so far
   uint32_t prefix = 0, mask = 0;
   int need = C;  // how many keys still to take among those matching the prefix
   if (C < T) {
     for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int b = threadIdx.x; b < 256; b += kSelThreads) hist[b] = 0;
+      for (int b = tid; b < 256; b += kSelThreads) hist[b] = 0;
       __syncthreads();
-      for (int t = threadIdx.x; t < T; t += kSelThreads) {
-        const uint32_t k = key[t];
+#pragma unroll 4
+      for (int t = tid; t < T; t += kSelThreads) {
+        const uint32_t k = K(t);
         if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255], 1);
       }
       __syncthreads();
-      if (threadIdx.x == 0) {
-        int above = 0, dgt = 255;
-        for (; dgt > 0; --dgt) {
-          if (above + hist[dgt] >= need) break;
-          above += hist[dgt];
+      // digit holding the need-th largest key: thread i looks at digit 255 - i;
+      // a prefix sum in that (descending) order gives the keys above each digit
+      {
+        const int dg = 255 - tid;
+        const int v = tid < 256 ? hist[dg] : 0;
+        int tot;
+        const int incl = block_incl_sum(v, wsum, tot);
+        if (tid < 256 && incl - v < need && need <= incl) {
+          sh_digit = dg;
+          sh_need = need - (incl - v);
         }
-        sh_digit = dgt;
-        sh_need = need - above;
       }
       __syncthreads();
       prefix |= (uint32_t)sh_digit << shift;
       mask |= 255u << shift;
       need = sh_need;
-      __syncthreads();
     }
   }
-  // keep keys above the threshold and the first `need` keys equal to it;
-  // with C == T every key is kept
+  // Keep keys above the threshold and the first `need` keys equal to it
+  // (every key when C == T). Thread i owns tokens [i*S, (i+1)*S): one scan of
+  // its counts gives how many kept keys precede each of its tokens.
   const bool all = C >= T;
-  int eq_seen = 0, taken = 0;
-  for (int t0 = 0; t0 < T; t0 += kSelThreads) {
-    const int t = t0 + threadIdx.x;
-    const uint32_t k = t < T ? key[t] : 0u;
-    const bool gt = t < T && (all || k > prefix);
-    const bool eq = t < T && !all && k == prefix;
-    int eq_total;
-    const int eq_rank = eq_seen + block_excl_count(eq, wsum, eq_total);
-    const bool keep = gt || (eq && eq_rank < need);
-    int keep_total;
-    const int pos = taken + block_excl_count(keep, wsum, keep_total);
+  const int S = (T + kSelThreads - 1) / kSelThreads;
+  const int tb = tid * S, te = min(T, tb + S);
+  int ngt = 0, neq = 0;
+  for (int t = tb; t < te; ++t) {
+    const uint32_t k = K(t);
+    ngt += (all || k > prefix) ? 1 : 0;
+    neq += (!all && k == prefix) ? 1 : 0;
+  }
+  int tot;
+  const int gt_before = block_incl_sum(ngt, wsum, tot) - ngt;
+  const int eq_before = block_incl_sum(neq, wsum, tot) - neq;
+  int g = gt_before, q = eq_before;
+  for (int t = tb; t < te; ++t) {
+    const uint32_t k = K(t);
+    const bool gt = all || k > prefix;
+    const bool eq = !all && k == prefix;
+    const bool keep = gt || (eq && q < need);
+    const int pos = g + min(q, need);
     if (keep && pos < C) {  // exactly C keys are kept; the bound only guards the store
       const int r = e * C + pos;
       sorted_token[r] = t;
       dest[(size_t)t * E + e] = r;
       gate[(size_t)t * E + e] = __uint_as_float(k);
     }
-    eq_seen += eq_total;
-    taken += keep_total;
+    g += gt ? 1 : 0;
+    q += eq ? 1 : 0;
   }
 }
 

@@ -271,6 +271,20 @@ __device__ __forceinline__ void dma16(const void* g, void* lds_base) {
 
 __device__ __forceinline__ int swz128(int r, int c) { return c ^ ((r >> 1) & 7); }
 
+// Scheduling hint for a sub-step: alternate one MFMA with one LDS fragment
+// read NR times, then the remaining MFMAs, so the reads for the next
+// sub-step hide behind this one's MFMAs instead of queueing up behind a
+// single lgkmcnt(0) wait.
+template <int NM, int NR>
+__device__ __forceinline__ void interleave_mfma_reads() {
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+}
+
 // One entry of a launch's work list: the block's tile and K range. The
 // lists are built on the device by big_plan, so a GEMM block starts with one
 // uniform load instead of searching the tile map.
@@ -606,10 +620,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
   for (int j = 0; j < ns; ++j) {
     MOE_RD(1, f1a, f1b);
     MOE_MM(f0a, f0b);
+    if constexpr (ACT) interleave_mfma_reads<TN * TM, TN + TM>();
     MOE_RD(2, f0a, f0b);
     MOE_MM(f1a, f1b);
+    if constexpr (ACT) interleave_mfma_reads<TN * TM, TN + TM>();
     MOE_RD(3, f1a, f1b);
     MOE_MM(f0a, f0b);
+    if constexpr (ACT) interleave_mfma_reads<TN * TM, TN + TM>();
     if (j + 1 < ns) {
       // step j+1 landed (only the weight half of step j+2 may be in flight),
       // and this wave's reads of step j are done before its slots are refilled
@@ -628,10 +645,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
         issue(Q0{}, j + 3, b2);
         issue(Q1{}, j + 3, b3);
       }
-      MOE_SLOTS(j + 1);
-      MOE_RD(0, f0a, f0b);
     }
+    // the first fragments of step j+1 (after the last step these read stale
+    // slots into registers nobody uses)
+    MOE_SLOTS(j + 1);
+    MOE_RD(0, f0a, f0b);
     MOE_MM(f1a, f1b);
+    if constexpr (ACT) interleave_mfma_reads<TN * TM, TN + TM>();
   }
   };
   if (active) main_loop(std::true_type{});

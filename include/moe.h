@@ -170,6 +170,59 @@ int moe_expert_choice(const float *logits, int T, int E, int C, float *scores, i
                       moe_stream_t stream);
 
 /*
+ * Host-resident experts streamed on demand   [Trilemma page 3.1: an expert
+ * container holding metadata and an LRU of loaded experts, an expert loaded
+ * when routing selects it; 3.2: routing returns indices, the executor loads
+ * the active experts, then runs the grouped FFN; Guide page 5.3: hot experts
+ * resident, cold ones fetched into an LRU cache]. The experts' weights live
+ * in host memory (pinned by the caller, so copies are asynchronous); S
+ * device slots hold the loaded ones.
+ *
+ * moe_cache_state_bytes(E, S): size of the caller-owned host state block
+ *   (0 for E < 1, S < 1 or E > 512). moe_cache_init(state, E, S): all slots
+ *   empty.
+ * moe_cache_step(state, counts, ntensors, host_base, dev_base,
+ *                bytes_per_expert, slot_of_dev, phase_of_dev, n_loaded,
+ *                compute_stream, copy_stream):
+ *   counts [E] (host, e.g. moe_permute's counts read back): experts with
+ *   count > 0 are needed. A needed expert already in a slot is a hit (phase
+ *   0); a needed one that is not takes the least recently used slot this
+ *   step does not need (phase 1) and, for each of the ntensors tensors, its
+ *   bytes_per_expert[i] bytes at host_base[i] + e*bytes are copied to
+ *   dev_base[i] + slot*bytes on copy_stream. phase -1: not needed. The slot
+ *   table [E] and the phases [E] are then copied to slot_of_dev /
+ *   phase_of_dev (device, may be NULL) on compute_stream; *n_loaded (may be
+ *   NULL) gets the number of experts copied. Status 2 if one step needs more
+ *   experts than slots. The state must not change while an earlier step's
+ *   table copy is pending (a synchronising read of the next counts on the
+ *   compute stream guarantees it).
+ * moe_cache_slot_of(state, slot_of, phase_of): host copies of the tables.
+ */
+size_t moe_cache_state_bytes(int E, int S);
+int moe_cache_init(void *state, int E, int S);
+int moe_cache_step(void *state, const int32_t *counts, int ntensors, const void *const *host_base,
+                   void *const *dev_base, const size_t *bytes_per_expert, int32_t *slot_of_dev,
+                   int32_t *phase_of_dev, int *n_loaded, moe_stream_t compute_stream,
+                   moe_stream_t copy_stream);
+int moe_cache_slot_of(const void *state, int32_t *slot_of, int32_t *phase_of);
+
+/*
+ * Grouped expert FFN over cached experts   [as moe_grouped_ffn; Trilemma
+ * page 3.2 for running the loaded experts]: the same computation, with
+ * expert e's weights at slot slot_of[e] of w1 [S][h][d], b1 [S][h], w2
+ * [S][d][h], b2 [S][d], and only the experts with phase_of[e] == phase
+ * computed (run phase 0 while the misses are copied, then phase 1 after
+ * the copy stream's work). bf16 only, decode-size batches (T*k <= 4*E and
+ * <= 1024, the weight-streaming path): status 2 otherwise. Same workspace
+ * as moe_grouped_ffn.
+ */
+int moe_grouped_ffn_cached(const void *x, int dtype, int T, int d, int h, int E, int k,
+                           const int32_t *offsets, const int32_t *sorted_token,
+                           const int32_t *slot_of, const int32_t *phase_of, int phase,
+                           const void *w1, const void *b1, const void *w2, const void *b2,
+                           void *y_perm, void *ws, size_t ws_bytes, moe_stream_t stream);
+
+/*
  * Load-balancing auxiliary loss   [Routing page, load_balancing_loss]:
  *   f[e] = prob_sum[e] / T,  P[e] = counts[e] / T,  loss = E * sum_e f[e]*P[e]
  * counts are before capacity drops, so sum_e P[e] = k. prob_sum [E] fp32,

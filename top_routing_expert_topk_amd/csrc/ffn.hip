@@ -1013,16 +1013,22 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// With an expert cache (slot_of != NULL) expert e's weights sit in device slot
+// slot_of[e] of the weight arrays, and only experts with phase_of[e] == phase
+// run, so a launch can cover the resident experts while others are copied in.
 template <bool GATHER, bool SILU>
 __global__ __launch_bounds__(256) void decode_bf16(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ sorted_token,
     const int32_t* __restrict__ offsets, const uint16_t* __restrict__ w,
-    const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int E, int N, int K) {
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int E, int N, int K,
+    const int32_t* __restrict__ slot_of, const int32_t* __restrict__ phase_of, int phase) {
   extern __shared__ __align__(16) uint16_t sx[];  // [DG][K]
   const int e = blockIdx.y;
   const int r0 = offsets[e];
   const int cnt = offsets[e + 1] - r0;
   if (cnt <= 0) return;
+  if (phase_of && phase_of[e] != phase) return;
+  const int ew = slot_of ? slot_of[e] : e;  // where expert e's weights are
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nw = blockIdx.x * DRPB + wave * DRPW;
   const int kchunks = K / 8;
@@ -1043,8 +1049,8 @@ __global__ __launch_bounds__(256) void decode_bf16(
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int g = 0; g < DG; ++g) acc[a][g] = 0.0f;
-      const uint16_t* w0 = w + ((size_t)e * N + (n < N ? n : N - 1)) * K;
-      const uint16_t* w1 = w + ((size_t)e * N + (n + 1 < N ? n + 1 : N - 1)) * K;
+      const uint16_t* w0 = w + ((size_t)ew * N + (n < N ? n : N - 1)) * K;
+      const uint16_t* w1 = w + ((size_t)ew * N + (n + 1 < N ? n + 1 : N - 1)) * K;
       for (int kb = 0; kb < K; kb += 8 * 512) {
         u32x4 wa[8], wb[8];
 #pragma unroll
@@ -1073,7 +1079,7 @@ __global__ __launch_bounds__(256) void decode_bf16(
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
         const int na = n + a;
-        const float b = (bias && na < N) ? bf16_to_f32(bias[(size_t)e * N + na]) : 0.0f;
+        const float b = (bias && na < N) ? bf16_to_f32(bias[(size_t)ew * N + na]) : 0.0f;
 #pragma unroll
         for (int g = 0; g < DG; ++g) {
           if (g < ng) {
@@ -1249,6 +1255,29 @@ int launch_pring(const uint16_t* x, const int32_t* sorted_token, const int32_t* 
   return launch_status();
 }
 
+// Both FFN GEMMs through the weight-streaming kernel (H in the workspace).
+int launch_decode(const uint16_t* x, const int32_t* sorted_token, const int32_t* offsets,
+                  const uint16_t* w1, const uint16_t* b1, const uint16_t* w2, const uint16_t* b2,
+                  uint16_t* H, uint16_t* y, int E, int d, int h, const int32_t* slot_of,
+                  const int32_t* phase_of, int phase, hipStream_t s) {
+  const size_t lds1 = (size_t)DG * d * 2, lds2 = (size_t)DG * h * 2;
+  if (lds1 > 160 * 1024 || lds2 > 160 * 1024) return MOE_ERR_UNSUPPORTED;
+  if (lds1 > 65536 &&
+      hipFuncSetAttribute((const void*)decode_bf16<true, true>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1) != hipSuccess)
+    return MOE_ERR_LAUNCH;
+  if (lds2 > 65536 &&
+      hipFuncSetAttribute((const void*)decode_bf16<false, false>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2) != hipSuccess)
+    return MOE_ERR_LAUNCH;
+  hipLaunchKernelGGL((decode_bf16<true, true>), dim3(ceil_div(h, DRPB), E), dim3(256), lds1, s, x,
+                     sorted_token, offsets, w1, b1, H, E, h, d, slot_of, phase_of, phase);
+  hipLaunchKernelGGL((decode_bf16<false, false>), dim3(ceil_div(d, DRPB), E), dim3(256), lds2, s,
+                     (const uint16_t*)H, sorted_token, offsets, w2, b2, y, E, d, h, slot_of,
+                     phase_of, phase);
+  return launch_status();
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -1286,23 +1315,9 @@ extern "C" int moe_grouped_ffn(const void* x, int dtype, int T, int d, int h, in
 
   const uint16_t* xb = (const uint16_t*)x;
   if (use_decode(rows, E)) {
-    const size_t lds1 = (size_t)DG * d * 2, lds2 = (size_t)DG * h * 2;
-    if (lds1 > 160 * 1024 || lds2 > 160 * 1024) return MOE_ERR_UNSUPPORTED;
-    if (lds1 > 65536 &&
-        hipFuncSetAttribute((const void*)decode_bf16<true, true>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1) != hipSuccess)
-      return MOE_ERR_LAUNCH;
-    if (lds2 > 65536 &&
-        hipFuncSetAttribute((const void*)decode_bf16<false, false>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2) != hipSuccess)
-      return MOE_ERR_LAUNCH;
-    hipLaunchKernelGGL((decode_bf16<true, true>), dim3(ceil_div(h, DRPB), E), dim3(256), lds1, s,
-                       xb, sorted_token, offsets, (const uint16_t*)w1, (const uint16_t*)b1,
-                       (uint16_t*)H, E, h, d);
-    hipLaunchKernelGGL((decode_bf16<false, false>), dim3(ceil_div(d, DRPB), E), dim3(256), lds2, s,
-                       (const uint16_t*)H, sorted_token, offsets, (const uint16_t*)w2,
-                       (const uint16_t*)b2, (uint16_t*)y_perm, E, d, h);
-    return launch_status();
+    return launch_decode(xb, sorted_token, offsets, (const uint16_t*)w1, (const uint16_t*)b1,
+                         (const uint16_t*)w2, (const uint16_t*)b2, (uint16_t*)H,
+                         (uint16_t*)y_perm, E, d, h, nullptr, nullptr, 0, s);
   }
 
   if (use_ring(rows, E, T, d, h))
@@ -1322,4 +1337,27 @@ extern "C" int moe_grouped_ffn(const void* x, int dtype, int T, int d, int h, in
   return launch_gemms_bf16<64>(xb, sorted_token, offsets, tile_start, (const uint16_t*)w1,
                                (const uint16_t*)b1, (const uint16_t*)w2, (const uint16_t*)b2,
                                (uint16_t*)H, (uint16_t*)y_perm, E, d, h, mslots, s);
+}
+
+extern "C" int moe_grouped_ffn_cached(const void* x, int dtype, int T, int d, int h, int E, int k,
+                                      const int32_t* offsets, const int32_t* sorted_token,
+                                      const int32_t* slot_of, const int32_t* phase_of, int phase,
+                                      const void* w1, const void* b1, const void* w2,
+                                      const void* b2, void* y_perm, void* ws, size_t ws_bytes,
+                                      moe_stream_t stream) {
+  if (T < 0 || d < 1 || h < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID;
+  if (dtype != MOE_BF16) return dtype == MOE_F32 ? MOE_ERR_UNSUPPORTED : MOE_ERR_INVALID;
+  if (E > kMaxE) return MOE_ERR_UNSUPPORTED;
+  const long rows = (long)T * k;
+  if (!use_decode(rows, E) && rows > 0) return MOE_ERR_UNSUPPORTED;
+  if ((d % 64) != 0 || (h % 64) != 0) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!x || !offsets || !sorted_token || !slot_of || !phase_of || !w1 || !w2 || !y_perm)
+    return MOE_ERR_INVALID;
+  if (!ws || ws_bytes < ffn_ws(T, d, h, E, k)) return MOE_ERR_WORKSPACE;
+  void* H = (unsigned char*)ws + ffn_plan_bytes(T, d, h, E, k);
+  return launch_decode((const uint16_t*)x, sorted_token, offsets, (const uint16_t*)w1,
+                       (const uint16_t*)b1, (const uint16_t*)w2, (const uint16_t*)b2,
+                       (uint16_t*)H, (uint16_t*)y_perm, E, d, h, slot_of, phase_of, phase,
+                       (hipStream_t)stream);
 }

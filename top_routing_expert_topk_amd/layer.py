@@ -139,3 +139,79 @@ def moe_layer_forward_ec(x, w_gate, gate_bias, w1, b1, w2, b2, C, residual=False
                       b.y_perm, b.ws_ffn, stream)
     N.moe_combine(b.y_perm, b.dest_row, b.gate, T, E, d, x if residual else None, b.out, stream)
     return b
+
+
+class ExpertCache:
+    """Experts held in pinned host memory, S of them in device slots (LRU).
+
+    Allocation and bookkeeping only: the slot policy and the copies run in
+    libmoe (moe_cache_step), the FFN over the slots in moe_grouped_ffn_cached.
+    """
+
+    def __init__(self, w1, b1, w2, b2, S: int, device):
+        import numpy as np
+        self.E, self.h, self.d = w1.shape
+        self.S = S
+        dev = torch.device(device)
+        self.host = []   # pinned host copies [E][...]
+        self.slots = []  # device slots [S][...]
+        for t in (w1, b1, w2, b2):
+            if t is None:
+                self.host.append(None)
+                self.slots.append(None)
+                continue
+            hcopy = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+            hcopy.copy_(t)
+            self.host.append(hcopy)
+            self.slots.append(torch.empty((S,) + tuple(t.shape[1:]), dtype=t.dtype, device=dev))
+        self.state = np.zeros(N.moe_cache_state_bytes(self.E, S), np.uint8)
+        N.moe_cache_init(self.state, self.E, S)
+        self.slot_of = torch.empty((self.E,), dtype=torch.int32, device=dev)
+        self.phase_of = torch.empty((self.E,), dtype=torch.int32, device=dev)
+        self.copy_stream = torch.cuda.Stream(dev)  # default priority
+        self.loaded = 0
+
+    def step(self, counts_host, stream):
+        """Plan one step and enqueue the misses' copies; returns an event the
+        compute stream waits on before the misses' FFN."""
+        pairs = [(h, s) for h, s in zip(self.host, self.slots) if h is not None]
+        # the slots being refilled may still be read by the previous step
+        self.copy_stream.wait_stream(stream)
+        self.loaded = N.moe_cache_step(self.state, counts_host, [p[0] for p in pairs],
+                                       [p[1] for p in pairs], self.slot_of, self.phase_of,
+                                       stream, self.copy_stream)
+        ev = torch.cuda.Event()
+        ev.record(self.copy_stream)
+        return ev
+
+
+def moe_layer_forward_cached(x, w_gate, gate_bias, cache: ExpertCache, k, renorm=True,
+                             capacity=-1, residual=False, want_logits=False,
+                             bufs: MoEBuffers | None = None, stream=None,
+                             out_dtype=torch.float32) -> MoEBuffers:
+    """Token-choice layer over host-resident experts: route and permute, read
+    the counts back (one synchronisation), load the missing experts on the
+    copy stream while the resident ones run, then run the loaded ones."""
+    T, d = x.shape
+    E = w_gate.shape[0]
+    h = cache.h
+    if bufs is None:
+        bufs = MoEBuffers(T, d, h, E, k, x.dtype, x.device, out_dtype)
+    b = bufs
+    s = torch.cuda.current_stream() if stream is None else stream
+    N.moe_router_topk(x, w_gate, gate_bias, E, k, renorm, b.logits if want_logits else None,
+                      b.topk_idx, b.topk_gate, b.prob_sum, b.ws_router, s)
+    N.moe_permute(b.topk_idx, T, k, E, capacity, b.counts, b.offsets, b.dest_row,
+                  b.sorted_token, b.ws_permute, s)
+    with torch.cuda.stream(s):
+        counts = b.counts.cpu().numpy()
+    ready = cache.step(counts, s)
+    w1s, b1s, w2s, b2s = cache.slots
+    for phase in (0, 1):
+        if phase == 1:
+            s.wait_event(ready)
+        N.moe_grouped_ffn_cached(x, T, d, h, E, k, b.offsets, b.sorted_token, cache.slot_of,
+                                 cache.phase_of, phase, w1s, b1s, w2s, b2s, b.y_perm, b.ws_ffn, s)
+    N.moe_combine(b.y_perm, b.dest_row, b.topk_gate, T, k, d, x if residual else None, b.out, s)
+    N.moe_aux_loss(b.prob_sum, b.counts, T, E, b.f, b.P, b.loss, s)
+    return b

@@ -54,8 +54,16 @@ def lib():
         L.moe_combine.argtypes = [P, I, P, P, I, I, I, P, P, I, P]
         L.moe_aux_loss.argtypes = [P, P, I, I, P, P, P, P]
         L.moe_expert_choice.argtypes = [P, I, I, I, P, P, P, P, P, P]
+        L.moe_cache_state_bytes.argtypes = [I, I]
+        L.moe_cache_state_bytes.restype = Z
+        L.moe_cache_init.argtypes = [P, I, I]
+        L.moe_cache_step.argtypes = [P, P, I, P, P, P, P, P, P, P, P]
+        L.moe_cache_slot_of.argtypes = [P, P, P]
+        L.moe_grouped_ffn_cached.argtypes = [P, I, I, I, I, I, I, P, P, P, P, I, P, P, P, P, P,
+                                             P, Z, P]
         for f in ("moe_router_topk", "moe_permute", "moe_grouped_ffn", "moe_combine",
-                  "moe_aux_loss", "moe_expert_choice"):
+                  "moe_aux_loss", "moe_expert_choice", "moe_cache_init", "moe_cache_step",
+                  "moe_cache_slot_of", "moe_grouped_ffn_cached"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -151,3 +159,61 @@ def moe_expert_choice(logits, T, E, C, scores, offsets, sorted_token, dest_row, 
     _check("moe_expert_choice", lib().moe_expert_choice(
         _p(logits), T, E, int(C), _p(scores), _p(offsets), _p(sorted_token), _p(dest_row),
         _p(gate), _stream(stream)))
+
+
+# ------------------------------------------------------------ expert cache ----
+# The cache state and the per-step counts live in host memory (numpy arrays).
+
+def _host_ptr(a):
+    import numpy as np
+    if a is None:
+        return None
+    assert isinstance(a, np.ndarray) and a.flags["C_CONTIGUOUS"], "host arrays must be contiguous"
+    return a.ctypes.data
+
+
+def moe_cache_state_bytes(E, S) -> int:
+    return int(lib().moe_cache_state_bytes(E, S))
+
+
+def moe_cache_init(state, E, S):
+    _check("moe_cache_init", lib().moe_cache_init(_host_ptr(state), E, S))
+
+
+def moe_cache_step(state, counts, host_tensors, dev_tensors, slot_of_dev, phase_of_dev,
+                   compute_stream=None, copy_stream=None) -> int:
+    """host_tensors / dev_tensors: per-expert-major tensors ([E][...] pinned host, [S][...]
+    device); returns the number of experts copied."""
+    import numpy as np
+    n = len(host_tensors)
+    assert len(dev_tensors) == n
+    hb = (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in host_tensors])
+    db = (ctypes.c_void_p * max(n, 1))(*[_p(t) for t in dev_tensors])
+    nb = (ctypes.c_size_t * max(n, 1))(*[t[0].numel() * t.element_size() for t in host_tensors])
+    for t in host_tensors:
+        if t.is_cuda or not t.is_pinned():
+            raise ValueError("host expert tensors must be pinned host memory")
+    loaded = ctypes.c_int(0)
+    counts = np.ascontiguousarray(counts, dtype=np.int32)
+    _check("moe_cache_step", lib().moe_cache_step(
+        _host_ptr(state), _host_ptr(counts), n, hb if n else None, db if n else None,
+        nb if n else None, _p(slot_of_dev), _p(phase_of_dev), ctypes.byref(loaded),
+        _stream(compute_stream), _stream(copy_stream)))
+    return loaded.value
+
+
+def moe_cache_slot_of(state, E):
+    import numpy as np
+    slot = np.empty(E, np.int32)
+    phase = np.empty(E, np.int32)
+    _check("moe_cache_slot_of", lib().moe_cache_slot_of(_host_ptr(state), _host_ptr(slot),
+                                                        _host_ptr(phase)))
+    return slot, phase
+
+
+def moe_grouped_ffn_cached(x, T, d, h, E, k, offsets, sorted_token, slot_of, phase_of, phase,
+                           w1, b1, w2, b2, y_perm, ws, stream=None):
+    _check("moe_grouped_ffn_cached", lib().moe_grouped_ffn_cached(
+        _p(x), _dt(x), T, d, h, E, k, _p(offsets), _p(sorted_token), _p(slot_of), _p(phase_of),
+        int(phase), _p(w1), _p(b1), _p(w2), _p(b2), _p(y_perm), _p(ws), _nbytes(ws),
+        _stream(stream)))

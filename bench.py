@@ -31,7 +31,9 @@ CALLS = ("router", "permute", "ffn", "combine", "aux")
 EC_CALLS = ("router", "choice", "ffn", "combine")  # Expert Choice layer
 # tokens whose expert FFN the CPU baseline evaluates (routing always covers all T)
 CPU_SAMPLE = {"tiny_fp32": 256, "mixtral_prefill": 2048, "switch_top1_cap": 8192, "decode": 32,
-              "deepseek_v3": 512, "switch_expert_choice": 2048}
+              "deepseek_v3": 512, "switch_expert_choice": 2048, "decode_offload": 32}
+PCIE_GBS = 64.0             # PCIe 5.0 x16, one direction
+OFFLOAD_BATCHES = 16        # distinct token batches the offload workload cycles through
 
 
 def parse():
@@ -160,6 +162,69 @@ def _cpu_baseline_ec(cfg, inp, x, wg, gb, toks, host_w, fetch):
             "extrapolated": toks.size < cfg.T, "seconds": t2 - t0}
 
 
+def bench_offload(args, cfg, inp, dev):
+    """Layer over host-resident experts: each step routes a new batch (cycling
+    through OFFLOAD_BATCHES seeded batches resident in HBM), reads the counts
+    back, copies the missing experts from pinned host memory into the LRU
+    slots while the resident ones run, then runs the loaded ones."""
+    import torch
+    import top_routing_expert_topk_amd as moe
+    T, d, h, E, k = cfg.T, cfg.d, cfg.h, cfg.E, cfg.k
+    gen = torch.Generator(device=dev)
+    xs = []
+    for i in range(OFFLOAD_BATCHES):
+        gen.manual_seed(int(np.random.SeedSequence([20261203, cfg.cfg_id, 99, i]).generate_state(1)[0]))
+        xs.append(torch.randn((T, d), generator=gen, device=dev).to(cfg.torch_dtype))
+    cache = moe.ExpertCache(inp["w1"], inp["b1"], inp["w2"], inp["b2"], cfg.offload_slots, dev)
+    del inp["w1"], inp["w2"]  # the experts now live in host memory and device slots only
+    torch.cuda.empty_cache()
+    bufs = moe.MoEBuffers(T, d, h, E, k, cfg.torch_dtype, dev)
+    stream = torch.cuda.Stream(dev)  # default priority
+    expert_bytes = sum(t[0].numel() * t.element_size() for t in cache.host if t is not None)
+
+    def step(i):
+        moe.moe_layer_forward_cached(xs[i % OFFLOAD_BATCHES], inp["w_gate"], inp["gate_bias"],
+                                     cache, k, cfg.renorm, cfg.capacity, cfg.residual,
+                                     bufs=bufs, stream=stream)
+        return cache.loaded
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    loads, touched = [], []
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.warmup, args.warmup + args.steps):
+        loads.append(step(i))
+        touched.append(int((bufs.counts.cpu() > 0).sum()))
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    loaded = float(np.mean(loads))
+    pcie_bytes = loaded * expert_bytes
+    out = {
+        "metric": METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "T": T, "d": d, "h": h, "E": E, "k": k,
+                   "renorm": bool(cfg.renorm), "capacity": cfg.capacity,
+                   "residual": bool(cfg.residual), "routing": cfg.routing,
+                   "offload_slots": cfg.offload_slots, "parallelism": "single GPU"},
+        "offload": {"experts_loaded_per_step": loaded,
+                    "experts_touched_per_step": float(np.mean(touched)),
+                    "hit_rate": 1.0 - float(np.sum(loads)) / max(1, int(np.sum(touched))),
+                    "expert_bytes": expert_bytes, "pcie_bytes_per_step": pcie_bytes,
+                    "pcie_GBps_over_step": pcie_bytes / (ms_step * 1e-3) / 1e9,
+                    "pcie_peak_GBps": PCIE_GBS},
+        "wall_ms_per_step": wall * 1e3 / args.steps,
+        "device": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -180,6 +245,8 @@ def main():
     torch.cuda.set_device(dev)
     inp = mi.make_inputs(cfg, dev)
     torch.cuda.synchronize()
+    if cfg.offload_slots > 0:
+        return bench_offload(args, cfg, inp, dev)
     T, d, h, E, k = cfg.T, cfg.d, cfg.h, cfg.E, cfg.k
     ec = cfg.routing == "expert_choice"
     calls = EC_CALLS if ec else CALLS

@@ -44,6 +44,7 @@ class MoEConfig:
     zipf_gate_bias: bool = False
     expert_bias: bool = True
     routing: str = "topk"       # "topk" (tokens choose k experts) or "expert_choice"
+    offload_slots: int = 0      # > 0: experts live in host memory, this many device slots
 
     @property
     def torch_dtype(self):
@@ -67,6 +68,10 @@ CONFIGS = {
     "decode": MoEConfig("decode", 3, T=32, d=4096, h=4096, E=64, k=2),
     # DeepSeek-V3-shaped routed experts: 256 experts, top-8, d=7168, hidden 2048
     "deepseek_v3": MoEConfig("deepseek_v3", 4, T=8192, d=7168, h=2048, E=256, k=8),
+    # decode with the experts in pinned host memory and 56 of 64 in device
+    # slots (LRU); each step routes a new batch of 32 tokens
+    "decode_offload": MoEConfig("decode_offload", 3, T=32, d=4096, h=4096, E=64, k=2,
+                                offload_slots=56),
     # Expert Choice on the Switch-shaped layer (same inputs, same Zipf-skewed
     # router): each of the 128 experts takes its 80 highest-probability tokens
     "switch_expert_choice": MoEConfig("switch_expert_choice", 2, T=8192, d=768, h=3072, E=128,

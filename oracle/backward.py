@@ -1,0 +1,189 @@
+"""CPU oracle for the backward pass of one MoE layer -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this module. It shares nothing with the GPU library.
+
+What it computes: the gradients of the scalar
+
+    L = sum_t <dout[t], out[t]> + daux * aux_loss
+
+with respect to every input of the layer (x, W_g, b_g, W1, b1, W2, b2), where
+out and aux_loss are the forward of ``oracle.moe_forward``: the gate equation
+G(x) = softmax(TopK(x . W_g)) and output sum_i G_i E_i(x) of the routing page
+"MoE混合专家模型路由机制原理与稀疏激活实现" (section "MoE混合专家模型架构与门控路由原理"),
+its Expert w2(silu(w1 x + b1)) + b2 and load_balancing_loss E * sum f * P
+(section "Top-K门控路由的PyTorch实现"), and its capacity rule (section
+"Expert Choice路由策略与容量因子调优"). The aux loss exists to be trained
+against (same section; the router of "MoE模型稀疏推理原理与生产落地实战",
+section 2.3, is trained jointly with the experts and keeps its two largest
+logits before the softmax so that gradients reach them).
+
+Readings (where the pages say nothing about gradients):
+  - the top-k selection, the expert counts and the capacity drop are
+    piecewise constant in the inputs: no gradient flows through them, only
+    through the gate values, the expert FFNs and the probabilities of the
+    aux loss;
+  - a dropped (token, slot) contributes nothing to out, so its gate gets no
+    gradient; with renormalised gates the kept gates still depend on the
+    dropped slot's logit through the renormalisation;
+  - aux_loss = E * sum_e (prob_sum_e / T) * (counts_e / T): the gradient
+    reaches the probabilities, d aux / d p[t,e] = E * counts_e / T^2.
+
+The chain rule is written out step by step, in reverse order of the forward,
+in double precision from the exact input values; a library matmul does each
+contraction. Every function below names the forward step it differentiates.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import oracle as fwd
+
+
+def widen(a) -> np.ndarray:
+    """float32 -> float64, bf16 bit patterns (uint16) -> float64, both exact."""
+    if a is None:
+        return None
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (np.ascontiguousarray(a).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def silu(z):
+    """SiLU(z) = z / (1 + e^-z) (the Expert's activation)."""
+    return z * sigmoid(z)
+
+
+def silu_grad(z):
+    """d/dz [z s(z)] = s(z) + z s(z) (1 - s(z)), s the logistic function."""
+    s = sigmoid(z)
+    return s * (1.0 + z * (1.0 - s))
+
+
+def softmax(lg):
+    """p[t,e] = exp(l - max) / sum_e exp(l - max): the router's softmax over all experts."""
+    z = np.exp(lg - lg.max(axis=1, keepdims=True))
+    return z / z.sum(axis=1, keepdims=True)
+
+
+def softmax_grad(p, dp):
+    """Backward of a row softmax: dl = p * (dp - sum_e p dp)."""
+    return p * (dp - (p * dp).sum(axis=1, keepdims=True))
+
+
+def gate_grad(lg, idx, gate, dgate, renorm: bool):
+    """Backward of the gates to the logits.
+
+    renorm: g_j = exp(l_{S_j}) / sum_{i in S} exp(l_{S_i}), the softmax over
+    the k selected logits (the masked-softmax form of the gate equation):
+    dl[S_j] = g_j (dg_j - sum_i g_i dg_i), zero for unselected experts.
+    Otherwise g_j = p[t, S_j] (the full softmax): the gate gradients land on
+    p and go through the softmax backward.
+    """
+    T, E = lg.shape
+    k = idx.shape[1]
+    dl = np.zeros((T, E), np.float64)
+    rows = np.repeat(np.arange(T), k)
+    if renorm:
+        inner = (gate * dgate).sum(axis=1, keepdims=True)
+        np.add.at(dl, (rows, idx.ravel()), (gate * (dgate - inner)).ravel())
+        return dl
+    dp = np.zeros((T, E), np.float64)
+    np.add.at(dp, (rows, idx.ravel()), dgate.ravel())
+    return softmax_grad(softmax(lg), dp)
+
+
+def aux_grad(lg, counts, daux: float):
+    """Backward of aux = E * sum_e (sum_t p[t,e] / T) (counts_e / T) to the logits."""
+    T, E = lg.shape
+    dp = np.broadcast_to(daux * E * counts.astype(np.float64) / (float(T) * T), (T, E))
+    return softmax_grad(softmax(lg), dp)
+
+
+def expert_backward(xe, w1e, b1e, w2e, b2e, dy):
+    """Backward of y = W2 SiLU(W1 x + b1) + b2 over the rows of one expert.
+
+    xe [n, d] (the expert's input rows), dy [n, d]. Returns (y, dx, dW1, db1,
+    dW2, db2) with y the forward output of the rows (the gate's gradient needs
+    it).
+    """
+    z = xe @ w1e.T + (0.0 if b1e is None else b1e)
+    a = silu(z)
+    y = a @ w2e.T + (0.0 if b2e is None else b2e)
+    dw2 = dy.T @ a
+    db2 = dy.sum(axis=0)
+    da = dy @ w2e
+    dz = da * silu_grad(z)
+    dw1 = dz.T @ xe
+    db1 = dz.sum(axis=0)
+    dx = dz @ w1e
+    return y, dx, dw1, db1, dw2, db2
+
+
+def moe_backward(x, w_gate, w1, b1, w2, b2, k: int, renorm: bool, capacity: int, dout,
+                 daux: float = 0.0, gate_bias=None, residual: bool = False, lg=None):
+    """Gradients of L = <dout, out> + daux * aux_loss for the whole layer.
+
+    ``lg``: logits to route from (same-logits mode, e.g. the GPU's fp32
+    logits); computed in double when None. Routing, counts and the
+    permutation come from the forward oracle. Returns a dict with dx,
+    dw_gate, dgate_bias (None without a router bias), dw1, db1, dw2, db2 and
+    the intermediates dlogits [T,E], dgate [T,k], y_rows [R,d] (the forward
+    output of each kept row, in permuted order).
+    """
+    X = widen(x)
+    Wg = widen(w_gate)
+    W1, W2 = widen(w1), widen(w2)
+    B1, B2 = widen(b1), widen(b2)
+    dO = widen(dout)
+    T, d = X.shape
+    E, h = W1.shape[0], W1.shape[1]
+    if lg is None:
+        lg = fwd.logits(x, w_gate, gate_bias)
+    lg = np.asarray(lg, dtype=np.float64)
+    idx, gate, _ = fwd.route(lg, k, renorm)
+    counts, offsets, dest, st = fwd.permute(idx, E, capacity)
+    R = int(offsets[E])
+    slot_of_row = np.empty(R, np.int64)  # flat slot t*k + j of each kept row
+    kept = np.nonzero(dest >= 0)[0]
+    slot_of_row[dest[kept]] = kept
+
+    dx = dO.copy() if residual else np.zeros((T, d), np.float64)
+    dw1 = np.zeros((E, h, d), np.float64)
+    dw2 = np.zeros((E, d, h), np.float64)
+    db1 = np.zeros((E, h), np.float64)
+    db2 = np.zeros((E, d), np.float64)
+    dgate = np.zeros(T * k, np.float64)
+    y_rows = np.zeros((R, d), np.float64)
+    gflat = gate.ravel()
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        tok = st[r0:r1]
+        slots = slot_of_row[r0:r1]
+        # combine: out[t] += g[t,j] y[row]  ->  dy[row] = g dout[t]
+        dy = gflat[slots][:, None] * dO[tok]
+        y, dxe, dw1[e], db1[e], dw2[e], db2[e] = expert_backward(
+            X[tok], W1[e], None if B1 is None else B1[e], W2[e], None if B2 is None else B2[e], dy)
+        # ... and dg[t,j] = <dout[t], y[row]>
+        dgate[slots] = (dO[tok] * y).sum(axis=1)
+        y_rows[r0:r1] = y
+        # the expert's input rows are gathered from x: scatter-add back
+        np.add.at(dx, tok, dxe)
+    dgate = dgate.reshape(T, k)
+    dl = gate_grad(lg, idx, gate, dgate, renorm)
+    if daux:
+        dl = dl + aux_grad(lg, counts, daux)
+    # logits = x W_g^T + b_g
+    dw_gate = dl.T @ X
+    dgate_bias = None if gate_bias is None else dl.sum(axis=0)
+    dx += dl @ Wg
+    return dict(dx=dx, dw_gate=dw_gate, dgate_bias=dgate_bias, dw1=dw1, db1=db1, dw2=dw2,
+                db2=db2, dlogits=dl, dgate=dgate, y_rows=y_rows, idx=idx, gate=gate,
+                counts=counts, offsets=offsets, dest_row=dest, sorted_token=st, logits=lg)

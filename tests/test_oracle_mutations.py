@@ -54,3 +54,40 @@ def test_mutant_is_caught(name, tmp_path):
                         os.path.join(ROOT, "tests", "test_oracle_pins.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
+
+
+# Slips in the backward oracle (numpy source), caught by its own pins.
+BWD_SRC = os.path.join(ROOT, "oracle", "backward.py")
+BWD_MUTANTS = {
+    "silu_grad_drops_z_term": ("return s * (1.0 + z * (1.0 - s))", "return s"),
+    "silu_grad_sign": ("return s * (1.0 + z * (1.0 - s))", "return s * (1.0 - z * (1.0 - s))"),
+    "softmax_grad_no_centering": ("return p * (dp - (p * dp).sum(axis=1, keepdims=True))",
+                                  "return p * dp"),
+    "renorm_no_centering": ("(gate * (dgate - inner)).ravel()", "(gate * dgate).ravel()"),
+    "no_renorm_skips_softmax": ("return softmax_grad(softmax(lg), dp)\n\n\ndef aux_grad",
+                                "return dp\n\n\ndef aux_grad"),
+    "aux_over_T_once": ("/ (float(T) * T)", "/ float(T)"),
+    "aux_missing_E": ("daux * E * counts", "daux * counts"),
+    "dw2_from_preactivation": ("dw2 = dy.T @ a", "dw2 = dy.T @ z"),
+    "db1_before_silu_grad": ("db1 = dz.sum(axis=0)", "db1 = da.sum(axis=0)"),
+    "dx_misses_router": ("dx += dl @ Wg", "dx = dx"),
+    "dgate_from_scaled_dy": ("dgate[slots] = (dO[tok] * y).sum(axis=1)",
+                             "dgate[slots] = (dy * y).sum(axis=1)"),
+    "residual_gradient_dropped": ("dx = dO.copy() if residual else", "dx = 0.0 * dO if residual else"),
+    "dy_ignores_gate": ("dy = gflat[slots][:, None] * dO[tok]", "dy = dO[tok]"),
+    "dx_reversed_columns": ("dx = dz @ w1e", "dx = dz @ w1e[:, ::-1]"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_backward_mutant_is_caught(name, tmp_path):
+    old, new = BWD_MUTANTS[name]
+    src = open(BWD_SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    mut = tmp_path / "backward_mut.py"
+    mut.write_text(src.replace(old, new))
+    env = dict(os.environ, MOE_ORACLE_BWD=str(mut), OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_backward.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"

@@ -58,7 +58,13 @@ enum moe_status {
 
 enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
 
-enum moe_op { MOE_OP_ROUTER = 0, MOE_OP_PERMUTE = 1, MOE_OP_FFN = 2 };
+enum moe_op {
+    MOE_OP_ROUTER = 0,
+    MOE_OP_PERMUTE = 1,
+    MOE_OP_FFN = 2,
+    MOE_OP_FFN_BWD = 3,   /* moe_grouped_ffn_backward */
+    MOE_OP_ROUTER_BWD = 4 /* moe_router_weight_backward */
+};
 
 /* Static text for a status code (host memory, never freed). */
 const char *moe_status_string(int status);
@@ -231,6 +237,87 @@ int moe_grouped_ffn_cached(const void *x, int dtype, int T, int d, int h, int E,
  */
 int moe_aux_loss(const float *prob_sum, const int32_t *counts, int T, int E, float *f, float *P,
                  float *loss, moe_stream_t stream);
+
+/* ===================================================================== *
+ * Backward pass of the layer: gradients of                               *
+ *   L = sum_t <dout[t], out[t]> + daux * aux_loss                        *
+ * through the forward above [Routing page: gate equation, output         *
+ * equation, Expert, MoELayer, load_balancing_loss; Sparse-inference page *
+ * 2.3: the router is trained jointly and its kept logits pass the        *
+ * softmax so gradients reach them]. Top-k selection, counts and capacity *
+ * drops carry no gradient; the gradient reaches the gate values, the     *
+ * router probabilities of the aux loss and every product. Call order:    *
+ * moe_combine_backward -> moe_router_backward -> moe_grouped_ffn_backward *
+ * -> moe_gather_backward and moe_router_weight_backward. Same            *
+ * conventions as the forward: device pointers, caller-owned buffers,     *
+ * asynchronous on `stream`, status codes as above.                        *
+ * ===================================================================== */
+
+/*
+ * Combine backward: for every kept slot (t, j) (r = dest_row[t*k+j] >= 0)
+ *   dy_perm[r] = topk_gate[t,j] * dout[t]          (dtype, [T*k][d] rows)
+ *   dgate[t,j] = sum_i dout[t,i] * y_perm[r,i]     (fp32, fixed-order sum)
+ * and dgate = 0 for dropped slots. y_perm: the forward's expert outputs.
+ * k <= 512 (Expert Choice layouts included).
+ */
+int moe_combine_backward(const void *y_perm, int dtype, const int32_t *dest_row,
+                         const float *topk_gate, int T, int k, int d, const void *dout,
+                         void *dy_perm, float *dgate, moe_stream_t stream);
+
+/*
+ * Router backward to the logits (fp32 [T][E]):
+ *   renorm = 1: dlogits[t, S_j] += g_j (dgate_j - sum_i g_i dgate_i)
+ *   renorm = 0: dp[t, S_j] += dgate_j
+ *   aux (daux != 0): dp[t, e] += daux * E * counts[e] / T^2
+ *   dlogits[t] += p (dp - <p, dp>),  p = softmax(logits[t]) recomputed.
+ * logits, topk_idx, topk_gate: the forward router's outputs; counts: the
+ * permute's pre-drop counts (read only when daux != 0). E <= 512.
+ */
+int moe_router_backward(const float *logits, const int32_t *topk_idx, const float *topk_gate,
+                        const float *dgate, const int32_t *counts, int T, int E, int k,
+                        int renorm, float daux, float *dlogits, moe_stream_t stream);
+
+/*
+ * Grouped expert FFN backward over the permutation of the forward
+ * (offsets, sorted_token from moe_permute), for each expert e and its rows:
+ *   Z = W1[e] x[sorted_token] + b1[e]          (recomputed, workspace)
+ *   dZ = (dy_perm W2[e]) * SiLU'(Z)
+ *   dx_perm = dZ W1[e]                         ([T*k][d], rows [0, R))
+ *   dw1[e] = dZ^T X_e,  db1[e] = sum of dZ rows        (dw1 [E][h][d])
+ *   dw2[e] = dy_perm^T SiLU(Z),  db2[e] = sum of dy rows (dw2 [E][d][h])
+ * Weight and bias gradients are overwritten (zero for experts without
+ * rows); db1 / db2 may be NULL (no bias). Gradients have the layer dtype;
+ * products accumulate in fp32. bf16: d and h multiples of 256 (status 2
+ * otherwise). Workspace: moe_workspace_size(MOE_OP_FFN_BWD, ...), which
+ * holds the transposed weights and activations.
+ */
+int moe_grouped_ffn_backward(const void *x, int dtype, int T, int d, int h, int E, int k,
+                             const int32_t *offsets, const int32_t *sorted_token, const void *w1,
+                             const void *b1, const void *w2, const void *dy_perm, void *dx_perm,
+                             void *dw1, void *db1, void *dw2, void *db2, void *ws,
+                             size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * Input gradient:
+ *   dx[t] = sum_e dlogits[t,e] w_gate[e]        (e ascending; if dlogits)
+ *         + dout_residual[t]                    (if not NULL: residual layers)
+ *         + sum_j dx_perm[dest_row[t*k+j]]      (kept slots, j ascending)
+ * summed in fp32, stored in dtype. k, E <= 512.
+ */
+int moe_gather_backward(const void *dx_perm, int dtype, const int32_t *dest_row, int T, int k,
+                        int d, const void *dout_residual, const float *dlogits,
+                        const void *w_gate, int E, void *dx, moe_stream_t stream);
+
+/*
+ * Router weight gradients:
+ *   dw_gate[e][i] = sum_t dlogits[t,e] x[t,i]   (dtype [E][d])
+ *   dgate_bias[e] = sum_t dlogits[t,e]          (fp32 [E], may be NULL)
+ * Sums run over fixed token ranges in a fixed order. Workspace:
+ * moe_workspace_size(MOE_OP_ROUTER_BWD, ...).
+ */
+int moe_router_weight_backward(const void *x, int dtype, int T, int d, int E,
+                               const float *dlogits, void *dw_gate, float *dgate_bias, void *ws,
+                               size_t ws_bytes, moe_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -25,7 +25,7 @@ import torch
 
 BASE_SEED = 20261203
 
-TENSOR_IDS = {"x": 0, "w_gate": 1, "w1": 2, "b1": 3, "w2": 4, "b2": 5}
+TENSOR_IDS = {"x": 0, "w_gate": 1, "w1": 2, "b1": 3, "w2": 4, "b2": 5, "dout": 6}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -139,6 +139,11 @@ def make_inputs(cfg: MoEConfig, device="cpu") -> dict:
             b1[e].copy_(b)
             b2[e].copy_(dd)
     return dict(x=x, w_gate=wg, gate_bias=gb, w1=w1, b1=b1, w2=w2, b2=b2)
+
+
+def make_dout(cfg: MoEConfig, device="cpu") -> torch.Tensor:
+    """Upstream gradient of the layer output for the backward pass: [T, d] ~ N(0, 1)."""
+    return _randn((cfg.T, cfg.d), 1.0, cfg.cfg_id, "dout", 0, device, cfg.torch_dtype)
 
 
 def to_host_array(t):

@@ -126,7 +126,8 @@ def expert_backward(xe, w1e, b1e, w2e, b2e, dy):
 
 
 def moe_backward(x, w_gate, w1, b1, w2, b2, k: int, renorm: bool, capacity: int, dout,
-                 daux: float = 0.0, gate_bias=None, residual: bool = False, lg=None):
+                 daux: float = 0.0, gate_bias=None, residual: bool = False, lg=None,
+                 want_scale: bool = False):
     """Gradients of L = <dout, out> + daux * aux_loss for the whole layer.
 
     ``lg``: logits to route from (same-logits mode, e.g. the GPU's fp32
@@ -135,6 +136,11 @@ def moe_backward(x, w_gate, w1, b1, w2, b2, k: int, renorm: bool, capacity: int,
     dw_gate, dgate_bias (None without a router bias), dw1, db1, dw2, db2 and
     the intermediates dlogits [T,E], dgate [T,k], y_rows [R,d] (the forward
     output of each kept row, in permuted order).
+
+    ``want_scale``: also return ``scale``, a dict with the same keys holding
+    for every element the sum of the absolute values of the products it is
+    made of, carried through the chain (see ``_scales``): the yardstick of a
+    rounding-error bound, not a gradient.
     """
     X = widen(x)
     Wg = widen(w_gate)
@@ -184,6 +190,73 @@ def moe_backward(x, w_gate, w1, b1, w2, b2, k: int, renorm: bool, capacity: int,
     dw_gate = dl.T @ X
     dgate_bias = None if gate_bias is None else dl.sum(axis=0)
     dx += dl @ Wg
-    return dict(dx=dx, dw_gate=dw_gate, dgate_bias=dgate_bias, dw1=dw1, db1=db1, dw2=dw2,
-                db2=db2, dlogits=dl, dgate=dgate, y_rows=y_rows, idx=idx, gate=gate,
-                counts=counts, offsets=offsets, dest_row=dest, sorted_token=st, logits=lg)
+    res = dict(dx=dx, dw_gate=dw_gate, dgate_bias=dgate_bias, dw1=dw1, db1=db1, dw2=dw2,
+               db2=db2, dlogits=dl, dgate=dgate, y_rows=y_rows, idx=idx, gate=gate,
+               counts=counts, offsets=offsets, dest_row=dest, sorted_token=st, logits=lg)
+    if want_scale:
+        res["scale"] = _scales(X, Wg, W1, B1, W2, dO, lg, idx, gate, dest, st, offsets,
+                               slot_of_row, y_rows, renorm, residual, gate_bias is not None,
+                               B2 is not None, counts, daux)
+    return res
+
+
+def _scales(X, Wg, W1, B1, W2, dO, lg, idx, gate, dest, st, offsets, slot_of_row, y_rows,
+            renorm, residual, has_gate_bias, has_b2, counts, daux):
+    """Per-element magnitude M of every gradient: the backward run again on
+    absolute values, so that |result| <= M (triangle inequality) and each
+    rounded operand or product that feeds an element contributes at most
+    its own relative error times M. Where z, the pre-activation, is itself
+    a rounded value, the magnitudes also carry the change of the function
+    of z under a relative change u of z: SiLU moves by at most
+    |SiLU'(z) z| u, counted as |SiLU(z)| + |SiLU'(z) z| / 4, and SiLU'
+    by at most |z| u / 2 (|SiLU''| <= 1/2), counted as |SiLU'(z)| + |z| / 8
+    (so that four relative errors u of the magnitude cover the roundings
+    of z, of the operands and of the result)."""
+    T, d = X.shape
+    E, h = W1.shape[0], W1.shape[1]
+    k = idx.shape[1]
+    aX, aO = np.abs(X), np.abs(dO)
+    m_dx = aO.copy() if residual else np.zeros((T, d))
+    m = {n: np.zeros(s) for n, s in (("dw1", (E, h, d)), ("dw2", (E, d, h)), ("db1", (E, h)),
+                                     ("db2", (E, d)))}
+    m_dg = np.zeros(T * k)
+    gflat = gate.ravel()
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        tok = st[r0:r1]
+        slots = slot_of_row[r0:r1]
+        z = X[tok] @ W1[e].T + (0.0 if B1 is None else B1[e])
+        ady = np.abs(gflat[slots])[:, None] * aO[tok]
+        m["dw2"][e] = ady.T @ (np.abs(silu(z)) + np.abs(silu_grad(z) * z) / 4.0)
+        m["db2"][e] = ady.sum(axis=0)
+        adz = (ady @ np.abs(W2[e])) * (np.abs(silu_grad(z)) + np.abs(z) / 8.0)
+        m["dw1"][e] = adz.T @ aX[tok]
+        m["db1"][e] = adz.sum(axis=0)
+        np.add.at(m_dx, tok, adz @ np.abs(W1[e]))
+        m_dg[slots] = (aO[tok] * np.abs(y_rows[r0:r1])).sum(axis=1)
+    m_dg = m_dg.reshape(T, k)
+    ag = np.abs(gate)
+    rows = np.repeat(np.arange(T), k)
+    m_dl = np.zeros((T, E))
+    if renorm:
+        inner = (ag * m_dg).sum(axis=1, keepdims=True)
+        np.add.at(m_dl, (rows, idx.ravel()), (ag * (m_dg + inner)).ravel())
+    else:
+        p = softmax(lg)
+        mdp = np.zeros((T, E))
+        np.add.at(mdp, (rows, idx.ravel()), m_dg.ravel())
+        m_dl = p * (mdp + (p * mdp).sum(axis=1, keepdims=True))
+    if daux:
+        p = softmax(lg)
+        dpa = np.broadcast_to(abs(daux) * E * counts.astype(np.float64) / (float(T) * T), (T, E))
+        m_dl = m_dl + p * (dpa + (p * dpa).sum(axis=1, keepdims=True))
+    m_dx += m_dl @ np.abs(Wg)
+    m.update(dx=m_dx, dw_gate=m_dl.T @ aX, dgate_bias=m_dl.sum(axis=0) if has_gate_bias else None,
+             dgate=m_dg, dlogits=m_dl)
+    if not has_b2:
+        m["db2"] = None
+    if B1 is None:
+        m["db1"] = None
+    return m

@@ -1,0 +1,128 @@
+"""GPU parity of the layer backward: the HIP path through the C-ABI against the backward oracle.
+
+The forward runs first (want_logits) and the oracle differentiates the layer
+routed from the same fp32 logits, so selection, counts and drops are those
+of the GPU run (checked bit-exact by the forward tests). Every element of
+every gradient tensor, and of the intermediates dgate and dlogits, is
+compared with the oracle's float64 value:
+
+    |err_i| <= tol * RMS(ref) + c * M_i
+
+tol is the forward's bar (1e-5 fp32, 2e-2 bf16), RMS over the whole tensor.
+M_i is the oracle's magnitude of element i (the sum of the absolute values
+of the products it is made of, carried through the chain). bf16 layers
+round dY, Z, SiLU(Z), dZ (twice), dX_perm and every gradient to bf16 (2^-9
+relative each); a chain of up to eight such roundings bounds the error by
+2^-6 M_i, so c = 2^-6. fp32 layers: c = 2^-16 covers fp32 accumulation in
+any order over up to 256 terms (256 * 2^-24). With one or two rows per
+expert the rounding of a single product is the whole error, which is why an
+RMS-only bar cannot hold there (a 1-row weight gradient carries 2-3 relative
+roundings of 2^-9 on an element several times the tensor's RMS).
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+from oracle import backward as bwd
+from top_routing_expert_topk_amd import moe_layer_backward, moe_layer_forward
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": (1e-5, 2.0 ** -16), "bf16": (2e-2, 2.0 ** -6)}
+DAUX = 0.5
+
+BASE = mi.CONFIGS["mixtral_prefill"]
+SW = mi.CONFIGS["switch_top1_cap"]
+CASES = {
+    # about 128 rows per expert: short tiles in every GEMM
+    "mix_small": BASE.with_(name="mix_small", T=512, d=256, h=512),
+    # about 768 rows per expert: whole tiles, split tail tiles, ragged ends
+    "mix_rows": BASE.with_(name="mix_rows", T=1536, d=256, h=768, E=4),
+    # top-1 without renormalisation, capacity drops, router bias, residual
+    "switch_small": SW.with_(name="switch_small", T=1024, d=256, h=512, E=16, capacity=80),
+    # top-8 of 32
+    "deepseek_small": mi.CONFIGS["deepseek_v3"].with_(name="deepseek_small", T=256, d=512, h=256,
+                                                      E=32),
+    # most experts receive no row: their weight gradients must be zero
+    "sparse_experts": BASE.with_(name="sparse_experts", T=24, d=256, h=256, E=64),
+    # every assignment dropped: only the residual and the aux loss remain
+    "capacity_zero": SW.with_(name="capacity_zero", T=300, d=256, h=256, E=8, capacity=0),
+    "tiny_fp32": mi.CONFIGS["tiny_fp32"],
+    # widths that are not multiples of anything, fp32
+    "f32_ragged": mi.CONFIGS["tiny_fp32"].with_(name="f32_ragged", T=77, d=96, h=200, E=5,
+                                                capacity=25, residual=True),
+}
+
+
+def _np(t):
+    return None if t is None else t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def run_backward(cfg, daux=DAUX):
+    inp = mi.make_inputs(cfg, "cuda")
+    dout = mi.make_dout(cfg, "cuda")
+    fwd = moe_layer_forward(inp["x"], inp["w_gate"], inp["gate_bias"], inp["w1"], inp["b1"],
+                            inp["w2"], inp["b2"], cfg.k, cfg.renorm, cfg.capacity, cfg.residual,
+                            want_logits=True, out_dtype=cfg.torch_dtype)
+    g = moe_layer_backward(fwd, inp["x"], inp["w_gate"], inp["gate_bias"], inp["w1"], inp["b1"],
+                           inp["w2"], inp["b2"], dout, cfg.renorm, cfg.residual, daux)
+    torch.cuda.synchronize()
+    return inp, dout, fwd, g
+
+
+def oracle_backward(cfg, inp, dout, fwd, daux=DAUX):
+    h = {n: mi.to_host_array(v) for n, v in inp.items() if v is not None}
+    return bwd.moe_backward(h["x"], h["w_gate"], h["w1"], h.get("b1"), h["w2"], h.get("b2"),
+                            cfg.k, cfg.renorm, cfg.capacity, mi.to_host_array(dout), daux,
+                            gate_bias=h.get("gate_bias"), residual=cfg.residual,
+                            lg=fwd.logits.cpu().numpy(), want_scale=True)
+
+
+def compare(cfg, g, ref, label):
+    tol, c = TOL[cfg.dtype]
+    errs = {}
+    pairs = dict(dx=g.dx, dw_gate=g.dw_gate, dgate_bias=g.dgate_bias, dw1=g.dw1, db1=g.db1,
+                 dw2=g.dw2, db2=g.db2, dgate=g.dgate, dlogits=g.dlogits)
+    for name, got in pairs.items():
+        want = ref[name]
+        if want is None:
+            assert got is None, name
+            continue
+        got = _np(got).reshape(want.shape)
+        if not want.size:
+            continue
+        rms = float(np.sqrt(np.mean(want ** 2)))
+        err = np.abs(got - want)
+        bound = tol * rms + c * ref["scale"][name]
+        worst = float((err / np.maximum(bound, 1e-300)).max())
+        errs[name] = (float(err.max()), rms, worst)
+        i = np.unravel_index(int(np.argmax(err - bound)), err.shape)
+        assert worst <= 1.0, (f"{label} {name}: err {err[i]} at {i} exceeds its bound {bound[i]} "
+                              f"(RMS {rms}, ref {want[i]}, got {got[i]})")
+    return errs
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_backward_every_element(name):
+    cfg = CASES[name]
+    print(f"[bwd] {name}: T={cfg.T} d={cfg.d} h={cfg.h} E={cfg.E} k={cfg.k} cap={cfg.capacity} "
+          f"{cfg.dtype}", flush=True)
+    inp, dout, fwd, g = run_backward(cfg)
+    ref = oracle_backward(cfg, inp, dout, fwd)
+    errs = compare(cfg, g, ref, name)
+    print(f"[bwd] {name}: " + ", ".join(f"{k}={e / r if r else 0:.2e}/{w:.2f}"
+                                        for k, (e, r, w) in errs.items()), flush=True)
+    # experts without rows have exactly zero weight gradients
+    empty = np.nonzero(np.diff(ref["offsets"]) == 0)[0]
+    for e in empty:
+        assert not bool(g.dw1[e].any()) and not bool(g.dw2[e].any()), f"expert {e}"
+
+
+def test_backward_is_deterministic():
+    cfg = CASES["mix_rows"]
+    _, _, _, g1 = run_backward(cfg)
+    keep = {n: getattr(g1, n).clone() for n in ("dx", "dw1", "dw2", "db1", "db2", "dw_gate")}
+    _, _, _, g2 = run_backward(cfg)
+    for n, v in keep.items():
+        assert torch.equal(v, getattr(g2, n)), n

@@ -152,3 +152,62 @@ def test_binding_refuses_host_tensors():
     x = torch.zeros(4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         N.moe_combine(x, x, x, 4, 1, 64, None, x)
+
+
+def test_backward_workspace_sizes():
+    """FFN backward: the forward plan, Z and dZ (4 B each), the tail partials,
+    both transposed weight sets and two transposed activation arrays of
+    max(d, h) rows by the padded row count; router weight backward: fp32
+    partials over at most 8 token ranges."""
+    for T, d, h, E, k in [(4096, 4096, 14336, 8, 2), (8192, 7168, 2048, 256, 8),
+                          (256, 128, 256, 8, 2), (1, 256, 256, 512, 16)]:
+        rows, rp = T * k, _ceil(T * k + 63 * E, 64) * 64
+        need = (N.moe_workspace_size(N.MOE_OP_FFN, T, d, h, E, k) - rows * h * 4
+                - 256 * 256 * 256 * 4)  # the plan part of the forward workspace
+        need += 2 * rows * h * 4 + 256 * 256 * 256 * 4 + 2 * E * d * h * 2 + 2 * max(d, h) * rp * 2
+        assert N.moe_workspace_size(N.MOE_OP_FFN_BWD, T, d, h, E, k) >= need
+        s = min(8, max(1, T // 1024))
+        assert N.moe_workspace_size(N.MOE_OP_ROUTER_BWD, T, d, h, E, k) >= s * E * d * 4
+    assert N.moe_workspace_size(N.MOE_OP_FFN_BWD, 10, 256, 256, 600, 2) == 0
+
+
+def test_backward_calls_reject_bad_arguments():
+    L = N.lib()
+    # combine backward
+    assert L.moe_combine_backward(BAD, 1, BAD, BAD, -1, 2, 64, BAD, BAD, BAD, None) == 1
+    assert L.moe_combine_backward(BAD, 2, BAD, BAD, 4, 2, 64, BAD, BAD, BAD, None) == 1
+    assert L.moe_combine_backward(BAD, 1, BAD, BAD, 4, 513, 64, BAD, BAD, BAD, None) == 2
+    assert L.moe_combine_backward(BAD, 1, BAD, BAD, 4, 2, 64, None, BAD, BAD, None) == 1
+    assert L.moe_combine_backward(None, 1, BAD, BAD, 0, 2, 64, None, None, None, None) == 0
+    # router backward
+    F = ctypes.c_float
+    assert L.moe_router_backward(BAD, BAD, BAD, BAD, BAD, 4, 8, 9, 1, F(0), BAD, None) == 1
+    assert L.moe_router_backward(BAD, BAD, BAD, BAD, BAD, 4, 600, 2, 1, F(0), BAD, None) == 2
+    assert L.moe_router_backward(BAD, BAD, BAD, BAD, None, 4, 8, 2, 1, F(0.5), BAD, None) == 1
+    assert L.moe_router_backward(BAD, BAD, BAD, None, BAD, 4, 8, 2, 1, F(0), BAD, None) == 1
+
+    # grouped FFN backward
+    def ffn(dtype=1, T=10, d=256, h=512, E=8, k=2, w1=BAD, dy=BAD, ws=BAD, wsb=1 << 40):
+        return L.moe_grouped_ffn_backward(BAD, dtype, T, d, h, E, k, BAD, BAD, w1, None, BAD, dy,
+                                          BAD, BAD, None, BAD, None, ws, wsb, None)
+    assert ffn(T=-1) == 1
+    assert ffn(dtype=3) == 1
+    assert ffn(k=9) == 1
+    assert ffn(E=600, k=2) == 2
+    assert ffn(w1=None) == 1
+    assert ffn(dy=None) == 1
+    assert ffn(wsb=100) == 4
+    assert ffn(ws=None) == 4
+    assert ffn(d=192) == 2   # bf16 tiles need multiples of 256
+    assert ffn(h=320) == 2
+
+    # gather backward
+    assert L.moe_gather_backward(BAD, 1, BAD, -1, 2, 64, None, None, None, 8, BAD, None) == 1
+    assert L.moe_gather_backward(BAD, 1, BAD, 4, 2, 64, None, BAD, None, 8, BAD, None) == 1
+    assert L.moe_gather_backward(BAD, 1, BAD, 4, 2, 64, None, None, None, 600, BAD, None) == 2
+    assert L.moe_gather_backward(None, 1, BAD, 4, 2, 64, None, None, None, 8, BAD, None) == 1
+    # router weight backward
+    assert L.moe_router_weight_backward(BAD, 1, -1, 64, 8, BAD, BAD, None, BAD, 1 << 30, None) == 1
+    assert L.moe_router_weight_backward(BAD, 1, 64, 64, 600, BAD, BAD, None, BAD, 1 << 30, None) == 2
+    assert L.moe_router_weight_backward(BAD, 1, 64, 64, 8, None, BAD, None, BAD, 1 << 30, None) == 1
+    assert L.moe_router_weight_backward(BAD, 1, 64, 64, 8, BAD, BAD, None, BAD, 16, None) == 4

@@ -226,3 +226,20 @@ def test_dropped_assignments_get_no_expert_gradient():
     assert np.all(g["dw1"] == 0) and np.all(g["db2"] == 0) and np.all(g["dgate"] == 0)
     want = bwd.widen(dout) + g["dlogits"] @ bwd.widen(p["w_gate"])
     np.testing.assert_allclose(g["dx"], want, rtol=1e-14, atol=1e-14)
+
+
+def test_error_scales_bound_the_gradients():
+    """The magnitudes returned with want_scale are sums of absolute values
+    of the terms of each element, so they bound the gradient itself."""
+    p, dout = _layer(71, 40, 12, 10, 6, True)
+    for renorm, k, cap in ((True, 2, -1), (False, 1, 8), (True, 3, 15)):
+        g = _backward(p, dout, 0.3, k, renorm, cap, True)
+        g2 = bwd.moe_backward(p["x"], p["w_gate"], p["w1"], p["b1"], p["w2"], p["b2"], k, renorm,
+                              cap, dout, 0.0, gate_bias=p["gate_bias"], residual=True,
+                              want_scale=True)
+        for name, M in g2["scale"].items():
+            ref = g2[name]
+            assert M.shape == ref.shape, name
+            assert np.all(M >= np.abs(ref) * (1 - 1e-12) - 1e-15), name
+        # daux only moves dlogits and what follows from it
+        np.testing.assert_allclose(g2["dw1"], g["dw1"], rtol=0, atol=0)

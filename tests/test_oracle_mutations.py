@@ -66,7 +66,8 @@ BWD_MUTANTS = {
     "renorm_no_centering": ("(gate * (dgate - inner)).ravel()", "(gate * dgate).ravel()"),
     "no_renorm_skips_softmax": ("return softmax_grad(softmax(lg), dp)\n\n\ndef aux_grad",
                                 "return dp\n\n\ndef aux_grad"),
-    "aux_over_T_once": ("/ (float(T) * T)", "/ float(T)"),
+    "aux_over_T_once": ("daux * E * counts.astype(np.float64) / (float(T) * T)",
+                        "daux * E * counts.astype(np.float64) / float(T)"),
     "aux_missing_E": ("daux * E * counts", "daux * counts"),
     "dw2_from_preactivation": ("dw2 = dy.T @ a", "dw2 = dy.T @ z"),
     "db1_before_silu_grad": ("db1 = dz.sum(axis=0)", "db1 = da.sum(axis=0)"),

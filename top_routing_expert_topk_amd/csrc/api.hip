@@ -22,6 +22,9 @@ extern "C" size_t moe_workspace_size(int op, int T, int d, int h, int E, int k) 
     case MOE_OP_ROUTER: return d < 1 ? 0 : router_ws(T, d, E);
     case MOE_OP_PERMUTE: return permute_ws(T, k, E);
     case MOE_OP_FFN: return (h < 1 || d < 1) ? 0 : ffn_ws(T, d, h, E, k);
+    case MOE_OP_FFN_BWD:
+      return (h < 1 || d < 1 || E > kMaxE) ? 0 : ffn_bwd_layout(T, d, h, E, k).total;
+    case MOE_OP_ROUTER_BWD: return (d < 1 || E > kMaxE) ? 0 : router_bwd_ws(T, d, E);
     default: return 0;
   }
 }

@@ -1,0 +1,484 @@
+// Backward of the router, combine and gather steps of one MoE layer: the
+// gradients of L = <dout, out> + daux * aux_loss through
+//   out[t] = (residual ? x[t] : 0) + sum_j g[t,j] y[dest[t,j]]
+//     (output equation of page "MoE混合专家模型路由机制原理与稀疏激活实现",
+//      section "门控路由原理", slot-by-slot as its MoELayer accumulates);
+//   g = softmax over the top-k logits (renorm) or p[t, S_j] (no renorm),
+//     p = softmax of the logits over all experts (gate equation, TopKRouter);
+//   aux_loss = E * sum_e (sum_t p[t,e] / T) (counts_e / T)
+//     (load_balancing_loss of the same page; the counts carry no gradient);
+//   logits = x W_g^T (+ b_g).
+// Selection, counts and capacity drops are piecewise constant: gradients
+// flow through the gate values, the probabilities and the products only.
+//
+// Kernels:
+//   combine_bwd     per token: dY[row] = g * dout[t] for each kept slot and
+//                   dg[t,j] = <dout[t], y[row]> (fp32, fixed-order reduction)
+//   router_bwd      one wave per token: dlogits from dg (renormalised top-k
+//                   softmax or full-softmax backward) plus the aux term
+//   gather_bwd      dx[t] = dout[t] (residual) + sum_j dXp[dest[t,j]]
+//                   + sum_e dlogits[t,e] W_g[e], 16 tokens per block
+//   wgate_partial   dW_g partial sums over token ranges (64 x 64 tiles)
+//   wgate_reduce    partials summed in range order; db_g over all tokens
+#include <type_traits>
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float* v);
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float* v) {
+  const u32x4 r = *(const u32x4*)p;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v[2 * q] = bf16lo(r[q]);
+    v[2 * q + 1] = bf16hi(r[q]);
+  }
+}
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float* v) {
+  const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v[q] = a[q];
+    v[4 + q] = b[q];
+  }
+}
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const float* v);
+template <>
+__device__ __forceinline__ void store8<uint16_t>(uint16_t* p, const float* v) {
+  u32x4 o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
+  *(u32x4*)p = o;
+}
+template <>
+__device__ __forceinline__ void store8<float>(float* p, const float* v) {
+  *(f32x4*)p = f32x4{v[0], v[1], v[2], v[3]};
+  *(f32x4*)(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+}
+template <typename T>
+__device__ __forceinline__ float ld1(const T* p) {
+  if constexpr (std::is_same<T, uint16_t>::value) return bf16_to_f32(*p);
+  else return *p;
+}
+template <typename T>
+__device__ __forceinline__ void st1(T* p, float v) {
+  if constexpr (std::is_same<T, uint16_t>::value) *p = (uint16_t)f32_to_bf16(v);
+  else *p = v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Sum of one float per thread over a 256-thread block, same order every run;
+// every thread gets the result.
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+  v = wave_sum(v);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// ------------------------------------------------------------- combine ---
+// One block per token. vec: d % 8 == 0 (8 elements per thread per pass).
+template <typename T>
+__global__ __launch_bounds__(256) void combine_bwd(const T* __restrict__ y,
+                                                   const int32_t* __restrict__ dest,
+                                                   const float* __restrict__ gate, int k, int d,
+                                                   const T* __restrict__ dout, T* __restrict__ dy,
+                                                   float* __restrict__ dgate, bool vec) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  const T* go = dout + (size_t)t * d;
+  for (int j = 0; j < k; ++j) {
+    const int r = dest[(size_t)t * k + j];
+    if (r < 0) {  // dropped: no output, no gradient
+      if (threadIdx.x == 0) dgate[(size_t)t * k + j] = 0.0f;
+      continue;
+    }
+    const float g = gate[(size_t)t * k + j];
+    const T* yr = y + (size_t)r * d;
+    T* dr = dy + (size_t)r * d;
+    float dot = 0.0f;
+    if (vec) {
+      for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
+        float a[8], b[8], o[8];
+        load8<T>(go + c, a);
+        load8<T>(yr + c, b);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          dot = fmaf(a[q], b[q], dot);
+          o[q] = g * a[q];
+        }
+        store8<T>(dr + c, o);
+      }
+    } else {
+      for (int c = threadIdx.x; c < d; c += 256) {
+        const float a = ld1<T>(go + c);
+        dot = fmaf(a, ld1<T>(yr + c), dot);
+        st1<T>(dr + c, g * a);
+      }
+    }
+    dot = block_sum256(dot, red);
+    if (threadIdx.x == 0) dgate[(size_t)t * k + j] = dot;
+  }
+}
+
+// -------------------------------------------------------------- router ---
+constexpr int kRbTokens = 4;  // tokens per block, one wave each
+constexpr int kPer = kMaxE / 64;
+
+__global__ __launch_bounds__(256) void router_bwd(const float* __restrict__ logits,
+                                                  const int32_t* __restrict__ idx,
+                                                  const float* __restrict__ gate,
+                                                  const float* __restrict__ dgate,
+                                                  const int32_t* __restrict__ counts, int T, int E,
+                                                  int k, int renorm, float aux_scale,
+                                                  float* __restrict__ dlogits) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kRbTokens + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* l = logits + (size_t)t * E;
+  float p[kPer], dl[kPer], dp[kPer];
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = lane + 64 * i;
+    p[i] = e < E ? l[e] : -INFINITY;
+    m = fmaxf(m, p[i]);
+    dl[i] = 0.0f;
+    dp[i] = 0.0f;
+  }
+  m = wave_max(m);
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    p[i] = lane + 64 * i < E ? expf(p[i] - m) : 0.0f;
+    s += p[i];
+  }
+  s = wave_sum(s);
+  const float inv = 1.0f / s;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) p[i] *= inv;
+
+  const int32_t* it = idx + (size_t)t * k;
+  const float* gt = gate + (size_t)t * k;
+  const float* dgt = dgate + (size_t)t * k;
+  if (renorm) {
+    // dl[S_j] = g_j (dg_j - sum_i g_i dg_i)
+    float inner = 0.0f;
+    for (int j = 0; j < k; ++j) inner = fmaf(gt[j], dgt[j], inner);
+    for (int j = 0; j < k; ++j) {
+      const int e = it[j];
+      const float v = gt[j] * (dgt[j] - inner);
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (e == lane + 64 * i) dl[i] += v;
+    }
+  } else {
+    // g_j = p[S_j]: dp[S_j] += dg_j, then the softmax backward
+    for (int j = 0; j < k; ++j) {
+      const int e = it[j];
+      const float v = dgt[j];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (e == lane + 64 * i) dp[i] += v;
+    }
+  }
+  // aux: d/dp[t,e] = daux E counts_e / T^2
+  if (aux_scale != 0.0f) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E) dp[i] += aux_scale * (float)counts[e];
+    }
+  }
+  float pdp = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) pdp = fmaf(p[i], dp[i], pdp);
+  pdp = wave_sum(pdp);
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = lane + 64 * i;
+    if (e < E) dlogits[(size_t)t * E + e] = dl[i] + p[i] * (dp[i] - pdp);
+  }
+}
+
+// -------------------------------------------------------------- gather ---
+constexpr int kGbTokens = 16;  // tokens per block
+constexpr int kGbCols = 256 * 8;
+
+// Grid (ceil(T / 16), ceil(d / 2048)); d % 8 == 0. Each thread owns 8
+// columns of the block's 16 tokens.
+template <typename T>
+__global__ __launch_bounds__(256) void gather_bwd(const T* __restrict__ dxp,
+                                                  const int32_t* __restrict__ dest, int Tn, int k,
+                                                  int d, const T* __restrict__ dres,
+                                                  const float* __restrict__ dlogits,
+                                                  const T* __restrict__ wg, int E,
+                                                  T* __restrict__ dx) {
+  __shared__ float sdl[kGbTokens][kMaxE];
+  const int t0 = blockIdx.x * kGbTokens;
+  const int nt = min(kGbTokens, Tn - t0);
+  if (dlogits) {
+    for (int i = threadIdx.x; i < nt * E; i += 256) sdl[i / E][i % E] = dlogits[(size_t)t0 * E + i];
+    __syncthreads();
+  }
+  const int c = blockIdx.y * kGbCols + threadIdx.x * 8;
+  if (c >= d) return;
+  float acc[kGbTokens][8];
+#pragma unroll
+  for (int tt = 0; tt < kGbTokens; ++tt)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[tt][q] = 0.0f;
+  // router term first, experts in ascending order
+  if (dlogits) {
+    for (int e = 0; e < E; ++e) {
+      float w[8];
+      load8<T>(wg + (size_t)e * d + c, w);
+#pragma unroll
+      for (int tt = 0; tt < kGbTokens; ++tt) {
+        const float a = sdl[tt][e];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[tt][q] = fmaf(a, w[q], acc[tt][q]);
+      }
+    }
+  }
+#pragma unroll
+  for (int tt = 0; tt < kGbTokens; ++tt) {
+    if (tt < nt) {
+      const int t = t0 + tt;
+      float v[8];
+      if (dres) {
+        load8<T>(dres + (size_t)t * d + c, v);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[tt][q] += v[q];
+      }
+      for (int j = 0; j < k; ++j) {
+        const int r = dest[(size_t)t * k + j];
+        if (r >= 0) {
+          load8<T>(dxp + (size_t)r * d + c, v);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc[tt][q] += v[q];
+        }
+      }
+      store8<T>(dx + (size_t)t * d + c, acc[tt]);
+    }
+  }
+}
+
+// Any d: one thread per (token, column), same sum order as gather_bwd.
+template <typename T>
+__global__ __launch_bounds__(256) void gather_bwd_scalar(const T* __restrict__ dxp,
+                                                         const int32_t* __restrict__ dest, int Tn,
+                                                         int k, int d, const T* __restrict__ dres,
+                                                         const float* __restrict__ dlogits,
+                                                         const T* __restrict__ wg, int E,
+                                                         T* __restrict__ dx) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long)Tn * d) return;
+  const int t = (int)(i / d), c = (int)(i % d);
+  float a = 0.0f;
+  if (dlogits)
+    for (int e = 0; e < E; ++e) a = fmaf(dlogits[(size_t)t * E + e], ld1<T>(wg + (size_t)e * d + c), a);
+  if (dres) a += ld1<T>(dres + i);
+  for (int j = 0; j < k; ++j) {
+    const int r = dest[(size_t)t * k + j];
+    if (r >= 0) a += ld1<T>(dxp + (size_t)r * d + c);
+  }
+  st1<T>(dx + i, a);
+}
+
+// ------------------------------------------------------- router weights ---
+constexpr int kWgTile = 64;
+constexpr int kWgTok = 16;
+
+// part[s][e][c] = sum over tokens t of range s (in order) of dl[t][e] x[t][c].
+// Grid (ceil(E/64), ceil(d/64), S); thread (ty, tx) owns experts 4ty..4ty+3
+// and columns 4tx..4tx+3 of the tile.
+template <typename T>
+__global__ __launch_bounds__(256) void wgate_partial(const T* __restrict__ x,
+                                                     const float* __restrict__ dl, int Tn, int d,
+                                                     int E, int S, float* __restrict__ part) {
+  __shared__ float sx[kWgTok][kWgTile + 4];
+  __shared__ float se[kWgTok][kWgTile + 4];
+  const int e0 = blockIdx.x * kWgTile, c0 = blockIdx.y * kWgTile, s = blockIdx.z;
+  const int tb = (int)((long)s * Tn / S), te = (int)((long)(s + 1) * Tn / S);
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  float acc[4][4] = {};
+  for (int t0 = tb; t0 < te; t0 += kWgTok) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = tid + 256 * i, tt = q / kWgTile, col = q % kWgTile, t = t0 + tt;
+      const bool live = t < te;
+      sx[tt][col] = (live && c0 + col < d) ? ld1<T>(x + (size_t)t * d + c0 + col) : 0.0f;
+      se[tt][col] = (live && e0 + col < E) ? dl[(size_t)t * E + e0 + col] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int tt = 0; tt < kWgTok; ++tt) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = se[tt][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = sx[tt][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = e0 + ty * 4 + i;
+    if (e >= E) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = c0 + tx * 4 + j;
+      if (c < d) part[((size_t)s * E + e) * d + c] = acc[i][j];
+    }
+  }
+}
+
+// dW_g[e][c] = sum_s part[s][e][c] (s ascending); grid (ceil(E*d / 256)).
+template <typename T>
+__global__ __launch_bounds__(256) void wgate_reduce(const float* __restrict__ part, int E, int d,
+                                                    int S, T* __restrict__ dwg) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long)E * d) return;
+  float a = 0.0f;
+  for (int s = 0; s < S; ++s) a += part[(size_t)s * E * d + i];
+  st1<T>(dwg + i, a);
+}
+
+// db_g[e] = sum_t dl[t][e]: one block per expert, fixed-order tree.
+__global__ __launch_bounds__(256) void gate_bias_grad(const float* __restrict__ dl, int Tn, int E,
+                                                      float* __restrict__ dbg) {
+  __shared__ float red[4];
+  const int e = blockIdx.x;
+  float a = 0.0f;
+  for (int t = threadIdx.x; t < Tn; t += 256) a += dl[(size_t)t * E + e];
+  a = block_sum256(a, red);
+  if (threadIdx.x == 0) dbg[e] = a;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int moe_combine_backward(const void* y_perm, int dtype, const int32_t* dest_row,
+                                    const float* topk_gate, int T, int k, int d, const void* dout,
+                                    void* dy_perm, float* dgate, moe_stream_t stream) {
+  if (T < 0 || k < 1 || d < 1) return MOE_ERR_INVALID;
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_INVALID;
+  if (k > kMaxE) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!y_perm || !dest_row || !topk_gate || !dout || !dy_perm || !dgate) return MOE_ERR_INVALID;
+  hipStream_t s = (hipStream_t)stream;
+  const bool vec = (d % 8) == 0;
+  if (dtype == MOE_BF16)
+    hipLaunchKernelGGL(combine_bwd<uint16_t>, dim3(T), dim3(256), 0, s, (const uint16_t*)y_perm,
+                       dest_row, topk_gate, k, d, (const uint16_t*)dout, (uint16_t*)dy_perm, dgate,
+                       vec);
+  else
+    hipLaunchKernelGGL(combine_bwd<float>, dim3(T), dim3(256), 0, s, (const float*)y_perm, dest_row,
+                       topk_gate, k, d, (const float*)dout, (float*)dy_perm, dgate, vec);
+  return launch_status();
+}
+
+extern "C" int moe_router_backward(const float* logits, const int32_t* topk_idx,
+                                   const float* topk_gate, const float* dgate,
+                                   const int32_t* counts, int T, int E, int k, int renorm,
+                                   float daux, float* dlogits, moe_stream_t stream) {
+  if (T < 0 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID;
+  if (E > kMaxE) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_idx || !topk_gate || !dgate || !dlogits) return MOE_ERR_INVALID;
+  if (daux != 0.0f && !counts) return MOE_ERR_INVALID;
+  const float aux_scale = daux * (float)E / ((float)T * (float)T);
+  hipLaunchKernelGGL(router_bwd, dim3(ceil_div(T, kRbTokens)), dim3(256), 0, (hipStream_t)stream,
+                     logits, topk_idx, topk_gate, dgate, counts, T, E, k, renorm ? 1 : 0, aux_scale,
+                     dlogits);
+  return launch_status();
+}
+
+extern "C" int moe_gather_backward(const void* dx_perm, int dtype, const int32_t* dest_row, int T,
+                                   int k, int d, const void* dout_residual,
+                                   const float* dlogits, const void* w_gate, int E, void* dx,
+                                   moe_stream_t stream) {
+  if (T < 0 || k < 1 || d < 1 || E < 1) return MOE_ERR_INVALID;
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_INVALID;
+  if (E > kMaxE || k > kMaxE) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!dx_perm || !dest_row || !dx || (dlogits && !w_gate)) return MOE_ERR_INVALID;
+  hipStream_t s = (hipStream_t)stream;
+  if ((d % 8) == 0) {
+    const dim3 g(ceil_div(T, kGbTokens), ceil_div(d, kGbCols));
+    if (dtype == MOE_BF16)
+      hipLaunchKernelGGL(gather_bwd<uint16_t>, g, dim3(256), 0, s, (const uint16_t*)dx_perm,
+                         dest_row, T, k, d, (const uint16_t*)dout_residual, dlogits,
+                         (const uint16_t*)w_gate, E, (uint16_t*)dx);
+    else
+      hipLaunchKernelGGL(gather_bwd<float>, g, dim3(256), 0, s, (const float*)dx_perm, dest_row, T,
+                         k, d, (const float*)dout_residual, dlogits, (const float*)w_gate, E,
+                         (float*)dx);
+  } else {
+    const dim3 g(ceil_div((long)T * d, 256));
+    if (dtype == MOE_BF16)
+      hipLaunchKernelGGL(gather_bwd_scalar<uint16_t>, g, dim3(256), 0, s, (const uint16_t*)dx_perm,
+                         dest_row, T, k, d, (const uint16_t*)dout_residual, dlogits,
+                         (const uint16_t*)w_gate, E, (uint16_t*)dx);
+    else
+      hipLaunchKernelGGL(gather_bwd_scalar<float>, g, dim3(256), 0, s, (const float*)dx_perm,
+                         dest_row, T, k, d, (const float*)dout_residual, dlogits,
+                         (const float*)w_gate, E, (float*)dx);
+  }
+  return launch_status();
+}
+
+extern "C" int moe_router_weight_backward(const void* x, int dtype, int T, int d, int E,
+                                          const float* dlogits, void* dw_gate, float* dgate_bias,
+                                          void* ws, size_t ws_bytes, moe_stream_t stream) {
+  if (T < 0 || d < 1 || E < 1) return MOE_ERR_INVALID;
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_INVALID;
+  if (E > kMaxE) return MOE_ERR_UNSUPPORTED;
+  if (!dw_gate || (T > 0 && (!x || !dlogits))) return MOE_ERR_INVALID;
+  if (!ws || ws_bytes < router_bwd_ws(T, d, E)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const int S = router_bwd_splits(T);
+  float* part = (float*)ws;
+  const dim3 g(ceil_div(E, kWgTile), ceil_div(d, kWgTile), S);
+  if (dtype == MOE_BF16)
+    hipLaunchKernelGGL(wgate_partial<uint16_t>, g, dim3(256), 0, s, (const uint16_t*)x, dlogits, T,
+                       d, E, S, part);
+  else
+    hipLaunchKernelGGL(wgate_partial<float>, g, dim3(256), 0, s, (const float*)x, dlogits, T, d, E,
+                       S, part);
+  const dim3 gr(ceil_div((long)E * d, 256));
+  if (dtype == MOE_BF16)
+    hipLaunchKernelGGL(wgate_reduce<uint16_t>, gr, dim3(256), 0, s, (const float*)part, E, d, S,
+                       (uint16_t*)dw_gate);
+  else
+    hipLaunchKernelGGL(wgate_reduce<float>, gr, dim3(256), 0, s, (const float*)part, E, d, S,
+                       (float*)dw_gate);
+  if (dgate_bias)
+    hipLaunchKernelGGL(gate_bias_grad, dim3(E), dim3(256), 0, s, dlogits, T, E, dgate_bias);
+  return launch_status();
+}

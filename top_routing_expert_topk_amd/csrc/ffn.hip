@@ -28,41 +28,16 @@
 #include <type_traits>
 
 #include "moe_internal.h"
+#include "ring_gemm.h"
+#include "tile_map.h"
 
 namespace moe {
 namespace {
 
 constexpr int KC = 64;  // bf16 K elements per LDS stage (128 bytes per row)
 
-// ---------------------------------------------------------------- tile map --
-__global__ __launch_bounds__(512) void build_tile_map(const int32_t* __restrict__ offsets, int E,
-                                                      int BM, int32_t* __restrict__ tile_start) {
-  __shared__ int sc[2][kMaxE];
-  const int e = threadIdx.x;
-  int v = 0;
-  if (e < E) v = (offsets[e + 1] - offsets[e] + BM - 1) / BM;
-  int cur = 0;
-  sc[0][e] = v;
-  __syncthreads();
-  for (int off = 1; off < kMaxE; off <<= 1) {
-    const int s = sc[cur][e] + (e >= off ? sc[cur][e - off] : 0);
-    sc[cur ^ 1][e] = s;
-    cur ^= 1;
-    __syncthreads();
-  }
-  if (e < E) tile_start[e + 1] = sc[cur][e];
-  if (e == 0) tile_start[0] = 0;
-}
-
-// Expert e with tile_start[e] <= ms < tile_start[e+1] (ms < tile_start[E]).
-__device__ __forceinline__ int find_expert(const int32_t* __restrict__ tile_start, int E, int ms) {
-  int lo = 0, hi = E;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (tile_start[mid] <= ms) lo = mid; else hi = mid;
-  }
-  return lo;
-}
+// The tile map (build_tile_map, find_expert) and the fp32 FMA GEMM live in
+// tile_map.h (shared with the backward pass).
 
 // ------------------------------------------------------------- MFMA GEMM --
 // Block tile: BN weight rows (output features) x BM permuted rows. Four waves
@@ -195,473 +170,8 @@ __global__ __launch_bounds__(256) void gemm_bf16(
   }
 }
 
-// ---------------------------------- MFMA GEMM, 256 x 256 tiles, DMA ring --
-// For experts with a few hundred rows or more. Block tile 256 weight rows x
-// 256 permuted rows, eight waves (two per SIMD, so one wave's MFMAs cover the
-// other's waits) in a 2 x 4 grid, each owning 128 x 64 of the tile as 4 x 2
-// v_mfma_f32_32x32x16_bf16 tiles (128 accumulator floats per lane).
-//
-// v_mfma_f32_32x32x16_bf16: lane l supplies row l%32 and k-octet l/32 of each
-// operand (A = 32 weight rows x 16 k, B = 16 k x 32 permuted rows) and
-// receives D[n = 8*(v/4) + 4*(l/32) + v%4][row = l%32], v = 0..15, i.e. four
-// runs of 4 consecutive output features of one row.
-//
-// Data path: direct global->LDS DMA (16 bytes per lane, no VGPR round trip)
-// of full 128-byte row segments: one DMA instruction moves 8 rows x 64
-// columns, touching 8 cache lines (32-column segments would touch 16 half
-// lines for the same bytes, and the L1/L2 path serves requests, not bytes).
-// A 64-column step of a tile needs four 16 KB blocks (weight rows 0-127 and
-// 128-255, permuted rows 0-127 and 128-255), held in a ring of ten block slots
-// (all 160 KB of LDS): block b of the tile's sequence (step b/4, part b%4)
-// lives in slot b % 10. While step j is computed, step j+1 is landing and
-// half of step j+2 is in flight; at the end of step j, once every wave's
-// fragment reads of it have completed, its four slots take the second half
-// of step j+2 and the first half of step j+3 (1.5 steps, 96 KB, in flight).
-// The ring barrier is an s_barrier with a compiler memory clobber: it keeps
-// LDS accesses on their side without draining the DMA queue, which a
-// workgroup fence would do.
-//
-// LDS rows are 128 bytes (8 chunks of 16 B); chunk c of row r sits at
-// c ^ ((r >> 1) & 7). A ds_read_b128 is served 16 lanes (256 bytes) at a
-// time, and 16 consecutive rows at one chunk then hit 16 distinct 16-byte
-// bank groups. Lane l of a DMA instruction writes chunk slot l%8 of row l/8,
-// so it fetches chunk (l%8) ^ swizzle(row).
-constexpr int kBigBM = 256;          // permuted rows per tile
-constexpr int kBigBN = kBigBNTile;   // weight rows (output features) per tile
-constexpr int kRS = 64;              // K columns per step
-constexpr int kRBlk = 128 * kRS;     // bf16 elements per block (16 KB)
-constexpr int kRSlots = 10;
-constexpr int kMaxSplit = 8;         // K ranges per tail tile
-constexpr int kReduceSlices = 8;     // row slices per tail tile in the reduction
-constexpr int kGroupN = 4;           // weight-row tiles per group of the tile order
-constexpr int kRingWaves = 8;        // waves per 256 x 256 tile
-static_assert(kBigBN == 256, "tile");
-
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-// At most BASE + n vector memory operations outstanding, n in 0..8 (uniform).
-template <int BASE>
-__device__ __forceinline__ void wait_vmcnt_le(int n) {
-  switch (n) {
-    case 0: wait_vmcnt<BASE>(); break;
-    case 1: wait_vmcnt<BASE + 1>(); break;
-    case 2: wait_vmcnt<BASE + 2>(); break;
-    case 3: wait_vmcnt<BASE + 3>(); break;
-    case 4: wait_vmcnt<BASE + 4>(); break;
-    case 5: wait_vmcnt<BASE + 5>(); break;
-    case 6: wait_vmcnt<BASE + 6>(); break;
-    case 7: wait_vmcnt<BASE + 7>(); break;
-    default: wait_vmcnt<BASE + 8>(); break;
-  }
-}
-// Workgroup barrier that the compiler may not move memory accesses across.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-// One 16-byte direct global->LDS load per lane; the LDS address is the
-// wave-uniform base plus 16 * lane.
-__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
-}
-
-__device__ __forceinline__ int swz128(int r, int c) { return c ^ ((r >> 1) & 7); }
-
-// Scheduling hint for a sub-step: alternate one MFMA with one LDS fragment
-// read NR times, then the remaining MFMAs, so the reads for the next
-// sub-step hide behind this one's MFMAs instead of queueing up behind a
-// single lgkmcnt(0) wait.
-template <int NM, int NR>
-__device__ __forceinline__ void interleave_mfma_reads() {
-#pragma unroll
-  for (int i = 0; i < NR; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
-}
-
-// One entry of a launch's work list: the block's tile and K range. The
-// lists are built on the device by big_plan, so a GEMM block starts with one
-// uniform load instead of searching the tile map.
-struct alignas(16) BigWork {
-  int e;           // expert, -1: no work for this block
-  int row0, rows;  // permuted rows of the tile
-  int n0;          // first output feature
-  int kbeg, kend;  // K range in kRS-column steps
-  int unit;        // fp32 partial slot of a split tail tile, -1 for a whole tile
-  int ms;          // row block (index into the token table of the tile's rows)
-};
-static_assert(sizeof(BigWork) == kWorkBytes, "work entry size");
-// Per launch: tiles = whole tiles + tail tiles; the `full` first tiles (a
-// whole number of rounds over the kTailSlots resident blocks) run whole, the
-// `tail` remaining ones are each cut into `split` K ranges so that the last
-// round fills every CU.
-struct BigHdr {
-  int full, tail, split, tiles;
-};
-
-// Largest e with ts[e] <= v (ts in LDS, ts[0] = 0 <= v).
-__device__ __forceinline__ int find_le(const int* ts, int E, int v) {
-  int lo = 0, hi = E;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (ts[mid] <= v) lo = mid; else hi = mid;
-  }
-  return lo;
-}
-
-// Work lists of both GEMMs of the FFN (N = nt * kBigBN features, nk K steps,
-// BM permuted rows per tile). Tile order: expert-major; inside an expert,
-// groups of kGroupN weight-row tiles, inside a group the expert's row blocks.
-// REMAP: entry b is the work of hardware block b, whole tiles dealt to the
-// XCDs in contiguous ranges of that order (block b runs on XCD b % 8), so each
-// XCD's L2 sees a few weight and row panels at a time. Otherwise entries are
-// in that order (whole tiles, then the K ranges of the tail tiles) and the
-// persistent kernel deals them out itself.
-template <int BM, bool REMAP>
-__global__ __launch_bounds__(512) void big_plan(const int32_t* __restrict__ offsets, int E,
-                                                int nt1, int nk1, int g1, int nt2, int nk2,
-                                                int g2, BigHdr* __restrict__ hdr,
-                                                BigWork* __restrict__ list1,
-                                                BigWork* __restrict__ list2,
-                                                const int32_t* __restrict__ sorted_token,
-                                                int32_t* __restrict__ tok_tab) {
-  __shared__ int sc[2][kMaxE];
-  __shared__ int ts[kMaxE + 1];
-  const int x = threadIdx.x;  // blockDim == kMaxE
-  int cur = 0;
-  sc[0][x] = x < E ? (offsets[x + 1] - offsets[x] + BM - 1) / BM : 0;
-  __syncthreads();
-  for (int off = 1; off < kMaxE; off <<= 1) {
-    const int v = sc[cur][x] + (x >= off ? sc[cur][x - off] : 0);
-    sc[cur ^ 1][x] = v;
-    cur ^= 1;
-    __syncthreads();
-  }
-  ts[x + 1] = sc[cur][x];
-  if (x == 0) ts[0] = 0;
-  __syncthreads();
-
-  const int i = blockIdx.x * kMaxE + x;
-  if (i >= g1 + g2) {
-    // token table: entry ms * BM + r = the token of row r of row block ms,
-    // rows past the block's last one repeating it
-    if (!tok_tab) return;
-    const int j = i - g1 - g2, ms = j / BM, r = j % BM;
-    if (ms >= ts[E]) return;
-    const int e = find_le(ts, E, ms);
-    const int row0 = offsets[e] + (ms - ts[e]) * BM;
-    const int rows = min(BM, offsets[e + 1] - row0);
-    tok_tab[j] = sorted_token[row0 + (r < rows ? r : rows - 1)];
-    return;
-  }
-  const bool second = i >= g1;
-  const int b = second ? i - g1 : i;
-  if (second && b >= g2) return;
-  const int nt = second ? nt2 : nt1, nk = second ? nk2 : nk1;
-  BigWork* list = second ? list2 : list1;
-
-  BigHdr sp;
-  sp.tiles = ts[E] * nt;
-  sp.tail = sp.tiles % kTailSlots;
-  sp.full = sp.tiles - sp.tail;
-  sp.split = 1;
-  if (sp.tail > 0) sp.split = max(1, min(min(kTailSlots / sp.tail, kMaxSplit), nk));
-  if (b == 0) hdr[second ? 1 : 0] = sp;
-
-  BigWork w;
-  w.e = -1;
-  w.row0 = w.rows = w.n0 = w.kbeg = w.kend = 0;
-  w.unit = -1;
-  w.ms = 0;
-  int t = -1, p = 0, split = 1;
-  if (b < sp.full) {
-    const int per = sp.full >> 3;
-    t = REMAP ? (b & 7) * per + (b >> 3) : b;
-  } else if (b - sp.full < sp.tail * sp.split) {
-    const int u = b - sp.full;
-    split = sp.split;
-    t = sp.full + u / split;
-    p = u % split;
-  }
-  if (t >= 0) {
-    const int e = find_le(ts, E, t / nt);  // experts own nt * (ts[e+1] - ts[e]) tiles
-    const int mt = ts[e + 1] - ts[e];
-    const int l = t - ts[e] * nt;
-    const int g = l / (mt * kGroupN);
-    const int gs = min(kGroupN, nt - g * kGroupN);
-    const int l2 = l - g * mt * kGroupN;
-    const int mi = l2 / gs, ni = g * kGroupN + l2 % gs;
-    w.e = e;
-    w.row0 = offsets[e] + mi * BM;
-    w.rows = min(BM, offsets[e + 1] - w.row0);
-    w.n0 = ni * kBigBN;
-    w.kbeg = p * nk / split;
-    w.kend = (p + 1) * nk / split;
-    w.unit = split > 1 ? (t - sp.full) * split + p : -1;
-    w.ms = ts[e] + mi;
-  }
-  list[b] = w;
-}
-
-// Epilogue of a 256 x 256 tile, each of NW waves holding 128 x (32 TM) of it
-// as 4 x TM 32x32 MFMA accumulators. A split tail tile stores its fp32 partial
-// [256 rows][256 features] for big_tail_reduce; a whole tile adds the bias,
-// applies SiLU if asked, rounds to bf16 into LDS (ot, the idle ring), and
-// leaves with 16-byte stores of whole rows: 32 lanes write one 512-byte row.
-// LDS rows are padded by 16 bytes so the 32 rows a wave writes at one feature
-// offset spread over the banks.
-template <int NW, int TM, bool SILU>
-__device__ __forceinline__ void big_store(f32x16 (&acc)[4][TM], uint16_t* ot, size_t ot_bytes,
-                                          const BigWork& wk, const uint16_t* __restrict__ bias,
-                                          uint16_t* __restrict__ out, float* __restrict__ part,
-                                          int N, int wn, int wm, int lane, int tid) {
-  constexpr int BM = kBigBM, BN = kBigBN, TN = 4, WTN = 128, WTM = 32 * TM;
-  const int ch = lane >> 5;
-  if (wk.unit >= 0) {
-    float* pp = part + (size_t)wk.unit * (BM * BN);
-#pragma unroll
-    for (int i = 0; i < TN; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int nl = wn * WTN + i * 32 + 8 * q + 4 * ch;
-#pragma unroll
-        for (int j = 0; j < TM; ++j) {
-          const int m = wm * WTM + j * 32 + (lane & 31);
-          *(f32x4*)(pp + m * BN + nl) =
-              f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-        }
-      }
-    return;
-  }
-  constexpr int OSTR = BN + 8;  // LDS row stride in bf16 elements
-  (void)ot_bytes;  // callers static_assert BM * OSTR * 2 <= ot_bytes
-  lds_barrier();  // every wave is done reading the ring
-#pragma unroll
-  for (int i = 0; i < TN; ++i) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int nl = wn * WTN + i * 32 + 8 * q + 4 * ch;
-      float bv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (bias) {
-        const u32x2 bb = *(const u32x2*)(bias + (size_t)wk.e * N + wk.n0 + nl);
-        bv[0] = bf16lo(bb[0]);
-        bv[1] = bf16hi(bb[0]);
-        bv[2] = bf16lo(bb[1]);
-        bv[3] = bf16hi(bb[1]);
-      }
-#pragma unroll
-      for (int j = 0; j < TM; ++j) {
-        const int m = wm * WTM + j * 32 + (lane & 31);
-        float v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          v[u] = acc[i][j][4 * q + u] + bv[u];
-          if (SILU) v[u] = silu_bf16(v[u]);
-        }
-        u32x2 o;
-        o[0] = pack_bf16x2(v[0], v[1]);
-        o[1] = pack_bf16x2(v[2], v[3]);
-        *(u32x2*)(ot + m * OSTR + nl) = o;
-      }
-    }
-  }
-  __syncthreads();
-  constexpr int CPR = BN / 8;  // 16-byte chunks per row
-#pragma unroll 4
-  for (int c = tid; c < BM * CPR; c += NW * 64) {
-    const int m = c / CPR, cc = c % CPR;
-    if (m < wk.rows)
-      *(u32x4*)(out + (size_t)(wk.row0 + m) * N + wk.n0 + cc * 8) =
-          *(const u32x4*)(ot + m * OSTR + cc * 8);
-  }
-}
-
-template <int NW, bool GATHER, bool SILU>
-__global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
-    const uint16_t* __restrict__ act, const int32_t* __restrict__ sorted_token,
-    const BigWork* __restrict__ work, const uint16_t* __restrict__ w,
-    const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, float* __restrict__ part, int N,
-    int K) {
-  constexpr int BM = kBigBM, BN = kBigBN;
-  constexpr int WM = NW / 2;          // waves along the permuted rows (2 along the weight rows)
-  constexpr int TN = 4, TM = 8 / WM;  // 32x32 MFMA tiles per wave
-  constexpr int WTM = 32 * TM;        // permuted rows per wave
-  constexpr int IPB = 16 / NW;        // DMA instructions per wave per 16 KB block
-  static_assert(NW == 4 || NW == 8, "waves");
-  __shared__ __align__(1024) uint16_t ring[kRSlots * kRBlk];
-  static_assert((size_t)BM * (BN + 8) * 2 <= sizeof(ring), "output tile must fit the ring");
-
-  const BigWork wk = work[blockIdx.x];
-  if (wk.e < 0) return;
-  const int e = wk.e, row0 = wk.row0, rows = wk.rows, n0 = wk.n0, kbeg = wk.kbeg;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // Waves alternate along the weight rows, so the waves holding the first
-  // permuted rows sit on different SIMDs (wave w runs on SIMD w % 4).
-  const int wn = wave % 2, wm = wave / 2;
-  // Tiles with few rows (an expert's last row block) skip the work of rows
-  // past the last: a wave whose permuted rows are all past it issues no
-  // MFMAs, and DMA instructions whose 8 rows are all past it are not issued.
-  const bool active = wm * WTM < rows;
-  auto b_live = [&](int q, int i) { return (q - 2) * 128 + i * NW * 8 + wave * 8 < rows; };
-  int nbi = 0;  // activation DMA instructions this wave issues per step
-#pragma unroll
-  for (int q = 2; q < 4; ++q)
-#pragma unroll
-    for (int i = 0; i < IPB; ++i) nbi += b_live(q, i) ? 1 : 0;
-
-  // part q of a step: 0/1 weight rows 0-127 / 128-255, 2/3 permuted rows 0-127 /
-  // 128-255; each wave moves row groups (i * NW + wave) * 8 .. +7, i < IPB.
-  // Weight rows are one per-lane base plus a uniform row offset; activation
-  // rows are gathered, kept as 32-bit element offsets (R * K < 2^31 is
-  // checked on the host). The swizzle depends on r only through (r >> 1) & 7,
-  // which the uniform offsets (multiples of 8 rows) leave unchanged.
-  const int r0 = wave * 8 + (lane >> 3);
-  const int c0 = swz128(r0, lane & 7) * 8;
-  const uint16_t* wbase = w + ((size_t)e * N + n0 + r0) * K + c0;
-  uint32_t boff[2][IPB];
-#pragma unroll
-  for (int q = 0; q < 2; ++q)
-#pragma unroll
-    for (int i = 0; i < IPB; ++i) {
-      const int pr = q * 128 + i * NW * 8 + r0;
-      const int rr = row0 + (pr < rows ? pr : rows - 1);
-      const uint32_t tok = GATHER ? (uint32_t)sorted_token[rr] : (uint32_t)rr;
-      boff[q][i] = tok * (uint32_t)K + c0;
-    }
-  auto issue = [&](auto qc, int step, int slot) {
-    constexpr int q = decltype(qc)::value;
-    const int koff = (kbeg + step) * kRS;
-    uint16_t* dst = ring + slot * kRBlk;
-#pragma unroll
-    for (int i = 0; i < IPB; ++i) {
-      if (q >= 2 && !b_live(q, i)) continue;
-      const uint16_t* g = q < 2 ? wbase + (size_t)(q * 128 + i * NW * 8) * K + koff
-                                : act + boff[q & 1][i] + koff;
-      dma16(g, dst + (i * NW + wave) * 8 * kRS);
-    }
-  };
-  using Q0 = std::integral_constant<int, 0>;
-  using Q1 = std::integral_constant<int, 1>;
-  using Q2 = std::integral_constant<int, 2>;
-  using Q3 = std::integral_constant<int, 3>;
-
-  f32x16 acc[TN][TM];
-#pragma unroll
-  for (int i = 0; i < TN; ++i)
-#pragma unroll
-    for (int j = 0; j < TM; ++j) acc[i][j] = f32x16{};
-
-  const int ns = wk.kend - kbeg;
-  // blocks 0..9: steps 0 and 1, and the weight half of step 2
-#pragma unroll
-  for (int st = 0; st < 2; ++st)
-    if (st < ns) {
-      issue(Q0{}, st, 4 * st);
-      issue(Q1{}, st, 4 * st + 1);
-      issue(Q2{}, st, 4 * st + 2);
-      issue(Q3{}, st, 4 * st + 3);
-    }
-  if (2 < ns) {
-    issue(Q0{}, 2, 8);
-    issue(Q1{}, 2, 9);
-  }
-
-  const int ch = lane >> 5;
-  const int bq = (wm * WTM) >> 7;      // the permuted-row block this wave reads
-  const int br = (wm * WTM) & 127;     // its first row inside that block
-  bf16x8 f0a[TN], f0b[TM], f1a[TN], f1b[TM];
-  int sa, sb;  // slots of this wave's weight block and permuted-row block in the current step
-#define MOE_SLOTS(step)                                    \
-  do {                                                     \
-    const int b_ = (4 * (step)) % kRSlots;                 \
-    const int a_ = b_ + wn, c_ = b_ + 2 + bq;              \
-    sa = a_ < kRSlots ? a_ : a_ - kRSlots;                 \
-    sb = c_ < kRSlots ? c_ : c_ - kRSlots;                 \
-  } while (0)
-#define MOE_RD(sub, FA, FB)                                                            \
-  if constexpr (ACT) {                                                                 \
-    const uint16_t* sa_ = ring + sa * kRBlk;                                           \
-    const uint16_t* sb_ = ring + sb * kRBlk;                                           \
-    _Pragma("unroll") for (int i = 0; i < TN; ++i) {                                   \
-      const int r = i * 32 + (lane & 31);                                              \
-      FA[i] = *(const bf16x8*)(sa_ + r * kRS + swz128(r, 2 * (sub) + ch) * 8);         \
-    }                                                                                  \
-    _Pragma("unroll") for (int j = 0; j < TM; ++j) {                                   \
-      const int r = br + j * 32 + (lane & 31);                                         \
-      FB[j] = *(const bf16x8*)(sb_ + r * kRS + swz128(r, 2 * (sub) + ch) * 8);         \
-    }                                                                                  \
-  }
-#define MOE_MM(FA, FB)                                                                 \
-  do {                                                                                 \
-    if constexpr (ACT)                                                                 \
-    _Pragma("unroll") for (int i = 0; i < TN; ++i)                                     \
-    _Pragma("unroll") for (int j = 0; j < TM; ++j)                                     \
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[i], FB[j], acc[i][j], 0, 0, 0); \
-  } while (0)
-
-  // step 0 landed: the blocks of steps 1 and 2 may still be in flight, i.e.
-  // this wave's DMAs of step 1 (both weight halves and its nbi activation
-  // instructions) and of the weight half of step 2
-  if (ns > 2) wait_vmcnt_le<4 * IPB>(nbi); else if (ns > 1) wait_vmcnt_le<2 * IPB>(nbi); else wait_vmcnt<0>();
-  lds_barrier();
-  // the loop twice over: with MFMAs for waves that own live rows, without
-  // for the others (barriers and DMA issue are the same)
-  auto main_loop = [&](auto act_c) {
-  constexpr bool ACT = decltype(act_c)::value;
-  MOE_SLOTS(0);
-  MOE_RD(0, f0a, f0b);
-  for (int j = 0; j < ns; ++j) {
-    MOE_RD(1, f1a, f1b);
-    MOE_MM(f0a, f0b);
-    if constexpr (ACT) interleave_mfma_reads<TN * TM, TN + TM>();
-    MOE_RD(2, f0a, f0b);
-    MOE_MM(f1a, f1b);
-    if constexpr (ACT) interleave_mfma_reads<TN * TM, TN + TM>();
-    MOE_RD(3, f1a, f1b);
-    MOE_MM(f0a, f0b);
-    if constexpr (ACT) interleave_mfma_reads<TN * TM, TN + TM>();
-    if (j + 1 < ns) {
-      // step j+1 landed (only the weight half of step j+2 may be in flight),
-      // and this wave's reads of step j are done before its slots are refilled
-      if (j + 2 < ns) wait_vmcnt<2 * IPB>(); else wait_vmcnt<0>();
-      wait_lgkmcnt0();
-      lds_barrier();
-      const int b0 = (4 * j) % kRSlots;
-      const int b1 = b0 + 1 < kRSlots ? b0 + 1 : b0 + 1 - kRSlots;
-      const int b2 = b0 + 2 < kRSlots ? b0 + 2 : b0 + 2 - kRSlots;
-      const int b3 = b0 + 3 < kRSlots ? b0 + 3 : b0 + 3 - kRSlots;
-      if (j + 2 < ns) {
-        issue(Q2{}, j + 2, b0);
-        issue(Q3{}, j + 2, b1);
-      }
-      if (j + 3 < ns) {
-        issue(Q0{}, j + 3, b2);
-        issue(Q1{}, j + 3, b3);
-      }
-    }
-    // the first fragments of step j+1 (after the last step these read stale
-    // slots into registers nobody uses)
-    MOE_SLOTS(j + 1);
-    MOE_RD(0, f0a, f0b);
-    MOE_MM(f1a, f1b);
-    if constexpr (ACT) interleave_mfma_reads<TN * TM, TN + TM>();
-  }
-  };
-  if (active) main_loop(std::true_type{});
-  else main_loop(std::false_type{});
-#undef MOE_SLOTS
-#undef MOE_RD
-#undef MOE_MM
-
-  big_store<NW, TM, SILU>(acc, ring, sizeof(ring), wk, bias, out, part, N, wn, wm, lane, tid);
-}
+// The 256 x 256 DMA-ring GEMM, its work lists, epilogue and tail reduction
+// live in ring_gemm.h (shared with the backward pass).
 
 // ------------------------------------------------ persistent DMA-ring GEMM --
 // One block per CU walks its share of the launch's tiles with a single DMA
@@ -941,52 +451,6 @@ __global__ __launch_bounds__(512) void gemm_bf16_pring(
 #undef MOE_MM
 }
 
-// Tail tiles: out = act(sum_p partial[p] + bias), partials summed in order of
-// their K-range, so the result does not depend on timing. kReduceSlices
-// blocks per tail tile, each over BM/8 rows; a thread owns 8 consecutive
-// features of every 8th row of its slice.
-template <int BM, bool SILU>
-__global__ __launch_bounds__(256) void big_tail_reduce(const BigHdr* __restrict__ hdr,
-                                                       const BigWork* __restrict__ work,
-                                                       const uint16_t* __restrict__ bias,
-                                                       const float* __restrict__ part,
-                                                       uint16_t* __restrict__ out, int N) {
-  const BigHdr sp = *hdr;
-  const int tt = blockIdx.x / kReduceSlices, slice = blockIdx.x % kReduceSlices;
-  if (tt >= sp.tail || sp.split < 2) return;
-  const BigWork tile = work[sp.full + tt * sp.split];  // the tile's first K range
-  const int nl = (threadIdx.x & 31) * 8;
-  float bv[8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u)
-    bv[u] = bias ? bf16_to_f32(bias[(size_t)tile.e * N + tile.n0 + nl + u]) : 0.0f;
-  constexpr int RS = BM / kReduceSlices;
-  const float* base = part + (size_t)tt * sp.split * (BM * kBigBN);
-  const int mend = min(tile.rows, (slice + 1) * RS);
-  for (int m = slice * RS + (threadIdx.x >> 5); m < mend; m += 8) {
-    float v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = 0.0f;
-    for (int p = 0; p < sp.split; ++p) {
-      const float* src = base + (size_t)p * (BM * kBigBN) + m * kBigBN + nl;
-      const f32x4 lo = *(const f32x4*)src, hi = *(const f32x4*)(src + 4);
-      v[0] += lo[0]; v[1] += lo[1]; v[2] += lo[2]; v[3] += lo[3];
-      v[4] += hi[0]; v[5] += hi[1]; v[6] += hi[2]; v[7] += hi[3];
-    }
-    u32x4 o;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float a = v[2 * q] + bv[2 * q], c = v[2 * q + 1] + bv[2 * q + 1];
-      if (SILU) {
-        a = silu_bf16(a);
-        c = silu_bf16(c);
-      }
-      o[q] = pack_bf16x2(a, c);
-    }
-    *(u32x4*)(out + (size_t)(tile.row0 + m) * N + tile.n0 + nl) = o;
-  }
-}
-
 // ------------------------------------------------------ decode streaming --
 // Grid (ceil(N / 16), E). Each wave owns 4 consecutive output features and
 // computes them for up to G rows of expert e at a time; the rows' activations
@@ -1093,81 +557,6 @@ __global__ __launch_bounds__(256) void decode_bf16(
     __syncthreads();
   }
 }
-
-// ---------------------------------------------------------------- fp32 ----
-constexpr int FB = 64;   // tile edge
-constexpr int FKC = 16;  // K step
-
-template <bool GATHER, bool SILU>
-__global__ __launch_bounds__(256) void gemm_f32(
-    const float* __restrict__ act, const int32_t* __restrict__ sorted_token,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_start,
-    const float* __restrict__ w, const float* __restrict__ bias, float* __restrict__ out, int E,
-    int N, int K, int mslots) {
-  __shared__ float sW[FKC][FB + 4];
-  __shared__ float sX[FKC][FB + 4];
-  const int ms = blockIdx.x % mslots, nt = blockIdx.x / mslots;
-  const int total = tile_start[E];
-  if (ms >= total) return;
-  const int e = find_expert(tile_start, E, ms);
-  const int row0 = offsets[e] + (ms - tile_start[e]) * FB;
-  const int rows = min(FB, offsets[e + 1] - row0);
-  const int n0 = nt * FB;
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-
-  size_t xsrc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (tid + 256 * i) / FKC;
-    const int rr = row0 + (r < rows ? r : rows - 1);
-    xsrc[i] = GATHER ? (size_t)sorted_token[rr] : (size_t)rr;
-  }
-  float acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
-
-  for (int k0 = 0; k0 < K; k0 += FKC) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, r = c / FKC, kk = c % FKC;
-      const int n = n0 + r, kg = k0 + kk;
-      sW[kk][r] = (n < N && kg < K) ? w[((size_t)e * N + n) * K + kg] : 0.0f;
-      sX[kk][r] = (r < rows && kg < K) ? act[xsrc[i] * K + kg] : 0.0f;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < FKC; ++kk) {
-      float a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = sW[kk][tx * 4 + i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = sX[kk][ty * 4 + j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int n = n0 + tx * 4 + i;
-    if (n >= N) continue;
-    const float b = bias ? bias[(size_t)e * N + n] : 0.0f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = ty * 4 + j;
-      if (m < rows) {
-        float v = acc[i][j] + b;
-        if (SILU) v = silu(v);
-        out[(size_t)(row0 + m) * N + n] = v;
-      }
-    }
-  }
-}
-
 // ------------------------------------------------------------ dispatch ----
 constexpr int kBM = 128;
 
@@ -1212,14 +601,16 @@ int launch_ring(const uint16_t* x, const int32_t* sorted_token, const int32_t* o
   hipLaunchKernelGGL((big_plan<kBigBM, true>), dim3(ceil_div(g1 + g2, kMaxE)), dim3(kMaxE), 0, s,
                      offsets, E, h / kBigBN, d / kRS, g1, d / kBigBN, h / kRS, g2, hdr, list1, list2,
                      sorted_token, (int32_t*)nullptr);
-  hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, true, true>), dim3(g1), dim3(kRingWaves * 64), 0, s,
-                     x, sorted_token, list1, w1, b1, H, part, h, d);
-  hipLaunchKernelGGL((big_tail_reduce<kBigBM, true>), gr, dim3(256), 0, s, hdr, list1, b1, part, H,
-                     h);
-  hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, false, false>), dim3(g2), dim3(kRingWaves * 64),
-                     0, s, H, sorted_token, list2, w2, b2, y, part, d, h);
-  hipLaunchKernelGGL((big_tail_reduce<kBigBM, false>), gr, dim3(256), 0, s, hdr + 1, list2, b2, part,
-                     y, d);
+  hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, true, kEpiSilu>), dim3(g1), dim3(kRingWaves * 64),
+                     0, s, x, sorted_token, list1, w1, b1, H, part, h, d, (size_t)h * d, 0,
+                     (const uint16_t*)nullptr);
+  hipLaunchKernelGGL((big_tail_reduce<kBigBM, kEpiSilu>), gr, dim3(256), 0, s, hdr, list1, b1, part,
+                     H, h, (const uint16_t*)nullptr);
+  hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, false, kEpiBias>), dim3(g2), dim3(kRingWaves * 64),
+                     0, s, H, sorted_token, list2, w2, b2, y, part, d, h, (size_t)d * h, 0,
+                     (const uint16_t*)nullptr);
+  hipLaunchKernelGGL((big_tail_reduce<kBigBM, kEpiBias>), gr, dim3(256), 0, s, hdr + 1, list2, b2,
+                     part, y, d, (const uint16_t*)nullptr);
   return launch_status();
 }
 
@@ -1247,11 +638,12 @@ int launch_pring(const uint16_t* x, const int32_t* sorted_token, const int32_t* 
                      list2, sorted_token, tok);
   hipLaunchKernelGGL((gemm_bf16_pring<BM, true, true>), dim3(kTailSlots), dim3(512), 0, s, x, tok,
                      hdr, list1, w1, b1, H, part, h, d);
-  hipLaunchKernelGGL((big_tail_reduce<BM, true>), gr, dim3(256), 0, s, hdr, list1, b1, part, H, h);
+  hipLaunchKernelGGL((big_tail_reduce<BM, kEpiSilu>), gr, dim3(256), 0, s, hdr, list1, b1, part, H, h,
+                     (const uint16_t*)nullptr);
   hipLaunchKernelGGL((gemm_bf16_pring<BM, false, false>), dim3(kTailSlots), dim3(512), 0, s, H,
                      (const int32_t*)nullptr, hdr + 1, list2, w2, b2, y, part, d, h);
-  hipLaunchKernelGGL((big_tail_reduce<BM, false>), gr, dim3(256), 0, s, hdr + 1, list2, b2, part, y,
-                     d);
+  hipLaunchKernelGGL((big_tail_reduce<BM, kEpiBias>), gr, dim3(256), 0, s, hdr + 1, list2, b2, part,
+                     y, d, (const uint16_t*)nullptr);
   return launch_status();
 }
 

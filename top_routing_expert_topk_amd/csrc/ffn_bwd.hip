@@ -1,0 +1,458 @@
+// Backward pass of the grouped expert FFN (the Expert module of page
+// "MoE混合专家模型路由机制原理与稀疏激活实现", section "Top-K门控路由的PyTorch实现",
+// y = W2 SiLU(W1 x + b1) + b2, run over each expert's rows of the
+// permutation). Given dY (the gradient of the permuted outputs) it returns
+//   dZ  = (dY W2[e]) * SiLU'(Z),   Z = W1[e] x[sorted_token] + b1[e]
+//   dXp = dZ W1[e]                 (per permuted row, summed into dx later)
+//   dW2[e] = dY_e^T SiLU(Z_e),  db2[e] = sum of dY_e rows
+//   dW1[e] = dZ_e^T X_e,        db1[e] = sum of dZ_e rows
+// Z is recomputed from x rather than kept from the forward.
+//
+// bf16 data path: every product runs on the 256 x 256 DMA-ring MFMA GEMM,
+// whose operands are K-contiguous rows. The data gradients contract over
+// the weights' leading index, so the weights are first transposed into the
+// workspace (W^T[e] is the forward layout of the transposed product). The
+// weight gradients contract over the rows of an expert: dY, SiLU(Z), dZ and
+// the gathered x rows are transposed into [feature][row] arrays in which
+// every expert's rows form a segment padded with zeros to a multiple of 64,
+// so an expert's K range is whole 64-column steps; one tile per (expert,
+// 256 x 256 output block) runs over its expert's segment.
+//
+// fp32 data path: FMA tiles read the operands in place.
+#include "moe_internal.h"
+#include "ring_gemm.h"
+#include "tile_map.h"
+
+namespace moe {
+namespace {
+
+constexpr int kTB = 64;  // transpose tile edge; also the row padding of an expert segment
+
+// wt[e][b][a] = w[e][a][b] for bf16 w [E][A][B], 64 x 64 tiles through LDS.
+__global__ __launch_bounds__(256) void transpose_w(const uint16_t* __restrict__ w, int A, int B,
+                                                   uint16_t* __restrict__ wt) {
+  __shared__ uint32_t tile[kTB][kTB / 2 + 1];  // bf16 pairs, row i = source row a0 + i
+  const int b0 = blockIdx.x * kTB, a0 = blockIdx.y * kTB;
+  const size_t eo = (size_t)blockIdx.z * A * B;
+  const int tid = threadIdx.x, ch = tid & 7;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int i = pass * 32 + (tid >> 3);
+    const u32x4 v = *(const u32x4*)(w + eo + (size_t)(a0 + i) * B + b0 + ch * 8);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) tile[i][ch * 4 + q] = v[q];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int c = pass * 32 + (tid >> 3);  // destination row b0 + c
+    const int sh = (c & 1) * 16;
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t lo = (tile[ch * 8 + 2 * q][c >> 1] >> sh) & 0xFFFFu;
+      const uint32_t hi = (tile[ch * 8 + 2 * q + 1][c >> 1] >> sh) & 0xFFFFu;
+      o[q] = lo | (hi << 16);
+    }
+    *(u32x4*)(wt + eo + (size_t)(b0 + c) * A + a0 + ch * 8) = o;
+  }
+}
+
+// Padded transpose of an expert-ordered row array: for the 64-row segment p
+// of expert e (pt[e] <= p < pt[e+1], pt in 64-row units),
+//   dst[c][64 p + i] = f(src[row][c]),  row = offsets[e] + 64 (p - pt[e]) + i,
+// and 0 where row is past the expert's last. MODE 0: f = identity; 1: f =
+// SiLU (bf16 in, bf16 out); 2: the row is gathered, src[sorted_token[row]].
+template <int MODE>
+__global__ __launch_bounds__(256) void transpose_pad(const uint16_t* __restrict__ src,
+                                                     const int32_t* __restrict__ sorted_token,
+                                                     const int32_t* __restrict__ offsets,
+                                                     const int32_t* __restrict__ pt, int E, int C,
+                                                     size_t ldd, uint16_t* __restrict__ dst) {
+  __shared__ uint32_t tile[kTB][kTB / 2 + 1];
+  const int p = blockIdx.x, c0 = blockIdx.y * kTB;
+  if (p >= pt[E]) return;
+  const int e = find_expert(pt, E, p);
+  const int r0 = offsets[e] + (p - pt[e]) * kTB, rend = offsets[e + 1];
+  const int tid = threadIdx.x, ch = tid & 7;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int i = pass * 32 + (tid >> 3);
+    const int r = r0 + i;
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (r < rend) {
+      const size_t srow = MODE == 2 ? (size_t)sorted_token[r] : (size_t)r;
+      v = *(const u32x4*)(src + srow * C + c0 + ch * 8);
+      if (MODE == 1) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = pack_bf16x2(silu_bf16(bf16lo(v[q])), silu_bf16(bf16hi(v[q])));
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) tile[i][ch * 4 + q] = v[q];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int c = pass * 32 + (tid >> 3);
+    const int sh = (c & 1) * 16;
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t lo = (tile[ch * 8 + 2 * q][c >> 1] >> sh) & 0xFFFFu;
+      const uint32_t hi = (tile[ch * 8 + 2 * q + 1][c >> 1] >> sh) & 0xFFFFu;
+      o[q] = lo | (hi << 16);
+    }
+    *(u32x4*)(dst + (size_t)(c0 + c) * ldd + (size_t)p * kTB + ch * 8) = o;
+  }
+}
+
+// Work list of a weight-gradient GEMM: one whole tile per (expert, 256-row
+// block of the M output rows, 256 output features), K range = the expert's
+// padded segment (empty for an expert with no rows: the tile stores zeros).
+// Tile order as in big_plan (expert-major, groups of kGroupN feature tiles,
+// row blocks inside a group); when the count allows, hardware block b (on
+// XCD b % 8) takes tile (b % 8) * tiles/8 + b / 8, so each XCD works through
+// one contiguous range.
+__global__ __launch_bounds__(256) void wgrad_plan(const int32_t* __restrict__ pt, int E, int mt,
+                                                  int nt, BigWork* __restrict__ list) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  const int tiles = E * mt * nt;
+  if (b >= tiles) return;
+  const int t = (tiles & 7) == 0 ? (b & 7) * (tiles >> 3) + (b >> 3) : b;
+  const int e = t / (mt * nt), l = t % (mt * nt);
+  const int g = l / (mt * kGroupN);
+  const int gs = min(kGroupN, nt - g * kGroupN);
+  const int l2 = l - g * mt * kGroupN;
+  BigWork w;
+  w.e = e;
+  w.row0 = (l2 / gs) * kBigBM;
+  w.rows = kBigBM;
+  w.n0 = (g * kGroupN + l2 % gs) * kBigBN;
+  w.kbeg = pt[e];
+  w.kend = pt[e + 1];
+  w.unit = -1;
+  w.ms = 0;
+  list[b] = w;
+}
+
+// db[e][c] = sum of g[row][c] over expert e's rows in ascending order.
+// Grid (ceil(C / 512), E); a thread owns two adjacent features.
+template <typename T>
+__global__ __launch_bounds__(256) void bias_grad(const T* __restrict__ g,
+                                                 const int32_t* __restrict__ offsets, int C,
+                                                 T* __restrict__ db) {
+  const int e = blockIdx.y, c = (blockIdx.x * 256 + threadIdx.x) * 2;
+  if (c >= C) return;
+  const int r0 = offsets[e], r1 = offsets[e + 1];
+  float a0 = 0.0f, a1 = 0.0f;
+  if constexpr (std::is_same<T, uint16_t>::value) {
+    int r = r0;
+    for (; r + 4 <= r1; r += 4) {
+      uint32_t v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = *(const uint32_t*)(g + (size_t)(r + u) * C + c);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        a0 += bf16lo(v[u]);
+        a1 += bf16hi(v[u]);
+      }
+    }
+    for (; r < r1; ++r) {
+      const uint32_t v = *(const uint32_t*)(g + (size_t)r * C + c);
+      a0 += bf16lo(v);
+      a1 += bf16hi(v);
+    }
+    *(uint32_t*)(db + (size_t)e * C + c) = pack_bf16x2(a0, a1);
+  } else {
+    const bool two = c + 1 < C;
+    for (int r = r0; r < r1; ++r) {
+      a0 += g[(size_t)r * C + c];
+      if (two) a1 += g[(size_t)r * C + c + 1];
+    }
+    db[(size_t)e * C + c] = a0;
+    if (two) db[(size_t)e * C + c + 1] = a1;
+  }
+}
+
+// fp32: d/dz SiLU(z) with the library exp.
+__device__ __forceinline__ float silu_grad_f32(float z) {
+  const float s = 1.0f / (1.0f + expf(-z));
+  return s * (1.0f + z * (1.0f - s));
+}
+
+// fp32 data gradient: out[r][n] = (sum_k a[r][k] w[e][k][n]) (* SiLU'(z[r][n])
+// when DSILU) over expert e's rows (64-row tiles of the tile map), w [E][K][N].
+template <bool DSILU>
+__global__ __launch_bounds__(256) void gemm_f32_dgrad(
+    const float* __restrict__ a, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ tile_start, const float* __restrict__ w,
+    const float* __restrict__ z, float* __restrict__ out, int E, int N, int K, int mslots) {
+  __shared__ float sW[FKC][FB + 4];
+  __shared__ float sA[FKC][FB + 4];
+  const int ms = blockIdx.x % mslots, nt = blockIdx.x / mslots;
+  if (ms >= tile_start[E]) return;
+  const int e = find_expert(tile_start, E, ms);
+  const int row0 = offsets[e] + (ms - tile_start[e]) * FB;
+  const int rows = min(FB, offsets[e + 1] - row0);
+  const int n0 = nt * FB;
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += FKC) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;
+      {  // weights: consecutive threads along n
+        const int r = c % FB, kk = c / FB, n = n0 + r, kg = k0 + kk;
+        sW[kk][r] = (n < N && kg < K) ? w[((size_t)e * K + kg) * N + n] : 0.0f;
+      }
+      {  // rows: consecutive threads along k
+        const int r = c / FKC, kk = c % FKC, kg = k0 + kk;
+        sA[kk][r] = (r < rows && kg < K) ? a[(size_t)(row0 + r) * K + kg] : 0.0f;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < FKC; ++kk) {
+      float wv[4], av[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wv[i] = sW[kk][tx * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) av[j] = sA[kk][ty * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(wv[i], av[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = n0 + tx * 4 + i;
+    if (n >= N) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = ty * 4 + j;
+      if (m < rows) {
+        const size_t o = (size_t)(row0 + m) * N + n;
+        out[o] = DSILU ? acc[i][j] * silu_grad_f32(z[o]) : acc[i][j];
+      }
+    }
+  }
+}
+
+// fp32 weight gradient: out[e][m][n] = sum over expert e's rows r (in
+// order) of a[r][m] * f(b[src(r)][n]), src(r) = sorted_token[r] when GATHER,
+// f = SiLU when SILU. Grid (ceil(M/64) * ceil(N/64), E).
+template <bool GATHER, bool SILU>
+__global__ __launch_bounds__(256) void gemm_f32_wgrad(const float* __restrict__ a,
+                                                      const float* __restrict__ b,
+                                                      const int32_t* __restrict__ sorted_token,
+                                                      const int32_t* __restrict__ offsets, int M,
+                                                      int N, float* __restrict__ out) {
+  __shared__ float sA[FKC][FB + 4];
+  __shared__ float sB[FKC][FB + 4];
+  const int nmt = (M + FB - 1) / FB;
+  const int m0 = (blockIdx.x % nmt) * FB, n0 = (blockIdx.x / nmt) * FB, e = blockIdx.y;
+  const int r0 = offsets[e], r1 = offsets[e + 1];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  float acc[4][4] = {};
+  for (int k0 = r0; k0 < r1; k0 += FKC) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i, col = c % FB, kk = c / FB, r = k0 + kk;
+      const bool live = r < r1;
+      const int m = m0 + col, n = n0 + col;
+      sA[kk][col] = (live && m < M) ? a[(size_t)r * M + m] : 0.0f;
+      float v = 0.0f;
+      if (live && n < N) {
+        const size_t src = GATHER ? (size_t)sorted_token[r] : (size_t)r;
+        v = b[src * N + n];
+        if (SILU) v = silu(v);
+      }
+      sB[kk][col] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < FKC; ++kk) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[i] = sA[kk][tx * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bv[j] = sB[kk][ty * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + tx * 4 + i;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + ty * 4 + j;
+      if (n < N) out[((size_t)e * M + m) * N + n] = acc[i][j];
+    }
+  }
+}
+
+int ffn_backward_f32(const float* x, int T, int d, int h, int E, int k, const int32_t* offsets,
+                     const int32_t* sorted_token, const float* w1, const float* b1,
+                     const float* w2, const float* dy, float* dxp, float* dw1, float* db1,
+                     float* dw2, float* db2, void* ws, hipStream_t s) {
+  const FfnBwdLayout L = ffn_bwd_layout(T, d, h, E, k);
+  unsigned char* base = (unsigned char*)ws;
+  int32_t* tile_start = (int32_t*)base;
+  float* Z = (float*)(base + L.z);
+  float* dZ = (float*)(base + L.dz);
+  const long rows = (long)T * k;
+  const int nonempty = (int)(rows < E ? rows : E);
+  const int mslots = ceil_div(rows, FB) + nonempty;
+  hipLaunchKernelGGL(build_tile_map, dim3(1), dim3(512), 0, s, offsets, E, FB, tile_start);
+  if (rows > 0) {
+    hipLaunchKernelGGL((gemm_f32<true, false>), dim3(mslots * ceil_div(h, FB)), dim3(256), 0, s, x,
+                       sorted_token, offsets, tile_start, w1, b1, Z, E, h, d, mslots);
+    // dZ = (dY W2[e]) * SiLU'(Z): W2[e] is [d][h] = [K][N]
+    hipLaunchKernelGGL((gemm_f32_dgrad<true>), dim3(mslots * ceil_div(h, FB)), dim3(256), 0, s, dy,
+                       offsets, tile_start, w2, Z, dZ, E, h, d, mslots);
+    // dXp = dZ W1[e]: W1[e] is [h][d] = [K][N]
+    hipLaunchKernelGGL((gemm_f32_dgrad<false>), dim3(mslots * ceil_div(d, FB)), dim3(256), 0, s, dZ,
+                       offsets, tile_start, w1, (const float*)nullptr, dxp, E, d, h, mslots);
+  }
+  const dim3 g2(ceil_div(d, FB) * ceil_div(h, FB), E);
+  hipLaunchKernelGGL((gemm_f32_wgrad<false, true>), g2, dim3(256), 0, s, dy, (const float*)Z,
+                     sorted_token, offsets, d, h, dw2);
+  hipLaunchKernelGGL((gemm_f32_wgrad<true, false>), g2, dim3(256), 0, s, (const float*)dZ, x,
+                     sorted_token, offsets, h, d, dw1);
+  if (db2)
+    hipLaunchKernelGGL((bias_grad<float>), dim3(ceil_div(d, 512), E), dim3(256), 0, s, dy, offsets,
+                       d, db2);
+  if (db1)
+    hipLaunchKernelGGL((bias_grad<float>), dim3(ceil_div(h, 512), E), dim3(256), 0, s,
+                       (const float*)dZ, offsets, h, db1);
+  return launch_status();
+}
+
+int ffn_backward_bf16(const uint16_t* x, int T, int d, int h, int E, int k,
+                      const int32_t* offsets, const int32_t* sorted_token, const uint16_t* w1,
+                      const uint16_t* b1, const uint16_t* w2, const uint16_t* dy, uint16_t* dxp,
+                      uint16_t* dw1, uint16_t* db1, uint16_t* dw2, uint16_t* db2, void* ws,
+                      hipStream_t s) {
+  const FfnBwdLayout L = ffn_bwd_layout(T, d, h, E, k);
+  unsigned char* base = (unsigned char*)ws;
+  const long rows = (long)T * k;
+  const size_t rp = (size_t)ffn_bwd_rpad(T, E, k);
+  BigHdr* hdr = (BigHdr*)base;
+  const int g1 = ffn_big_grid(rows, E, h, kBigBM), g2 = ffn_big_grid(rows, E, d, kBigBM);
+  BigWork* list1 = (BigWork*)(base + 256);
+  BigWork* list2 = list1 + g1;
+  int32_t* pt = (int32_t*)(base + L.pt);
+  const int md = d / kBigBN, mh = h / kBigBN;
+  BigWork* wl2 = (BigWork*)(base + L.wl);  // dW2: M = d, N = h
+  BigWork* wl1 = wl2 + (size_t)E * md * mh;  // dW1: M = h, N = d
+  uint16_t* Z = (uint16_t*)(base + L.z);
+  uint16_t* dZ = (uint16_t*)(base + L.dz);
+  float* part = (float*)(base + L.part);
+  uint16_t* w1t = (uint16_t*)(base + L.w1t);
+  uint16_t* w2t = (uint16_t*)(base + L.w2t);
+  uint16_t* ta = (uint16_t*)(base + L.ta);
+  uint16_t* tb = (uint16_t*)(base + L.tb);
+  const uint16_t* none = nullptr;
+  const dim3 gr(kTailSlots * kReduceSlices), rb(kRingWaves * 64);
+  const int nwt = E * md * mh;
+
+  hipLaunchKernelGGL((big_plan<kBigBM, true>), dim3(ceil_div(g1 + g2, kMaxE)), dim3(kMaxE), 0, s,
+                     offsets, E, mh, d / kRS, g1, md, h / kRS, g2, hdr, list1, list2, sorted_token,
+                     (int32_t*)nullptr);
+  hipLaunchKernelGGL(build_tile_map, dim3(1), dim3(512), 0, s, offsets, E, kTB, pt);
+  hipLaunchKernelGGL(wgrad_plan, dim3(ceil_div(nwt, 256)), dim3(256), 0, s, (const int32_t*)pt, E,
+                     md, mh, wl2);
+  hipLaunchKernelGGL(wgrad_plan, dim3(ceil_div(nwt, 256)), dim3(256), 0, s, (const int32_t*)pt, E,
+                     mh, md, wl1);
+  // W2[e] [d][h] -> W2^T[e] [h][d];  W1[e] [h][d] -> W1^T[e] [d][h]
+  hipLaunchKernelGGL(transpose_w, dim3(h / kTB, d / kTB, E), dim3(256), 0, s, w2, d, h, w2t);
+  hipLaunchKernelGGL(transpose_w, dim3(d / kTB, h / kTB, E), dim3(256), 0, s, w1, h, d, w1t);
+  // Z = W1[e] x + b1 (the forward's first product without the activation)
+  hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, true, kEpiBias>), dim3(g1), rb, 0, s, x,
+                     sorted_token, list1, w1, b1, Z, part, h, d, (size_t)h * d, 0, none);
+  hipLaunchKernelGGL((big_tail_reduce<kBigBM, kEpiBias>), gr, dim3(256), 0, s, hdr, list1, b1, part,
+                     Z, h, none);
+  // dZ = (dY W2[e]) * SiLU'(Z)
+  hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, false, kEpiDSilu>), dim3(g1), rb, 0, s, dy,
+                     (const int32_t*)nullptr, list1, (const uint16_t*)w2t, none, dZ, part, h, d,
+                     (size_t)h * d, 0, (const uint16_t*)Z);
+  hipLaunchKernelGGL((big_tail_reduce<kBigBM, kEpiDSilu>), gr, dim3(256), 0, s, hdr, list1, none,
+                     part, dZ, h, (const uint16_t*)Z);
+  // dW2[e] = dY_e^T SiLU(Z_e)
+  const int nseg = (int)(rp / kTB);
+  hipLaunchKernelGGL((transpose_pad<0>), dim3(nseg, d / kTB), dim3(256), 0, s, dy,
+                     (const int32_t*)nullptr, offsets, (const int32_t*)pt, E, d, rp, ta);
+  hipLaunchKernelGGL((transpose_pad<1>), dim3(nseg, h / kTB), dim3(256), 0, s, (const uint16_t*)Z,
+                     (const int32_t*)nullptr, offsets, (const int32_t*)pt, E, h, rp, tb);
+  hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, false, kEpiBias>), dim3(nwt), rb, 0, s,
+                     (const uint16_t*)ta, (const int32_t*)nullptr, (const BigWork*)wl2,
+                     (const uint16_t*)tb, none, dw2, part, h, (int)rp, (size_t)0, d, none);
+  // dW1[e] = dZ_e^T X_e
+  hipLaunchKernelGGL((transpose_pad<2>), dim3(nseg, d / kTB), dim3(256), 0, s, x, sorted_token,
+                     offsets, (const int32_t*)pt, E, d, rp, ta);
+  hipLaunchKernelGGL((transpose_pad<0>), dim3(nseg, h / kTB), dim3(256), 0, s, (const uint16_t*)dZ,
+                     (const int32_t*)nullptr, offsets, (const int32_t*)pt, E, h, rp, tb);
+  hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, false, kEpiBias>), dim3(nwt), rb, 0, s,
+                     (const uint16_t*)tb, (const int32_t*)nullptr, (const BigWork*)wl1,
+                     (const uint16_t*)ta, none, dw1, part, d, (int)rp, (size_t)0, h, none);
+  // dXp = dZ W1[e]
+  hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, false, kEpiBias>), dim3(g2), rb, 0, s,
+                     (const uint16_t*)dZ, (const int32_t*)nullptr, list2, (const uint16_t*)w1t, none,
+                     dxp, part, d, h, (size_t)d * h, 0, none);
+  hipLaunchKernelGGL((big_tail_reduce<kBigBM, kEpiBias>), gr, dim3(256), 0, s, hdr + 1, list2, none,
+                     part, dxp, d, none);
+  if (db2)
+    hipLaunchKernelGGL((bias_grad<uint16_t>), dim3(ceil_div(d, 512), E), dim3(256), 0, s, dy,
+                       offsets, d, db2);
+  if (db1)
+    hipLaunchKernelGGL((bias_grad<uint16_t>), dim3(ceil_div(h, 512), E), dim3(256), 0, s,
+                       (const uint16_t*)dZ, offsets, h, db1);
+  return launch_status();
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int moe_grouped_ffn_backward(const void* x, int dtype, int T, int d, int h, int E, int k,
+                                        const int32_t* offsets, const int32_t* sorted_token,
+                                        const void* w1, const void* b1, const void* w2,
+                                        const void* dy_perm, void* dx_perm, void* dw1, void* db1,
+                                        void* dw2, void* db2, void* ws, size_t ws_bytes,
+                                        moe_stream_t stream) {
+  if (T < 0 || d < 1 || h < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID;
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_INVALID;
+  if (E > kMaxE) return MOE_ERR_UNSUPPORTED;
+  const long rows = (long)T * k;
+  if (rows > 0x7FFFFFFFL) return MOE_ERR_UNSUPPORTED;
+  if (!offsets || !w1 || !w2 || !dw1 || !dw2) return MOE_ERR_INVALID;
+  if (rows > 0 && (!x || !sorted_token || !dy_perm || !dx_perm)) return MOE_ERR_INVALID;
+  if (!ws || ws_bytes < ffn_bwd_layout(T, d, h, E, k).total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == MOE_F32)
+    return ffn_backward_f32((const float*)x, T, d, h, E, k, offsets, sorted_token,
+                            (const float*)w1, (const float*)b1, (const float*)w2,
+                            (const float*)dy_perm, (float*)dx_perm, (float*)dw1, (float*)db1,
+                            (float*)dw2, (float*)db2, ws, s);
+  // bf16: 256 x 256 tiles on both widths; 32-bit element offsets of every
+  // row operand (the gathered x rows, the permuted rows and the padded
+  // transposed arrays)
+  const long rp = ffn_bwd_rpad(T, E, k);
+  if ((d % kBigBN) != 0 || (h % kBigBN) != 0) return MOE_ERR_UNSUPPORTED;
+  if ((long)T * d >= (1L << 31) || rows * d >= (1L << 31) || rows * h >= (1L << 31) ||
+      (long)(d > h ? d : h) * rp >= (1L << 31))
+    return MOE_ERR_UNSUPPORTED;
+  return ffn_backward_bf16((const uint16_t*)x, T, d, h, E, k, offsets, sorted_token,
+                           (const uint16_t*)w1, (const uint16_t*)b1, (const uint16_t*)w2,
+                           (const uint16_t*)dy_perm, (uint16_t*)dx_perm, (uint16_t*)dw1,
+                           (uint16_t*)db1, (uint16_t*)dw2, (uint16_t*)db2, ws, s);
+}

@@ -43,6 +43,13 @@ __device__ __forceinline__ float silu_bf16(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
 }
 
+// d/dz SiLU(z) = s (1 + z (1 - s)), s = 1 / (1 + e^-z); same hardware exp2
+// and reciprocal as silu_bf16.
+__device__ __forceinline__ float silu_grad(float z) {
+  const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
+  return s * (1.0f + z * (1.0f - s));
+}
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
   return (1ull << __lane_id()) - 1ull;
 }
@@ -131,6 +138,54 @@ inline size_t ffn_hidden_bytes(int T, int h, int k) { return align_up((size_t)T 
 inline size_t ffn_partial_bytes() { return (size_t)kTailSlots * 256 * 256 * sizeof(float); }
 inline size_t ffn_ws(int T, int d, int h, int E, int k) {
   return ffn_plan_bytes(T, d, h, E, k) + ffn_hidden_bytes(T, h, k) + ffn_partial_bytes();
+}
+
+// Router weight backward: fp32 partial dW_g over S token ranges [S][E][d].
+inline int router_bwd_splits(int T) {
+  const int s = T / 1024;
+  return s < 1 ? 1 : (s > 8 ? 8 : s);
+}
+inline size_t router_bwd_ws(int T, int d, int E) {
+  return align_up((size_t)router_bwd_splits(T) * E * d * sizeof(float), 256);
+}
+
+// FFN backward: [plan of the forward-shaped GEMMs (ffn_plan_bytes)]
+//   [pt: E+1 int32, padded 64-row segment starts] [wgrad work lists: 2 x E x
+//   (d/256)(h/256) entries] [Z: T*k*h x 4 B] [dZ: T*k*h x 4 B]
+//   [tail partials] [W1^T: E*d*h bf16] [W2^T: E*h*d bf16]
+//   [TA, TB: max(d,h) x Rp bf16 each]
+// Rp bounds the padded row count: every expert's rows rounded up to 64.
+inline long ffn_bwd_rpad(int T, int E, int k) {
+  return (long)align_up((size_t)T * k + 63 * (size_t)E, 64);
+}
+struct FfnBwdLayout {
+  size_t pt, wl, z, dz, part, w1t, w2t, ta, tb, total;
+};
+inline FfnBwdLayout ffn_bwd_layout(int T, int d, int h, int E, int k) {
+  FfnBwdLayout L;
+  const size_t rows = (size_t)T * k, rp = (size_t)ffn_bwd_rpad(T, E, k);
+  const size_t wide = (size_t)(d > h ? d : h);
+  size_t o = ffn_plan_bytes(T, d, h, E, k);
+  L.pt = o;
+  o += align_up((size_t)(kMaxE + 1) * sizeof(int32_t), 256);
+  L.wl = o;
+  o += align_up((size_t)2 * E * (d / kBigBNTile) * (h / kBigBNTile) * kWorkBytes, 256);
+  L.z = o;
+  o += align_up(rows * h * 4, 256);
+  L.dz = o;
+  o += align_up(rows * h * 4, 256);
+  L.part = o;
+  o += ffn_partial_bytes();
+  L.w1t = o;
+  o += align_up((size_t)E * d * h * 2, 256);
+  L.w2t = o;
+  o += align_up((size_t)E * d * h * 2, 256);
+  L.ta = o;
+  o += align_up(wide * rp * 2, 256);
+  L.tb = o;
+  o += align_up(wide * rp * 2, 256);
+  L.total = o;
+  return L;
 }
 
 }  // namespace moe

@@ -215,3 +215,71 @@ def moe_layer_forward_cached(x, w_gate, gate_bias, cache: ExpertCache, k, renorm
     N.moe_combine(b.y_perm, b.dest_row, b.topk_gate, T, k, d, x if residual else None, b.out, s)
     N.moe_aux_loss(b.prob_sum, b.counts, T, E, b.f, b.P, b.loss, s)
     return b
+
+
+@dataclasses.dataclass
+class MoEGrads:
+    """Gradients and scratch of one token-choice layer backward."""
+    T: int
+    d: int
+    h: int
+    E: int
+    k: int
+    dtype: torch.dtype
+    device: torch.device
+    has_b1: bool = True
+    has_b2: bool = True
+    has_gate_bias: bool = False
+
+    def __post_init__(self):
+        T, d, h, E, k = self.T, self.d, self.h, self.E, self.k
+        dev, dt, f32 = self.device, self.dtype, torch.float32
+        self.dy_perm = torch.empty((T * k, d), dtype=dt, device=dev)
+        self.dgate = torch.empty((T, k), dtype=f32, device=dev)
+        self.dlogits = torch.empty((T, E), dtype=f32, device=dev)
+        self.dx_perm = torch.empty((T * k, d), dtype=dt, device=dev)
+        self.dx = torch.empty((T, d), dtype=dt, device=dev)
+        self.dw_gate = torch.empty((E, d), dtype=dt, device=dev)
+        self.dgate_bias = torch.empty((E,), dtype=f32, device=dev) if self.has_gate_bias else None
+        self.dw1 = torch.empty((E, h, d), dtype=dt, device=dev)
+        self.db1 = torch.empty((E, h), dtype=dt, device=dev) if self.has_b1 else None
+        self.dw2 = torch.empty((E, d, h), dtype=dt, device=dev)
+        self.db2 = torch.empty((E, d), dtype=dt, device=dev) if self.has_b2 else None
+
+        def ws(op):
+            n = N.moe_workspace_size(op, T, d, h, E, k)
+            return torch.empty((max(n, 1),), dtype=torch.uint8, device=dev)
+
+        self.ws_ffn = ws(N.MOE_OP_FFN_BWD)
+        self.ws_router = ws(N.MOE_OP_ROUTER_BWD)
+
+
+def moe_layer_backward(fwd: MoEBuffers, x, w_gate, gate_bias, w1, b1, w2, b2, dout, renorm=True,
+                       residual=False, daux=0.0, grads: MoEGrads | None = None,
+                       stream=None) -> MoEGrads:
+    """Enqueue the backward of a token-choice layer whose forward ran with
+    want_logits=True into ``fwd``. dout [T][d] in the layer dtype; daux is
+    the weight of the aux loss in the differentiated scalar. Returns the
+    gradient buffers (valid once the stream runs):
+      moe_combine_backward -> moe_router_backward -> moe_grouped_ffn_backward
+      -> moe_gather_backward -> moe_router_weight_backward
+    """
+    T, d = x.shape
+    E = w_gate.shape[0]
+    h = w1.shape[1]
+    k = fwd.k
+    if grads is None:
+        grads = MoEGrads(T, d, h, E, k, x.dtype, x.device, b1 is not None, b2 is not None,
+                         gate_bias is not None)
+    g = grads
+    N.moe_combine_backward(fwd.y_perm, fwd.dest_row, fwd.topk_gate, T, k, d, dout, g.dy_perm,
+                           g.dgate, stream)
+    N.moe_router_backward(fwd.logits, fwd.topk_idx, fwd.topk_gate, g.dgate, fwd.counts, T, E, k,
+                          renorm, daux, g.dlogits, stream)
+    N.moe_grouped_ffn_backward(x, T, d, h, E, k, fwd.offsets, fwd.sorted_token, w1, b1, w2,
+                               g.dy_perm, g.dx_perm, g.dw1, g.db1, g.dw2, g.db2, g.ws_ffn, stream)
+    N.moe_gather_backward(g.dx_perm, fwd.dest_row, T, k, d, dout if residual else None, g.dlogits,
+                          w_gate, E, g.dx, stream)
+    N.moe_router_weight_backward(x, T, d, E, g.dlogits, g.dw_gate, g.dgate_bias, g.ws_router,
+                                 stream)
+    return g

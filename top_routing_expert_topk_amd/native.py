@@ -19,7 +19,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "moe.h")
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_LAUNCH, MOE_ERR_WORKSPACE = range(5)
 MOE_F32, MOE_BF16 = 0, 1
-MOE_OP_ROUTER, MOE_OP_PERMUTE, MOE_OP_FFN = 0, 1, 2
+MOE_OP_ROUTER, MOE_OP_PERMUTE, MOE_OP_FFN, MOE_OP_FFN_BWD, MOE_OP_ROUTER_BWD = 0, 1, 2, 3, 4
 
 _DTYPE = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
 
@@ -61,9 +61,18 @@ def lib():
         L.moe_cache_slot_of.argtypes = [P, P, P]
         L.moe_grouped_ffn_cached.argtypes = [P, I, I, I, I, I, I, P, P, P, P, I, P, P, P, P, P,
                                              P, Z, P]
+        F = ctypes.c_float
+        L.moe_combine_backward.argtypes = [P, I, P, P, I, I, I, P, P, P, P]
+        L.moe_router_backward.argtypes = [P, P, P, P, P, I, I, I, I, F, P, P]
+        L.moe_grouped_ffn_backward.argtypes = [P, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P,
+                                               P, P, P, Z, P]
+        L.moe_gather_backward.argtypes = [P, I, P, I, I, I, P, P, P, I, P, P]
+        L.moe_router_weight_backward.argtypes = [P, I, I, I, I, P, P, P, P, Z, P]
         for f in ("moe_router_topk", "moe_permute", "moe_grouped_ffn", "moe_combine",
                   "moe_aux_loss", "moe_expert_choice", "moe_cache_init", "moe_cache_step",
-                  "moe_cache_slot_of", "moe_grouped_ffn_cached"):
+                  "moe_cache_slot_of", "moe_grouped_ffn_cached", "moe_combine_backward",
+                  "moe_router_backward", "moe_grouped_ffn_backward", "moe_gather_backward",
+                  "moe_router_weight_backward"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -217,3 +226,40 @@ def moe_grouped_ffn_cached(x, T, d, h, E, k, offsets, sorted_token, slot_of, pha
         _p(x), _dt(x), T, d, h, E, k, _p(offsets), _p(sorted_token), _p(slot_of), _p(phase_of),
         int(phase), _p(w1), _p(b1), _p(w2), _p(b2), _p(y_perm), _p(ws), _nbytes(ws),
         _stream(stream)))
+
+
+# ---------------------------------------------------------------- backward ----
+
+def moe_combine_backward(y_perm, dest_row, topk_gate, T, k, d, dout, dy_perm, dgate,
+                         stream=None):
+    _check("moe_combine_backward", lib().moe_combine_backward(
+        _p(y_perm), _dt(y_perm), _p(dest_row), _p(topk_gate), T, k, d, _p(dout), _p(dy_perm),
+        _p(dgate), _stream(stream)))
+
+
+def moe_router_backward(logits, topk_idx, topk_gate, dgate, counts, T, E, k, renorm, daux,
+                        dlogits, stream=None):
+    _check("moe_router_backward", lib().moe_router_backward(
+        _p(logits), _p(topk_idx), _p(topk_gate), _p(dgate), _p(counts), T, E, k,
+        int(bool(renorm)), float(daux), _p(dlogits), _stream(stream)))
+
+
+def moe_grouped_ffn_backward(x, T, d, h, E, k, offsets, sorted_token, w1, b1, w2, dy_perm,
+                             dx_perm, dw1, db1, dw2, db2, ws, stream=None):
+    _check("moe_grouped_ffn_backward", lib().moe_grouped_ffn_backward(
+        _p(x), _dt(w1), T, d, h, E, k, _p(offsets), _p(sorted_token), _p(w1), _p(b1), _p(w2),
+        _p(dy_perm), _p(dx_perm), _p(dw1), _p(db1), _p(dw2), _p(db2), _p(ws), _nbytes(ws),
+        _stream(stream)))
+
+
+def moe_gather_backward(dx_perm, dest_row, T, k, d, dout_residual, dlogits, w_gate, E, dx,
+                        stream=None):
+    _check("moe_gather_backward", lib().moe_gather_backward(
+        _p(dx_perm), _dt(dx), _p(dest_row), T, k, d, _p(dout_residual), _p(dlogits),
+        _p(w_gate), E, _p(dx), _stream(stream)))
+
+
+def moe_router_weight_backward(x, T, d, E, dlogits, dw_gate, dgate_bias, ws, stream=None):
+    _check("moe_router_weight_backward", lib().moe_router_weight_backward(
+        _p(x), _dt(dw_gate), T, d, E, _p(dlogits), _p(dw_gate), _p(dgate_bias), _p(ws),
+        _nbytes(ws), _stream(stream)))

@@ -9,6 +9,11 @@ call of every timed step.
 
 The default workload is the Mixtral-shaped prefill layer (T=4096, d=4096,
 expert hidden 14336, 8 experts, top-2, bf16). Prints one JSON line.
+
+--backward times a training step instead: the forward (with logits kept)
+followed by the backward calls (combine, router, grouped FFN, gather,
+router weights) on a seeded upstream gradient, and reports the backward's
+grouped FFN against the MFMA roofline.
 """
 from __future__ import annotations
 
@@ -29,9 +34,14 @@ METRIC = "routed tokens/sec per MoE layer fwd (bf16, 1 GPU) + % of MFMA/HBM roof
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CALLS = ("router", "permute", "ffn", "combine", "aux")
 EC_CALLS = ("router", "choice", "ffn", "combine")  # Expert Choice layer
+BWD_CALLS = ("combine_bwd", "router_bwd", "ffn_bwd", "gather_bwd", "router_weight_bwd")
+TRAIN_METRIC = "routed tokens/sec per MoE layer fwd+bwd (bf16, 1 GPU) + % of MFMA roofline"
 # tokens whose expert FFN the CPU baseline evaluates (routing always covers all T)
 CPU_SAMPLE = {"tiny_fp32": 256, "mixtral_prefill": 2048, "switch_top1_cap": 8192, "decode": 32,
               "deepseek_v3": 512, "switch_expert_choice": 2048, "decode_offload": 32}
+# tokens of the sub-batch the backward CPU baseline differentiates
+BWD_CPU_SAMPLE = {"tiny_fp32": 256, "mixtral_prefill": 256, "switch_top1_cap": 1024,
+                  "deepseek_v3": 64}
 PCIE_GBS = 64.0             # PCIe 5.0 x16, one direction
 OFFLOAD_BATCHES = 16        # distinct token batches the offload workload cycles through
 
@@ -43,6 +53,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="mixtral_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time forward + backward (a training step) instead of the forward")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="JSON with HBM bytes per dominant-call launch from rocprofv3 counters")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -225,6 +237,126 @@ def bench_offload(args, cfg, inp, dev):
     print(json.dumps(out), flush=True)
 
 
+def cpu_baseline_backward(cfg, inp, dout, sample_n):
+    """The backward oracle timed on this host over the first sample_n tokens
+    (routing, every expert's forward and backward products and the router
+    gradients of that sub-batch), extrapolated to T tokens."""
+    import moe_inputs as mi
+    from oracle import backward as bwd
+    n = min(sample_n, cfg.T)
+    h = {k: mi.to_host_array(v) for k, v in inp.items() if v is not None}
+    x = h["x"][:n]
+    g = mi.to_host_array(dout)[:n]
+    t0 = time.perf_counter()
+    bwd.moe_backward(x, h["w_gate"], h["w1"], h.get("b1"), h["w2"], h.get("b2"), cfg.k,
+                     cfg.renorm, cfg.capacity, g, 0.01, gate_bias=h.get("gate_bias"),
+                     residual=cfg.residual)
+    t = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    return {"value": n / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"forward products and full backward of the layer over the first {n} of "
+                       f"{cfg.T} tokens ({t:.2f} s; weight gradients over those tokens' rows), "
+                       f"rate per token; double precision numpy, {threads} threads on "
+                       f"{cpu_model()}"),
+            "extrapolated": n < cfg.T, "seconds": t}
+
+
+def bench_backward(args, cfg, inp, dev):
+    """Training step: forward with the logits kept, then the five backward
+    calls on a seeded upstream gradient (aux-loss weight 0.01)."""
+    import torch
+    import moe_inputs as mi
+    import top_routing_expert_topk_amd as moe
+    from top_routing_expert_topk_amd import native as N
+    T, d, h, E, k = cfg.T, cfg.d, cfg.h, cfg.E, cfg.k
+    daux = 0.01
+    dout = mi.make_dout(cfg, dev)
+    bufs = moe.MoEBuffers(T, d, h, E, k, cfg.torch_dtype, dev, cfg.torch_dtype)
+    grads = moe.MoEGrads(T, d, h, E, k, cfg.torch_dtype, dev, inp["b1"] is not None,
+                         inp["b2"] is not None, inp["gate_bias"] is not None)
+    stream = torch.cuda.Stream(dev)  # default priority
+    x, wg, gb = inp["x"], inp["w_gate"], inp["gate_bias"]
+    w1, b1, w2, b2 = inp["w1"], inp["b1"], inp["w2"], inp["b2"]
+
+    def step(ev=None):
+        b, g = bufs, grads
+        if ev is not None:
+            ev[0].record(stream)
+        moe.moe_layer_forward(x, wg, gb, w1, b1, w2, b2, k, cfg.renorm, cfg.capacity,
+                              cfg.residual, want_logits=True, bufs=b, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        N.moe_combine_backward(b.y_perm, b.dest_row, b.topk_gate, T, k, d, dout, g.dy_perm,
+                               g.dgate, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        N.moe_router_backward(b.logits, b.topk_idx, b.topk_gate, g.dgate, b.counts, T, E, k,
+                              cfg.renorm, daux, g.dlogits, stream)
+        if ev is not None:
+            ev[3].record(stream)
+        N.moe_grouped_ffn_backward(x, T, d, h, E, k, b.offsets, b.sorted_token, w1, b1, w2,
+                                   g.dy_perm, g.dx_perm, g.dw1, g.db1, g.dw2, g.db2, g.ws_ffn,
+                                   stream)
+        if ev is not None:
+            ev[4].record(stream)
+        N.moe_gather_backward(g.dx_perm, b.dest_row, T, k, d, dout if cfg.residual else None,
+                              g.dlogits, wg, E, g.dx, stream)
+        if ev is not None:
+            ev[5].record(stream)
+        N.moe_router_weight_backward(x, T, d, E, g.dlogits, g.dw_gate, g.dgate_bias,
+                                     g.ws_router, stream)
+        if ev is not None:
+            ev[6].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    calls = ("forward",) + BWD_CALLS
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+              for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {c: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in events]))
+          for j, c in enumerate(calls)}
+    ms_step = events[0][0].elapsed_time(events[-1][len(calls)]) / args.steps
+    R = int(bufs.offsets[-1])
+    # algorithmic work of the backward FFN: dH, dX, dW1, dW2 (2 R d h each);
+    # the recomputation of Z is extra work and not counted
+    flop = 8.0 * R * d * h
+    t_bwd = ms["ffn_bwd"] * 1e-3
+    if cfg.dtype == "bf16":
+        roof = {"bound": "mfma", "achieved": flop / t_bwd / 1e12, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "alu", "achieved": flop / t_bwd / 1e12, "peak": PEAK_F32_TFLOPS,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = ("moe_grouped_ffn_backward (Z recompute, dZ, dX_perm, dW1, dW2 on the "
+                      "MFMA ring GEMM, weight and activation transposes, bias sums)")
+    roof["per_launch"] = {"flop": flop, "rows": R}
+    out = {
+        "metric": TRAIN_METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name + "_train", "T": T, "d": d, "h": h, "E": E, "k": k,
+                   "renorm": bool(cfg.renorm), "capacity": cfg.capacity,
+                   "residual": bool(cfg.residual), "routing": cfg.routing, "daux": daux,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "ms_per_call": ms,
+        "wall_ms_per_step": wall * 1e3 / args.steps,
+        "device": torch.cuda.get_device_name(dev),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_backward(cfg, inp, dout, BWD_CPU_SAMPLE.get(cfg.name, 64))
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -247,6 +379,8 @@ def main():
     torch.cuda.synchronize()
     if cfg.offload_slots > 0:
         return bench_offload(args, cfg, inp, dev)
+    if args.backward:
+        return bench_backward(args, cfg, inp, dev)
     T, d, h, E, k = cfg.T, cfg.d, cfg.h, cfg.E, cfg.k
     ec = cfg.routing == "expert_choice"
     calls = EC_CALLS if ec else CALLS

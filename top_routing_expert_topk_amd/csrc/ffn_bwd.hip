@@ -8,10 +8,9 @@
 //   dW1[e] = dZ_e^T X_e,        db1[e] = sum of dZ_e rows
 // Z is recomputed from x rather than kept from the forward.
 //
-// bf16 data path: every product runs on the 256 x 256 DMA-ring MFMA GEMM,
-// whose operands are K-contiguous rows. The data gradients contract over
-// the weights' leading index, so the weights are first transposed into the
-// workspace (W^T[e] is the forward layout of the transposed product). The
+// bf16 data path: every product runs on the 256 x 256 DMA-ring MFMA GEMM.
+// The data gradients contract over the weights' leading index: the ring
+// reads the weights in place, K-major, through LDS transpose loads. The
 // weight gradients contract over the rows of an expert: dY, SiLU(Z), dZ and
 // the gathered x rows are transposed into [feature][row] arrays in which
 // every expert's rows form a segment padded with zeros to a multiple of 64,
@@ -27,36 +26,6 @@ namespace moe {
 namespace {
 
 constexpr int kTB = 64;  // transpose tile edge; also the row padding of an expert segment
-
-// wt[e][b][a] = w[e][a][b] for bf16 w [E][A][B], 64 x 64 tiles through LDS.
-__global__ __launch_bounds__(256) void transpose_w(const uint16_t* __restrict__ w, int A, int B,
-                                                   uint16_t* __restrict__ wt) {
-  __shared__ uint32_t tile[kTB][kTB / 2 + 1];  // bf16 pairs, row i = source row a0 + i
-  const int b0 = blockIdx.x * kTB, a0 = blockIdx.y * kTB;
-  const size_t eo = (size_t)blockIdx.z * A * B;
-  const int tid = threadIdx.x, ch = tid & 7;
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int i = pass * 32 + (tid >> 3);
-    const u32x4 v = *(const u32x4*)(w + eo + (size_t)(a0 + i) * B + b0 + ch * 8);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) tile[i][ch * 4 + q] = v[q];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int c = pass * 32 + (tid >> 3);  // destination row b0 + c
-    const int sh = (c & 1) * 16;
-    u32x4 o;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t lo = (tile[ch * 8 + 2 * q][c >> 1] >> sh) & 0xFFFFu;
-      const uint32_t hi = (tile[ch * 8 + 2 * q + 1][c >> 1] >> sh) & 0xFFFFu;
-      o[q] = lo | (hi << 16);
-    }
-    *(u32x4*)(wt + eo + (size_t)(b0 + c) * A + a0 + ch * 8) = o;
-  }
-}
 
 // Padded transpose of an expert-ordered row array: for the 64-row segment p
 // of expert e (pt[e] <= p < pt[e+1], pt in 64-row units),
@@ -136,43 +105,54 @@ __global__ __launch_bounds__(256) void wgrad_plan(const int32_t* __restrict__ pt
   list[b] = w;
 }
 
-// db[e][c] = sum of g[row][c] over expert e's rows in ascending order.
-// Grid (ceil(C / 512), E); a thread owns two adjacent features.
-template <typename T>
-__global__ __launch_bounds__(256) void bias_grad(const T* __restrict__ g,
-                                                 const int32_t* __restrict__ offsets, int C,
-                                                 T* __restrict__ db) {
-  const int e = blockIdx.y, c = (blockIdx.x * 256 + threadIdx.x) * 2;
-  if (c >= C) return;
-  const int r0 = offsets[e], r1 = offsets[e + 1];
+// db[e][c] = sum of g[row][c] over expert e's rows: bf16 rows, grid
+// (C / 128, E). Thread (p, c2) owns features 2 c2, 2 c2 + 1 of the block's
+// 128 and sums rows p, p + 4, p + 8, ... of the expert (four loads in
+// flight); the four partial sums are then added in order p = 0..3.
+__global__ __launch_bounds__(256) void bias_grad_bf16(const uint16_t* __restrict__ g,
+                                                      const int32_t* __restrict__ offsets, int C,
+                                                      uint16_t* __restrict__ db) {
+  __shared__ float part[4][128];
+  const int e = blockIdx.y, cp = threadIdx.x & 63, ph = threadIdx.x >> 6;
+  const int c = blockIdx.x * 128 + 2 * cp;
+  const int r1 = offsets[e + 1];
   float a0 = 0.0f, a1 = 0.0f;
-  if constexpr (std::is_same<T, uint16_t>::value) {
-    int r = r0;
-    for (; r + 4 <= r1; r += 4) {
-      uint32_t v[4];
+  int r = offsets[e] + ph;
+  for (; r + 12 < r1; r += 16) {
+    uint32_t v[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = *(const uint32_t*)(g + (size_t)(r + u) * C + c);
+    for (int u = 0; u < 4; ++u) v[u] = *(const uint32_t*)(g + (size_t)(r + 4 * u) * C + c);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        a0 += bf16lo(v[u]);
-        a1 += bf16hi(v[u]);
-      }
+    for (int u = 0; u < 4; ++u) {
+      a0 += bf16lo(v[u]);
+      a1 += bf16hi(v[u]);
     }
-    for (; r < r1; ++r) {
-      const uint32_t v = *(const uint32_t*)(g + (size_t)r * C + c);
-      a0 += bf16lo(v);
-      a1 += bf16hi(v);
-    }
-    *(uint32_t*)(db + (size_t)e * C + c) = pack_bf16x2(a0, a1);
-  } else {
-    const bool two = c + 1 < C;
-    for (int r = r0; r < r1; ++r) {
-      a0 += g[(size_t)r * C + c];
-      if (two) a1 += g[(size_t)r * C + c + 1];
-    }
-    db[(size_t)e * C + c] = a0;
-    if (two) db[(size_t)e * C + c + 1] = a1;
   }
+  for (; r < r1; r += 4) {
+    const uint32_t v = *(const uint32_t*)(g + (size_t)r * C + c);
+    a0 += bf16lo(v);
+    a1 += bf16hi(v);
+  }
+  part[ph][2 * cp] = a0;
+  part[ph][2 * cp + 1] = a1;
+  __syncthreads();
+  if (ph == 0) {
+    const float s0 = ((part[0][2 * cp] + part[1][2 * cp]) + part[2][2 * cp]) + part[3][2 * cp];
+    const float s1 =
+        ((part[0][2 * cp + 1] + part[1][2 * cp + 1]) + part[2][2 * cp + 1]) + part[3][2 * cp + 1];
+    *(uint32_t*)(db + (size_t)e * C + c) = pack_bf16x2(s0, s1);
+  }
+}
+
+// fp32 rows, any C: grid (ceil(C / 256), E), one feature per thread.
+__global__ __launch_bounds__(256) void bias_grad_f32(const float* __restrict__ g,
+                                                     const int32_t* __restrict__ offsets, int C,
+                                                     float* __restrict__ db) {
+  const int e = blockIdx.y, c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= C) return;
+  float a = 0.0f;
+  for (int r = offsets[e]; r < offsets[e + 1]; ++r) a += g[(size_t)r * C + c];
+  db[(size_t)e * C + c] = a;
 }
 
 // fp32: d/dz SiLU(z) with the library exp.
@@ -328,10 +308,10 @@ int ffn_backward_f32(const float* x, int T, int d, int h, int E, int k, const in
   hipLaunchKernelGGL((gemm_f32_wgrad<true, false>), g2, dim3(256), 0, s, (const float*)dZ, x,
                      sorted_token, offsets, h, d, dw1);
   if (db2)
-    hipLaunchKernelGGL((bias_grad<float>), dim3(ceil_div(d, 512), E), dim3(256), 0, s, dy, offsets,
-                       d, db2);
+    hipLaunchKernelGGL(bias_grad_f32, dim3(ceil_div(d, 256), E), dim3(256), 0, s, dy, offsets, d,
+                       db2);
   if (db1)
-    hipLaunchKernelGGL((bias_grad<float>), dim3(ceil_div(h, 512), E), dim3(256), 0, s,
+    hipLaunchKernelGGL(bias_grad_f32, dim3(ceil_div(h, 256), E), dim3(256), 0, s,
                        (const float*)dZ, offsets, h, db1);
   return launch_status();
 }
@@ -356,8 +336,6 @@ int ffn_backward_bf16(const uint16_t* x, int T, int d, int h, int E, int k,
   uint16_t* Z = (uint16_t*)(base + L.z);
   uint16_t* dZ = (uint16_t*)(base + L.dz);
   float* part = (float*)(base + L.part);
-  uint16_t* w1t = (uint16_t*)(base + L.w1t);
-  uint16_t* w2t = (uint16_t*)(base + L.w2t);
   uint16_t* ta = (uint16_t*)(base + L.ta);
   uint16_t* tb = (uint16_t*)(base + L.tb);
   const uint16_t* none = nullptr;
@@ -372,18 +350,15 @@ int ffn_backward_bf16(const uint16_t* x, int T, int d, int h, int E, int k,
                      md, mh, wl2);
   hipLaunchKernelGGL(wgrad_plan, dim3(ceil_div(nwt, 256)), dim3(256), 0, s, (const int32_t*)pt, E,
                      mh, md, wl1);
-  // W2[e] [d][h] -> W2^T[e] [h][d];  W1[e] [h][d] -> W1^T[e] [d][h]
-  hipLaunchKernelGGL(transpose_w, dim3(h / kTB, d / kTB, E), dim3(256), 0, s, w2, d, h, w2t);
-  hipLaunchKernelGGL(transpose_w, dim3(d / kTB, h / kTB, E), dim3(256), 0, s, w1, h, d, w1t);
   // Z = W1[e] x + b1 (the forward's first product without the activation)
   hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, true, kEpiBias>), dim3(g1), rb, 0, s, x,
                      sorted_token, list1, w1, b1, Z, part, h, d, (size_t)h * d, 0, none);
   hipLaunchKernelGGL((big_tail_reduce<kBigBM, kEpiBias>), gr, dim3(256), 0, s, hdr, list1, b1, part,
                      Z, h, none);
-  // dZ = (dY W2[e]) * SiLU'(Z)
-  hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, false, kEpiDSilu>), dim3(g1), rb, 0, s, dy,
-                     (const int32_t*)nullptr, list1, (const uint16_t*)w2t, none, dZ, part, h, d,
-                     (size_t)h * d, 0, (const uint16_t*)Z);
+  // dZ = (dY W2[e]) * SiLU'(Z): W2[e] is [d][h], K-major for this product
+  hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, false, kEpiDSilu, true>), dim3(g1), rb, 0, s, dy,
+                     (const int32_t*)nullptr, list1, w2, none, dZ, part, h, d, (size_t)h * d, 0,
+                     (const uint16_t*)Z);
   hipLaunchKernelGGL((big_tail_reduce<kBigBM, kEpiDSilu>), gr, dim3(256), 0, s, hdr, list1, none,
                      part, dZ, h, (const uint16_t*)Z);
   // dW2[e] = dY_e^T SiLU(Z_e)
@@ -403,18 +378,17 @@ int ffn_backward_bf16(const uint16_t* x, int T, int d, int h, int E, int k,
   hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, false, kEpiBias>), dim3(nwt), rb, 0, s,
                      (const uint16_t*)tb, (const int32_t*)nullptr, (const BigWork*)wl1,
                      (const uint16_t*)ta, none, dw1, part, d, (int)rp, (size_t)0, h, none);
-  // dXp = dZ W1[e]
-  hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, false, kEpiBias>), dim3(g2), rb, 0, s,
-                     (const uint16_t*)dZ, (const int32_t*)nullptr, list2, (const uint16_t*)w1t, none,
-                     dxp, part, d, h, (size_t)d * h, 0, none);
+  // dXp = dZ W1[e]: W1[e] is [h][d], K-major for this product
+  hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, false, kEpiBias, true>), dim3(g2), rb, 0, s,
+                     (const uint16_t*)dZ, (const int32_t*)nullptr, list2, w1, none, dxp, part, d, h,
+                     (size_t)d * h, 0, none);
   hipLaunchKernelGGL((big_tail_reduce<kBigBM, kEpiBias>), gr, dim3(256), 0, s, hdr + 1, list2, none,
                      part, dxp, d, none);
   if (db2)
-    hipLaunchKernelGGL((bias_grad<uint16_t>), dim3(ceil_div(d, 512), E), dim3(256), 0, s, dy,
-                       offsets, d, db2);
+    hipLaunchKernelGGL(bias_grad_bf16, dim3(d / 128, E), dim3(256), 0, s, dy, offsets, d, db2);
   if (db1)
-    hipLaunchKernelGGL((bias_grad<uint16_t>), dim3(ceil_div(h, 512), E), dim3(256), 0, s,
-                       (const uint16_t*)dZ, offsets, h, db1);
+    hipLaunchKernelGGL(bias_grad_bf16, dim3(h / 128, E), dim3(256), 0, s, (const uint16_t*)dZ,
+                       offsets, h, db1);
   return launch_status();
 }
 

@@ -152,14 +152,13 @@ inline size_t router_bwd_ws(int T, int d, int E) {
 // FFN backward: [plan of the forward-shaped GEMMs (ffn_plan_bytes)]
 //   [pt: E+1 int32, padded 64-row segment starts] [wgrad work lists: 2 x E x
 //   (d/256)(h/256) entries] [Z: T*k*h x 4 B] [dZ: T*k*h x 4 B]
-//   [tail partials] [W1^T: E*d*h bf16] [W2^T: E*h*d bf16]
-//   [TA, TB: max(d,h) x Rp bf16 each]
+//   [tail partials] [TA, TB: max(d,h) x Rp bf16 each]
 // Rp bounds the padded row count: every expert's rows rounded up to 64.
 inline long ffn_bwd_rpad(int T, int E, int k) {
   return (long)align_up((size_t)T * k + 63 * (size_t)E, 64);
 }
 struct FfnBwdLayout {
-  size_t pt, wl, z, dz, part, w1t, w2t, ta, tb, total;
+  size_t pt, wl, z, dz, part, ta, tb, total;
 };
 inline FfnBwdLayout ffn_bwd_layout(int T, int d, int h, int E, int k) {
   FfnBwdLayout L;
@@ -176,10 +175,6 @@ inline FfnBwdLayout ffn_bwd_layout(int T, int d, int h, int E, int k) {
   o += align_up(rows * h * 4, 256);
   L.part = o;
   o += ffn_partial_bytes();
-  L.w1t = o;
-  o += align_up((size_t)E * d * h * 2, 256);
-  L.w2t = o;
-  o += align_up((size_t)E * d * h * 2, 256);
   L.ta = o;
   o += align_up(wide * rp * 2, 256);
   L.tb = o;

@@ -106,6 +106,27 @@ constexpr int kEpiBias = 0;
 constexpr int kEpiSilu = 1;
 constexpr int kEpiDSilu = 2;
 
+// MFMA operand fragment of a K-major weight block in LDS (64 k-rows x 128
+// features, 256-byte rows, chunk c of row k at c ^ 4 (k % 4)): lane l gets
+// the 8 consecutive k (16 sub .. +15, octet l / 32) of feature 32 i + l % 32
+// from two transpose loads of 4 k each. The block pointer is restrict: the
+// ring's own waits order these reads after the DMA that filled the block, as
+// for the plain fragment reads, and without alias information the compiler
+// would drain every DMA in flight before each transpose load.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+__device__ __forceinline__ bf16x8 tr_frag(const uint16_t* __restrict__ blk, int sub, int i,
+                                          int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int row = sub * 16 + 8 * (g >> 1) + (j >> 2);
+  const int col = i * 32 + 16 * (g & 1) + 4 * (j & 3);
+  const int off = row * 128 + (((col >> 3) ^ (4 * (j >> 2))) << 3) + (col & 4);
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(blk + off));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(blk + off + 4 * 128));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // One entry of a launch's work list: the block's tile and K range. The
 // lists are built on the device by big_plan, so a GEMM block starts with one
 // uniform load instead of searching the tile map.
@@ -319,7 +340,20 @@ __device__ __forceinline__ void big_store(f32x16 (&acc)[4][TM], uint16_t* ot, si
 // weight rows are K-contiguous with row stride K (the work item's K range
 // may be a part of it); src(row) = sorted_token[row] (GATHER) or row; expert
 // e's weights start at w + e * wes; output rows as in big_store.
-template <int NW, bool GATHER, int EPI>
+//
+// WT: the weights are stored K-major instead, w[e][k][n] with rows of N
+// features, as when a product runs through a weight matrix in the direction
+// opposite to the forward's. The DMA then moves 64 k-rows x 128 features
+// per 16 KB block (256-byte LDS rows, 16-byte chunk c of row k at
+// c ^ 4 (k % 4)), and the weight fragments come from LDS transpose loads:
+// ds_read_b64_tr_b16 gives each lane of a 16-lane group one feature of a 4 k
+// x 16 feature tile (lane j of the group addresses row j / 4, features
+// 4 (j % 4) .. +3, and receives the 4 k of feature j), so two of them make
+// the 8 consecutive k an MFMA operand lane holds. The 32 lanes of a half
+// wave read 64 bytes of each of four rows, which the swizzle spreads over
+// all 256 bytes of the LDS banks (the plain layout would put the four rows
+// on the same banks).
+template <int NW, bool GATHER, int EPI, bool WT = false>
 __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ sorted_token,
     const BigWork* __restrict__ work, const uint16_t* __restrict__ w,
@@ -361,7 +395,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
   // which the uniform offsets (multiples of 8 rows) leave unchanged.
   const int r0 = wave * 8 + (lane >> 3);
   const int c0 = swz128(r0, lane & 7) * 8;
-  const uint16_t* wbase = w + (size_t)e * wes + (size_t)(n0 + r0) * K + c0;
+  // WT: this lane moves k-row (lane / 16) of each 4-row DMA group, chunk
+  // slot lane % 16, which holds feature chunk (lane % 16) ^ 4 ((lane / 16) % 4)
+  const uint16_t* wbase =
+      WT ? w + (size_t)e * wes + (size_t)(lane >> 4) * N + n0 + (((lane & 15) ^ (4 * (lane >> 4))) << 3)
+         : w + (size_t)e * wes + (size_t)(n0 + r0) * K + c0;
   uint32_t boff[2][IPB];
 #pragma unroll
   for (int q = 0; q < 2; ++q)
@@ -379,8 +417,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
 #pragma unroll
     for (int i = 0; i < IPB; ++i) {
       if (q >= 2 && !b_live(q, i)) continue;
-      const uint16_t* g = q < 2 ? wbase + (size_t)(q * 128 + i * NW * 8) * K + koff
-                                : act + boff[q & 1][i] + koff;
+      const uint16_t* g;
+      if constexpr (WT)
+        g = q < 2 ? wbase + (size_t)(koff + (i * NW + wave) * 4) * N + q * 128
+                  : act + boff[q & 1][i] + koff;
+      else
+        g = q < 2 ? wbase + (size_t)(q * 128 + i * NW * 8) * K + koff
+                  : act + boff[q & 1][i] + koff;
       dma16(g, dst + (i * NW + wave) * 8 * kRS);
     }
   };
@@ -411,6 +454,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
   }
 
   const int ch = lane >> 5;
+  // LDS fragment reads paired with MFMAs by the scheduling hint (the
+  // transpose path issues two reads per weight fragment)
+  constexpr int kNR = WT ? TN * TM : TN + TM;
   const int bq = (wm * WTM) >> 7;      // the permuted-row block this wave reads
   const int br = (wm * WTM) & 127;     // its first row inside that block
   bf16x8 f0a[TN], f0b[TM], f1a[TN], f1b[TM];
@@ -427,8 +473,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
     const uint16_t* sa_ = ring + sa * kRBlk;                                           \
     const uint16_t* sb_ = ring + sb * kRBlk;                                           \
     _Pragma("unroll") for (int i = 0; i < TN; ++i) {                                   \
-      const int r = i * 32 + (lane & 31);                                              \
-      FA[i] = *(const bf16x8*)(sa_ + r * kRS + swz128(r, 2 * (sub) + ch) * 8);         \
+      if constexpr (WT) {                                                              \
+        FA[i] = tr_frag(sa_, (sub), i, lane);                                          \
+      } else {                                                                         \
+        const int r = i * 32 + (lane & 31);                                            \
+        FA[i] = *(const bf16x8*)(sa_ + r * kRS + swz128(r, 2 * (sub) + ch) * 8);       \
+      }                                                                                \
     }                                                                                  \
     _Pragma("unroll") for (int j = 0; j < TM; ++j) {                                   \
       const int r = br + j * 32 + (lane & 31);                                         \
@@ -457,13 +507,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
   for (int j = 0; j < ns; ++j) {
     MOE_RD(1, f1a, f1b);
     MOE_MM(f0a, f0b);
-    if constexpr (ACT) interleave_mfma_reads<TN * TM, TN + TM>();
+    if constexpr (ACT) interleave_mfma_reads<TN * TM, kNR>();
     MOE_RD(2, f0a, f0b);
     MOE_MM(f1a, f1b);
-    if constexpr (ACT) interleave_mfma_reads<TN * TM, TN + TM>();
+    if constexpr (ACT) interleave_mfma_reads<TN * TM, kNR>();
     MOE_RD(3, f1a, f1b);
     MOE_MM(f0a, f0b);
-    if constexpr (ACT) interleave_mfma_reads<TN * TM, TN + TM>();
+    if constexpr (ACT) interleave_mfma_reads<TN * TM, kNR>();
     if (j + 1 < ns) {
       // step j+1 landed (only the weight half of step j+2 may be in flight),
       // and this wave's reads of step j are done before its slots are refilled
@@ -488,7 +538,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
     MOE_SLOTS(j + 1);
     MOE_RD(0, f0a, f0b);
     MOE_MM(f1a, f1b);
-    if constexpr (ACT) interleave_mfma_reads<TN * TM, TN + TM>();
+    if constexpr (ACT) interleave_mfma_reads<TN * TM, kNR>();
   }
   };
   if (active) main_loop(std::true_type{});

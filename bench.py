@@ -10,8 +10,8 @@ call of every timed step.
 The default workload is the Mixtral-shaped prefill layer (T=4096, d=4096,
 expert hidden 14336, 8 experts, top-2, bf16). Prints one JSON line.
 
---backward times a training step instead: the forward (with logits kept)
-followed by the backward calls (combine, router, grouped FFN, gather,
+--backward times a training step instead: the forward (keeping the logits,
+pre-activations and hidden rows) followed by the backward calls (combine, router, grouped FFN, gather,
 router weights) on a seeded upstream gradient, and reports the backward's
 grouped FFN against the MFMA roofline.
 """
@@ -271,7 +271,7 @@ def bench_backward(args, cfg, inp, dev):
     T, d, h, E, k = cfg.T, cfg.d, cfg.h, cfg.E, cfg.k
     daux = 0.01
     dout = mi.make_dout(cfg, dev)
-    bufs = moe.MoEBuffers(T, d, h, E, k, cfg.torch_dtype, dev, cfg.torch_dtype)
+    bufs = moe.MoEBuffers(T, d, h, E, k, cfg.torch_dtype, dev, cfg.torch_dtype, train=True)
     grads = moe.MoEGrads(T, d, h, E, k, cfg.torch_dtype, dev, inp["b1"] is not None,
                          inp["b2"] is not None, inp["gate_bias"] is not None)
     stream = torch.cuda.Stream(dev)  # default priority
@@ -283,7 +283,7 @@ def bench_backward(args, cfg, inp, dev):
         if ev is not None:
             ev[0].record(stream)
         moe.moe_layer_forward(x, wg, gb, w1, b1, w2, b2, k, cfg.renorm, cfg.capacity,
-                              cfg.residual, want_logits=True, bufs=b, stream=stream)
+                              cfg.residual, bufs=b, stream=stream, train=True)
         if ev is not None:
             ev[1].record(stream)
         N.moe_combine_backward(b.y_perm, b.dest_row, b.topk_gate, T, k, d, dout, g.dy_perm,
@@ -295,8 +295,8 @@ def bench_backward(args, cfg, inp, dev):
         if ev is not None:
             ev[3].record(stream)
         N.moe_grouped_ffn_backward(x, T, d, h, E, k, b.offsets, b.sorted_token, w1, b1, w2,
-                                   g.dy_perm, g.dx_perm, g.dw1, g.db1, g.dw2, g.db2, g.ws_ffn,
-                                   stream)
+                                   g.dy_perm, b.z_perm, b.h_perm, g.dx_perm, g.dw1, g.db1, g.dw2,
+                                   g.db2, g.ws_ffn, stream)
         if ev is not None:
             ev[4].record(stream)
         N.moe_gather_backward(g.dx_perm, b.dest_row, T, k, d, dout if cfg.residual else None,
@@ -323,8 +323,7 @@ def bench_backward(args, cfg, inp, dev):
           for j, c in enumerate(calls)}
     ms_step = events[0][0].elapsed_time(events[-1][len(calls)]) / args.steps
     R = int(bufs.offsets[-1])
-    # algorithmic work of the backward FFN: dH, dX, dW1, dW2 (2 R d h each);
-    # the recomputation of Z is extra work and not counted
+    # algorithmic work of the backward FFN: dH, dX, dW1, dW2 (2 R d h each)
     flop = 8.0 * R * d * h
     t_bwd = ms["ffn_bwd"] * 1e-3
     if cfg.dtype == "bf16":
@@ -335,8 +334,8 @@ def bench_backward(args, cfg, inp, dev):
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = None
-    roof["kernel"] = ("moe_grouped_ffn_backward (Z recompute, dZ, dX_perm, dW1, dW2 on the "
-                      "MFMA ring GEMM, weight and activation transposes, bias sums)")
+    roof["kernel"] = ("moe_grouped_ffn_backward (dZ, dX_perm, dW1, dW2 on the MFMA ring GEMM, "
+                      "activation transposes, bias sums)")
     roof["per_launch"] = {"flop": flop, "rows": R}
     out = {
         "metric": TRAIN_METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,

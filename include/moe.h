@@ -247,8 +247,9 @@ int moe_aux_loss(const float *prob_sum, const int32_t *counts, int T, int E, flo
  * softmax so gradients reach them]. Top-k selection, counts and capacity *
  * drops carry no gradient; the gradient reaches the gate values, the     *
  * router probabilities of the aux loss and every product. Call order:    *
- * moe_combine_backward -> moe_router_backward -> moe_grouped_ffn_backward *
- * -> moe_gather_backward and moe_router_weight_backward. Same            *
+ * (forward with moe_grouped_ffn_train), moe_combine_backward ->          *
+ * moe_router_backward -> moe_grouped_ffn_backward ->                      *
+ * moe_gather_backward and moe_router_weight_backward. Same               *
  * conventions as the forward: device pointers, caller-owned buffers,     *
  * asynchronous on `stream`, status codes as above.                        *
  * ===================================================================== */
@@ -278,13 +279,30 @@ int moe_router_backward(const float *logits, const int32_t *topk_idx, const floa
                         int renorm, float daux, float *dlogits, moe_stream_t stream);
 
 /*
+ * Grouped expert FFN forward for training   [as moe_grouped_ffn]: the same
+ * computation and outputs, and also keeps, for every kept row r, the
+ * pre-activation z_perm[r] = W1[e] x[sorted_token[r]] + b1[e] and the hidden
+ * row h_perm[r] = SiLU(z) (both [T*k][h] in the layer dtype, rows [0, R)
+ * written) for moe_grouped_ffn_backward. h_perm holds exactly the hidden
+ * rows the second product reads, so y_perm equals moe_grouped_ffn's bit for
+ * bit. Same workspace as moe_grouped_ffn.
+ */
+int moe_grouped_ffn_train(const void *x, int dtype, int T, int d, int h, int E, int k,
+                          const int32_t *offsets, const int32_t *sorted_token, const void *w1,
+                          const void *b1, const void *w2, const void *b2, void *y_perm,
+                          void *z_perm, void *h_perm, void *ws, size_t ws_bytes,
+                          moe_stream_t stream);
+
+/*
  * Grouped expert FFN backward over the permutation of the forward
  * (offsets, sorted_token from moe_permute), for each expert e and its rows:
- *   Z = W1[e] x[sorted_token] + b1[e]          (recomputed, workspace)
+ *   Z = W1[e] x[sorted_token] + b1[e]          (z_perm and H = h_perm from
+ *                                              moe_grouped_ffn_train, or,
+ *                                              both NULL, recomputed)
  *   dZ = (dy_perm W2[e]) * SiLU'(Z)
  *   dx_perm = dZ W1[e]                         ([T*k][d], rows [0, R))
  *   dw1[e] = dZ^T X_e,  db1[e] = sum of dZ rows        (dw1 [E][h][d])
- *   dw2[e] = dy_perm^T SiLU(Z),  db2[e] = sum of dy rows (dw2 [E][d][h])
+ *   dw2[e] = dy_perm^T H,  db2[e] = sum of dy rows       (dw2 [E][d][h])
  * Weight and bias gradients are overwritten (zero for experts without
  * rows); db1 / db2 may be NULL (no bias). Gradients have the layer dtype;
  * products accumulate in fp32. bf16: d and h multiples of 256 (status 2
@@ -293,9 +311,10 @@ int moe_router_backward(const float *logits, const int32_t *topk_idx, const floa
  */
 int moe_grouped_ffn_backward(const void *x, int dtype, int T, int d, int h, int E, int k,
                              const int32_t *offsets, const int32_t *sorted_token, const void *w1,
-                             const void *b1, const void *w2, const void *dy_perm, void *dx_perm,
-                             void *dw1, void *db1, void *dw2, void *db2, void *ws,
-                             size_t ws_bytes, moe_stream_t stream);
+                             const void *b1, const void *w2, const void *dy_perm,
+                             const void *z_perm, const void *h_perm, void *dx_perm, void *dw1,
+                             void *db1, void *dw2, void *db2, void *ws, size_t ws_bytes,
+                             moe_stream_t stream);
 
 /*
  * Input gradient:

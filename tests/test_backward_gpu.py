@@ -59,12 +59,14 @@ def _np(t):
     return None if t is None else t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def run_backward(cfg, daux=DAUX):
+def run_backward(cfg, daux=DAUX, train=True):
+    """train: the forward keeps Z and H for the backward; otherwise the
+    backward recomputes Z."""
     inp = mi.make_inputs(cfg, "cuda")
     dout = mi.make_dout(cfg, "cuda")
     fwd = moe_layer_forward(inp["x"], inp["w_gate"], inp["gate_bias"], inp["w1"], inp["b1"],
                             inp["w2"], inp["b2"], cfg.k, cfg.renorm, cfg.capacity, cfg.residual,
-                            want_logits=True, out_dtype=cfg.torch_dtype)
+                            want_logits=True, out_dtype=cfg.torch_dtype, train=train)
     g = moe_layer_backward(fwd, inp["x"], inp["w_gate"], inp["gate_bias"], inp["w1"], inp["b1"],
                            inp["w2"], inp["b2"], dout, cfg.renorm, cfg.residual, daux)
     torch.cuda.synchronize()
@@ -126,3 +128,72 @@ def test_backward_is_deterministic():
     _, _, _, g2 = run_backward(cfg)
     for n, v in keep.items():
         assert torch.equal(v, getattr(g2, n)), n
+
+
+@pytest.mark.parametrize("name", ["mix_rows", "switch_small", "tiny_fp32", "sparse_experts"])
+def test_kept_and_recomputed_preactivations_agree(name):
+    """With the forward's Z the backward skips recomputing it. Z is the same
+    bf16(acc + b1) either way, so everything that follows from dZ is
+    identical; dW2 reads H, which the forward rounds from the unrounded z,
+    so it only agrees within the bar (fp32 layers: identical)."""
+    cfg = CASES[name]
+    inp, dout, fwd, g_keep = run_backward(cfg, train=True)
+    _, _, _, g_re = run_backward(cfg, train=False)
+    for n in ("dx", "dw1", "db1", "db2", "dgate", "dlogits", "dw_gate"):
+        assert torch.equal(getattr(g_keep, n), getattr(g_re, n)), n
+    if cfg.dtype == "f32":
+        assert torch.equal(g_keep.dw2, g_re.dw2)
+    ref = oracle_backward(cfg, inp, dout, fwd)
+    compare(cfg, g_re, ref, name + " recomputed")
+
+
+TRAIN_PATHS = {
+    "ring": CASES["mix_rows"],                        # 768 rows per expert
+    "persistent": CASES["switch_small"],              # about 64 rows per expert
+    "streaming": CASES["sparse_experts"],             # 48 rows over 64 experts
+    "tiles128": BASE.with_(name="tiles128", T=300, d=384, h=640),
+    "tiles64": BASE.with_(name="tiles64", T=200, d=192, h=320),
+    "fp32": CASES["f32_ragged"],
+}
+
+
+@pytest.mark.parametrize("path", list(TRAIN_PATHS))
+def test_training_forward_keeps_z_and_h(path):
+    """moe_grouped_ffn_train on every FFN path: y_perm equals
+    moe_grouped_ffn's bit for bit; z_perm is W1 x + b1 rounded once to the
+    layer dtype (|err| <= 2^-8 |z| + 1.1 d 2^-24 M, M = sum |x w1| + |b1|:
+    one rounding plus fp32 accumulation over d terms in any order); h_perm is
+    SiLU of the unrounded z (|SiLU'| <= 1.1). fp32 layers: 2^-16 |z| instead
+    of 2^-8 |z|."""
+    import moe_inputs as mi2
+    from top_routing_expert_topk_amd import native as N
+    cfg = TRAIN_PATHS[path]
+    inp = mi2.make_inputs(cfg, "cuda")
+    b = moe_layer_forward(inp["x"], inp["w_gate"], inp["gate_bias"], inp["w1"], inp["b1"],
+                          inp["w2"], inp["b2"], cfg.k, cfg.renorm, cfg.capacity, cfg.residual,
+                          train=True)
+    y_train = b.y_perm.clone()
+    N.moe_grouped_ffn(inp["x"], cfg.T, cfg.d, cfg.h, cfg.E, cfg.k, b.offsets, b.sorted_token,
+                      inp["w1"], inp["b1"], inp["w2"], inp["b2"], b.y_perm, b.ws_ffn)
+    torch.cuda.synchronize()
+    R = int(b.offsets[-1])
+    assert torch.equal(y_train[:R], b.y_perm[:R])
+    X = bwd.widen(mi2.to_host_array(inp["x"]))
+    W1 = bwd.widen(mi2.to_host_array(inp["w1"]))
+    B1 = bwd.widen(mi2.to_host_array(inp["b1"]))
+    off = b.offsets.cpu().numpy()
+    st = b.sorted_token.cpu().numpy()
+    z_gpu = _np(b.z_perm[:R])
+    h_gpu = _np(b.h_perm[:R])
+    c = 2.0 ** -16 if cfg.dtype == "f32" else 2.0 ** -8
+    for e in range(cfg.E):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if r1 == r0:
+            continue
+        xe = X[st[r0:r1]]
+        z = xe @ W1[e].T + B1[e]
+        M = np.abs(xe) @ np.abs(W1[e]).T + np.abs(B1[e])
+        hz = bwd.silu(z)
+        acc = 1.1 * cfg.d * 2.0 ** -24 * M  # fp32 accumulation over d terms, through SiLU'
+        assert np.all(np.abs(z_gpu[r0:r1] - z) <= c * np.abs(z) + acc), f"z, expert {e}"
+        assert np.all(np.abs(h_gpu[r0:r1] - hz) <= c * np.abs(hz) + acc), f"h, expert {e}"

@@ -187,9 +187,10 @@ def test_backward_calls_reject_bad_arguments():
     assert L.moe_router_backward(BAD, BAD, BAD, None, BAD, 4, 8, 2, 1, F(0), BAD, None) == 1
 
     # grouped FFN backward
-    def ffn(dtype=1, T=10, d=256, h=512, E=8, k=2, w1=BAD, dy=BAD, ws=BAD, wsb=1 << 40):
+    def ffn(dtype=1, T=10, d=256, h=512, E=8, k=2, w1=BAD, dy=BAD, z=None, hh=None, ws=BAD,
+            wsb=1 << 40):
         return L.moe_grouped_ffn_backward(BAD, dtype, T, d, h, E, k, BAD, BAD, w1, None, BAD, dy,
-                                          BAD, BAD, None, BAD, None, ws, wsb, None)
+                                          z, hh, BAD, BAD, None, BAD, None, ws, wsb, None)
     assert ffn(T=-1) == 1
     assert ffn(dtype=3) == 1
     assert ffn(k=9) == 1
@@ -200,6 +201,17 @@ def test_backward_calls_reject_bad_arguments():
     assert ffn(ws=None) == 4
     assert ffn(d=192) == 2   # bf16 tiles need multiples of 256
     assert ffn(h=320) == 2
+    assert ffn(z=BAD) == 1   # the kept pre-activations come with the hidden rows
+    assert ffn(hh=BAD) == 1
+
+    # training forward: as moe_grouped_ffn, plus both kept arrays
+    def train(z=BAD, hh=BAD, d=128, wsb=1 << 40):
+        return L.moe_grouped_ffn_train(BAD, 1, 10, d, 256, 8, 2, BAD, BAD, BAD, None, BAD, None,
+                                       BAD, z, hh, BAD, wsb, None)
+    assert train(z=None) == 1
+    assert train(hh=None) == 1
+    assert train(d=100) == 2
+    assert train(wsb=16) == 4
 
     # gather backward
     assert L.moe_gather_backward(BAD, 1, BAD, -1, 2, 64, None, None, None, 8, BAD, None) == 1

@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256) void gemm_bf16(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ sorted_token,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_start,
     const uint16_t* __restrict__ w, const uint16_t* __restrict__ bias,
-    uint16_t* __restrict__ out, int E, int N, int K, int mslots) {
+    uint16_t* __restrict__ out, int E, int N, int K, int mslots, uint16_t* __restrict__ zout) {
   constexpr int TN = BN / 32, TM = BM / 32;  // 16-wide tiles per wave
   constexpr int AL = BN * 8 / 256, BL = BM * 8 / 256;  // 16-byte chunks per thread
   __shared__ __align__(16) uint16_t sA[2][BN * KC];
@@ -157,10 +157,16 @@ __global__ __launch_bounds__(256) void gemm_bf16(
       if (m < rows) {
         float v[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          v[q] = acc[i][j][q] + bv[q];
-          if (SILU) v[q] = silu_bf16(v[q]);
+        for (int q = 0; q < 4; ++q) v[q] = acc[i][j][q] + bv[q];
+        if (SILU && zout) {
+          u32x2 z;
+          z[0] = pack_bf16x2(v[0], v[1]);
+          z[1] = pack_bf16x2(v[2], v[3]);
+          *(u32x2*)(zout + (size_t)(row0 + m) * N + n) = z;
         }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (SILU) v[q] = silu_bf16(v[q]);
         u32x2 o;
         o[0] = pack_bf16x2(v[0], v[1]);
         o[1] = pack_bf16x2(v[2], v[3]);
@@ -225,7 +231,8 @@ __global__ __launch_bounds__(512) void gemm_bf16_pring(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ tok_tab,
     const BigHdr* __restrict__ hdr, const BigWork* __restrict__ units,
     const uint16_t* __restrict__ w, const uint16_t* __restrict__ bias,
-    uint16_t* __restrict__ out, float* __restrict__ part, int N, int K) {
+    uint16_t* __restrict__ out, float* __restrict__ part, int N, int K,
+    uint16_t* __restrict__ zout) {
   using C = PRing<BM>;
   constexpr int P = C::P, S = C::S, AHEAD = C::AHEAD, NBQ = C::NBQ;
   constexpr int TN = C::TN, TM = C::TM, WM = C::WM, WTN = C::WTN, WTM = C::WTM;
@@ -425,10 +432,16 @@ __global__ __launch_bounds__(512) void gemm_bf16_pring(
               const int m = wm * WTM + j * 32 + (lane & 31);
               float v[4];
 #pragma unroll
-              for (int t = 0; t < 4; ++t) {
-                v[t] = acc[i][j][4 * q + t] + bv[t];
-                if (SILU) v[t] = silu_bf16(v[t]);
+              for (int t = 0; t < 4; ++t) v[t] = acc[i][j][4 * q + t] + bv[t];
+              if (SILU && zout && m < uc.rows) {
+                u32x2 z;
+                z[0] = pack_bf16x2(v[0], v[1]);
+                z[1] = pack_bf16x2(v[2], v[3]);
+                *(u32x2*)(zout + (size_t)(uc.row0 + m) * N + uc.n0 + nl) = z;
               }
+#pragma unroll
+              for (int t = 0; t < 4; ++t)
+                if (SILU) v[t] = silu_bf16(v[t]);
               if (m < uc.rows) {
                 u32x2 o;
                 o[0] = pack_bf16x2(v[0], v[1]);
@@ -485,7 +498,8 @@ __global__ __launch_bounds__(256) void decode_bf16(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ sorted_token,
     const int32_t* __restrict__ offsets, const uint16_t* __restrict__ w,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int E, int N, int K,
-    const int32_t* __restrict__ slot_of, const int32_t* __restrict__ phase_of, int phase) {
+    const int32_t* __restrict__ slot_of, const int32_t* __restrict__ phase_of, int phase,
+    uint16_t* __restrict__ zout) {
   extern __shared__ __align__(16) uint16_t sx[];  // [DG][K]
   const int e = blockIdx.y;
   const int r0 = offsets[e];
@@ -548,6 +562,8 @@ __global__ __launch_bounds__(256) void decode_bf16(
         for (int g = 0; g < DG; ++g) {
           if (g < ng) {
             float v = wave_sum(acc[a][g]) + b;
+            if (SILU && zout && lane == 0 && na < N)
+              zout[(size_t)(r0 + g0 + g) * N + na] = (uint16_t)f32_to_bf16(v);
             if (SILU) v = silu_bf16(v);
             if (lane == 0 && na < N) out[(size_t)(r0 + g0 + g) * N + na] = (uint16_t)f32_to_bf16(v);
           }
@@ -564,11 +580,12 @@ template <int BN>
 int launch_gemms_bf16(const uint16_t* x, const int32_t* sorted_token, const int32_t* offsets,
                       const int32_t* tile_start, const uint16_t* w1, const uint16_t* b1,
                       const uint16_t* w2, const uint16_t* b2, uint16_t* H, uint16_t* y, int E,
-                      int d, int h, int mslots, hipStream_t s) {
+                      int d, int h, int mslots, uint16_t* zout, hipStream_t s) {
   hipLaunchKernelGGL((gemm_bf16<BN, kBM, true, true>), dim3(mslots * (h / BN)), dim3(256), 0, s, x,
-                     sorted_token, offsets, tile_start, w1, b1, H, E, h, d, mslots);
+                     sorted_token, offsets, tile_start, w1, b1, H, E, h, d, mslots, zout);
   hipLaunchKernelGGL((gemm_bf16<BN, kBM, false, false>), dim3(mslots * (d / BN)), dim3(256), 0, s,
-                     H, sorted_token, offsets, tile_start, w2, b2, y, E, d, h, mslots);
+                     H, sorted_token, offsets, tile_start, w2, b2, y, E, d, h, mslots,
+                     (uint16_t*)nullptr);
   return launch_status();
 }
 
@@ -590,9 +607,8 @@ bool use_ring128(long rows, int E, int T, int d, int h) {
 
 int launch_ring(const uint16_t* x, const int32_t* sorted_token, const int32_t* offsets, void* plan,
                 const uint16_t* w1, const uint16_t* b1, const uint16_t* w2, const uint16_t* b2,
-                uint16_t* H, uint16_t* y, int E, int d, int h, int T, int k, long rows,
-                hipStream_t s) {
-  float* part = (float*)((unsigned char*)H + ffn_hidden_bytes(T, h, k));
+                uint16_t* H, uint16_t* y, float* part, uint16_t* zout, int E, int d, int h,
+                long rows, hipStream_t s) {
   const int g1 = ffn_big_grid(rows, E, h, kBigBM), g2 = ffn_big_grid(rows, E, d, kBigBM);
   BigHdr* hdr = (BigHdr*)plan;
   BigWork* list1 = (BigWork*)((unsigned char*)plan + 256);
@@ -603,14 +619,14 @@ int launch_ring(const uint16_t* x, const int32_t* sorted_token, const int32_t* o
                      sorted_token, (int32_t*)nullptr);
   hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, true, kEpiSilu>), dim3(g1), dim3(kRingWaves * 64),
                      0, s, x, sorted_token, list1, w1, b1, H, part, h, d, (size_t)h * d, 0,
-                     (const uint16_t*)nullptr);
+                     (const uint16_t*)nullptr, zout);
   hipLaunchKernelGGL((big_tail_reduce<kBigBM, kEpiSilu>), gr, dim3(256), 0, s, hdr, list1, b1, part,
-                     H, h, (const uint16_t*)nullptr);
+                     H, h, (const uint16_t*)nullptr, zout);
   hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, false, kEpiBias>), dim3(g2), dim3(kRingWaves * 64),
                      0, s, H, sorted_token, list2, w2, b2, y, part, d, h, (size_t)d * h, 0,
-                     (const uint16_t*)nullptr);
+                     (const uint16_t*)nullptr, (uint16_t*)nullptr);
   hipLaunchKernelGGL((big_tail_reduce<kBigBM, kEpiBias>), gr, dim3(256), 0, s, hdr + 1, list2, b2,
-                     part, y, d, (const uint16_t*)nullptr);
+                     part, y, d, (const uint16_t*)nullptr, (uint16_t*)nullptr);
   return launch_status();
 }
 
@@ -618,9 +634,8 @@ int launch_ring(const uint16_t* x, const int32_t* sorted_token, const int32_t* o
 template <int BM>
 int launch_pring(const uint16_t* x, const int32_t* sorted_token, const int32_t* offsets,
                  void* plan, const uint16_t* w1, const uint16_t* b1, const uint16_t* w2,
-                 const uint16_t* b2, uint16_t* H, uint16_t* y, int E, int d, int h, int T, int k,
-                 long rows, hipStream_t s) {
-  float* part = (float*)((unsigned char*)H + ffn_hidden_bytes(T, h, k));
+                 const uint16_t* b2, uint16_t* H, uint16_t* y, float* part, uint16_t* zout, int E,
+                 int d, int h, int T, int k, long rows, hipStream_t s) {
   const int g1 = ffn_big_grid(rows, E, h, BM), g2 = ffn_big_grid(rows, E, d, BM);
   BigHdr* hdr = (BigHdr*)plan;
   BigWork* list1 = (BigWork*)((unsigned char*)plan + 256);
@@ -637,13 +652,14 @@ int launch_pring(const uint16_t* x, const int32_t* sorted_token, const int32_t* 
                      s, offsets, E, h / kBigBN, d / kRS, g1, d / kBigBN, h / kRS, g2, hdr, list1,
                      list2, sorted_token, tok);
   hipLaunchKernelGGL((gemm_bf16_pring<BM, true, true>), dim3(kTailSlots), dim3(512), 0, s, x, tok,
-                     hdr, list1, w1, b1, H, part, h, d);
+                     hdr, list1, w1, b1, H, part, h, d, zout);
   hipLaunchKernelGGL((big_tail_reduce<BM, kEpiSilu>), gr, dim3(256), 0, s, hdr, list1, b1, part, H, h,
-                     (const uint16_t*)nullptr);
+                     (const uint16_t*)nullptr, zout);
   hipLaunchKernelGGL((gemm_bf16_pring<BM, false, false>), dim3(kTailSlots), dim3(512), 0, s, H,
-                     (const int32_t*)nullptr, hdr + 1, list2, w2, b2, y, part, d, h);
+                     (const int32_t*)nullptr, hdr + 1, list2, w2, b2, y, part, d, h,
+                     (uint16_t*)nullptr);
   hipLaunchKernelGGL((big_tail_reduce<BM, kEpiBias>), gr, dim3(256), 0, s, hdr + 1, list2, b2, part,
-                     y, d, (const uint16_t*)nullptr);
+                     y, d, (const uint16_t*)nullptr, (uint16_t*)nullptr);
   return launch_status();
 }
 
@@ -651,7 +667,7 @@ int launch_pring(const uint16_t* x, const int32_t* sorted_token, const int32_t* 
 int launch_decode(const uint16_t* x, const int32_t* sorted_token, const int32_t* offsets,
                   const uint16_t* w1, const uint16_t* b1, const uint16_t* w2, const uint16_t* b2,
                   uint16_t* H, uint16_t* y, int E, int d, int h, const int32_t* slot_of,
-                  const int32_t* phase_of, int phase, hipStream_t s) {
+                  const int32_t* phase_of, int phase, uint16_t* zout, hipStream_t s) {
   const size_t lds1 = (size_t)DG * d * 2, lds2 = (size_t)DG * h * 2;
   if (lds1 > 160 * 1024 || lds2 > 160 * 1024) return MOE_ERR_UNSUPPORTED;
   if (lds1 > 65536 &&
@@ -663,10 +679,10 @@ int launch_decode(const uint16_t* x, const int32_t* sorted_token, const int32_t*
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2) != hipSuccess)
     return MOE_ERR_LAUNCH;
   hipLaunchKernelGGL((decode_bf16<true, true>), dim3(ceil_div(h, DRPB), E), dim3(256), lds1, s, x,
-                     sorted_token, offsets, w1, b1, H, E, h, d, slot_of, phase_of, phase);
+                     sorted_token, offsets, w1, b1, H, E, h, d, slot_of, phase_of, phase, zout);
   hipLaunchKernelGGL((decode_bf16<false, false>), dim3(ceil_div(d, DRPB), E), dim3(256), lds2, s,
                      (const uint16_t*)H, sorted_token, offsets, w2, b2, y, E, d, h, slot_of,
-                     phase_of, phase);
+                     phase_of, phase, (uint16_t*)nullptr);
   return launch_status();
 }
 
@@ -675,10 +691,65 @@ int launch_decode(const uint16_t* x, const int32_t* sorted_token, const int32_t*
 
 using namespace moe;
 
-extern "C" int moe_grouped_ffn(const void* x, int dtype, int T, int d, int h, int E, int k,
-                               const int32_t* offsets, const int32_t* sorted_token, const void* w1,
-                               const void* b1, const void* w2, const void* b2, void* y_perm,
-                               void* ws, size_t ws_bytes, moe_stream_t stream) {
+namespace moe {
+namespace {
+
+// The grouped FFN with its hidden rows H at `hidden` (the workspace, or a
+// caller buffer) and, when zout is not NULL, the pre-activations Z = W1 x +
+// b1 written there too. Sizes and pointers are checked by the callers.
+int grouped_ffn(const void* x, int dtype, int T, int d, int h, int E, int k,
+                const int32_t* offsets, const int32_t* sorted_token, const void* w1,
+                const void* b1, const void* w2, const void* b2, void* y_perm, void* ws,
+                void* hidden, void* zout, hipStream_t s) {
+  const long rows = (long)T * k;
+  int32_t* tile_start = (int32_t*)ws;
+  void* H = hidden;
+  float* part = (float*)((unsigned char*)ws + ffn_plan_bytes(T, d, h, E, k) +
+                         ffn_hidden_bytes(T, h, k));
+  const int nonempty = (int)(rows < E ? rows : E);
+
+  if (dtype == MOE_F32) {
+    const int mslots = ceil_div(rows, FB) + nonempty;
+    hipLaunchKernelGGL(build_tile_map, dim3(1), dim3(512), 0, s, offsets, E, FB, tile_start);
+    hipLaunchKernelGGL((gemm_f32<true, true>), dim3(mslots * ceil_div(h, FB)), dim3(256), 0, s,
+                       (const float*)x, sorted_token, offsets, tile_start, (const float*)w1,
+                       (const float*)b1, (float*)H, E, h, d, mslots, (float*)zout);
+    hipLaunchKernelGGL((gemm_f32<false, false>), dim3(mslots * ceil_div(d, FB)), dim3(256), 0, s,
+                       (const float*)H, sorted_token, offsets, tile_start, (const float*)w2,
+                       (const float*)b2, (float*)y_perm, E, d, h, mslots, (float*)nullptr);
+    return launch_status();
+  }
+
+  const uint16_t* xb = (const uint16_t*)x;
+  uint16_t* zb = (uint16_t*)zout;
+  if (use_decode(rows, E)) {
+    return launch_decode(xb, sorted_token, offsets, (const uint16_t*)w1, (const uint16_t*)b1,
+                         (const uint16_t*)w2, (const uint16_t*)b2, (uint16_t*)H,
+                         (uint16_t*)y_perm, E, d, h, nullptr, nullptr, 0, zb, s);
+  }
+
+  if (use_ring(rows, E, T, d, h))
+    return launch_ring(xb, sorted_token, offsets, ws, (const uint16_t*)w1, (const uint16_t*)b1,
+                       (const uint16_t*)w2, (const uint16_t*)b2, (uint16_t*)H, (uint16_t*)y_perm,
+                       part, zb, E, d, h, rows, s);
+  if (use_ring128(rows, E, T, d, h))
+    return launch_pring<128>(xb, sorted_token, offsets, ws, (const uint16_t*)w1,
+                             (const uint16_t*)b1, (const uint16_t*)w2, (const uint16_t*)b2,
+                             (uint16_t*)H, (uint16_t*)y_perm, part, zb, E, d, h, T, k, rows, s);
+  const int mslots = ceil_div(rows, kBM) + nonempty;
+  hipLaunchKernelGGL(build_tile_map, dim3(1), dim3(512), 0, s, offsets, E, kBM, tile_start);
+  if ((d % 128) == 0 && (h % 128) == 0)
+    return launch_gemms_bf16<128>(xb, sorted_token, offsets, tile_start, (const uint16_t*)w1,
+                                  (const uint16_t*)b1, (const uint16_t*)w2, (const uint16_t*)b2,
+                                  (uint16_t*)H, (uint16_t*)y_perm, E, d, h, mslots, zb, s);
+  return launch_gemms_bf16<64>(xb, sorted_token, offsets, tile_start, (const uint16_t*)w1,
+                               (const uint16_t*)b1, (const uint16_t*)w2, (const uint16_t*)b2,
+                               (uint16_t*)H, (uint16_t*)y_perm, E, d, h, mslots, zb, s);
+}
+
+int ffn_check(const void* x, int dtype, int T, int d, int h, int E, int k,
+              const int32_t* offsets, const int32_t* sorted_token, const void* w1,
+              const void* w2, const void* y_perm, const void* ws, size_t ws_bytes) {
   if (T < 0 || d < 1 || h < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID;
   if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_INVALID;
   if (E > kMaxE) return MOE_ERR_UNSUPPORTED;
@@ -688,47 +759,35 @@ extern "C" int moe_grouped_ffn(const void* x, int dtype, int T, int d, int h, in
   if (rows == 0) return MOE_OK;
   if (!x || !offsets || !sorted_token || !w1 || !w2 || !y_perm) return MOE_ERR_INVALID;
   if (!ws || ws_bytes < ffn_ws(T, d, h, E, k)) return MOE_ERR_WORKSPACE;
-  hipStream_t s = (hipStream_t)stream;
-  int32_t* tile_start = (int32_t*)ws;
+  return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_grouped_ffn(const void* x, int dtype, int T, int d, int h, int E, int k,
+                               const int32_t* offsets, const int32_t* sorted_token, const void* w1,
+                               const void* b1, const void* w2, const void* b2, void* y_perm,
+                               void* ws, size_t ws_bytes, moe_stream_t stream) {
+  const int st = ffn_check(x, dtype, T, d, h, E, k, offsets, sorted_token, w1, w2, y_perm, ws,
+                           ws_bytes);
+  if (st != MOE_OK || (long)T * k == 0) return st;
   void* H = (unsigned char*)ws + ffn_plan_bytes(T, d, h, E, k);
-  const int nonempty = (int)(rows < E ? rows : E);
+  return grouped_ffn(x, dtype, T, d, h, E, k, offsets, sorted_token, w1, b1, w2, b2, y_perm, ws,
+                     H, nullptr, (hipStream_t)stream);
+}
 
-  if (dtype == MOE_F32) {
-    const int mslots = ceil_div(rows, FB) + nonempty;
-    hipLaunchKernelGGL(build_tile_map, dim3(1), dim3(512), 0, s, offsets, E, FB, tile_start);
-    hipLaunchKernelGGL((gemm_f32<true, true>), dim3(mslots * ceil_div(h, FB)), dim3(256), 0, s,
-                       (const float*)x, sorted_token, offsets, tile_start, (const float*)w1,
-                       (const float*)b1, (float*)H, E, h, d, mslots);
-    hipLaunchKernelGGL((gemm_f32<false, false>), dim3(mslots * ceil_div(d, FB)), dim3(256), 0, s,
-                       (const float*)H, sorted_token, offsets, tile_start, (const float*)w2,
-                       (const float*)b2, (float*)y_perm, E, d, h, mslots);
-    return launch_status();
-  }
-
-  const uint16_t* xb = (const uint16_t*)x;
-  if (use_decode(rows, E)) {
-    return launch_decode(xb, sorted_token, offsets, (const uint16_t*)w1, (const uint16_t*)b1,
-                         (const uint16_t*)w2, (const uint16_t*)b2, (uint16_t*)H,
-                         (uint16_t*)y_perm, E, d, h, nullptr, nullptr, 0, s);
-  }
-
-  if (use_ring(rows, E, T, d, h))
-    return launch_ring(xb, sorted_token, offsets, ws, (const uint16_t*)w1, (const uint16_t*)b1,
-                       (const uint16_t*)w2, (const uint16_t*)b2, (uint16_t*)H, (uint16_t*)y_perm,
-                       E, d, h, T, k, rows, s);
-  if (use_ring128(rows, E, T, d, h))
-    return launch_pring<128>(xb, sorted_token, offsets, ws, (const uint16_t*)w1,
-                             (const uint16_t*)b1, (const uint16_t*)w2, (const uint16_t*)b2,
-                             (uint16_t*)H, (uint16_t*)y_perm, E, d, h, T, k, rows, s);
-  const int mslots = ceil_div(rows, kBM) + nonempty;
-  hipLaunchKernelGGL(build_tile_map, dim3(1), dim3(512), 0, s, offsets, E, kBM, tile_start);
-  if ((d % 128) == 0 && (h % 128) == 0)
-    return launch_gemms_bf16<128>(xb, sorted_token, offsets, tile_start, (const uint16_t*)w1,
-                                  (const uint16_t*)b1, (const uint16_t*)w2, (const uint16_t*)b2,
-                                  (uint16_t*)H, (uint16_t*)y_perm, E, d, h, mslots, s);
-  return launch_gemms_bf16<64>(xb, sorted_token, offsets, tile_start, (const uint16_t*)w1,
-                               (const uint16_t*)b1, (const uint16_t*)w2, (const uint16_t*)b2,
-                               (uint16_t*)H, (uint16_t*)y_perm, E, d, h, mslots, s);
+extern "C" int moe_grouped_ffn_train(const void* x, int dtype, int T, int d, int h, int E, int k,
+                                     const int32_t* offsets, const int32_t* sorted_token,
+                                     const void* w1, const void* b1, const void* w2,
+                                     const void* b2, void* y_perm, void* z_perm, void* h_perm,
+                                     void* ws, size_t ws_bytes, moe_stream_t stream) {
+  const int st = ffn_check(x, dtype, T, d, h, E, k, offsets, sorted_token, w1, w2, y_perm, ws,
+                           ws_bytes);
+  if (st != MOE_OK || (long)T * k == 0) return st;
+  if (!z_perm || !h_perm) return MOE_ERR_INVALID;
+  return grouped_ffn(x, dtype, T, d, h, E, k, offsets, sorted_token, w1, b1, w2, b2, y_perm, ws,
+                     h_perm, z_perm, (hipStream_t)stream);
 }
 
 extern "C" int moe_grouped_ffn_cached(const void* x, int dtype, int T, int d, int h, int E, int k,
@@ -751,5 +810,5 @@ extern "C" int moe_grouped_ffn_cached(const void* x, int dtype, int T, int d, in
   return launch_decode((const uint16_t*)x, sorted_token, offsets, (const uint16_t*)w1,
                        (const uint16_t*)b1, (const uint16_t*)w2, (const uint16_t*)b2,
                        (uint16_t*)H, (uint16_t*)y_perm, E, d, h, slot_of, phase_of, phase,
-                       (hipStream_t)stream);
+                       (uint16_t*)nullptr, (hipStream_t)stream);
 }

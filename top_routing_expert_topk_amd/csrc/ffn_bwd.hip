@@ -6,7 +6,8 @@
 //   dXp = dZ W1[e]                 (per permuted row, summed into dx later)
 //   dW2[e] = dY_e^T SiLU(Z_e),  db2[e] = sum of dY_e rows
 //   dW1[e] = dZ_e^T X_e,        db1[e] = sum of dZ_e rows
-// Z is recomputed from x rather than kept from the forward.
+// Z and SiLU(Z) come from a forward that kept them (moe_grouped_ffn_train);
+// without them Z is recomputed from x here.
 //
 // bf16 data path: every product runs on the 256 x 256 DMA-ring MFMA GEMM.
 // The data gradients contract over the weights' leading index: the ring
@@ -281,20 +282,24 @@ __global__ __launch_bounds__(256) void gemm_f32_wgrad(const float* __restrict__ 
 
 int ffn_backward_f32(const float* x, int T, int d, int h, int E, int k, const int32_t* offsets,
                      const int32_t* sorted_token, const float* w1, const float* b1,
-                     const float* w2, const float* dy, float* dxp, float* dw1, float* db1,
-                     float* dw2, float* db2, void* ws, hipStream_t s) {
+                     const float* w2, const float* dy, const float* zin, const float* hin,
+                     float* dxp, float* dw1, float* db1, float* dw2, float* db2, void* ws,
+                     hipStream_t s) {
   const FfnBwdLayout L = ffn_bwd_layout(T, d, h, E, k);
   unsigned char* base = (unsigned char*)ws;
   int32_t* tile_start = (int32_t*)base;
-  float* Z = (float*)(base + L.z);
+  float* Zw = (float*)(base + L.z);
+  const float* Z = zin ? zin : Zw;
   float* dZ = (float*)(base + L.dz);
   const long rows = (long)T * k;
   const int nonempty = (int)(rows < E ? rows : E);
   const int mslots = ceil_div(rows, FB) + nonempty;
   hipLaunchKernelGGL(build_tile_map, dim3(1), dim3(512), 0, s, offsets, E, FB, tile_start);
   if (rows > 0) {
-    hipLaunchKernelGGL((gemm_f32<true, false>), dim3(mslots * ceil_div(h, FB)), dim3(256), 0, s, x,
-                       sorted_token, offsets, tile_start, w1, b1, Z, E, h, d, mslots);
+    if (!zin)
+      hipLaunchKernelGGL((gemm_f32<true, false>), dim3(mslots * ceil_div(h, FB)), dim3(256), 0, s,
+                         x, sorted_token, offsets, tile_start, w1, b1, Zw, E, h, d, mslots,
+                         (float*)nullptr);
     // dZ = (dY W2[e]) * SiLU'(Z): W2[e] is [d][h] = [K][N]
     hipLaunchKernelGGL((gemm_f32_dgrad<true>), dim3(mslots * ceil_div(h, FB)), dim3(256), 0, s, dy,
                        offsets, tile_start, w2, Z, dZ, E, h, d, mslots);
@@ -303,8 +308,12 @@ int ffn_backward_f32(const float* x, int T, int d, int h, int E, int k, const in
                        offsets, tile_start, w1, (const float*)nullptr, dxp, E, d, h, mslots);
   }
   const dim3 g2(ceil_div(d, FB) * ceil_div(h, FB), E);
-  hipLaunchKernelGGL((gemm_f32_wgrad<false, true>), g2, dim3(256), 0, s, dy, (const float*)Z,
-                     sorted_token, offsets, d, h, dw2);
+  if (hin)
+    hipLaunchKernelGGL((gemm_f32_wgrad<false, false>), g2, dim3(256), 0, s, dy, hin, sorted_token,
+                       offsets, d, h, dw2);
+  else
+    hipLaunchKernelGGL((gemm_f32_wgrad<false, true>), g2, dim3(256), 0, s, dy, Z, sorted_token,
+                       offsets, d, h, dw2);
   hipLaunchKernelGGL((gemm_f32_wgrad<true, false>), g2, dim3(256), 0, s, (const float*)dZ, x,
                      sorted_token, offsets, h, d, dw1);
   if (db2)
@@ -318,9 +327,9 @@ int ffn_backward_f32(const float* x, int T, int d, int h, int E, int k, const in
 
 int ffn_backward_bf16(const uint16_t* x, int T, int d, int h, int E, int k,
                       const int32_t* offsets, const int32_t* sorted_token, const uint16_t* w1,
-                      const uint16_t* b1, const uint16_t* w2, const uint16_t* dy, uint16_t* dxp,
-                      uint16_t* dw1, uint16_t* db1, uint16_t* dw2, uint16_t* db2, void* ws,
-                      hipStream_t s) {
+                      const uint16_t* b1, const uint16_t* w2, const uint16_t* dy,
+                      const uint16_t* zin, const uint16_t* hin, uint16_t* dxp, uint16_t* dw1,
+                      uint16_t* db1, uint16_t* dw2, uint16_t* db2, void* ws, hipStream_t s) {
   const FfnBwdLayout L = ffn_bwd_layout(T, d, h, E, k);
   unsigned char* base = (unsigned char*)ws;
   const long rows = (long)T * k;
@@ -333,8 +342,10 @@ int ffn_backward_bf16(const uint16_t* x, int T, int d, int h, int E, int k,
   const int md = d / kBigBN, mh = h / kBigBN;
   BigWork* wl2 = (BigWork*)(base + L.wl);  // dW2: M = d, N = h
   BigWork* wl1 = wl2 + (size_t)E * md * mh;  // dW1: M = h, N = d
-  uint16_t* Z = (uint16_t*)(base + L.z);
+  uint16_t* Zw = (uint16_t*)(base + L.z);
+  const uint16_t* Z = zin ? zin : Zw;
   uint16_t* dZ = (uint16_t*)(base + L.dz);
+  uint16_t* const nz = nullptr;
   float* part = (float*)(base + L.part);
   uint16_t* ta = (uint16_t*)(base + L.ta);
   uint16_t* tb = (uint16_t*)(base + L.tb);
@@ -350,26 +361,32 @@ int ffn_backward_bf16(const uint16_t* x, int T, int d, int h, int E, int k,
                      md, mh, wl2);
   hipLaunchKernelGGL(wgrad_plan, dim3(ceil_div(nwt, 256)), dim3(256), 0, s, (const int32_t*)pt, E,
                      mh, md, wl1);
-  // Z = W1[e] x + b1 (the forward's first product without the activation)
-  hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, true, kEpiBias>), dim3(g1), rb, 0, s, x,
-                     sorted_token, list1, w1, b1, Z, part, h, d, (size_t)h * d, 0, none);
-  hipLaunchKernelGGL((big_tail_reduce<kBigBM, kEpiBias>), gr, dim3(256), 0, s, hdr, list1, b1, part,
-                     Z, h, none);
+  if (!zin) {
+    // Z = W1[e] x + b1 (the forward's first product without the activation)
+    hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, true, kEpiBias>), dim3(g1), rb, 0, s, x,
+                       sorted_token, list1, w1, b1, Zw, part, h, d, (size_t)h * d, 0, none, nz);
+    hipLaunchKernelGGL((big_tail_reduce<kBigBM, kEpiBias>), gr, dim3(256), 0, s, hdr, list1, b1,
+                       part, Zw, h, none, nz);
+  }
   // dZ = (dY W2[e]) * SiLU'(Z): W2[e] is [d][h], K-major for this product
   hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, false, kEpiDSilu, true>), dim3(g1), rb, 0, s, dy,
                      (const int32_t*)nullptr, list1, w2, none, dZ, part, h, d, (size_t)h * d, 0,
-                     (const uint16_t*)Z);
+                     Z, nz);
   hipLaunchKernelGGL((big_tail_reduce<kBigBM, kEpiDSilu>), gr, dim3(256), 0, s, hdr, list1, none,
-                     part, dZ, h, (const uint16_t*)Z);
+                     part, dZ, h, Z, nz);
   // dW2[e] = dY_e^T SiLU(Z_e)
   const int nseg = (int)(rp / kTB);
   hipLaunchKernelGGL((transpose_pad<0>), dim3(nseg, d / kTB), dim3(256), 0, s, dy,
                      (const int32_t*)nullptr, offsets, (const int32_t*)pt, E, d, rp, ta);
-  hipLaunchKernelGGL((transpose_pad<1>), dim3(nseg, h / kTB), dim3(256), 0, s, (const uint16_t*)Z,
-                     (const int32_t*)nullptr, offsets, (const int32_t*)pt, E, h, rp, tb);
+  if (hin)
+    hipLaunchKernelGGL((transpose_pad<0>), dim3(nseg, h / kTB), dim3(256), 0, s, hin,
+                       (const int32_t*)nullptr, offsets, (const int32_t*)pt, E, h, rp, tb);
+  else
+    hipLaunchKernelGGL((transpose_pad<1>), dim3(nseg, h / kTB), dim3(256), 0, s, Z,
+                       (const int32_t*)nullptr, offsets, (const int32_t*)pt, E, h, rp, tb);
   hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, false, kEpiBias>), dim3(nwt), rb, 0, s,
                      (const uint16_t*)ta, (const int32_t*)nullptr, (const BigWork*)wl2,
-                     (const uint16_t*)tb, none, dw2, part, h, (int)rp, (size_t)0, d, none);
+                     (const uint16_t*)tb, none, dw2, part, h, (int)rp, (size_t)0, d, none, nz);
   // dW1[e] = dZ_e^T X_e
   hipLaunchKernelGGL((transpose_pad<2>), dim3(nseg, d / kTB), dim3(256), 0, s, x, sorted_token,
                      offsets, (const int32_t*)pt, E, d, rp, ta);
@@ -377,13 +394,13 @@ int ffn_backward_bf16(const uint16_t* x, int T, int d, int h, int E, int k,
                      (const int32_t*)nullptr, offsets, (const int32_t*)pt, E, h, rp, tb);
   hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, false, kEpiBias>), dim3(nwt), rb, 0, s,
                      (const uint16_t*)tb, (const int32_t*)nullptr, (const BigWork*)wl1,
-                     (const uint16_t*)ta, none, dw1, part, d, (int)rp, (size_t)0, h, none);
+                     (const uint16_t*)ta, none, dw1, part, d, (int)rp, (size_t)0, h, none, nz);
   // dXp = dZ W1[e]: W1[e] is [h][d], K-major for this product
   hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, false, kEpiBias, true>), dim3(g2), rb, 0, s,
                      (const uint16_t*)dZ, (const int32_t*)nullptr, list2, w1, none, dxp, part, d, h,
-                     (size_t)d * h, 0, none);
+                     (size_t)d * h, 0, none, nz);
   hipLaunchKernelGGL((big_tail_reduce<kBigBM, kEpiBias>), gr, dim3(256), 0, s, hdr + 1, list2, none,
-                     part, dxp, d, none);
+                     part, dxp, d, none, nz);
   if (db2)
     hipLaunchKernelGGL(bias_grad_bf16, dim3(d / 128, E), dim3(256), 0, s, dy, offsets, d, db2);
   if (db1)
@@ -400,7 +417,8 @@ using namespace moe;
 extern "C" int moe_grouped_ffn_backward(const void* x, int dtype, int T, int d, int h, int E, int k,
                                         const int32_t* offsets, const int32_t* sorted_token,
                                         const void* w1, const void* b1, const void* w2,
-                                        const void* dy_perm, void* dx_perm, void* dw1, void* db1,
+                                        const void* dy_perm, const void* z_perm,
+                                        const void* h_perm, void* dx_perm, void* dw1, void* db1,
                                         void* dw2, void* db2, void* ws, size_t ws_bytes,
                                         moe_stream_t stream) {
   if (T < 0 || d < 1 || h < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID;
@@ -410,13 +428,15 @@ extern "C" int moe_grouped_ffn_backward(const void* x, int dtype, int T, int d, 
   if (rows > 0x7FFFFFFFL) return MOE_ERR_UNSUPPORTED;
   if (!offsets || !w1 || !w2 || !dw1 || !dw2) return MOE_ERR_INVALID;
   if (rows > 0 && (!x || !sorted_token || !dy_perm || !dx_perm)) return MOE_ERR_INVALID;
+  if ((z_perm == nullptr) != (h_perm == nullptr)) return MOE_ERR_INVALID;
   if (!ws || ws_bytes < ffn_bwd_layout(T, d, h, E, k).total) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   if (dtype == MOE_F32)
     return ffn_backward_f32((const float*)x, T, d, h, E, k, offsets, sorted_token,
                             (const float*)w1, (const float*)b1, (const float*)w2,
-                            (const float*)dy_perm, (float*)dx_perm, (float*)dw1, (float*)db1,
-                            (float*)dw2, (float*)db2, ws, s);
+                            (const float*)dy_perm, (const float*)z_perm, (const float*)h_perm,
+                            (float*)dx_perm, (float*)dw1, (float*)db1, (float*)dw2, (float*)db2,
+                            ws, s);
   // bf16: 256 x 256 tiles on both widths; 32-bit element offsets of every
   // row operand (the gathered x rows, the permuted rows and the padded
   // transposed arrays)
@@ -427,6 +447,7 @@ extern "C" int moe_grouped_ffn_backward(const void* x, int dtype, int T, int d, 
     return MOE_ERR_UNSUPPORTED;
   return ffn_backward_bf16((const uint16_t*)x, T, d, h, E, k, offsets, sorted_token,
                            (const uint16_t*)w1, (const uint16_t*)b1, (const uint16_t*)w2,
-                           (const uint16_t*)dy_perm, (uint16_t*)dx_perm, (uint16_t*)dw1,
+                           (const uint16_t*)dy_perm, (const uint16_t*)z_perm,
+                           (const uint16_t*)h_perm, (uint16_t*)dx_perm, (uint16_t*)dw1,
                            (uint16_t*)db1, (uint16_t*)dw2, (uint16_t*)db2, ws, s);
 }

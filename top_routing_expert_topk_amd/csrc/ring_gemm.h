@@ -260,13 +260,15 @@ __global__ __launch_bounds__(512) void big_plan(const int32_t* __restrict__ offs
 // offset spread over the banks. kEpiDSilu multiplies by SiLU'(z) in that last
 // pass, where z arrives in the same 16-byte row chunks as the output leaves
 // (the product is taken of the bf16-rounded accumulator). Output row of tile
-// row m: e * ores + row0 + m.
+// row m: e * ores + row0 + m. kEpiSilu with zout: the pre-activation
+// acc + bias also leaves, to zout, in a first pass through the same staging.
 template <int NW, int TM, int EPI>
 __device__ __forceinline__ void big_store(f32x16 (&acc)[4][TM], uint16_t* ot, size_t ot_bytes,
                                           const BigWork& wk, const uint16_t* __restrict__ bias,
                                           uint16_t* __restrict__ out, float* __restrict__ part,
                                           int N, int ores, const uint16_t* __restrict__ zin,
-                                          int wn, int wm, int lane, int tid) {
+                                          uint16_t* __restrict__ zout, int wn, int wm, int lane,
+                                          int tid) {
   constexpr int BM = kBigBM, BN = kBigBN, TN = 4, WTN = 128, WTM = 32 * TM;
   const int ch = lane >> 5;
   if (wk.unit >= 0) {
@@ -286,8 +288,43 @@ __device__ __forceinline__ void big_store(f32x16 (&acc)[4][TM], uint16_t* ot, si
     return;
   }
   constexpr int OSTR = BN + 8;  // LDS row stride in bf16 elements
+  constexpr int CPR = BN / 8;   // 16-byte chunks per row
   (void)ot_bytes;  // callers static_assert BM * OSTR * 2 <= ot_bytes
   lds_barrier();  // every wave is done reading the ring
+  if (EPI == kEpiSilu && zout) {
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int nl = wn * WTN + i * 32 + 8 * q + 4 * ch;
+        float bv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (bias) {
+          const u32x2 bb = *(const u32x2*)(bias + (size_t)wk.e * N + wk.n0 + nl);
+          bv[0] = bf16lo(bb[0]);
+          bv[1] = bf16hi(bb[0]);
+          bv[2] = bf16lo(bb[1]);
+          bv[3] = bf16hi(bb[1]);
+        }
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+          const int m = wm * WTM + j * 32 + (lane & 31);
+          u32x2 o;
+          o[0] = pack_bf16x2(acc[i][j][4 * q] + bv[0], acc[i][j][4 * q + 1] + bv[1]);
+          o[1] = pack_bf16x2(acc[i][j][4 * q + 2] + bv[2], acc[i][j][4 * q + 3] + bv[3]);
+          *(u32x2*)(ot + m * OSTR + nl) = o;
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int c = tid; c < BM * CPR; c += NW * 64) {
+      const int m = c / CPR, cc = c % CPR;
+      if (m < wk.rows)
+        *(u32x4*)(zout + (size_t)(wk.row0 + m) * N + wk.n0 + cc * 8) =
+            *(const u32x4*)(ot + m * OSTR + cc * 8);
+    }
+    __syncthreads();
+  }
 #pragma unroll
   for (int i = 0; i < TN; ++i) {
 #pragma unroll
@@ -318,7 +355,6 @@ __device__ __forceinline__ void big_store(f32x16 (&acc)[4][TM], uint16_t* ot, si
     }
   }
   __syncthreads();
-  constexpr int CPR = BN / 8;  // 16-byte chunks per row
 #pragma unroll 4
   for (int c = tid; c < BM * CPR; c += NW * 64) {
     const int m = c / CPR, cc = c % CPR;
@@ -358,7 +394,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ sorted_token,
     const BigWork* __restrict__ work, const uint16_t* __restrict__ w,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, float* __restrict__ part, int N,
-    int K, size_t wes, int ores, const uint16_t* __restrict__ zin) {
+    int K, size_t wes, int ores, const uint16_t* __restrict__ zin, uint16_t* __restrict__ zout) {
   constexpr int BM = kBigBM, BN = kBigBN;
   constexpr int WM = NW / 2;          // waves along the permuted rows (2 along the weight rows)
   constexpr int TN = 4, TM = 8 / WM;  // 32x32 MFMA tiles per wave
@@ -547,8 +583,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
 #undef MOE_RD
 #undef MOE_MM
 
-  big_store<NW, TM, EPI>(acc, ring, sizeof(ring), wk, bias, out, part, N, ores, zin, wn, wm, lane,
-                         tid);
+  big_store<NW, TM, EPI>(acc, ring, sizeof(ring), wk, bias, out, part, N, ores, zin, zout, wn, wm,
+                         lane, tid);
 }
 
 
@@ -562,7 +598,8 @@ __global__ __launch_bounds__(256) void big_tail_reduce(const BigHdr* __restrict_
                                                        const uint16_t* __restrict__ bias,
                                                        const float* __restrict__ part,
                                                        uint16_t* __restrict__ out, int N,
-                                                       const uint16_t* __restrict__ zin) {
+                                                       const uint16_t* __restrict__ zin,
+                                                       uint16_t* __restrict__ zout) {
   const BigHdr sp = *hdr;
   const int tt = blockIdx.x / kReduceSlices, slice = blockIdx.x % kReduceSlices;
   if (tt >= sp.tail || sp.split < 2) return;
@@ -585,11 +622,12 @@ __global__ __launch_bounds__(256) void big_tail_reduce(const BigHdr* __restrict_
       v[0] += lo[0]; v[1] += lo[1]; v[2] += lo[2]; v[3] += lo[3];
       v[4] += hi[0]; v[5] += hi[1]; v[6] += hi[2]; v[7] += hi[3];
     }
-    u32x4 o, z;
+    u32x4 o, z, pre;
     if (EPI == kEpiDSilu) z = *(const u32x4*)(zin + (size_t)(tile.row0 + m) * N + tile.n0 + nl);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       float a = v[2 * q] + bv[2 * q], c = v[2 * q + 1] + bv[2 * q + 1];
+      pre[q] = pack_bf16x2(a, c);
       if (EPI == kEpiSilu) {
         a = silu_bf16(a);
         c = silu_bf16(c);
@@ -600,6 +638,7 @@ __global__ __launch_bounds__(256) void big_tail_reduce(const BigHdr* __restrict_
       o[q] = pack_bf16x2(a, c);
     }
     *(u32x4*)(out + (size_t)(tile.row0 + m) * N + tile.n0 + nl) = o;
+    if (EPI == kEpiSilu && zout) *(u32x4*)(zout + (size_t)(tile.row0 + m) * N + tile.n0 + nl) = pre;
   }
 }
 

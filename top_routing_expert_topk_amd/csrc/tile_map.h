@@ -48,7 +48,7 @@ __global__ __launch_bounds__(256) void gemm_f32(
     const float* __restrict__ act, const int32_t* __restrict__ sorted_token,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_start,
     const float* __restrict__ w, const float* __restrict__ bias, float* __restrict__ out, int E,
-    int N, int K, int mslots) {
+    int N, int K, int mslots, float* __restrict__ zout) {
   __shared__ float sW[FKC][FB + 4];
   __shared__ float sX[FKC][FB + 4];
   const int ms = blockIdx.x % mslots, nt = blockIdx.x / mslots;
@@ -106,6 +106,7 @@ __global__ __launch_bounds__(256) void gemm_f32(
       const int m = ty * 4 + j;
       if (m < rows) {
         float v = acc[i][j] + b;
+        if (SILU && zout) zout[(size_t)(row0 + m) * N + n] = v;
         if (SILU) v = silu(v);
         out[(size_t)(row0 + m) * N + n] = v;
       }

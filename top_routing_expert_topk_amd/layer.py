@@ -27,6 +27,7 @@ class MoEBuffers:
     dtype: torch.dtype
     device: torch.device
     out_dtype: torch.dtype = torch.float32  # combine output; fp32 keeps the sum unrounded
+    train: bool = False  # keep the pre-activations and hidden rows for the backward
 
     def __post_init__(self):
         T, d, h, E, k = self.T, self.d, self.h, self.E, self.k
@@ -45,6 +46,10 @@ class MoEBuffers:
         self.f = torch.empty((E,), dtype=f32, device=dev)
         self.P = torch.empty((E,), dtype=f32, device=dev)
         self.loss = torch.empty((1,), dtype=f32, device=dev)
+        self.z_perm = self.h_perm = None
+        if self.train:
+            self.z_perm = torch.empty((T * k, self.h), dtype=self.dtype, device=dev)
+            self.h_perm = torch.empty((T * k, self.h), dtype=self.dtype, device=dev)
 
         def ws(op):
             n = N.moe_workspace_size(op, T, d, h, E, k)
@@ -57,20 +62,26 @@ class MoEBuffers:
 
 def moe_layer_forward(x, w_gate, gate_bias, w1, b1, w2, b2, k, renorm=True, capacity=-1,
                       residual=False, want_logits=False, bufs: MoEBuffers | None = None,
-                      stream=None, out_dtype=torch.float32) -> MoEBuffers:
-    """Enqueue the whole layer; returns the buffers (outputs valid once the stream runs)."""
+                      stream=None, out_dtype=torch.float32, train=False) -> MoEBuffers:
+    """Enqueue the whole layer; returns the buffers (outputs valid once the stream runs).
+    train: keep the logits, pre-activations and hidden rows for moe_layer_backward."""
     T, d = x.shape
     E = w_gate.shape[0]
     h = w1.shape[1]
     if bufs is None:
-        bufs = MoEBuffers(T, d, h, E, k, x.dtype, x.device, out_dtype)
+        bufs = MoEBuffers(T, d, h, E, k, x.dtype, x.device, out_dtype, train)
+    want_logits = want_logits or train
     b = bufs
     N.moe_router_topk(x, w_gate, gate_bias, E, k, renorm, b.logits if want_logits else None,
                       b.topk_idx, b.topk_gate, b.prob_sum, b.ws_router, stream)
     N.moe_permute(b.topk_idx, T, k, E, capacity, b.counts, b.offsets, b.dest_row,
                   b.sorted_token, b.ws_permute, stream)
-    N.moe_grouped_ffn(x, T, d, h, E, k, b.offsets, b.sorted_token, w1, b1, w2, b2, b.y_perm,
-                      b.ws_ffn, stream)
+    if b.train:
+        N.moe_grouped_ffn_train(x, T, d, h, E, k, b.offsets, b.sorted_token, w1, b1, w2, b2,
+                                b.y_perm, b.z_perm, b.h_perm, b.ws_ffn, stream)
+    else:
+        N.moe_grouped_ffn(x, T, d, h, E, k, b.offsets, b.sorted_token, w1, b1, w2, b2, b.y_perm,
+                          b.ws_ffn, stream)
     N.moe_combine(b.y_perm, b.dest_row, b.topk_gate, T, k, d, x if residual else None, b.out,
                   stream)
     N.moe_aux_loss(b.prob_sum, b.counts, T, E, b.f, b.P, b.loss, stream)
@@ -258,7 +269,9 @@ def moe_layer_backward(fwd: MoEBuffers, x, w_gate, gate_bias, w1, b1, w2, b2, do
                        residual=False, daux=0.0, grads: MoEGrads | None = None,
                        stream=None) -> MoEGrads:
     """Enqueue the backward of a token-choice layer whose forward ran with
-    want_logits=True into ``fwd``. dout [T][d] in the layer dtype; daux is
+    want_logits=True into ``fwd`` (with train=True the backward reuses the
+    forward's pre-activations instead of recomputing them). dout [T][d] in
+    the layer dtype; daux is
     the weight of the aux loss in the differentiated scalar. Returns the
     gradient buffers (valid once the stream runs):
       moe_combine_backward -> moe_router_backward -> moe_grouped_ffn_backward
@@ -277,7 +290,8 @@ def moe_layer_backward(fwd: MoEBuffers, x, w_gate, gate_bias, w1, b1, w2, b2, do
     N.moe_router_backward(fwd.logits, fwd.topk_idx, fwd.topk_gate, g.dgate, fwd.counts, T, E, k,
                           renorm, daux, g.dlogits, stream)
     N.moe_grouped_ffn_backward(x, T, d, h, E, k, fwd.offsets, fwd.sorted_token, w1, b1, w2,
-                               g.dy_perm, g.dx_perm, g.dw1, g.db1, g.dw2, g.db2, g.ws_ffn, stream)
+                               g.dy_perm, fwd.z_perm, fwd.h_perm, g.dx_perm, g.dw1, g.db1, g.dw2,
+                               g.db2, g.ws_ffn, stream)
     N.moe_gather_backward(g.dx_perm, fwd.dest_row, T, k, d, dout if residual else None, g.dlogits,
                           w_gate, E, g.dx, stream)
     N.moe_router_weight_backward(x, T, d, E, g.dlogits, g.dw_gate, g.dgate_bias, g.ws_router,

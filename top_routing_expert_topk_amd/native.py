@@ -65,14 +65,16 @@ def lib():
         L.moe_combine_backward.argtypes = [P, I, P, P, I, I, I, P, P, P, P]
         L.moe_router_backward.argtypes = [P, P, P, P, P, I, I, I, I, F, P, P]
         L.moe_grouped_ffn_backward.argtypes = [P, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P,
-                                               P, P, P, Z, P]
+                                               P, P, P, P, P, Z, P]
+        L.moe_grouped_ffn_train.argtypes = [P, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, Z,
+                                            P]
         L.moe_gather_backward.argtypes = [P, I, P, I, I, I, P, P, P, I, P, P]
         L.moe_router_weight_backward.argtypes = [P, I, I, I, I, P, P, P, P, Z, P]
         for f in ("moe_router_topk", "moe_permute", "moe_grouped_ffn", "moe_combine",
                   "moe_aux_loss", "moe_expert_choice", "moe_cache_init", "moe_cache_step",
                   "moe_cache_slot_of", "moe_grouped_ffn_cached", "moe_combine_backward",
                   "moe_router_backward", "moe_grouped_ffn_backward", "moe_gather_backward",
-                  "moe_router_weight_backward"):
+                  "moe_router_weight_backward", "moe_grouped_ffn_train"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -245,11 +247,18 @@ def moe_router_backward(logits, topk_idx, topk_gate, dgate, counts, T, E, k, ren
 
 
 def moe_grouped_ffn_backward(x, T, d, h, E, k, offsets, sorted_token, w1, b1, w2, dy_perm,
-                             dx_perm, dw1, db1, dw2, db2, ws, stream=None):
+                             z_perm, h_perm, dx_perm, dw1, db1, dw2, db2, ws, stream=None):
     _check("moe_grouped_ffn_backward", lib().moe_grouped_ffn_backward(
         _p(x), _dt(w1), T, d, h, E, k, _p(offsets), _p(sorted_token), _p(w1), _p(b1), _p(w2),
-        _p(dy_perm), _p(dx_perm), _p(dw1), _p(db1), _p(dw2), _p(db2), _p(ws), _nbytes(ws),
-        _stream(stream)))
+        _p(dy_perm), _p(z_perm), _p(h_perm), _p(dx_perm), _p(dw1), _p(db1), _p(dw2), _p(db2),
+        _p(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_grouped_ffn_train(x, T, d, h, E, k, offsets, sorted_token, w1, b1, w2, b2, y_perm,
+                          z_perm, h_perm, ws, stream=None):
+    _check("moe_grouped_ffn_train", lib().moe_grouped_ffn_train(
+        _p(x), _dt(x), T, d, h, E, k, _p(offsets), _p(sorted_token), _p(w1), _p(b1), _p(w2),
+        _p(b2), _p(y_perm), _p(z_perm), _p(h_perm), _p(ws), _nbytes(ws), _stream(stream)))
 
 
 def moe_gather_backward(dx_perm, dest_row, T, k, d, dout_residual, dlogits, w_gate, E, dx,

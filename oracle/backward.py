@@ -260,3 +260,126 @@ def _scales(X, Wg, W1, B1, W2, dO, lg, idx, gate, dest, st, offsets, slot_of_row
     if B1 is None:
         m["db1"] = None
     return m
+
+
+def moe_backward_sampled(x, w_gate, fetch, k: int, renorm: bool, capacity: int, dout, daux: float,
+                         lg, gate_bias=None, residual: bool = False, tokens=(), w1_rows=(),
+                         w2_cols=(), b2_experts=()):
+    """Selected elements of the same gradients, each computed on its own, for
+    layers too large for ``moe_backward``.
+
+    fetch(e) -> (w1e, b1e, w2e, b2e) gives one expert's weights. Returns a
+    dict of (value, magnitude) pairs, the magnitude as in ``_scales``:
+      "dx":      [len(tokens), d] rows of dx, with "dgate" [n, k] and
+                 "dlogits" [n, E] of the same tokens;
+      "dw1":     {(e, n): row n of dW1[e] ([d])},  "db1": {(e, n): db1[e][n]};
+      "dw2":     {(e, n): column n of dW2[e] ([d])};
+      "db2":     {e: db2[e] ([d])}.
+    Every value follows the expert's rows r (token t_r, slot j_r, gate g_r):
+    dy_r = g_r dout[t_r], z_r = W1[e] x[t_r] + b1[e], dZ_r = (dy_r W2[e]) *
+    SiLU'(z_r).
+    """
+    X = widen(x)
+    Wg = widen(w_gate)
+    dO = widen(dout)
+    T, d = X.shape
+    E = Wg.shape[0]
+    lg = np.asarray(lg, dtype=np.float64)
+    idx, gate, _ = fwd.route(lg, k, renorm)
+    counts, offsets, dest, st = fwd.permute(idx, E, capacity)
+    R = int(offsets[E])
+    slot_of_row = np.empty(R, np.int64)
+    kept = np.nonzero(dest >= 0)[0]
+    slot_of_row[dest[kept]] = kept
+    gflat = gate.ravel()
+    cache = {}
+
+    def weights(e):
+        if e not in cache:
+            cache[e] = tuple(widen(a) for a in fetch(e))
+        return cache[e]
+
+    def rows_of(e):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        tok = st[r0:r1]
+        return tok, gflat[slot_of_row[r0:r1]]
+
+    out = {}
+    tokens = np.asarray(tokens, np.int64)
+    p = softmax(lg[tokens]) if tokens.size else np.zeros((0, E))
+    dxs, mdxs, dgs, mdgs, dls, mdls = [], [], [], [], [], []
+    for i, t in enumerate(tokens):
+        dx = dO[t].copy() if residual else np.zeros(d)
+        mdx = np.abs(dO[t]) if residual else np.zeros(d)
+        dg = np.zeros(k)
+        mdg = np.zeros(k)
+        for j in range(k):
+            r = dest[t * k + j]
+            if r < 0:
+                continue
+            w1e, b1e, w2e, b2e = weights(int(idx[t, j]))
+            z = w1e @ X[t] + (0.0 if b1e is None else b1e)
+            y = w2e @ silu(z) + (0.0 if b2e is None else b2e)
+            dg[j] = dO[t] @ y
+            mdg[j] = np.abs(dO[t]) @ np.abs(y)
+            dy = gflat[t * k + j] * dO[t]
+            dz = (dy @ w2e) * silu_grad(z)
+            dx += dz @ w1e
+            mdz = (np.abs(dy) @ np.abs(w2e)) * (np.abs(silu_grad(z)) + np.abs(z) / 8.0)
+            mdx += mdz @ np.abs(w1e)
+        # the router row of this token: gates, then the aux term
+        ag = np.abs(gate[t])
+        dl = np.zeros(E)
+        mdl = np.zeros(E)
+        if renorm:
+            inner = gate[t] @ dg
+            np.add.at(dl, idx[t], gate[t] * (dg - inner))
+            np.add.at(mdl, idx[t], ag * (mdg + ag @ mdg))
+        else:
+            dp = np.zeros(E)
+            mdp = np.zeros(E)
+            np.add.at(dp, idx[t], dg)
+            np.add.at(mdp, idx[t], mdg)
+            dl += p[i] * (dp - p[i] @ dp)
+            mdl += p[i] * (mdp + p[i] @ mdp)
+        if daux:
+            dpa = daux * E * counts.astype(np.float64) / (float(T) * T)
+            dl += p[i] * (dpa - p[i] @ dpa)
+            mdl += p[i] * (np.abs(dpa) + p[i] @ np.abs(dpa))
+        dx += dl @ Wg
+        mdx += mdl @ np.abs(Wg)
+        dxs.append(dx)
+        mdxs.append(mdx)
+        dgs.append(dg)
+        mdgs.append(mdg)
+        dls.append(dl)
+        mdls.append(mdl)
+    out["dx"] = (np.array(dxs).reshape(-1, d), np.array(mdxs).reshape(-1, d))
+    out["dgate"] = (np.array(dgs).reshape(-1, k), np.array(mdgs).reshape(-1, k))
+    out["dlogits"] = (np.array(dls).reshape(-1, E), np.array(mdls).reshape(-1, E))
+
+    out["dw1"], out["db1"], out["dw2"], out["db2"] = {}, {}, {}, {}
+    for e, n in w1_rows:
+        w1e, b1e, w2e, _ = weights(e)
+        tok, g = rows_of(e)
+        xe = X[tok]
+        dy = g[:, None] * dO[tok]
+        z = xe @ w1e[n] + (0.0 if b1e is None else b1e[n])
+        dzn = (dy @ w2e[:, n]) * silu_grad(z)
+        mdzn = (np.abs(dy) @ np.abs(w2e[:, n])) * (np.abs(silu_grad(z)) + np.abs(z) / 8.0)
+        out["dw1"][(e, n)] = (dzn @ xe, mdzn @ np.abs(xe))
+        out["db1"][(e, n)] = (dzn.sum(), mdzn.sum())
+    for e, n in w2_cols:
+        w1e, b1e, _, _ = weights(e)
+        tok, g = rows_of(e)
+        dy = g[:, None] * dO[tok]
+        z = X[tok] @ w1e[n] + (0.0 if b1e is None else b1e[n])
+        hn = silu(z)
+        mhn = np.abs(hn) + np.abs(silu_grad(z) * z) / 4.0
+        out["dw2"][(e, n)] = (hn @ dy, mhn @ np.abs(dy))
+    for e in b2_experts:
+        tok, g = rows_of(e)
+        dy = g[:, None] * dO[tok]
+        out["db2"][e] = (dy.sum(axis=0), np.abs(dy).sum(axis=0))
+    out.update(offsets=offsets, counts=counts, idx=idx)
+    return out

@@ -243,3 +243,36 @@ def test_error_scales_bound_the_gradients():
             assert np.all(M >= np.abs(ref) * (1 - 1e-12) - 1e-15), name
         # daux only moves dlogits and what follows from it
         np.testing.assert_allclose(g2["dw1"], g["dw1"], rtol=0, atol=0)
+
+
+def test_sampled_backward_matches_the_whole_one():
+    """moe_backward_sampled picks the same numbers out of the same chain as
+    moe_backward, for tokens, dW1 rows, dW2 columns and db2 of several
+    experts, in both gate modes, with drops and the aux term."""
+    for renorm, k, cap, res in ((True, 2, 9, False), (False, 1, 6, True)):
+        p, dout = _layer(81 + k, 30, 8, 12, 5, not renorm)
+        lg = orc.logits(p["x"], p["w_gate"], p.get("gate_bias"))
+        full = bwd.moe_backward(p["x"], p["w_gate"], p["w1"], p["b1"], p["w2"], p["b2"], k,
+                                renorm, cap, dout, 0.7, gate_bias=p.get("gate_bias"), residual=res,
+                                lg=lg, want_scale=True)
+        fetch = lambda e: (p["w1"][e], p["b1"][e], p["w2"][e], p["b2"][e])  # noqa: E731
+        toks = [0, 3, 17, 29]
+        rows = [(0, 1), (2, 11), (4, 0)]
+        cols = [(1, 5), (3, 0)]
+        sm = bwd.moe_backward_sampled(p["x"], p["w_gate"], fetch, k, renorm, cap, dout, 0.7, lg,
+                                      gate_bias=p.get("gate_bias"), residual=res, tokens=toks,
+                                      w1_rows=rows, w2_cols=cols, b2_experts=[0, 4])
+        sc = full["scale"]
+        for name in ("dx", "dgate", "dlogits"):
+            v, m = sm[name]
+            np.testing.assert_allclose(v, full[name][toks], rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(m, sc[name][toks], rtol=1e-12, atol=1e-13)
+        for (e, n) in rows:
+            np.testing.assert_allclose(sm["dw1"][(e, n)][0], full["dw1"][e][n], rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(sm["dw1"][(e, n)][1], sc["dw1"][e][n], rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(sm["db1"][(e, n)][0], full["db1"][e][n], rtol=1e-12, atol=1e-13)
+        for (e, n) in cols:
+            np.testing.assert_allclose(sm["dw2"][(e, n)][0], full["dw2"][e][:, n], rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(sm["dw2"][(e, n)][1], sc["dw2"][e][:, n], rtol=1e-12, atol=1e-13)
+        for e in (0, 4):
+            np.testing.assert_allclose(sm["db2"][e][0], full["db2"][e], rtol=1e-12, atol=1e-13)

@@ -331,7 +331,8 @@ int moe_gather_backward(const void *dx_perm, int dtype, const int32_t *dest_row,
  * Router weight gradients:
  *   dw_gate[e][i] = sum_t dlogits[t,e] x[t,i]   (dtype [E][d])
  *   dgate_bias[e] = sum_t dlogits[t,e]          (fp32 [E], may be NULL)
- * Sums run over fixed token ranges in a fixed order. Workspace:
+ * Sums run over fixed token ranges (their number depends only on T, d, E)
+ * in a fixed order. Workspace:
  * moe_workspace_size(MOE_OP_ROUTER_BWD, ...).
  */
 int moe_router_weight_backward(const void *x, int dtype, int T, int d, int E,

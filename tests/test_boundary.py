@@ -155,18 +155,20 @@ def test_binding_refuses_host_tensors():
 
 
 def test_backward_workspace_sizes():
-    """FFN backward: the forward plan, Z and dZ (4 B each), the tail partials
-    and two transposed activation arrays of max(d, h) rows by the padded row
-    count; router weight backward: fp32 partials over at most 8 token
-    ranges."""
+    """FFN backward: the forward plan, the weight-gradient work lists, Z and
+    dZ (4 B each), the tail partials and the gathered input rows; router
+    weight backward: fp32 partials over up to 64 token ranges (about 4096
+    blocks of 64 x 64 tiles, at least 16 tokens per range)."""
     for T, d, h, E, k in [(4096, 4096, 14336, 8, 2), (8192, 7168, 2048, 256, 8),
                           (256, 128, 256, 8, 2), (1, 256, 256, 512, 16)]:
-        rows, rp = T * k, _ceil(T * k + 63 * E, 64) * 64
+        rows = T * k
         need = (N.moe_workspace_size(N.MOE_OP_FFN, T, d, h, E, k) - rows * h * 4
                 - 256 * 256 * 256 * 4)  # the plan part of the forward workspace
-        need += 2 * rows * h * 4 + 256 * 256 * 256 * 4 + 2 * max(d, h) * rp * 2
+        need += (2 * E * (d // 256) * (h // 256) * 32 + 2 * rows * h * 4 + 256 * 256 * 256 * 4
+                 + rows * d * 2)
         assert N.moe_workspace_size(N.MOE_OP_FFN_BWD, T, d, h, E, k) >= need
-        s = min(8, max(1, T // 1024))
+        tiles = _ceil(E, 64) * _ceil(d, 64)
+        s = max(1, min(_ceil(4096, tiles), 64, T // 16))
         assert N.moe_workspace_size(N.MOE_OP_ROUTER_BWD, T, d, h, E, k) >= s * E * d * 4
     assert N.moe_workspace_size(N.MOE_OP_FFN_BWD, 10, 256, 256, 600, 2) == 0
 

@@ -66,12 +66,14 @@ BWD_MUTANTS = {
     "renorm_no_centering": ("(gate * (dgate - inner)).ravel()", "(gate * dgate).ravel()"),
     "no_renorm_skips_softmax": ("return softmax_grad(softmax(lg), dp)\n\n\ndef aux_grad",
                                 "return dp\n\n\ndef aux_grad"),
-    "aux_over_T_once": ("daux * E * counts.astype(np.float64) / (float(T) * T)",
-                        "daux * E * counts.astype(np.float64) / float(T)"),
-    "aux_missing_E": ("daux * E * counts", "daux * counts"),
+    "aux_over_T_once": ("np.broadcast_to(daux * E * counts.astype(np.float64) / (float(T) * T), (T, E))",
+                        "np.broadcast_to(daux * E * counts.astype(np.float64) / float(T), (T, E))"),
+    "aux_missing_E": ("np.broadcast_to(daux * E * counts.astype(np.float64) / (float(T) * T), (T, E))",
+                      "np.broadcast_to(daux * counts.astype(np.float64) / (float(T) * T), (T, E))"),
     "dw2_from_preactivation": ("dw2 = dy.T @ a", "dw2 = dy.T @ z"),
     "db1_before_silu_grad": ("db1 = dz.sum(axis=0)", "db1 = da.sum(axis=0)"),
-    "dx_misses_router": ("dx += dl @ Wg", "dx = dx"),
+    "dx_misses_router": ("dgate_bias = None if gate_bias is None else dl.sum(axis=0)\n    dx += dl @ Wg",
+                         "dgate_bias = None if gate_bias is None else dl.sum(axis=0)\n    dx = dx"),
     "dgate_from_scaled_dy": ("dgate[slots] = (dO[tok] * y).sum(axis=1)",
                              "dgate[slots] = (dy * y).sum(axis=1)"),
     "residual_gradient_dropped": ("dx = dO.copy() if residual else", "dx = 0.0 * dO if residual else"),

@@ -18,7 +18,8 @@
 //                   softmax or full-softmax backward) plus the aux term
 //   gather_bwd      dx[t] = dout[t] (residual) + sum_j dXp[dest[t,j]]
 //                   + sum_e dlogits[t,e] W_g[e], 16 tokens per block
-//   wgate_partial   dW_g partial sums over token ranges (64 x 64 tiles)
+//   wgate_partial   dW_g partial sums over token ranges (64 x 64 tiles, up to
+//                   64 ranges so that small E still fills the chip)
 //   wgate_reduce    partials summed in range order; db_g over all tokens
 #include <type_traits>
 
@@ -462,7 +463,7 @@ extern "C" int moe_router_weight_backward(const void* x, int dtype, int T, int d
   if (!dw_gate || (T > 0 && (!x || !dlogits))) return MOE_ERR_INVALID;
   if (!ws || ws_bytes < router_bwd_ws(T, d, E)) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
-  const int S = router_bwd_splits(T);
+  const int S = router_bwd_splits(T, d, E);
   float* part = (float*)ws;
   const dim3 g(ceil_div(E, kWgTile), ceil_div(d, kWgTile), S);
   if (dtype == MOE_BF16)

@@ -12,11 +12,10 @@
 // bf16 data path: every product runs on the 256 x 256 DMA-ring MFMA GEMM.
 // The data gradients contract over the weights' leading index: the ring
 // reads the weights in place, K-major, through LDS transpose loads. The
-// weight gradients contract over the rows of an expert: dY, SiLU(Z), dZ and
-// the gathered x rows are transposed into [feature][row] arrays in which
-// every expert's rows form a segment padded with zeros to a multiple of 64,
-// so an expert's K range is whole 64-column steps; one tile per (expert,
-// 256 x 256 output block) runs over its expert's segment.
+// weight gradients contract over the rows of an expert: both operands (dY
+// and H, dZ and the gathered x rows) are read K-major in place the same
+// way, one tile per (expert, 256 x 256 output block) over the expert's row
+// range, its ragged end masked in the last step.
 //
 // fp32 data path: FMA tiles read the operands in place.
 #include "moe_internal.h"
@@ -26,66 +25,44 @@
 namespace moe {
 namespace {
 
-constexpr int kTB = 64;  // transpose tile edge; also the row padding of an expert segment
+// Xp[r] = x[sorted_token[r]] for the kept rows (bf16, d % 8 == 0): the
+// gathered input rows the dW1 product reads K-major. Grid (ceil(R_max / 4)),
+// a wave per row; rows past offsets[E] exit.
+__global__ __launch_bounds__(256) void gather_rows(const uint16_t* __restrict__ x,
+                                                   const int32_t* __restrict__ sorted_token,
+                                                   const int32_t* __restrict__ offsets, int E,
+                                                   int d, uint16_t* __restrict__ xp) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= offsets[E]) return;
+  const uint16_t* src = x + (size_t)sorted_token[r] * d;
+  uint16_t* dst = xp + (size_t)r * d;
+  for (int c = (threadIdx.x & 63) * 8; c < d; c += 64 * 8) *(u32x4*)(dst + c) = *(const u32x4*)(src + c);
+}
 
-// Padded transpose of an expert-ordered row array: for the 64-row segment p
-// of expert e (pt[e] <= p < pt[e+1], pt in 64-row units),
-//   dst[c][64 p + i] = f(src[row][c]),  row = offsets[e] + 64 (p - pt[e]) + i,
-// and 0 where row is past the expert's last. MODE 0: f = identity; 1: f =
-// SiLU (bf16 in, bf16 out); 2: the row is gathered, src[sorted_token[row]].
-template <int MODE>
-__global__ __launch_bounds__(256) void transpose_pad(const uint16_t* __restrict__ src,
-                                                     const int32_t* __restrict__ sorted_token,
-                                                     const int32_t* __restrict__ offsets,
-                                                     const int32_t* __restrict__ pt, int E, int C,
-                                                     size_t ldd, uint16_t* __restrict__ dst) {
-  __shared__ uint32_t tile[kTB][kTB / 2 + 1];
-  const int p = blockIdx.x, c0 = blockIdx.y * kTB;
-  if (p >= pt[E]) return;
-  const int e = find_expert(pt, E, p);
-  const int r0 = offsets[e] + (p - pt[e]) * kTB, rend = offsets[e + 1];
-  const int tid = threadIdx.x, ch = tid & 7;
+// z <- SiLU(z) in place over the kept rows (bf16), when the backward had to
+// recompute Z: the dW2 product then reads these hidden rows.
+__global__ __launch_bounds__(256) void silu_rows(uint16_t* __restrict__ z,
+                                                 const int32_t* __restrict__ offsets, int E,
+                                                 int h) {
+  const long n = (long)offsets[E] * h / 8;
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
+    u32x4 v = *(u32x4*)(z + i * 8);
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int i = pass * 32 + (tid >> 3);
-    const int r = r0 + i;
-    u32x4 v = u32x4{0u, 0u, 0u, 0u};
-    if (r < rend) {
-      const size_t srow = MODE == 2 ? (size_t)sorted_token[r] : (size_t)r;
-      v = *(const u32x4*)(src + srow * C + c0 + ch * 8);
-      if (MODE == 1) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = pack_bf16x2(silu_bf16(bf16lo(v[q])), silu_bf16(bf16hi(v[q])));
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) tile[i][ch * 4 + q] = v[q];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int c = pass * 32 + (tid >> 3);
-    const int sh = (c & 1) * 16;
-    u32x4 o;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t lo = (tile[ch * 8 + 2 * q][c >> 1] >> sh) & 0xFFFFu;
-      const uint32_t hi = (tile[ch * 8 + 2 * q + 1][c >> 1] >> sh) & 0xFFFFu;
-      o[q] = lo | (hi << 16);
-    }
-    *(u32x4*)(dst + (size_t)(c0 + c) * ldd + (size_t)p * kTB + ch * 8) = o;
+    for (int q = 0; q < 4; ++q) v[q] = pack_bf16x2(silu_bf16(bf16lo(v[q])), silu_bf16(bf16hi(v[q])));
+    *(u32x4*)(z + i * 8) = v;
   }
 }
 
 // Work list of a weight-gradient GEMM: one whole tile per (expert, 256-row
 // block of the M output rows, 256 output features), K range = the expert's
-// padded segment (empty for an expert with no rows: the tile stores zeros).
+// rows [offsets[e], offsets[e+1]) (empty for an expert with no rows: the
+// tile stores zeros).
 // Tile order as in big_plan (expert-major, groups of kGroupN feature tiles,
 // row blocks inside a group); when the count allows, hardware block b (on
 // XCD b % 8) takes tile (b % 8) * tiles/8 + b / 8, so each XCD works through
 // one contiguous range.
-__global__ __launch_bounds__(256) void wgrad_plan(const int32_t* __restrict__ pt, int E, int mt,
-                                                  int nt, BigWork* __restrict__ list) {
+__global__ __launch_bounds__(256) void wgrad_plan(const int32_t* __restrict__ offsets, int E,
+                                                  int mt, int nt, BigWork* __restrict__ list) {
   const int b = blockIdx.x * 256 + threadIdx.x;
   const int tiles = E * mt * nt;
   if (b >= tiles) return;
@@ -99,8 +76,8 @@ __global__ __launch_bounds__(256) void wgrad_plan(const int32_t* __restrict__ pt
   w.row0 = (l2 / gs) * kBigBM;
   w.rows = kBigBM;
   w.n0 = (g * kGroupN + l2 % gs) * kBigBN;
-  w.kbeg = pt[e];
-  w.kend = pt[e + 1];
+  w.kbeg = offsets[e];
+  w.kend = offsets[e + 1];
   w.unit = -1;
   w.ms = 0;
   list[b] = w;
@@ -333,22 +310,19 @@ int ffn_backward_bf16(const uint16_t* x, int T, int d, int h, int E, int k,
   const FfnBwdLayout L = ffn_bwd_layout(T, d, h, E, k);
   unsigned char* base = (unsigned char*)ws;
   const long rows = (long)T * k;
-  const size_t rp = (size_t)ffn_bwd_rpad(T, E, k);
   BigHdr* hdr = (BigHdr*)base;
   const int g1 = ffn_big_grid(rows, E, h, kBigBM), g2 = ffn_big_grid(rows, E, d, kBigBM);
   BigWork* list1 = (BigWork*)(base + 256);
   BigWork* list2 = list1 + g1;
-  int32_t* pt = (int32_t*)(base + L.pt);
   const int md = d / kBigBN, mh = h / kBigBN;
-  BigWork* wl2 = (BigWork*)(base + L.wl);  // dW2: M = d, N = h
+  BigWork* wl2 = (BigWork*)(base + L.wl);    // dW2: M = d, N = h
   BigWork* wl1 = wl2 + (size_t)E * md * mh;  // dW1: M = h, N = d
   uint16_t* Zw = (uint16_t*)(base + L.z);
   const uint16_t* Z = zin ? zin : Zw;
   uint16_t* dZ = (uint16_t*)(base + L.dz);
+  uint16_t* xp = (uint16_t*)(base + L.xp);
   uint16_t* const nz = nullptr;
   float* part = (float*)(base + L.part);
-  uint16_t* ta = (uint16_t*)(base + L.ta);
-  uint16_t* tb = (uint16_t*)(base + L.tb);
   const uint16_t* none = nullptr;
   const dim3 gr(kTailSlots * kReduceSlices), rb(kRingWaves * 64);
   const int nwt = E * md * mh;
@@ -356,11 +330,13 @@ int ffn_backward_bf16(const uint16_t* x, int T, int d, int h, int E, int k,
   hipLaunchKernelGGL((big_plan<kBigBM, true>), dim3(ceil_div(g1 + g2, kMaxE)), dim3(kMaxE), 0, s,
                      offsets, E, mh, d / kRS, g1, md, h / kRS, g2, hdr, list1, list2, sorted_token,
                      (int32_t*)nullptr);
-  hipLaunchKernelGGL(build_tile_map, dim3(1), dim3(512), 0, s, offsets, E, kTB, pt);
-  hipLaunchKernelGGL(wgrad_plan, dim3(ceil_div(nwt, 256)), dim3(256), 0, s, (const int32_t*)pt, E,
-                     md, mh, wl2);
-  hipLaunchKernelGGL(wgrad_plan, dim3(ceil_div(nwt, 256)), dim3(256), 0, s, (const int32_t*)pt, E,
-                     mh, md, wl1);
+  hipLaunchKernelGGL(wgrad_plan, dim3(ceil_div(nwt, 256)), dim3(256), 0, s, offsets, E, md, mh,
+                     wl2);
+  hipLaunchKernelGGL(wgrad_plan, dim3(ceil_div(nwt, 256)), dim3(256), 0, s, offsets, E, mh, md,
+                     wl1);
+  if (rows > 0)
+    hipLaunchKernelGGL(gather_rows, dim3(ceil_div(rows, 4)), dim3(256), 0, s, x, sorted_token,
+                       offsets, E, d, xp);
   if (!zin) {
     // Z = W1[e] x + b1 (the forward's first product without the activation)
     hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, true, kEpiBias>), dim3(g1), rb, 0, s, x,
@@ -374,27 +350,19 @@ int ffn_backward_bf16(const uint16_t* x, int T, int d, int h, int E, int k,
                      Z, nz);
   hipLaunchKernelGGL((big_tail_reduce<kBigBM, kEpiDSilu>), gr, dim3(256), 0, s, hdr, list1, none,
                      part, dZ, h, Z, nz);
-  // dW2[e] = dY_e^T SiLU(Z_e)
-  const int nseg = (int)(rp / kTB);
-  hipLaunchKernelGGL((transpose_pad<0>), dim3(nseg, d / kTB), dim3(256), 0, s, dy,
-                     (const int32_t*)nullptr, offsets, (const int32_t*)pt, E, d, rp, ta);
-  if (hin)
-    hipLaunchKernelGGL((transpose_pad<0>), dim3(nseg, h / kTB), dim3(256), 0, s, hin,
-                       (const int32_t*)nullptr, offsets, (const int32_t*)pt, E, h, rp, tb);
-  else
-    hipLaunchKernelGGL((transpose_pad<1>), dim3(nseg, h / kTB), dim3(256), 0, s, Z,
-                       (const int32_t*)nullptr, offsets, (const int32_t*)pt, E, h, rp, tb);
-  hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, false, kEpiBias>), dim3(nwt), rb, 0, s,
-                     (const uint16_t*)ta, (const int32_t*)nullptr, (const BigWork*)wl2,
-                     (const uint16_t*)tb, none, dw2, part, h, (int)rp, (size_t)0, d, none, nz);
-  // dW1[e] = dZ_e^T X_e
-  hipLaunchKernelGGL((transpose_pad<2>), dim3(nseg, d / kTB), dim3(256), 0, s, x, sorted_token,
-                     offsets, (const int32_t*)pt, E, d, rp, ta);
-  hipLaunchKernelGGL((transpose_pad<0>), dim3(nseg, h / kTB), dim3(256), 0, s, (const uint16_t*)dZ,
-                     (const int32_t*)nullptr, offsets, (const int32_t*)pt, E, h, rp, tb);
-  hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, false, kEpiBias>), dim3(nwt), rb, 0, s,
-                     (const uint16_t*)tb, (const int32_t*)nullptr, (const BigWork*)wl1,
-                     (const uint16_t*)ta, none, dw1, part, d, (int)rp, (size_t)0, h, none, nz);
+  // H: the forward's, or SiLU of the recomputed Z (in place, Z is no longer read)
+  const uint16_t* H = hin;
+  if (!hin) {
+    hipLaunchKernelGGL(silu_rows, dim3(2048), dim3(256), 0, s, Zw, offsets, E, h);
+    H = Zw;
+  }
+  // dW2[e] = dY_e^T H_e, dW1[e] = dZ_e^T X_e: both operands K-major
+  hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, false, kEpiBias, true, true>), dim3(nwt), rb, 0, s,
+                     dy, (const int32_t*)nullptr, (const BigWork*)wl2, H, none, dw2, part, h, d,
+                     (size_t)0, d, none, nz);
+  hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, false, kEpiBias, true, true>), dim3(nwt), rb, 0, s,
+                     (const uint16_t*)dZ, (const int32_t*)nullptr, (const BigWork*)wl1,
+                     (const uint16_t*)xp, none, dw1, part, d, h, (size_t)0, h, none, nz);
   // dXp = dZ W1[e]: W1[e] is [h][d], K-major for this product
   hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, false, kEpiBias, true>), dim3(g2), rb, 0, s,
                      (const uint16_t*)dZ, (const int32_t*)nullptr, list2, w1, none, dxp, part, d, h,
@@ -440,10 +408,8 @@ extern "C" int moe_grouped_ffn_backward(const void* x, int dtype, int T, int d, 
   // bf16: 256 x 256 tiles on both widths; 32-bit element offsets of every
   // row operand (the gathered x rows, the permuted rows and the padded
   // transposed arrays)
-  const long rp = ffn_bwd_rpad(T, E, k);
   if ((d % kBigBN) != 0 || (h % kBigBN) != 0) return MOE_ERR_UNSUPPORTED;
-  if ((long)T * d >= (1L << 31) || rows * d >= (1L << 31) || rows * h >= (1L << 31) ||
-      (long)(d > h ? d : h) * rp >= (1L << 31))
+  if ((long)T * d >= (1L << 31) || rows * d >= (1L << 31) || rows * h >= (1L << 31))
     return MOE_ERR_UNSUPPORTED;
   return ffn_backward_bf16((const uint16_t*)x, T, d, h, E, k, offsets, sorted_token,
                            (const uint16_t*)w1, (const uint16_t*)b1, (const uint16_t*)w2,

@@ -140,33 +140,31 @@ inline size_t ffn_ws(int T, int d, int h, int E, int k) {
   return ffn_plan_bytes(T, d, h, E, k) + ffn_hidden_bytes(T, h, k) + ffn_partial_bytes();
 }
 
-// Router weight backward: fp32 partial dW_g over S token ranges [S][E][d].
-inline int router_bwd_splits(int T) {
-  const int s = T / 1024;
-  return s < 1 ? 1 : (s > 8 ? 8 : s);
+// Router weight backward: fp32 partial dW_g over S token ranges [S][E][d],
+// S chosen so that the 64 x 64 tiles times S make about 4096 blocks, with
+// at least 16 tokens per range and at most 64 ranges.
+inline int router_bwd_splits(int T, int d, int E) {
+  const int tiles = ceil_div(E, 64) * ceil_div(d, 64);
+  int s = ceil_div(4096, tiles);
+  if (s > 64) s = 64;
+  if (s > T / 16) s = T / 16;
+  return s < 1 ? 1 : s;
 }
 inline size_t router_bwd_ws(int T, int d, int E) {
-  return align_up((size_t)router_bwd_splits(T) * E * d * sizeof(float), 256);
+  return align_up((size_t)router_bwd_splits(T, d, E) * E * d * sizeof(float), 256);
 }
 
 // FFN backward: [plan of the forward-shaped GEMMs (ffn_plan_bytes)]
-//   [pt: E+1 int32, padded 64-row segment starts] [wgrad work lists: 2 x E x
-//   (d/256)(h/256) entries] [Z: T*k*h x 4 B] [dZ: T*k*h x 4 B]
-//   [tail partials] [TA, TB: max(d,h) x Rp bf16 each]
-// Rp bounds the padded row count: every expert's rows rounded up to 64.
-inline long ffn_bwd_rpad(int T, int E, int k) {
-  return (long)align_up((size_t)T * k + 63 * (size_t)E, 64);
-}
+//   [weight-gradient work lists: 2 x E x (d/256)(h/256) entries]
+//   [Z: T*k*h x 4 B] [dZ: T*k*h x 4 B] [tail partials]
+//   [gathered input rows: T*k*d bf16]
 struct FfnBwdLayout {
-  size_t pt, wl, z, dz, part, ta, tb, total;
+  size_t wl, z, dz, part, xp, total;
 };
 inline FfnBwdLayout ffn_bwd_layout(int T, int d, int h, int E, int k) {
   FfnBwdLayout L;
-  const size_t rows = (size_t)T * k, rp = (size_t)ffn_bwd_rpad(T, E, k);
-  const size_t wide = (size_t)(d > h ? d : h);
+  const size_t rows = (size_t)T * k;
   size_t o = ffn_plan_bytes(T, d, h, E, k);
-  L.pt = o;
-  o += align_up((size_t)(kMaxE + 1) * sizeof(int32_t), 256);
   L.wl = o;
   o += align_up((size_t)2 * E * (d / kBigBNTile) * (h / kBigBNTile) * kWorkBytes, 256);
   L.z = o;
@@ -175,10 +173,8 @@ inline FfnBwdLayout ffn_bwd_layout(int T, int d, int h, int E, int k) {
   o += align_up(rows * h * 4, 256);
   L.part = o;
   o += ffn_partial_bytes();
-  L.ta = o;
-  o += align_up(wide * rp * 2, 256);
-  L.tb = o;
-  o += align_up(wide * rp * 2, 256);
+  L.xp = o;
+  o += align_up(rows * d * 2, 256);
   L.total = o;
   return L;
 }

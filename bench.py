@@ -40,7 +40,7 @@ TRAIN_METRIC = "routed tokens/sec per MoE layer fwd+bwd (bf16, 1 GPU) + % of MFM
 CPU_SAMPLE = {"tiny_fp32": 256, "mixtral_prefill": 2048, "switch_top1_cap": 8192, "decode": 32,
               "deepseek_v3": 512, "switch_expert_choice": 2048, "decode_offload": 32}
 # tokens of the sub-batch the backward CPU baseline differentiates
-BWD_CPU_SAMPLE = {"tiny_fp32": 256, "mixtral_prefill": 256, "switch_top1_cap": 1024,
+BWD_CPU_SAMPLE = {"tiny_fp32": 256, "mixtral_prefill": 1024, "switch_top1_cap": 2048,
                   "deepseek_v3": 64}
 PCIE_GBS = 64.0             # PCIe 5.0 x16, one direction
 OFFLOAD_BATCHES = 16        # distinct token batches the offload workload cycles through
@@ -63,10 +63,12 @@ def parse():
 
 
 def ffn_source_hash() -> str:
-    """Hash of the grouped-FFN kernel source; counter data for another source is stale."""
+    """Hash of the grouped-FFN kernel sources; counter data for another source is stale."""
     import hashlib
-    path = os.path.join(ROOT, "top_routing_expert_topk_amd", "csrc", "ffn.hip")
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in ("ffn.hip", "ring_gemm.h", "tile_map.h", "moe_internal.h"):
+        h.update(open(os.path.join(ROOT, "top_routing_expert_topk_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(path, workload):
@@ -335,7 +337,7 @@ def bench_backward(args, cfg, inp, dev):
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = None
     roof["kernel"] = ("moe_grouped_ffn_backward (dZ, dX_perm, dW1, dW2 on the MFMA ring GEMM, "
-                      "activation transposes, bias sums)")
+                      "gathered input rows, bias sums)")
     roof["per_launch"] = {"flop": flop, "rows": R}
     out = {
         "metric": TRAIN_METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,

@@ -197,3 +197,49 @@ def test_training_forward_keeps_z_and_h(path):
         acc = 1.1 * cfg.d * 2.0 ** -24 * M  # fp32 accumulation over d terms, through SiLU'
         assert np.all(np.abs(z_gpu[r0:r1] - z) <= c * np.abs(z) + acc), f"z, expert {e}"
         assert np.all(np.abs(h_gpu[r0:r1] - hz) <= c * np.abs(hz) + acc), f"h, expert {e}"
+
+
+EDGE = {
+    "one_token": BASE.with_(name="one_token", T=1, d=256, h=256),
+    "one_expert": BASE.with_(name="one_expert", T=64, d=256, h=256, E=1, k=1),
+    "k_equals_E": BASE.with_(name="k_equals_E", T=64, d=256, h=512, E=4, k=4),
+    "top3_of_5_no_renorm": BASE.with_(name="top3_of_5_no_renorm", T=80, d=256, h=256, E=5, k=3,
+                                      renorm=False, residual=True),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+def test_backward_edge_cases(name):
+    cfg = EDGE[name]
+    inp, dout, fwd, g = run_backward(cfg)
+    ref = oracle_backward(cfg, inp, dout, fwd)
+    compare(cfg, g, ref, name)
+
+
+def test_backward_of_an_empty_batch():
+    """T = 0: the backward calls accept the empty batch, every weight and
+    bias gradient comes out zero (the calls still write them), and so does
+    the router's."""
+    from top_routing_expert_topk_amd import MoEGrads
+    from top_routing_expert_topk_amd import native as N
+    E, k, d, h = 8, 2, 256, 256
+    cfg = BASE.with_(name="empty", T=4, d=d, h=h, E=E)
+    inp = mi.make_inputs(cfg, "cuda")
+    x = inp["x"][:0]
+    g = MoEGrads(0, d, h, E, k, torch.bfloat16, torch.device("cuda"), True, True, True)
+    for n in ("dw1", "dw2", "db1", "db2", "dw_gate", "dgate_bias"):
+        getattr(g, n).fill_(7)
+    offsets = torch.zeros(E + 1, dtype=torch.int32, device="cuda")
+    none_i = torch.empty(0, dtype=torch.int32, device="cuda")
+    none_f = torch.empty((0, k), dtype=torch.float32, device="cuda")
+    N.moe_combine_backward(g.dy_perm, none_i, none_f, 0, k, d, x, g.dy_perm, g.dgate)
+    N.moe_router_backward(g.dlogits, none_i, none_f, g.dgate, offsets[:E], 0, E, k, True, 0.5,
+                          g.dlogits)
+    N.moe_grouped_ffn_backward(x, 0, d, h, E, k, offsets, none_i, inp["w1"], inp["b1"], inp["w2"],
+                               g.dy_perm, None, None, g.dx_perm, g.dw1, g.db1, g.dw2, g.db2,
+                               g.ws_ffn)
+    N.moe_gather_backward(g.dx_perm, none_i, 0, k, d, None, g.dlogits, inp["w_gate"], E, g.dx)
+    N.moe_router_weight_backward(x, 0, d, E, g.dlogits, g.dw_gate, g.dgate_bias, g.ws_router)
+    torch.cuda.synchronize()
+    for n in ("dw1", "dw2", "db1", "db2", "dw_gate", "dgate_bias"):
+        assert not bool(getattr(g, n).any()), n

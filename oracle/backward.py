@@ -383,3 +383,77 @@ def moe_backward_sampled(x, w_gate, fetch, k: int, renorm: bool, capacity: int, 
         out["db2"][e] = (dy.sum(axis=0), np.abs(dy).sum(axis=0))
     out.update(offsets=offsets, counts=counts, idx=idx)
     return out
+
+
+def moe_backward_ec(x, w_gate, w1, b1, w2, b2, C: int, dout, gate_bias=None,
+                    residual: bool = False, lg=None, score=None, want_scale: bool = False):
+    """Gradients of L = <dout, out> for an Expert Choice layer (``oracle.moe_forward_ec``).
+
+    The selection (each expert's C tokens) is piecewise constant; the gate of
+    a chosen pair (t, e) is p[t,e], the softmax over experts of token t's
+    logits, so the gate gradients land on p and go through the softmax
+    backward. ``lg`` / ``score``: as in ``moe_forward_ec`` (the selection is
+    made on ``score``, the gradient flows through the softmax of ``lg``).
+    Returns the keys of ``moe_backward`` (dgate is [T, E], 0 where not
+    chosen).
+    """
+    X = widen(x)
+    Wg = widen(w_gate)
+    W1, W2 = widen(w1), widen(w2)
+    B1, B2 = widen(b1), widen(b2)
+    dO = widen(dout)
+    T, d = X.shape
+    E, h = W1.shape[0], W1.shape[1]
+    if lg is None:
+        lg = fwd.logits(x, w_gate, gate_bias)
+    lg = np.asarray(lg, dtype=np.float64)
+    p = softmax(lg)
+    sel = p if score is None else np.asarray(score, dtype=np.float64)
+    offsets, st, dest, gate = fwd.expert_choice(sel, C)
+    gate = np.where(dest >= 0, p, 0.0)  # the gate is the probability itself
+    dx = dO.copy() if residual else np.zeros((T, d))
+    dw1 = np.zeros((E, h, d))
+    dw2 = np.zeros((E, d, h))
+    db1 = np.zeros((E, h))
+    db2 = np.zeros((E, d))
+    dgate = np.zeros((T, E))
+    mag = dict(dx=np.abs(dO) if residual else np.zeros((T, d)), dw1=np.zeros((E, h, d)),
+               dw2=np.zeros((E, d, h)), db1=np.zeros((E, h)), db2=np.zeros((E, d)),
+               dgate=np.zeros((T, E)))
+    for e in range(E):
+        tok = st[offsets[e]:offsets[e + 1]]
+        if tok.size == 0:
+            continue
+        dy = gate[tok, e][:, None] * dO[tok]
+        y, dxe, dw1[e], db1[e], dw2[e], db2[e] = expert_backward(
+            X[tok], W1[e], None if B1 is None else B1[e], W2[e], None if B2 is None else B2[e], dy)
+        dgate[tok, e] = (dO[tok] * y).sum(axis=1)
+        np.add.at(dx, tok, dxe)
+        if want_scale:
+            z = X[tok] @ W1[e].T + (0.0 if B1 is None else B1[e])
+            ady = np.abs(dy)
+            mag["dw2"][e] = ady.T @ (np.abs(silu(z)) + np.abs(silu_grad(z) * z) / 4.0)
+            mag["db2"][e] = ady.sum(axis=0)
+            adz = (ady @ np.abs(W2[e])) * (np.abs(silu_grad(z)) + np.abs(z) / 8.0)
+            mag["dw1"][e] = adz.T @ np.abs(X[tok])
+            mag["db1"][e] = adz.sum(axis=0)
+            np.add.at(mag["dx"], tok, adz @ np.abs(W1[e]))
+            mag["dgate"][tok, e] = (np.abs(dO[tok]) * np.abs(y)).sum(axis=1)
+    dl = softmax_grad(p, dgate)
+    dw_gate = dl.T @ X
+    dgate_bias = None if gate_bias is None else dl.sum(axis=0)
+    dx += dl @ Wg
+    res = dict(dx=dx, dw_gate=dw_gate, dgate_bias=dgate_bias, dw1=dw1, db1=db1, dw2=dw2,
+               db2=db2, dlogits=dl, dgate=dgate, offsets=offsets, sorted_token=st, dest_row=dest,
+               gate=gate, logits=lg)
+    if want_scale:
+        mdl = p * (mag["dgate"] + (p * mag["dgate"]).sum(axis=1, keepdims=True))
+        mag["dx"] += mdl @ np.abs(Wg)
+        mag.update(dlogits=mdl, dw_gate=mdl.T @ np.abs(X),
+                   dgate_bias=None if gate_bias is None else mdl.sum(axis=0))
+        if B1 is None:
+            mag["db1"] = None
+        if B2 is None:
+            mag["db2"] = None
+        res["scale"] = mag
+    return res

@@ -276,3 +276,59 @@ def test_sampled_backward_matches_the_whole_one():
             np.testing.assert_allclose(sm["dw2"][(e, n)][1], sc["dw2"][e][:, n], rtol=1e-12, atol=1e-13)
         for e in (0, 4):
             np.testing.assert_allclose(sm["db2"][e][0], full["db2"][e], rtol=1e-12, atol=1e-13)
+
+
+# ------------------------------------------------------------ Expert Choice --
+
+def _ec_loss(p, dout, C, res):
+    r = orc.moe_forward_ec(p["x"], p["w_gate"], p["w1"], p["b1"], p["w2"], p["b2"], C,
+                           gate_bias=p.get("gate_bias"), residual=res)
+    return float((dout * r["out"]).sum()), r
+
+
+@pytest.mark.parametrize("C,res,gb", [(3, False, False), (5, True, True), (9, True, False)])
+def test_expert_choice_finite_differences(C, res, gb):
+    """Central differences of <dout, out> through the Expert Choice forward
+    oracle, every input element of a tiny layer (selection unchanged by
+    every perturbation)."""
+    p, dout = _layer(91 + C, 9, 5, 6, 3, gb)
+    L0, r0 = _ec_loss(p, dout, C, res)
+    g = bwd.moe_backward_ec(p["x"], p["w_gate"], p["w1"], p["b1"], p["w2"], p["b2"], C, dout,
+                            gate_bias=p.get("gate_bias"), residual=res)
+    for pname, gname in GRAD_OF.items():
+        if pname not in p:
+            assert g[gname] is None
+            continue
+        a = p[pname]
+        num = np.zeros(a.shape)
+        for i in np.ndindex(a.shape):
+            keep = a[i]
+            a[i] = keep + H
+            Lp, rp = _ec_loss(p, dout, C, res)
+            a[i] = keep - H
+            Lm, rm = _ec_loss(p, dout, C, res)
+            a[i] = keep
+            for rr in (rp, rm):
+                assert np.array_equal(rr["dest_row"], r0["dest_row"]), f"{pname}{i} changes the selection"
+            num[i] = (Lp - Lm) / (2 * H)
+        scale = max(1.0, float(np.abs(g[gname]).max()))
+        err = float(np.abs(num - g[gname]).max())
+        assert err <= 2e-5 * scale, f"C={C} {gname}: max |fd - oracle| = {err}"
+
+
+def test_expert_choice_backward_invariants():
+    """Rows of dlogits sum to 0; C = T (every expert takes every token) is
+    the token-choice layer at k = E without renormalisation, so the two
+    backward oracles agree there; magnitudes bound the gradients."""
+    p, dout = _layer(97, 12, 6, 8, 4, True)
+    g = bwd.moe_backward_ec(p["x"], p["w_gate"], p["w1"], p["b1"], p["w2"], p["b2"], 4, dout,
+                            gate_bias=p["gate_bias"], residual=True, want_scale=True)
+    np.testing.assert_allclose(g["dlogits"].sum(axis=1), 0.0, atol=1e-13)
+    for name, M in g["scale"].items():
+        assert np.all(M >= np.abs(g[name]) * (1 - 1e-12) - 1e-15), name
+    ec = bwd.moe_backward_ec(p["x"], p["w_gate"], p["w1"], p["b1"], p["w2"], p["b2"], 12, dout,
+                             gate_bias=p["gate_bias"], residual=True)
+    tc = bwd.moe_backward(p["x"], p["w_gate"], p["w1"], p["b1"], p["w2"], p["b2"], 4, False, -1,
+                          dout, 0.0, gate_bias=p["gate_bias"], residual=True)
+    for name in ("dx", "dw_gate", "dgate_bias", "dw1", "db1", "dw2", "db2", "dlogits"):
+        np.testing.assert_allclose(ec[name], tc[name], rtol=1e-11, atol=1e-12)

@@ -79,6 +79,9 @@ BWD_MUTANTS = {
     "residual_gradient_dropped": ("dx = dO.copy() if residual else", "dx = 0.0 * dO if residual else"),
     "dy_ignores_gate": ("dy = gflat[slots][:, None] * dO[tok]", "dy = dO[tok]"),
     "dx_reversed_columns": ("dx = dz @ w1e", "dx = dz @ w1e[:, ::-1]"),
+    "ec_no_softmax_backward": ("dl = softmax_grad(p, dgate)", "dl = dgate"),
+    "ec_ungated_dy": ("dy = gate[tok, e][:, None] * dO[tok]", "dy = dO[tok]"),
+    "ec_gate_from_score": ("gate = np.where(dest >= 0, p, 0.0)", "gate = np.where(dest >= 0, 1.0, 0.0)"),
 }
 
 

@@ -41,7 +41,7 @@ CPU_SAMPLE = {"tiny_fp32": 256, "mixtral_prefill": 2048, "switch_top1_cap": 8192
               "deepseek_v3": 512, "switch_expert_choice": 2048, "decode_offload": 32}
 # tokens of the sub-batch the backward CPU baseline differentiates
 BWD_CPU_SAMPLE = {"tiny_fp32": 256, "mixtral_prefill": 1024, "switch_top1_cap": 2048,
-                  "deepseek_v3": 64}
+                  "deepseek_v3": 64, "switch_expert_choice": 2048}
 PCIE_GBS = 64.0             # PCIe 5.0 x16, one direction
 OFFLOAD_BATCHES = 16        # distinct token batches the offload workload cycles through
 
@@ -250,9 +250,15 @@ def cpu_baseline_backward(cfg, inp, dout, sample_n):
     x = h["x"][:n]
     g = mi.to_host_array(dout)[:n]
     t0 = time.perf_counter()
-    bwd.moe_backward(x, h["w_gate"], h["w1"], h.get("b1"), h["w2"], h.get("b2"), cfg.k,
-                     cfg.renorm, cfg.capacity, g, 0.01, gate_bias=h.get("gate_bias"),
-                     residual=cfg.residual)
+    if cfg.routing == "expert_choice":
+        # the sub-batch keeps the ratio of capacity to tokens
+        c = max(1, round(cfg.capacity * n / cfg.T))
+        bwd.moe_backward_ec(x, h["w_gate"], h["w1"], h.get("b1"), h["w2"], h.get("b2"), c, g,
+                            gate_bias=h.get("gate_bias"), residual=cfg.residual)
+    else:
+        bwd.moe_backward(x, h["w_gate"], h["w1"], h.get("b1"), h["w2"], h.get("b2"), cfg.k,
+                         cfg.renorm, cfg.capacity, g, 0.01, gate_bias=h.get("gate_bias"),
+                         residual=cfg.residual)
     t = time.perf_counter() - t0
     threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
     return {"value": n / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
@@ -271,11 +277,19 @@ def bench_backward(args, cfg, inp, dev):
     import top_routing_expert_topk_amd as moe
     from top_routing_expert_topk_amd import native as N
     T, d, h, E, k = cfg.T, cfg.d, cfg.h, cfg.E, cfg.k
-    daux = 0.01
+    ec = cfg.routing == "expert_choice"
+    daux = 0.0 if ec else 0.01
     dout = mi.make_dout(cfg, dev)
-    bufs = moe.MoEBuffers(T, d, h, E, k, cfg.torch_dtype, dev, cfg.torch_dtype, train=True)
+    if ec:
+        bufs = moe.ECBuffers(T, d, h, E, cfg.capacity, cfg.torch_dtype, dev, cfg.torch_dtype,
+                             train=True)
+        k = bufs.k_ffn  # FFN rows per token; the combine and router run with E slots
+    else:
+        bufs = moe.MoEBuffers(T, d, h, E, k, cfg.torch_dtype, dev, cfg.torch_dtype, train=True)
     grads = moe.MoEGrads(T, d, h, E, k, cfg.torch_dtype, dev, inp["b1"] is not None,
-                         inp["b2"] is not None, inp["gate_bias"] is not None)
+                         inp["b2"] is not None, inp["gate_bias"] is not None,
+                         slots=E if ec else 0)
+    slots = E if ec else k
     stream = torch.cuda.Stream(dev)  # default priority
     x, wg, gb = inp["x"], inp["w_gate"], inp["gate_bias"]
     w1, b1, w2, b2 = inp["w1"], inp["b1"], inp["w2"], inp["b2"]
@@ -284,16 +298,22 @@ def bench_backward(args, cfg, inp, dev):
         b, g = bufs, grads
         if ev is not None:
             ev[0].record(stream)
-        moe.moe_layer_forward(x, wg, gb, w1, b1, w2, b2, k, cfg.renorm, cfg.capacity,
-                              cfg.residual, bufs=b, stream=stream, train=True)
+        if ec:
+            moe.moe_layer_forward_ec(x, wg, gb, w1, b1, w2, b2, cfg.capacity, cfg.residual,
+                                     bufs=b, stream=stream, train=True)
+        else:
+            moe.moe_layer_forward(x, wg, gb, w1, b1, w2, b2, k, cfg.renorm, cfg.capacity,
+                                  cfg.residual, bufs=b, stream=stream, train=True)
         if ev is not None:
             ev[1].record(stream)
-        N.moe_combine_backward(b.y_perm, b.dest_row, b.topk_gate, T, k, d, dout, g.dy_perm,
-                               g.dgate, stream)
+        gate = b.gate if ec else b.topk_gate
+        N.moe_combine_backward(b.y_perm, b.dest_row, gate, T, slots, d, dout, g.dy_perm, g.dgate,
+                               stream)
         if ev is not None:
             ev[2].record(stream)
-        N.moe_router_backward(b.logits, b.topk_idx, b.topk_gate, g.dgate, b.counts, T, E, k,
-                              cfg.renorm, daux, g.dlogits, stream)
+        N.moe_router_backward(b.logits, None if ec else b.topk_idx, gate, g.dgate,
+                              None if ec else b.counts, T, E, slots, False if ec else cfg.renorm,
+                              daux, g.dlogits, stream)
         if ev is not None:
             ev[3].record(stream)
         N.moe_grouped_ffn_backward(x, T, d, h, E, k, b.offsets, b.sorted_token, w1, b1, w2,
@@ -301,8 +321,8 @@ def bench_backward(args, cfg, inp, dev):
                                    g.db2, g.ws_ffn, stream)
         if ev is not None:
             ev[4].record(stream)
-        N.moe_gather_backward(g.dx_perm, b.dest_row, T, k, d, dout if cfg.residual else None,
-                              g.dlogits, wg, E, g.dx, stream)
+        N.moe_gather_backward(g.dx_perm, b.dest_row, T, slots, d,
+                              dout if cfg.residual else None, g.dlogits, wg, E, g.dx, stream)
         if ev is not None:
             ev[5].record(stream)
         N.moe_router_weight_backward(x, T, d, E, g.dlogits, g.dw_gate, g.dgate_bias,

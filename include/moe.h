@@ -273,6 +273,9 @@ int moe_combine_backward(const void *y_perm, int dtype, const int32_t *dest_row,
  *   dlogits[t] += p (dp - <p, dp>),  p = softmax(logits[t]) recomputed.
  * logits, topk_idx, topk_gate: the forward router's outputs; counts: the
  * permute's pre-drop counts (read only when daux != 0). E <= 512.
+ * Expert Choice (moe_expert_choice's gate [T][E] as topk_gate, k = E,
+ * renorm = 0, daux = 0): topk_idx = NULL means slot j is expert j, and the
+ * gate of a chosen pair is its probability, so the same rule applies.
  */
 int moe_router_backward(const float *logits, const int32_t *topk_idx, const float *topk_gate,
                         const float *dgate, const int32_t *counts, int T, int E, int k,

@@ -187,6 +187,7 @@ def test_backward_calls_reject_bad_arguments():
     assert L.moe_router_backward(BAD, BAD, BAD, BAD, BAD, 4, 600, 2, 1, F(0), BAD, None) == 2
     assert L.moe_router_backward(BAD, BAD, BAD, BAD, None, 4, 8, 2, 1, F(0.5), BAD, None) == 1
     assert L.moe_router_backward(BAD, BAD, BAD, None, BAD, 4, 8, 2, 1, F(0), BAD, None) == 1
+    assert L.moe_router_backward(BAD, None, BAD, BAD, None, 4, 8, 2, 0, F(0), BAD, None) == 1  # no table: k = E
 
     # grouped FFN backward
     def ffn(dtype=1, T=10, d=256, h=512, E=8, k=2, w1=BAD, dy=BAD, z=None, hh=None, ws=BAD,

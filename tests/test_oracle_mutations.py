@@ -72,11 +72,22 @@ BWD_MUTANTS = {
                       "np.broadcast_to(daux * counts.astype(np.float64) / (float(T) * T), (T, E))"),
     "dw2_from_preactivation": ("dw2 = dy.T @ a", "dw2 = dy.T @ z"),
     "db1_before_silu_grad": ("db1 = dz.sum(axis=0)", "db1 = da.sum(axis=0)"),
-    "dx_misses_router": ("dgate_bias = None if gate_bias is None else dl.sum(axis=0)\n    dx += dl @ Wg",
-                         "dgate_bias = None if gate_bias is None else dl.sum(axis=0)\n    dx = dx"),
+    "dx_misses_router": ("# logits = x W_g^T + b_g\n    dw_gate = dl.T @ X\n"
+                         "    dgate_bias = None if gate_bias is None else dl.sum(axis=0)\n    dx += dl @ Wg",
+                         "# logits = x W_g^T + b_g\n    dw_gate = dl.T @ X\n"
+                         "    dgate_bias = None if gate_bias is None else dl.sum(axis=0)\n    dx = dx"),
+    "ec_dx_misses_router": ("dl = softmax_grad(p, dgate)\n    dw_gate = dl.T @ X\n"
+                            "    dgate_bias = None if gate_bias is None else dl.sum(axis=0)\n"
+                            "    dx += dl @ Wg",
+                            "dl = softmax_grad(p, dgate)\n    dw_gate = dl.T @ X\n"
+                            "    dgate_bias = None if gate_bias is None else dl.sum(axis=0)\n"
+                            "    dx = dx"),
     "dgate_from_scaled_dy": ("dgate[slots] = (dO[tok] * y).sum(axis=1)",
                              "dgate[slots] = (dy * y).sum(axis=1)"),
-    "residual_gradient_dropped": ("dx = dO.copy() if residual else", "dx = 0.0 * dO if residual else"),
+    "residual_gradient_dropped": ("dx = dO.copy() if residual else np.zeros((T, d), np.float64)",
+                                  "dx = 0.0 * dO if residual else np.zeros((T, d), np.float64)"),
+    "ec_residual_gradient_dropped": ("dx = dO.copy() if residual else np.zeros((T, d))",
+                                     "dx = 0.0 * dO if residual else np.zeros((T, d))"),
     "dy_ignores_gate": ("dy = gflat[slots][:, None] * dO[tok]", "dy = dO[tok]"),
     "dx_reversed_columns": ("dx = dz @ w1e", "dx = dz @ w1e[:, ::-1]"),
     "ec_no_softmax_backward": ("dl = softmax_grad(p, dgate)", "dl = dgate"),

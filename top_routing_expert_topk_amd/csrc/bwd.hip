@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256) void router_bwd(const float* __restrict__ logi
     float inner = 0.0f;
     for (int j = 0; j < k; ++j) inner = fmaf(gt[j], dgt[j], inner);
     for (int j = 0; j < k; ++j) {
-      const int e = it[j];
+      const int e = idx ? it[j] : j;
       const float v = gt[j] * (dgt[j] - inner);
 #pragma unroll
       for (int i = 0; i < kPer; ++i)
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(256) void router_bwd(const float* __restrict__ logi
   } else {
     // g_j = p[S_j]: dp[S_j] += dg_j, then the softmax backward
     for (int j = 0; j < k; ++j) {
-      const int e = it[j];
+      const int e = idx ? it[j] : j;  // no index table: slot j is expert j (Expert Choice)
       const float v = dgt[j];
 #pragma unroll
       for (int i = 0; i < kPer; ++i)
@@ -411,7 +411,8 @@ extern "C" int moe_router_backward(const float* logits, const int32_t* topk_idx,
   if (T < 0 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID;
   if (E > kMaxE) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
-  if (!logits || !topk_idx || !topk_gate || !dgate || !dlogits) return MOE_ERR_INVALID;
+  if (!logits || !topk_gate || !dgate || !dlogits) return MOE_ERR_INVALID;
+  if (!topk_idx && k != E) return MOE_ERR_INVALID;
   if (daux != 0.0f && !counts) return MOE_ERR_INVALID;
   const float aux_scale = daux * (float)E / ((float)T * (float)T);
   hipLaunchKernelGGL(router_bwd, dim3(ceil_div(T, kRbTokens)), dim3(256), 0, (hipStream_t)stream,

@@ -106,6 +106,7 @@ class ECBuffers:
     dtype: torch.dtype
     device: torch.device
     out_dtype: torch.dtype = torch.float32
+    train: bool = False  # keep the pre-activations and hidden rows for the backward
 
     def __post_init__(self):
         T, d, h, E = self.T, self.d, self.h, self.E
@@ -123,6 +124,10 @@ class ECBuffers:
         self.gate = torch.empty((T, E), dtype=f32, device=dev)
         self.y_perm = torch.empty((T * self.k_ffn, d), dtype=self.dtype, device=dev)
         self.out = torch.empty((T, d), dtype=self.out_dtype, device=dev)
+        self.z_perm = self.h_perm = None
+        if self.train:
+            self.z_perm = torch.empty((T * self.k_ffn, h), dtype=self.dtype, device=dev)
+            self.h_perm = torch.empty((T * self.k_ffn, h), dtype=self.dtype, device=dev)
 
         def ws(op, k):
             n = N.moe_workspace_size(op, T, d, h, E, k)
@@ -134,20 +139,25 @@ class ECBuffers:
 
 def moe_layer_forward_ec(x, w_gate, gate_bias, w1, b1, w2, b2, C, residual=False,
                          bufs: ECBuffers | None = None, stream=None,
-                         out_dtype=torch.float32) -> ECBuffers:
-    """Enqueue an Expert Choice layer; returns the buffers."""
+                         out_dtype=torch.float32, train=False) -> ECBuffers:
+    """Enqueue an Expert Choice layer; returns the buffers (train: keep Z and
+    H for moe_layer_backward_ec)."""
     T, d = x.shape
     E = w_gate.shape[0]
     h = w1.shape[1]
     if bufs is None:
-        bufs = ECBuffers(T, d, h, E, C, x.dtype, x.device, out_dtype)
+        bufs = ECBuffers(T, d, h, E, C, x.dtype, x.device, out_dtype, train)
     b = bufs
     N.moe_router_topk(x, w_gate, gate_bias, E, 1, True, b.logits, b.topk_idx, b.topk_gate, None,
                       b.ws_router, stream)
     N.moe_expert_choice(b.logits, T, E, C, b.scores, b.offsets, b.sorted_token, b.dest_row,
                         b.gate, stream)
-    N.moe_grouped_ffn(x, T, d, h, E, b.k_ffn, b.offsets, b.sorted_token, w1, b1, w2, b2,
-                      b.y_perm, b.ws_ffn, stream)
+    if b.train:
+        N.moe_grouped_ffn_train(x, T, d, h, E, b.k_ffn, b.offsets, b.sorted_token, w1, b1, w2,
+                                b2, b.y_perm, b.z_perm, b.h_perm, b.ws_ffn, stream)
+    else:
+        N.moe_grouped_ffn(x, T, d, h, E, b.k_ffn, b.offsets, b.sorted_token, w1, b1, w2, b2,
+                          b.y_perm, b.ws_ffn, stream)
     N.moe_combine(b.y_perm, b.dest_row, b.gate, T, E, d, x if residual else None, b.out, stream)
     return b
 
@@ -241,12 +251,13 @@ class MoEGrads:
     has_b1: bool = True
     has_b2: bool = True
     has_gate_bias: bool = False
+    slots: int = 0  # gate slots per token (0: k; Expert Choice: E)
 
     def __post_init__(self):
         T, d, h, E, k = self.T, self.d, self.h, self.E, self.k
         dev, dt, f32 = self.device, self.dtype, torch.float32
         self.dy_perm = torch.empty((T * k, d), dtype=dt, device=dev)
-        self.dgate = torch.empty((T, k), dtype=f32, device=dev)
+        self.dgate = torch.empty((T, self.slots or k), dtype=f32, device=dev)
         self.dlogits = torch.empty((T, E), dtype=f32, device=dev)
         self.dx_perm = torch.empty((T * k, d), dtype=dt, device=dev)
         self.dx = torch.empty((T, d), dtype=dt, device=dev)
@@ -294,6 +305,37 @@ def moe_layer_backward(fwd: MoEBuffers, x, w_gate, gate_bias, w1, b1, w2, b2, do
                                g.db2, g.ws_ffn, stream)
     N.moe_gather_backward(g.dx_perm, fwd.dest_row, T, k, d, dout if residual else None, g.dlogits,
                           w_gate, E, g.dx, stream)
+    N.moe_router_weight_backward(x, T, d, E, g.dlogits, g.dw_gate, g.dgate_bias, g.ws_router,
+                                 stream)
+    return g
+
+
+def moe_layer_backward_ec(fwd: ECBuffers, x, w_gate, gate_bias, w1, b1, w2, b2, dout,
+                          residual=False, grads: MoEGrads | None = None,
+                          stream=None) -> MoEGrads:
+    """Enqueue the backward of an Expert Choice layer whose forward ran into
+    ``fwd`` (train=True keeps Z and H). The same five calls as token choice,
+    with one gate slot per expert: the combine and gather run with k = E,
+    the router with no index table (slot j is expert j) and renorm = 0,
+    since a chosen pair's gate is its probability; no aux loss.
+    """
+    T, d = x.shape
+    E = w_gate.shape[0]
+    h = w1.shape[1]
+    k = fwd.k_ffn
+    if grads is None:
+        grads = MoEGrads(T, d, h, E, k, x.dtype, x.device, b1 is not None, b2 is not None,
+                         gate_bias is not None, slots=E)
+    g = grads
+    N.moe_combine_backward(fwd.y_perm, fwd.dest_row, fwd.gate, T, E, d, dout, g.dy_perm, g.dgate,
+                           stream)
+    N.moe_router_backward(fwd.logits, None, fwd.gate, g.dgate, None, T, E, E, False, 0.0,
+                          g.dlogits, stream)
+    N.moe_grouped_ffn_backward(x, T, d, h, E, k, fwd.offsets, fwd.sorted_token, w1, b1, w2,
+                               g.dy_perm, fwd.z_perm, fwd.h_perm, g.dx_perm, g.dw1, g.db1, g.dw2,
+                               g.db2, g.ws_ffn, stream)
+    N.moe_gather_backward(g.dx_perm, fwd.dest_row, T, E, d, dout if residual else None,
+                          g.dlogits, w_gate, E, g.dx, stream)
     N.moe_router_weight_backward(x, T, d, E, g.dlogits, g.dw_gate, g.dgate_bias, g.ws_router,
                                  stream)
     return g

@@ -28,6 +28,8 @@ CASES = {
                                 zipf_gate_bias=False), 205),
     "ec_fp32": (EC.with_(name="ec_fp32", T=77, d=96, h=200, E=5, dtype="f32",
                          zipf_gate_bias=False, residual=False), 20),
+    # the Switch-shaped workload as benched (T=8192, d=768, h=3072, E=128, C=80)
+    "ec_switch_full": (EC, EC.capacity),
 }
 
 

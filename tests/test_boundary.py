@@ -164,7 +164,7 @@ def test_backward_workspace_sizes():
         rows = T * k
         need = (N.moe_workspace_size(N.MOE_OP_FFN, T, d, h, E, k) - rows * h * 4
                 - 256 * 256 * 256 * 4)  # the plan part of the forward workspace
-        need += (2 * E * (d // 256) * (h // 256) * 32 + 2 * rows * h * 4 + 256 * 256 * 256 * 4
+        need += (4 * E * (d // 256) * (h // 256) * 32 + 2 * rows * h * 4 + 256 * 256 * 256 * 4
                  + rows * d * 2)
         assert N.moe_workspace_size(N.MOE_OP_FFN_BWD, T, d, h, E, k) >= need
         tiles = _ceil(E, 64) * _ceil(d, 64)

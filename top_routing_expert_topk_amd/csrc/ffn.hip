@@ -206,26 +206,6 @@ struct PRing {
   static constexpr int NBQ = BM / 128;          // permuted-row blocks per step
 };
 
-typedef const __attribute__((address_space(4))) uint32_t cu32;  // scalar-cache reads
-
-// A work-list entry read through the scalar cache (its index is uniform).
-struct WorkS {
-  int e, row0, rows, n0, kbeg, kend, unit, ms;
-};
-__device__ __forceinline__ WorkS load_work(const BigWork* __restrict__ units, int idx) {
-  cu32* p = (cu32*)(units + idx);
-  WorkS u;
-  u.e = __builtin_amdgcn_readfirstlane((int)p[0]);
-  u.row0 = __builtin_amdgcn_readfirstlane((int)p[1]);
-  u.rows = __builtin_amdgcn_readfirstlane((int)p[2]);
-  u.n0 = __builtin_amdgcn_readfirstlane((int)p[3]);
-  u.kbeg = __builtin_amdgcn_readfirstlane((int)p[4]);
-  u.kend = __builtin_amdgcn_readfirstlane((int)p[5]);
-  u.unit = __builtin_amdgcn_readfirstlane((int)p[6]);
-  u.ms = __builtin_amdgcn_readfirstlane((int)p[7]);
-  return u;
-}
-
 template <int BM, bool GATHER, bool SILU>
 __global__ __launch_bounds__(512) void gemm_bf16_pring(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ tok_tab,

@@ -9,13 +9,13 @@
 // Z and SiLU(Z) come from a forward that kept them (moe_grouped_ffn_train);
 // without them Z is recomputed from x here.
 //
-// bf16 data path: every product runs on the 256 x 256 DMA-ring MFMA GEMM.
-// The data gradients contract over the weights' leading index: the ring
-// reads the weights in place, K-major, through LDS transpose loads. The
-// weight gradients contract over the rows of an expert: both operands (dY
-// and H, dZ and the gathered x rows) are read K-major in place the same
-// way, one tile per (expert, 256 x 256 output block) over the expert's row
-// range, its ragged end masked in the last step.
+// bf16 data path: the data gradients run on the 256 x 256 DMA-ring MFMA
+// GEMM of the forward; they contract over the weights' leading index, so
+// the ring reads the weights in place, K-major, through LDS transpose
+// loads. The weight gradients contract over the rows of an expert: both
+// operands (dY and H, dZ and the gathered x rows) are read K-major in place
+// the same way by gemm_bf16_wgrad, one 256 x 128 tile per (expert, output
+// block) over the expert's row range, two blocks per CU.
 //
 // fp32 data path: FMA tiles read the operands in place.
 #include "moe_internal.h"
@@ -53,7 +53,12 @@ __global__ __launch_bounds__(256) void silu_rows(uint16_t* __restrict__ z,
   }
 }
 
-// Work list of a weight-gradient GEMM: one whole tile per (expert, 256-row
+constexpr int kWgBM = 128;             // m rows of a weight-gradient tile
+constexpr int kWgRows = 32;            // K rows per step
+constexpr int kWgBlk = kWgRows * 128;  // bf16 elements per block (8 KB)
+constexpr int kWgSlots = 10;
+
+// Work list of a weight-gradient GEMM: one whole tile per (expert, 128-row
 // block of the M output rows, 256 output features), K range = the expert's
 // rows [offsets[e], offsets[e+1]) (empty for an expert with no rows: the
 // tile stores zeros).
@@ -73,14 +78,163 @@ __global__ __launch_bounds__(256) void wgrad_plan(const int32_t* __restrict__ of
   const int l2 = l - g * mt * kGroupN;
   BigWork w;
   w.e = e;
-  w.row0 = (l2 / gs) * kBigBM;
-  w.rows = kBigBM;
+  w.row0 = (l2 / gs) * kWgBM;
+  w.rows = kWgBM;
   w.n0 = (g * kGroupN + l2 % gs) * kBigBN;
   w.kbeg = offsets[e];
   w.kend = offsets[e + 1];
   w.unit = -1;
   w.ms = 0;
   list[b] = w;
+}
+
+// Weight-gradient GEMM: out[e * ores + m0 + m][n0 + n] = sum over the rows r
+// of expert e ([kbeg, kend) of a wgrad_plan entry) of act[r][m0 + m] *
+// w[r][n0 + n], both operands K-major (rows of K and N elements). An expert
+// holds a few hundred rows or fewer, so a tile is a handful of K steps, and
+// a block alone on its CU would spend much of its time filling its pipeline
+// and draining its output tile with the MFMAs idle. Tiles are therefore
+// 256 n x 128 m on four waves (each 128 n x 64 m, 4 x 2 MFMA tiles) with
+// 80 KB of LDS, so two blocks share a CU and one's fill and stores overlap
+// the other's MFMAs (vmcnt is per wave, so neither waits on the other's
+// stores).
+// Data path: 32-row K steps of three 8 KB blocks (w features 0-127 and
+// 128-255, act features 0-127; 32 k-rows x 128 features, 256-byte rows,
+// chunk c of row k at c ^ 4 (k % 4)) in a ring of ten slots: block b of the
+// tile's sequence (step b / 3, part b % 3) in slot b % 10, so 3.3 steps are
+// resident and at the end of step j the blocks of step j+1 have landed while
+// up to four later ones are in flight. Fragments come from LDS transpose
+// loads (tr_frag). In the ragged last step the w rows past kend re-read row
+// kend - 1 and the act rows past it are fetched from a row of zeros, so those
+// k add nothing and the loop needs no mask; an expert without rows stores a
+// zero tile. The tile leaves through LDS as whole 512-byte rows.
+__device__ __align__(256) uint16_t g_zero_k[128];  // never written: zeros
+
+__global__ __launch_bounds__(256, 2) void gemm_bf16_wgrad(const uint16_t* __restrict__ act,
+                                                          const uint16_t* __restrict__ w,
+                                                          const BigWork* __restrict__ work,
+                                                          uint16_t* __restrict__ out, int N, int K,
+                                                          int ores) {
+  constexpr int NW = 4, P = 3, S = kWgSlots, AHEAD = S - 2 * P, IPB = 8 / NW;
+  constexpr int TN = 4, TM = 2, WTM = 32 * TM;
+  constexpr int OSTR = kBigBN + 8;  // staging row stride (bf16), padded for the banks
+  __shared__ __align__(1024) uint16_t ring[S * kWgBlk];
+  static_assert((size_t)kWgBM * OSTR * 2 <= sizeof(ring), "output tile must fit the ring");
+  const BigWork wk = work[blockIdx.x];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave % 2, wm = wave / 2;  // wave w runs on SIMD w
+  const int ch = lane >> 5;
+  // DMA: instruction (i, wave) moves k-rows 4 (i NW + wave) .. +3; this lane
+  // row lane / 16 of them, chunk slot lane % 16, which holds feature chunk
+  // (lane % 16) ^ 4 ((lane / 16) % 4)
+  const int tchunk = (((lane & 15) ^ (4 * (lane >> 4))) << 3);
+  const int ns = (wk.kend - wk.kbeg + kWgRows - 1) / kWgRows;
+  const int nblk = ns * P;
+  auto issue = [&](int bi) __attribute__((always_inline)) {
+    const int g = bi / P, q = bi - g * P;
+    uint16_t* dst = ring + (bi % S) * kWgBlk;
+#pragma unroll
+    for (int i = 0; i < IPB; ++i) {
+      const int r = wk.kbeg + g * kWgRows + (i * NW + wave) * 4 + (lane >> 4);
+      const uint16_t* src = q < 2 ? w + (size_t)min(r, wk.kend - 1) * N + wk.n0 + q * 128 + tchunk
+                          : r < wk.kend ? act + (size_t)r * K + wk.row0 + tchunk
+                                        : g_zero_k + tchunk;
+      dma16(src, dst + (i * NW + wave) * 4 * 128);
+    }
+  };
+
+  f32x16 acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) acc[i][j] = f32x16{};
+
+  if (ns > 0) {
+    for (int bi = 0; bi < S && bi < nblk; ++bi) issue(bi);
+    bf16x8 f0a[TN], f0b[TM], f1a[TN], f1b[TM];
+    int sa, sb;
+#define MOE_SLOTS(step)                                    \
+  do {                                                     \
+    const int b_ = (P * (step)) % S;                       \
+    const int a_ = b_ + wn, c_ = b_ + 2;                   \
+    sa = a_ < S ? a_ : a_ - S;                             \
+    sb = c_ < S ? c_ : c_ - S;                             \
+  } while (0)
+#define MOE_RD(sub, FA, FB)                                                              \
+  do {                                                                                   \
+    const uint16_t* sa_ = ring + sa * kWgBlk;                                            \
+    const uint16_t* sb_ = ring + sb * kWgBlk;                                            \
+    _Pragma("unroll") for (int i = 0; i < TN; ++i) FA[i] = tr_frag(sa_, (sub), i, lane); \
+    _Pragma("unroll") for (int j = 0; j < TM; ++j)                                       \
+      FB[j] = tr_frag(sb_, (sub), wm * TM + j, lane);                                    \
+  } while (0)
+#define MOE_MM(FA, FB)                                                                   \
+  do {                                                                                   \
+    _Pragma("unroll") for (int i = 0; i < TN; ++i)                                       \
+    _Pragma("unroll") for (int j = 0; j < TM; ++j)                                       \
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[i], FB[j], acc[i][j], 0, 0, 0); \
+  } while (0)
+    // step 0 landed: up to S - P later blocks may be in flight
+    static_assert((S - P) * IPB == 14 && S < 4 * P, "prologue wait counts");
+    if (nblk >= S) wait_vmcnt<(S - P) * IPB>();
+    else if (nblk == 3 * P) wait_vmcnt<2 * P * IPB>();
+    else if (nblk == 2 * P) wait_vmcnt<P * IPB>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    MOE_SLOTS(0);
+    MOE_RD(0, f0a, f0b);
+    for (int j = 0; j < ns; ++j) {
+      MOE_RD(1, f1a, f1b);
+      MOE_MM(f0a, f0b);
+      interleave_mfma_reads<TN * TM, TN * TM>();
+      if (j + 1 < ns) {
+        // step j+1 landed (only later blocks may be in flight), and this
+        // wave's reads of step j are done before its slots are refilled
+        const int issued = min(S + P * j, nblk), need = P * (j + 2) - 1;
+        wait_vmcnt_le<0>(min(issued - 1 - need, AHEAD) * IPB);
+        wait_lgkmcnt0();
+        lds_barrier();
+#pragma unroll
+        for (int u = 0; u < P; ++u)
+          if (S + P * j + u < nblk) issue(S + P * j + u);
+        MOE_SLOTS(j + 1);
+        MOE_RD(0, f0a, f0b);
+      }
+      MOE_MM(f1a, f1b);
+      interleave_mfma_reads<TN * TM, TN * TM>();
+    }
+#undef MOE_SLOTS
+#undef MOE_RD
+#undef MOE_MM
+  }
+
+  // epilogue: bf16 into the idle ring, then whole rows out
+  wait_lgkmcnt0();
+  lds_barrier();
+  uint16_t* ot = ring;
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int nl = wn * 128 + i * 32 + 8 * q + 4 * ch;
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        const int m = wm * WTM + j * 32 + (lane & 31);
+        u32x2 o;
+        o[0] = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+        o[1] = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        *(u32x2*)(ot + m * OSTR + nl) = o;
+      }
+    }
+  __syncthreads();
+  constexpr int CPR = kBigBN / 8;  // 16-byte chunks per row
+#pragma unroll 4
+  for (int c = tid; c < kWgBM * CPR; c += NW * 64) {
+    const int m = c / CPR, cc = c % CPR;
+    *(u32x4*)(out + ((size_t)wk.e * ores + wk.row0 + m) * N + wk.n0 + cc * 8) =
+        *(const u32x4*)(ot + m * OSTR + cc * 8);
+  }
 }
 
 // db[e][c] = sum of g[row][c] over expert e's rows: bf16 rows, grid
@@ -315,8 +469,9 @@ int ffn_backward_bf16(const uint16_t* x, int T, int d, int h, int E, int k,
   BigWork* list1 = (BigWork*)(base + 256);
   BigWork* list2 = list1 + g1;
   const int md = d / kBigBN, mh = h / kBigBN;
-  BigWork* wl2 = (BigWork*)(base + L.wl);    // dW2: M = d, N = h
-  BigWork* wl1 = wl2 + (size_t)E * md * mh;  // dW1: M = h, N = d
+  const int nw2 = E * (d / kWgBM) * mh, nw1 = E * (h / kWgBM) * md;
+  BigWork* wl2 = (BigWork*)(base + L.wl);  // dW2: M = d, N = h
+  BigWork* wl1 = wl2 + nw2;                // dW1: M = h, N = d
   uint16_t* Zw = (uint16_t*)(base + L.z);
   const uint16_t* Z = zin ? zin : Zw;
   uint16_t* dZ = (uint16_t*)(base + L.dz);
@@ -325,14 +480,13 @@ int ffn_backward_bf16(const uint16_t* x, int T, int d, int h, int E, int k,
   float* part = (float*)(base + L.part);
   const uint16_t* none = nullptr;
   const dim3 gr(kTailSlots * kReduceSlices), rb(kRingWaves * 64);
-  const int nwt = E * md * mh;
 
   hipLaunchKernelGGL((big_plan<kBigBM, true>), dim3(ceil_div(g1 + g2, kMaxE)), dim3(kMaxE), 0, s,
                      offsets, E, mh, d / kRS, g1, md, h / kRS, g2, hdr, list1, list2, sorted_token,
                      (int32_t*)nullptr);
-  hipLaunchKernelGGL(wgrad_plan, dim3(ceil_div(nwt, 256)), dim3(256), 0, s, offsets, E, md, mh,
+  hipLaunchKernelGGL(wgrad_plan, dim3(ceil_div(nw2, 256)), dim3(256), 0, s, offsets, E, d / kWgBM, mh,
                      wl2);
-  hipLaunchKernelGGL(wgrad_plan, dim3(ceil_div(nwt, 256)), dim3(256), 0, s, offsets, E, mh, md,
+  hipLaunchKernelGGL(wgrad_plan, dim3(ceil_div(nw1, 256)), dim3(256), 0, s, offsets, E, h / kWgBM, md,
                      wl1);
   if (rows > 0)
     hipLaunchKernelGGL(gather_rows, dim3(ceil_div(rows, 4)), dim3(256), 0, s, x, sorted_token,
@@ -357,12 +511,10 @@ int ffn_backward_bf16(const uint16_t* x, int T, int d, int h, int E, int k,
     H = Zw;
   }
   // dW2[e] = dY_e^T H_e, dW1[e] = dZ_e^T X_e: both operands K-major
-  hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, false, kEpiBias, true, true>), dim3(nwt), rb, 0, s,
-                     dy, (const int32_t*)nullptr, (const BigWork*)wl2, H, none, dw2, part, h, d,
-                     (size_t)0, d, none, nz);
-  hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, false, kEpiBias, true, true>), dim3(nwt), rb, 0, s,
-                     (const uint16_t*)dZ, (const int32_t*)nullptr, (const BigWork*)wl1,
-                     (const uint16_t*)xp, none, dw1, part, d, h, (size_t)0, h, none, nz);
+  hipLaunchKernelGGL(gemm_bf16_wgrad, dim3(nw2), dim3(256), 0, s, dy, H, (const BigWork*)wl2, dw2,
+                     h, d, d);
+  hipLaunchKernelGGL(gemm_bf16_wgrad, dim3(nw1), dim3(256), 0, s, (const uint16_t*)dZ,
+                     (const uint16_t*)xp, (const BigWork*)wl1, dw1, d, h, h);
   // dXp = dZ W1[e]: W1[e] is [h][d], K-major for this product
   hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, false, kEpiBias, true>), dim3(g2), rb, 0, s,
                      (const uint16_t*)dZ, (const int32_t*)nullptr, list2, w1, none, dxp, part, d, h,

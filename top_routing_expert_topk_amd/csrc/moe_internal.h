@@ -155,7 +155,7 @@ inline size_t router_bwd_ws(int T, int d, int E) {
 }
 
 // FFN backward: [plan of the forward-shaped GEMMs (ffn_plan_bytes)]
-//   [weight-gradient work lists: 2 x E x (d/256)(h/256) entries]
+//   [weight-gradient work lists: 2 x E x (d/128)(h/256) entries]
 //   [Z: T*k*h x 4 B] [dZ: T*k*h x 4 B] [tail partials]
 //   [gathered input rows: T*k*d bf16]
 struct FfnBwdLayout {
@@ -166,7 +166,7 @@ inline FfnBwdLayout ffn_bwd_layout(int T, int d, int h, int E, int k) {
   const size_t rows = (size_t)T * k;
   size_t o = ffn_plan_bytes(T, d, h, E, k);
   L.wl = o;
-  o += align_up((size_t)2 * E * (d / kBigBNTile) * (h / kBigBNTile) * kWorkBytes, 256);
+  o += align_up((size_t)4 * E * (d / kBigBNTile) * (h / kBigBNTile) * kWorkBytes, 256);
   L.z = o;
   o += align_up(rows * h * 4, 256);
   L.dz = o;

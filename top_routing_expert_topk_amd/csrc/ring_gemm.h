@@ -127,18 +127,6 @@ __device__ __forceinline__ bf16x8 tr_frag(const uint16_t* __restrict__ blk, int 
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// The fragment with its k elements from lim on set to zero (k = 0..7 in
-// lane order; lim <= 0 zeroes all, lim >= 8 keeps all).
-__device__ __forceinline__ bf16x8 keep_k_below(bf16x8 f, int lim) {
-  u32x4 v = __builtin_bit_cast(u32x4, f);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t lo = 2 * q < lim ? 0x0000FFFFu : 0u, hi = 2 * q + 1 < lim ? 0xFFFF0000u : 0u;
-    v[q] &= lo | hi;
-  }
-  return __builtin_bit_cast(bf16x8, v);
-}
-
 // One entry of a launch's work list: the block's tile and K range. The
 // lists are built on the device by big_plan, so a GEMM block starts with one
 // uniform load instead of searching the tile map.
@@ -151,6 +139,26 @@ struct alignas(16) BigWork {
   int ms;          // row block (index into the token table of the tile's rows)
 };
 static_assert(sizeof(BigWork) == kWorkBytes, "work entry size");
+typedef const __attribute__((address_space(4))) uint32_t cu32;  // scalar-cache reads
+
+// A work-list entry read through the scalar cache (its index is uniform).
+struct WorkS {
+  int e, row0, rows, n0, kbeg, kend, unit, ms;
+};
+__device__ __forceinline__ WorkS load_work(const BigWork* __restrict__ units, int idx) {
+  cu32* p = (cu32*)(units + idx);
+  WorkS u;
+  u.e = __builtin_amdgcn_readfirstlane((int)p[0]);
+  u.row0 = __builtin_amdgcn_readfirstlane((int)p[1]);
+  u.rows = __builtin_amdgcn_readfirstlane((int)p[2]);
+  u.n0 = __builtin_amdgcn_readfirstlane((int)p[3]);
+  u.kbeg = __builtin_amdgcn_readfirstlane((int)p[4]);
+  u.kend = __builtin_amdgcn_readfirstlane((int)p[5]);
+  u.unit = __builtin_amdgcn_readfirstlane((int)p[6]);
+  u.ms = __builtin_amdgcn_readfirstlane((int)p[7]);
+  return u;
+}
+
 // Per launch: tiles = whole tiles + tail tiles; the `full` first tiles (a
 // whole number of rounds over the kTailSlots resident blocks) run whole, the
 // `tail` remaining ones are each cut into `split` K ranges so that the last
@@ -401,15 +409,7 @@ __device__ __forceinline__ void big_store(f32x16 (&acc)[4][TM], uint16_t* ot, si
 // wave read 64 bytes of each of four rows, which the swizzle spreads over
 // all 256 bytes of the LDS banks (the plain layout would put the four rows
 // on the same banks).
-//
-// AT (with WT): both operands K-major, for products that contract over the
-// rows of an expert (weight gradients): out[e*ores + m][n] = sum over rows
-// r in [kbeg, kend) of act[r][m] w[r][n], act rows of K elements (the
-// output's M extent), w rows of N. The work item's K range is in rows, not
-// steps; a step's rows past kend read row kend - 1 (valid data of the same
-// expert) and the activation fragments of the last step zero the k beyond
-// kend, so ragged row ranges need no padding.
-template <int NW, bool GATHER, int EPI, bool WT = false, bool AT = false>
+template <int NW, bool GATHER, int EPI, bool WT = false>
 __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ sorted_token,
     const BigWork* __restrict__ work, const uint16_t* __restrict__ w,
@@ -453,7 +453,6 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
   const int c0 = swz128(r0, lane & 7) * 8;
   // WT: this lane moves k-row (lane / 16) of each 4-row DMA group, chunk
   // slot lane % 16, which holds feature chunk (lane % 16) ^ 4 ((lane / 16) % 4)
-  static_assert(!AT || WT, "K-major activations come with K-major weights");
   const int tchunk = (((lane & 15) ^ (4 * (lane >> 4))) << 3);
   const uint16_t* wbase =
       WT ? w + (size_t)e * wes + (size_t)(lane >> 4) * N + n0 + tchunk
@@ -470,17 +469,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
     }
   auto issue = [&](auto qc, int step, int slot) {
     constexpr int q = decltype(qc)::value;
-    const int koff = AT ? kbeg + step * kRS : (kbeg + step) * kRS;
+    const int koff = (kbeg + step) * kRS;
     uint16_t* dst = ring + slot * kRBlk;
 #pragma unroll
     for (int i = 0; i < IPB; ++i) {
-      if (!AT && q >= 2 && !b_live(q, i)) continue;
+      if (q >= 2 && !b_live(q, i)) continue;
       const uint16_t* g;
-      if constexpr (AT) {
-        const int r = min(koff + (i * NW + wave) * 4 + (lane >> 4), wk.kend - 1);
-        g = q < 2 ? w + (size_t)r * N + n0 + q * 128 + tchunk
-                  : act + (size_t)r * K + row0 + (q - 2) * 128 + tchunk;
-      } else if constexpr (WT)
+      if constexpr (WT)
         g = q < 2 ? wbase + (size_t)(koff + (i * NW + wave) * 4) * N + q * 128
                   : act + boff[q & 1][i] + koff;
       else
@@ -500,9 +495,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
 #pragma unroll
     for (int j = 0; j < TM; ++j) acc[i][j] = f32x16{};
 
-  const int ns = AT ? (wk.kend - kbeg + kRS - 1) / kRS : wk.kend - kbeg;
-  // rows of the last step (AT)
-  const int nlast = AT ? wk.kend - kbeg - (ns - 1) * kRS : kRS;
+  const int ns = wk.kend - kbeg;
   // blocks 0..9: steps 0 and 1, and the weight half of step 2
 #pragma unroll
   for (int st = 0; st < 2; ++st)
@@ -521,7 +514,6 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
   // LDS fragment reads paired with MFMAs by the scheduling hint (the
   // transpose path issues two reads per weight fragment)
   constexpr int kNR = WT ? TN * TM : TN + TM;
-  (void)nlast;
   const int bq = (wm * WTM) >> 7;      // the permuted-row block this wave reads
   const int br = (wm * WTM) & 127;     // its first row inside that block
   bf16x8 f0a[TN], f0b[TM], f1a[TN], f1b[TM];
@@ -546,19 +538,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
       }                                                                                \
     }                                                                                  \
     _Pragma("unroll") for (int j = 0; j < TM; ++j) {                                   \
-      if constexpr (AT) {                                                              \
-        FB[j] = tr_frag(sb_, (sub), (br >> 5) + j, lane);                              \
-      } else {                                                                         \
-        const int r = br + j * 32 + (lane & 31);                                       \
-        FB[j] = *(const bf16x8*)(sb_ + r * kRS + swz128(r, 2 * (sub) + ch) * 8);       \
-      }                                                                                \
-    }                                                                                  \
-  }
-#define MOE_MASK(sub, FB)                                                              \
-  if constexpr (AT && ACT) {                                                           \
-    if (j == ns - 1) {                                                                 \
-      const int lim_ = nlast - ((sub) * 16 + 8 * (lane >> 5));                         \
-      _Pragma("unroll") for (int jj = 0; jj < TM; ++jj) FB[jj] = keep_k_below(FB[jj], lim_); \
+      const int r = br + j * 32 + (lane & 31);                                         \
+      FB[j] = *(const bf16x8*)(sb_ + r * kRS + swz128(r, 2 * (sub) + ch) * 8);         \
     }                                                                                  \
   }
 #define MOE_MM(FA, FB)                                                                 \
@@ -582,15 +563,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
   MOE_RD(0, f0a, f0b);
   for (int j = 0; j < ns; ++j) {
     MOE_RD(1, f1a, f1b);
-    MOE_MASK(0, f0b);
     MOE_MM(f0a, f0b);
     if constexpr (ACT) interleave_mfma_reads<TN * TM, kNR>();
     MOE_RD(2, f0a, f0b);
-    MOE_MASK(1, f1b);
     MOE_MM(f1a, f1b);
     if constexpr (ACT) interleave_mfma_reads<TN * TM, kNR>();
     MOE_RD(3, f1a, f1b);
-    MOE_MASK(2, f0b);
     MOE_MM(f0a, f0b);
     if constexpr (ACT) interleave_mfma_reads<TN * TM, kNR>();
     if (j + 1 < ns) {
@@ -616,7 +594,6 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
     // slots into registers nobody uses)
     MOE_SLOTS(j + 1);
     MOE_RD(0, f0a, f0b);
-    MOE_MASK(3, f1b);
     MOE_MM(f1a, f1b);
     if constexpr (ACT) interleave_mfma_reads<TN * TM, kNR>();
   }
@@ -626,7 +603,6 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
 #undef MOE_SLOTS
 #undef MOE_RD
 #undef MOE_MM
-#undef MOE_MASK
 
   big_store<NW, TM, EPI>(acc, ring, sizeof(ring), wk, bias, out, part, N, ores, zin, zout, wn, wm,
                          lane, tid);

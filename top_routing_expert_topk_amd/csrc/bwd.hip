@@ -24,6 +24,7 @@
 #include <type_traits>
 
 #include "moe_internal.h"
+#include "ring_gemm.h"
 
 namespace moe {
 namespace {
@@ -96,7 +97,12 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
 }
 
 // ------------------------------------------------------------- combine ---
-// One block per token. vec: d % 8 == 0 (8 elements per thread per pass).
+// One block per token. The block first lists the token's kept slots in
+// slot order (a ballot per wave, 256 slots at a time) and writes dgate = 0
+// for the dropped ones, so a layer with many slots per token (Expert Choice:
+// one per expert, most of them empty) pays one coalesced read of its dest
+// row instead of a dependent read per slot. vec: d % 8 == 0 (8 elements per
+// thread per pass).
 template <typename T>
 __global__ __launch_bounds__(256) void combine_bwd(const T* __restrict__ y,
                                                    const int32_t* __restrict__ dest,
@@ -104,39 +110,60 @@ __global__ __launch_bounds__(256) void combine_bwd(const T* __restrict__ y,
                                                    const T* __restrict__ dout, T* __restrict__ dy,
                                                    float* __restrict__ dgate, bool vec) {
   __shared__ float red[4];
-  const int t = blockIdx.x;
+  __shared__ int kept[kMaxE];  // slot indices, then their rows
+  __shared__ int krow[kMaxE];
+  __shared__ int wcnt[4];
+  __shared__ int nkept;
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const T* go = dout + (size_t)t * d;
-  for (int j = 0; j < k; ++j) {
-    const int r = dest[(size_t)t * k + j];
-    if (r < 0) {  // dropped: no output, no gradient
-      if (threadIdx.x == 0) dgate[(size_t)t * k + j] = 0.0f;
-      continue;
+  int base = 0;
+  for (int j0 = 0; j0 < k; j0 += 256) {
+    const int j = j0 + tid;
+    const int r = j < k ? dest[(size_t)t * k + j] : -1;
+    if (j < k && r < 0) dgate[(size_t)t * k + j] = 0.0f;  // dropped: no output, no gradient
+    const uint64_t m = __ballot(r >= 0);
+    if (lane == 0) wcnt[wave] = __popcll(m);
+    __syncthreads();
+    int off = base;
+    for (int w2 = 0; w2 < wave; ++w2) off += wcnt[w2];
+    if (r >= 0) {
+      const int pos = off + __popcll(m & ((1ull << lane) - 1));
+      kept[pos] = j;
+      krow[pos] = r;
     }
+    base += wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+    __syncthreads();
+  }
+  if (tid == 0) nkept = base;
+  __syncthreads();
+  const int nk = nkept;
+  for (int q = 0; q < nk; ++q) {
+    const int j = kept[q], r = krow[q];
     const float g = gate[(size_t)t * k + j];
     const T* yr = y + (size_t)r * d;
     T* dr = dy + (size_t)r * d;
     float dot = 0.0f;
     if (vec) {
-      for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
+      for (int c = tid * 8; c < d; c += 256 * 8) {
         float a[8], b[8], o[8];
         load8<T>(go + c, a);
         load8<T>(yr + c, b);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          dot = fmaf(a[q], b[q], dot);
-          o[q] = g * a[q];
+        for (int u = 0; u < 8; ++u) {
+          dot = fmaf(a[u], b[u], dot);
+          o[u] = g * a[u];
         }
         store8<T>(dr + c, o);
       }
     } else {
-      for (int c = threadIdx.x; c < d; c += 256) {
+      for (int c = tid; c < d; c += 256) {
         const float a = ld1<T>(go + c);
         dot = fmaf(a, ld1<T>(yr + c), dot);
         st1<T>(dr + c, g * a);
       }
     }
     dot = block_sum256(dot, red);
-    if (threadIdx.x == 0) dgate[(size_t)t * k + j] = dot;
+    if (tid == 0) dgate[(size_t)t * k + j] = dot;
   }
 }
 
@@ -191,15 +218,20 @@ __global__ __launch_bounds__(256) void router_bwd(const float* __restrict__ logi
       for (int i = 0; i < kPer; ++i)
         if (e == lane + 64 * i) dl[i] += v;
     }
-  } else {
+  } else if (idx) {
     // g_j = p[S_j]: dp[S_j] += dg_j, then the softmax backward
     for (int j = 0; j < k; ++j) {
-      const int e = idx ? it[j] : j;  // no index table: slot j is expert j (Expert Choice)
+      const int e = it[j];
       const float v = dgt[j];
 #pragma unroll
       for (int i = 0; i < kPer; ++i)
         if (e == lane + 64 * i) dp[i] += v;
     }
+  } else {
+    // no index table: slot j is expert j (Expert Choice, k == E)
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      if (lane + 64 * i < E) dp[i] += dgt[lane + 64 * i];
   }
   // aux: d/dp[t,e] = daux E counts_e / T^2
   if (aux_scale != 0.0f) {
@@ -283,6 +315,195 @@ __global__ __launch_bounds__(256) void gather_bwd(const T* __restrict__ dxp,
   }
 }
 
+// bf16 layers with d % 128 == 0: the router term on the MFMA units. Grid
+// (ceil(T / 64), d / 128), four waves; a block owns 64 tokens x 128 columns.
+// 1. The kept slots of each token are listed in LDS in slot order (a ballot
+//    per 64 slots, four tokens' dest rows in flight per wave); past
+//    kGmSlots a token resumes reading its dest row in the gather.
+// 2. R = dlogits . W_g over 64-expert chunks: dlogits (fp32) is split into
+//    bf16 hi + lo (hi = bf16(v), lo = bf16(v - hi), so hi + lo keeps 16
+//    significant bits) and both halves multiply the bf16 W_g on
+//    v_mfma_f32_32x32x16_bf16 with fp32 accumulation. Operands are staged in
+//    LDS per chunk: [64 tokens][64 experts] hi and lo (128-byte rows,
+//    swizzled as the ring's) and W_g's [64 experts][128 columns] K-major
+//    block read by transpose loads; experts past E are zero on the dlogits
+//    side (W_g rows clamped to E - 1). Wave w owns columns 32 w .. +31 of
+//    all 64 tokens (two 32 x 32 tiles; lane = column, registers = tokens).
+// 3. R goes through LDS (fp32, rows of 136 floats: the two half-waves, four
+//    tokens apart, land on disjoint banks), and each thread then sums 8
+//    columns of a token in the order of gather_bwd: router term, residual,
+//    the kept slots in slot order.
+constexpr int kGmTok = 64, kGmCols = 128, kGmSlots = 16, kGmStr = 136;
+struct GmOps {
+  uint16_t wgs[64 * 128];      // W_g chunk, K-major transpose layout
+  uint16_t dls[2][64 * 64];    // dlogits chunk, hi and lo
+};
+union GmLds {
+  GmOps ops;
+  float racc[kGmTok * kGmStr];
+};
+
+__global__ __launch_bounds__(256) void gather_bwd_mfma(const uint16_t* __restrict__ dxp,
+                                                       const int32_t* __restrict__ dest, int Tn,
+                                                       int k, int d,
+                                                       const uint16_t* __restrict__ dres,
+                                                       const float* __restrict__ dlogits,
+                                                       const uint16_t* __restrict__ wg, int E,
+                                                       uint16_t* __restrict__ dx) {
+  __shared__ __align__(16) GmLds sm;
+  __shared__ int list[kGmTok][kGmSlots];
+  __shared__ int nlist[kGmTok], resume[kGmTok];
+  const int t0 = blockIdx.x * kGmTok, c0 = blockIdx.y * kGmCols;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // 1. kept slots: wave w lists tokens 16 w .. 16 w + 15, four at a time
+  for (int tq = 0; tq < 16; tq += 4) {
+    int cnt[4] = {0, 0, 0, 0}, res[4] = {k, k, k, k};
+    for (int j0 = 0; j0 < k; j0 += 64) {
+      int r[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = t0 + wave * 16 + tq + u, j = j0 + lane;
+        r[u] = (t < Tn && j < k) ? dest[(size_t)t * k + j] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint64_t m = __ballot(r[u] >= 0);
+        const int pos = cnt[u] + __popcll(m & ((1ull << lane) - 1));
+        const int tt = wave * 16 + tq + u;
+        if (r[u] >= 0 && pos < kGmSlots) list[tt][pos] = r[u];
+        if (r[u] >= 0 && pos == kGmSlots) res[u] = j0 + lane;  // the first slot not listed
+        cnt[u] += __popcll(m);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int tt = wave * 16 + tq + u;
+      // the lane that saw the first unlisted slot holds it; others hold k
+      int rs = res[u];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) rs = min(rs, __shfl_xor(rs, o));
+      if (lane == 0) {
+        nlist[tt] = min(cnt[u], kGmSlots);
+        resume[tt] = rs;
+      }
+    }
+  }
+
+  // 2. router term
+  f32x16 acc[2] = {f32x16{}, f32x16{}};
+  if (dlogits) {
+    for (int e0 = 0; e0 < E; e0 += 64) {
+      __syncthreads();  // the previous chunk's reads are done
+      // W_g rows e0 .. e0 + 63 (clamped), columns c0 .. c0 + 127: 16-byte
+      // chunk c of row r at c ^ 4 (r % 4)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q = tid + 256 * i, r = q >> 4, c = q & 15;
+        const u32x4 v = *(const u32x4*)(wg + (size_t)min(e0 + r, E - 1) * d + c0 + c * 8);
+        *(u32x4*)(sm.ops.wgs + r * 128 + ((c ^ (4 * (r & 3))) << 3)) = v;
+      }
+      // dlogits rows t0 .. t0 + 63, experts e0 .. e0 + 63: thread (row tid / 4,
+      // experts 16 (tid % 4) .. +15) -> hi and lo chunks 2 (tid % 4), +1
+      {
+        const int r = tid >> 2, qd = tid & 3, t = t0 + r;
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int e = e0 + qd * 16 + u;
+          v[u] = (t < Tn && e < E) ? dlogits[(size_t)t * E + e] : 0.0f;
+        }
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          u32x4 hi, lo;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float a = v[h2 * 8 + 2 * u], b = v[h2 * 8 + 2 * u + 1];
+            const uint32_t ph = pack_bf16x2(a, b);
+            hi[u] = ph;
+            lo[u] = pack_bf16x2(a - bf16lo(ph), b - bf16hi(ph));
+          }
+          const int ck = swz128(r, 2 * qd + h2);
+          *(u32x4*)(sm.ops.dls[0] + r * 64 + ck * 8) = hi;
+          *(u32x4*)(sm.ops.dls[1] + r * 64 + ck * 8) = lo;
+        }
+      }
+      __syncthreads();
+      const int nsub = min(4, (E - e0 + 15) / 16);
+      for (int sub = 0; sub < nsub; ++sub) {
+        const bf16x8 b = tr_frag(sm.ops.wgs, sub, wave, lane);
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) {
+          const int r = mi * 32 + (lane & 31);
+          const int ck = swz128(r, 2 * sub + (lane >> 5));
+          const bf16x8 ah = *(const bf16x8*)(sm.ops.dls[0] + r * 64 + ck * 8);
+          const bf16x8 al = *(const bf16x8*)(sm.ops.dls[1] + r * 64 + ck * 8);
+          acc[mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, b, acc[mi], 0, 0, 0);
+          acc[mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, b, acc[mi], 0, 0, 0);
+        }
+      }
+    }
+  }
+  // 3. router term through LDS, then the sums
+  __syncthreads();
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int tt = mi * 32 + 8 * (v / 4) + 4 * (lane >> 5) + (v & 3);
+      sm.racc[tt * kGmStr + wave * 32 + (lane & 31)] = acc[mi][v];
+    }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tt = (tid >> 4) + 16 * i, cc = tid & 15, t = t0 + tt;
+    if (t >= Tn) continue;
+    const int c = c0 + cc * 8;
+    float a[8], v[8];
+    const f32x4 lo = *(const f32x4*)(sm.racc + tt * kGmStr + cc * 8);
+    const f32x4 hi = *(const f32x4*)(sm.racc + tt * kGmStr + cc * 8 + 4);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      a[u] = lo[u];
+      a[4 + u] = hi[u];
+    }
+    if (dres) {
+      load8<uint16_t>(dres + (size_t)t * d + c, v);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a[u] += v[u];
+    }
+    const int n = nlist[tt];
+    int j = 0;
+    for (; j + 4 <= n; j += 4) {  // four rows in flight, added in slot order
+      u32x4 rv[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) rv[q] = *(const u32x4*)(dxp + (size_t)list[tt][j + q] * d + c);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          a[2 * u] += bf16lo(rv[q][u]);
+          a[2 * u + 1] += bf16hi(rv[q][u]);
+        }
+    }
+    for (; j < n; ++j) {
+      load8<uint16_t>(dxp + (size_t)list[tt][j] * d + c, v);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a[u] += v[u];
+    }
+    for (int j = resume[tt]; j < k; ++j) {  // slots past the listed ones (rare)
+      const int r = dest[(size_t)t * k + j];
+      if (r >= 0) {
+        load8<uint16_t>(dxp + (size_t)r * d + c, v);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) a[u] += v[u];
+      }
+    }
+    store8<uint16_t>(dx + (size_t)t * d + c, a);
+  }
+}
+
 // Any d: one thread per (token, column), same sum order as gather_bwd.
 template <typename T>
 __global__ __launch_bounds__(256) void gather_bwd_scalar(const T* __restrict__ dxp,
@@ -358,6 +579,106 @@ __global__ __launch_bounds__(256) void wgate_partial(const T* __restrict__ x,
 }
 
 // dW_g[e][c] = sum_s part[s][e][c] (s ascending); grid (ceil(E*d / 256)).
+// bf16 layers with d % 128 == 0: the same partial sums on the MFMA units.
+// Grid (ceil(E / 128), d / 128, S); four waves, each 64 experts x 64 columns
+// of the block's 128 x 128 tile (2 x 2 32x32 MFMA tiles; lane = column,
+// registers = experts). Both operands contract over tokens, their leading
+// index, so each 64-token chunk is staged K-major ([64 tokens][128
+// features], 16-byte chunk c of row r at c ^ 4 (r % 4)) and read by
+// transpose loads: x as bf16, dlogits split into bf16 hi + lo (hi =
+// bf16(v), lo = bf16(v - hi)), both multiplied with fp32 accumulation.
+// Tokens past the range and experts past E are zero on the dlogits side (x
+// rows clamped to the range's last).
+__global__ __launch_bounds__(256) void wgate_mfma(const uint16_t* __restrict__ x,
+                                                  const float* __restrict__ dl, int Tn, int d,
+                                                  int E, int S, float* __restrict__ part) {
+  __shared__ __align__(16) uint16_t sdl[2][64 * 128];
+  __shared__ __align__(16) uint16_t sx[64 * 128];
+  const int e0 = blockIdx.x * 128, c0 = blockIdx.y * 128, s = blockIdx.z;
+  const int tb = (int)((long)s * Tn / S), te = (int)((long)(s + 1) * Tn / S);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = f32x16{};
+  for (int t = tb; t < te; t += 64) {
+    __syncthreads();  // the previous chunk's reads are done
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = tid + 256 * i, r = q >> 4, c = q & 15;
+      const u32x4 v = *(const u32x4*)(x + (size_t)min(t + r, te - 1) * d + c0 + c * 8);
+      *(u32x4*)(sx + r * 128 + ((c ^ (4 * (r & 3))) << 3)) = v;
+    }
+    {
+      const int r = tid >> 2, qd = tid & 3, tr = t + r;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int e = e0 + qd * 32 + q * 8 + u;
+          v[u] = (tr < te && e < E) ? dl[(size_t)tr * E + e] : 0.0f;
+        }
+        u32x4 hi, lo;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t ph = pack_bf16x2(v[2 * u], v[2 * u + 1]);
+          hi[u] = ph;
+          lo[u] = pack_bf16x2(v[2 * u] - bf16lo(ph), v[2 * u + 1] - bf16hi(ph));
+        }
+        const int pos = r * 128 + (((qd * 4 + q) ^ (4 * (r & 3))) << 3);
+        *(u32x4*)(sdl[0] + pos) = hi;
+        *(u32x4*)(sdl[1] + pos) = lo;
+      }
+    }
+    __syncthreads();
+    const int nsub = min(4, (te - t + 15) / 16);
+    for (int sub = 0; sub < nsub; ++sub) {
+      bf16x8 b[2];
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) b[ni] = tr_frag(sx, sub, wn * 2 + ni, lane);
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        const bf16x8 ah = tr_frag(sdl[0], sub, wm * 2 + mi, lane);
+        const bf16x8 al = tr_frag(sdl[1], sub, wm * 2 + mi, lane);
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, b[ni], acc[mi][ni], 0, 0, 0);
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, b[ni], acc[mi][ni], 0, 0, 0);
+        }
+      }
+    }
+  }
+  float* ps = part + (size_t)s * E * d;
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int e = e0 + wm * 64 + mi * 32 + 8 * (v / 4) + 4 * (lane >> 5) + (v & 3);
+      if (e < E) {
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          ps[(size_t)e * d + c0 + wn * 64 + ni * 32 + (lane & 31)] = acc[mi][ni][v];
+      }
+    }
+}
+
+// Token ranges of the MFMA form: about 1024 blocks, at most 64 ranges and
+// at least 64 tokens per range (never more ranges than router_bwd_splits,
+// whose workspace holds the partials).
+inline int wgate_mfma_splits(int T, int d, int E) {
+  const int tiles = ceil_div(E, 128) * (d / 128);
+  int s = ceil_div(1024, tiles);
+  if (s > 64) s = 64;
+  if (s > T / 64) s = T / 64;
+  if (s < 1) s = 1;
+  const int cap = router_bwd_splits(T, d, E);
+  return s < cap ? s : cap;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void wgate_reduce(const float* __restrict__ part, int E, int d,
                                                     int S, T* __restrict__ dwg) {
@@ -431,7 +752,12 @@ extern "C" int moe_gather_backward(const void* dx_perm, int dtype, const int32_t
   if (T == 0) return MOE_OK;
   if (!dx_perm || !dest_row || !dx || (dlogits && !w_gate)) return MOE_ERR_INVALID;
   hipStream_t s = (hipStream_t)stream;
-  if ((d % 8) == 0) {
+  if (dtype == MOE_BF16 && (d % kGmCols) == 0) {
+    hipLaunchKernelGGL(gather_bwd_mfma, dim3(ceil_div(T, kGmTok), d / kGmCols), dim3(256), 0, s,
+                       (const uint16_t*)dx_perm, dest_row, T, k, d,
+                       (const uint16_t*)dout_residual, dlogits, (const uint16_t*)w_gate, E,
+                       (uint16_t*)dx);
+  } else if ((d % 8) == 0) {
     const dim3 g(ceil_div(T, kGbTokens), ceil_div(d, kGbCols));
     if (dtype == MOE_BF16)
       hipLaunchKernelGGL(gather_bwd<uint16_t>, g, dim3(256), 0, s, (const uint16_t*)dx_perm,
@@ -464,10 +790,14 @@ extern "C" int moe_router_weight_backward(const void* x, int dtype, int T, int d
   if (!dw_gate || (T > 0 && (!x || !dlogits))) return MOE_ERR_INVALID;
   if (!ws || ws_bytes < router_bwd_ws(T, d, E)) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
-  const int S = router_bwd_splits(T, d, E);
+  const bool mfma = dtype == MOE_BF16 && (d % 128) == 0;
+  const int S = mfma ? wgate_mfma_splits(T, d, E) : router_bwd_splits(T, d, E);
   float* part = (float*)ws;
   const dim3 g(ceil_div(E, kWgTile), ceil_div(d, kWgTile), S);
-  if (dtype == MOE_BF16)
+  if (mfma && T > 0)
+    hipLaunchKernelGGL(wgate_mfma, dim3(ceil_div(E, 128), d / 128, S), dim3(256), 0, s,
+                       (const uint16_t*)x, dlogits, T, d, E, S, part);
+  else if (dtype == MOE_BF16)
     hipLaunchKernelGGL(wgate_partial<uint16_t>, g, dim3(256), 0, s, (const uint16_t*)x, dlogits, T,
                        d, E, S, part);
   else

@@ -345,20 +345,30 @@ def bench_backward(args, cfg, inp, dev):
           for j, c in enumerate(calls)}
     ms_step = events[0][0].elapsed_time(events[-1][len(calls)]) / args.steps
     R = int(bufs.offsets[-1])
-    # algorithmic work of the backward FFN: dH, dX, dW1, dW2 (2 R d h each)
+    counts = np.diff(bufs.offsets.cpu().numpy())
+    touched = int((counts > 0).sum())
+    # algorithmic work of the backward FFN: dH, dX, dW1, dW2 (2 R d h each);
+    # its unavoidable HBM bytes: the touched experts' W1 and W2 read for the
+    # data gradients, and every expert's dW1, dW2, db1, db2 written
+    ebytes = 2 if cfg.dtype == "bf16" else 4
     flop = 8.0 * R * d * h
+    wbytes = (touched * 2 * d * h + E * (2 * d * h + d + h)) * ebytes
     t_bwd = ms["ffn_bwd"] * 1e-3
-    if cfg.dtype == "bf16":
+    if cfg.dtype != "bf16":
+        roof = {"bound": "alu", "achieved": flop / t_bwd / 1e12, "peak": PEAK_F32_TFLOPS,
+                "unit": "TFLOP/s"}
+    elif flop / max(wbytes, 1) > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
         roof = {"bound": "mfma", "achieved": flop / t_bwd / 1e12, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s"}
     else:
-        roof = {"bound": "alu", "achieved": flop / t_bwd / 1e12, "peak": PEAK_F32_TFLOPS,
-                "unit": "TFLOP/s"}
+        roof = {"bound": "hbm", "achieved": wbytes / t_bwd / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = None
-    roof["kernel"] = ("moe_grouped_ffn_backward (dZ, dX_perm, dW1, dW2 on the MFMA ring GEMM, "
-                      "gathered input rows, bias sums)")
-    roof["per_launch"] = {"flop": flop, "rows": R}
+    roof["kernel"] = ("moe_grouped_ffn_backward (dZ and dX_perm on the MFMA ring GEMM, dW1 and dW2 "
+                      "on the weight-gradient GEMM, gathered input rows, bias sums)")
+    roof["per_launch"] = {"flop": flop, "weight_bytes": wbytes, "rows": R,
+                          "touched_experts": touched}
     out = {
         "metric": TRAIN_METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,

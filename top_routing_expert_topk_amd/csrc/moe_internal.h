@@ -26,15 +26,15 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
 __device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 
-// fp32 -> bf16, round to nearest even (inputs are finite by contract).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+// fp32 -> bf16, round to nearest even (inputs are finite by contract): the
+// conversion lowers to gfx950's v_cvt_pk_bf16_f32, two values per
+// instruction.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return pack_bf16x2(f, 0.0f) & 0xFFFFu; }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 // SiLU from the hardware exp2 and reciprocal (about 1e-7 relative error), for

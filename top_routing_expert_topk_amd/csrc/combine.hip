@@ -53,6 +53,8 @@ __global__ __launch_bounds__(256) void combine_bf16(
       gj[j] = gate[(size_t)t * k + j];
     }
   }
+  // two column chunks per pass, so 2 (k + 1) row loads are in flight per lane
+#pragma unroll 2
   for (int c = lane * 8; c < d; c += 64 * 8) {
     float acc[8];
     if (resid) {

@@ -137,7 +137,48 @@ __global__ __launch_bounds__(256) void combine_bwd(const T* __restrict__ y,
   if (tid == 0) nkept = base;
   __syncthreads();
   const int nk = nkept;
-  for (int q = 0; q < nk; ++q) {
+  int q = 0;
+  if (vec) {
+    // eight kept slots per pass over the row: dout is read once per pass and
+    // their eight y rows are in flight together; each dot product is summed
+    // per thread in column order and reduced as block_sum256 does
+    __shared__ float red8[4][8];
+    for (; q + 8 <= nk; q += 8) {
+      float dot[8], g[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        dot[u] = 0.0f;
+        g[u] = gate[(size_t)t * k + kept[q + u]];
+      }
+      for (int c = tid * 8; c < d; c += 256 * 8) {
+        float a[8], b[8][8];
+        load8<T>(go + c, a);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) load8<T>(y + (size_t)krow[q + u] * d + c, b[u]);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          float o[8];
+#pragma unroll
+          for (int v = 0; v < 8; ++v) {
+            dot[u] = fmaf(a[v], b[u][v], dot[u]);
+            o[v] = g[u] * a[v];
+          }
+          store8<T>(dy + (size_t)krow[q + u] * d + c, o);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) dot[u] = wave_sum(dot[u]);
+      __syncthreads();
+      if (lane == 0)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) red8[wave][u] = dot[u];
+      __syncthreads();
+      if (tid < 8)
+        dgate[(size_t)t * k + kept[q + tid]] =
+            (red8[0][tid] + red8[1][tid]) + (red8[2][tid] + red8[3][tid]);
+    }
+  }
+  for (; q < nk; ++q) {  // one slot per pass
     const int j = kept[q], r = krow[q];
     const float g = gate[(size_t)t * k + j];
     const T* yr = y + (size_t)r * d;

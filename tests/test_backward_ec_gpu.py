@@ -28,6 +28,10 @@ CASES = {
                                 zipf_gate_bias=False), 205),
     "ec_fp32": (EC.with_(name="ec_fp32", T=77, d=96, h=200, E=5, dtype="f32",
                          zipf_gate_bias=False, residual=False), 20),
+    # every expert takes every token: 24 kept slots per token, more than the
+    # gather lists per token in LDS, and three passes of eight in the combine
+    "ec_many_slots": (EC.with_(name="ec_many_slots", T=40, d=256, h=256, E=24,
+                               zipf_gate_bias=False), 40),
     # the Switch-shaped workload as benched (T=8192, d=768, h=3072, E=128, C=80)
     "ec_switch_full": (EC, EC.capacity),
 }

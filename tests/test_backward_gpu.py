@@ -44,6 +44,11 @@ CASES = {
     # top-8 of 32
     "deepseek_small": mi.CONFIGS["deepseek_v3"].with_(name="deepseek_small", T=256, d=512, h=256,
                                                       E=32),
+    # top-16 of 40 (the router's largest k): as many kept slots per token as
+    # the gather lists in LDS, two of the combine's passes of eight, and 40
+    # experts ending in a partial 16-expert MFMA step of the router products
+    "many_slots": mi.CONFIGS["deepseek_v3"].with_(name="many_slots", T=96, d=256, h=256, E=40,
+                                                  k=16),
     # most experts receive no row: their weight gradients must be zero
     "sparse_experts": BASE.with_(name="sparse_experts", T=24, d=256, h=256, E=64),
     # every assignment dropped: only the residual and the aux loss remain

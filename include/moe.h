@@ -310,7 +310,9 @@ int moe_grouped_ffn_train(const void *x, int dtype, int T, int d, int h, int E, 
  * rows); db1 / db2 may be NULL (no bias). Gradients have the layer dtype;
  * products accumulate in fp32. bf16: d and h multiples of 256 (status 2
  * otherwise). Workspace: moe_workspace_size(MOE_OP_FFN_BWD, ...), which
- * holds the transposed weights and activations.
+ * holds the work lists, Z and dZ, split-K partials and the gathered input
+ * rows; every operand is read in place (K-major ones through LDS
+ * transpose loads).
  */
 int moe_grouped_ffn_backward(const void *x, int dtype, int T, int d, int h, int E, int k,
                              const int32_t *offsets, const int32_t *sorted_token, const void *w1,
@@ -321,10 +323,14 @@ int moe_grouped_ffn_backward(const void *x, int dtype, int T, int d, int h, int 
 
 /*
  * Input gradient:
- *   dx[t] = sum_e dlogits[t,e] w_gate[e]        (e ascending; if dlogits)
+ *   dx[t] = sum_e dlogits[t,e] w_gate[e]        (if dlogits)
  *         + dout_residual[t]                    (if not NULL: residual layers)
  *         + sum_j dx_perm[dest_row[t*k+j]]      (kept slots, j ascending)
- * summed in fp32, stored in dtype. k, E <= 512.
+ * summed in fp32 in that order, stored in dtype. k, E <= 512. The router
+ * term: bf16 layers with d % 128 == 0 compute it on the matrix cores from
+ * dlogits split into two bf16 parts (hi = bf16(v), lo = bf16(v - hi), 16
+ * significant bits) with fp32 accumulation; otherwise fp32 FMA, e
+ * ascending.
  */
 int moe_gather_backward(const void *dx_perm, int dtype, const int32_t *dest_row, int T, int k,
                         int d, const void *dout_residual, const float *dlogits,
@@ -335,7 +341,9 @@ int moe_gather_backward(const void *dx_perm, int dtype, const int32_t *dest_row,
  *   dw_gate[e][i] = sum_t dlogits[t,e] x[t,i]   (dtype [E][d])
  *   dgate_bias[e] = sum_t dlogits[t,e]          (fp32 [E], may be NULL)
  * Sums run over fixed token ranges (their number depends only on T, d, E)
- * in a fixed order. Workspace:
+ * in a fixed order. bf16 layers with d % 128 == 0 form dw_gate on the
+ * matrix cores with dlogits split into two bf16 parts as in
+ * moe_gather_backward; otherwise fp32 FMA. Workspace:
  * moe_workspace_size(MOE_OP_ROUTER_BWD, ...).
  */
 int moe_router_weight_backward(const void *x, int dtype, int T, int d, int E,

@@ -16,10 +16,16 @@
 //                   dg[t,j] = <dout[t], y[row]> (fp32, fixed-order reduction)
 //   router_bwd      one wave per token: dlogits from dg (renormalised top-k
 //                   softmax or full-softmax backward) plus the aux term
-//   gather_bwd      dx[t] = dout[t] (residual) + sum_j dXp[dest[t,j]]
-//                   + sum_e dlogits[t,e] W_g[e], 16 tokens per block
-//   wgate_partial   dW_g partial sums over token ranges (64 x 64 tiles, up to
-//                   64 ranges so that small E still fills the chip)
+//   gather_bwd_mfma dx[t] = sum_e dlogits[t,e] W_g[e] (on the matrix cores,
+//                   dlogits split into bf16 hi + lo) + dout[t] (residual)
+//                   + sum_j dXp[dest[t,j]], 64 tokens x 128 columns per
+//                   block, kept slots listed in LDS (bf16, d % 128 == 0)
+//   gather_bwd      the same sum in fp32 FMA, 16 tokens per block (fp32
+//                   layers and other widths)
+//   wgate_mfma      dW_g partial sums over token ranges on the matrix cores
+//                   (128 x 128 tiles, both operands K-major)
+//   wgate_partial   the same in fp32 FMA (64 x 64 tiles, up to 64 ranges so
+//                   that small E still fills the chip)
 //   wgate_reduce    partials summed in range order; db_g over all tokens
 #include <type_traits>
 

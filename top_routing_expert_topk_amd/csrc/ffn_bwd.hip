@@ -557,9 +557,8 @@ extern "C" int moe_grouped_ffn_backward(const void* x, int dtype, int T, int d, 
                             (const float*)dy_perm, (const float*)z_perm, (const float*)h_perm,
                             (float*)dx_perm, (float*)dw1, (float*)db1, (float*)dw2, (float*)db2,
                             ws, s);
-  // bf16: 256 x 256 tiles on both widths; 32-bit element offsets of every
-  // row operand (the gathered x rows, the permuted rows and the padded
-  // transposed arrays)
+  // bf16: 256-wide tiles on both widths; 32-bit element offsets of the
+  // gathered x rows and the permuted rows in the ring's DMA
   if ((d % kBigBN) != 0 || (h % kBigBN) != 0) return MOE_ERR_UNSUPPORTED;
   if ((long)T * d >= (1L << 31) || rows * d >= (1L << 31) || rows * h >= (1L << 31))
     return MOE_ERR_UNSUPPORTED;

@@ -44,6 +44,11 @@ CASES = {
     # top-8 of 32
     "deepseek_small": mi.CONFIGS["deepseek_v3"].with_(name="deepseek_small", T=256, d=512, h=256,
                                                       E=32),
+    # 32 experts of about 275 rows: an expert's last row block is one taller
+    # tile of up to 288 rows, in the forward and in the Z recompute; few
+    # tiles, so they are split along K
+    "taller_tiles": mi.CONFIGS["deepseek_v3"].with_(name="taller_tiles", T=1100, d=512, h=256,
+                                                    E=32),
     # top-16 of 40 (the router's largest k): as many kept slots per token as
     # the gather lists in LDS, two of the combine's passes of eight, and 40
     # experts ending in a partial 16-expert MFMA step of the router products
@@ -135,7 +140,8 @@ def test_backward_is_deterministic():
         assert torch.equal(v, getattr(g2, n)), n
 
 
-@pytest.mark.parametrize("name", ["mix_rows", "switch_small", "tiny_fp32", "sparse_experts"])
+@pytest.mark.parametrize("name", ["mix_rows", "taller_tiles", "switch_small", "tiny_fp32",
+                                  "sparse_experts"])
 def test_kept_and_recomputed_preactivations_agree(name):
     """With the forward's Z the backward skips recomputing it. Z is the same
     bf16(acc + b1) either way, so everything that follows from dZ is
@@ -154,6 +160,7 @@ def test_kept_and_recomputed_preactivations_agree(name):
 
 TRAIN_PATHS = {
     "ring": CASES["mix_rows"],                        # 768 rows per expert
+    "taller": CASES["taller_tiles"],                  # taller last tiles
     "persistent": CASES["switch_small"],              # about 64 rows per expert
     "streaming": CASES["sparse_experts"],             # 48 rows over 64 experts
     "tiles128": BASE.with_(name="tiles128", T=300, d=384, h=640),

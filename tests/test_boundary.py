@@ -52,8 +52,8 @@ def test_ffn_workspace_holds_the_tile_path_layout(T, d, h, E, k):
     """The FFN workspace must hold, for 128- and 256-row tiles alike: two
     32-byte work entries per tile and per split unit of both GEMMs, a token
     table of every row block (padded to the tile height), the hidden
-    activations (4 bytes per element at most) and 256 fp32 256x256 partial
-    tiles. Restated here from the layout, independently of the C++ sizing."""
+    activations (4 bytes per element at most) and 256 fp32 partial tiles of
+    up to 288 rows x 256 features. Restated here from the layout, independently of the C++ sizing."""
     rows = T * k
     need_plan = 0
     for bm in (128, 256):
@@ -61,7 +61,7 @@ def test_ffn_workspace_holds_the_tile_path_layout(T, d, h, E, k):
         lists = 256 + sum(_ceil(mslots * (n // 256) + 256, 8) * 8 for n in (h, d)) * 32
         table = mslots * bm * 4
         need_plan = max(need_plan, _ceil(lists, 256) * 256 + _ceil(table, 256) * 256)
-    need = need_plan + rows * h * 4 + 256 * 256 * 256 * 4
+    need = need_plan + rows * h * 4 + 256 * 288 * 256 * 4
     assert N.moe_workspace_size(N.MOE_OP_FFN, T, d, h, E, k) >= need
 
 
@@ -163,9 +163,10 @@ def test_backward_workspace_sizes():
                           (256, 128, 256, 8, 2), (1, 256, 256, 512, 16)]:
         rows = T * k
         need = (N.moe_workspace_size(N.MOE_OP_FFN, T, d, h, E, k) - rows * h * 4
-                - 256 * 256 * 256 * 4)  # the plan part of the forward workspace
-        need += (4 * E * (d // 256) * (h // 256) * 32 + 2 * rows * h * 4 + 256 * 256 * 256 * 4
-                 + rows * d * 2)
+                - 256 * 288 * 256 * 4)  # the plan part of the forward workspace
+        zr = 256 + _ceil((_ceil(rows, 256) + min(rows, E)) * (h // 256) + 256, 8) * 8 * 32
+        need += (4 * E * (d // 256) * (h // 256) * 32 + zr + 2 * rows * h * 4
+                 + 256 * 288 * 256 * 4 + rows * d * 2)
         assert N.moe_workspace_size(N.MOE_OP_FFN_BWD, T, d, h, E, k) >= need
         tiles = _ceil(E, 64) * _ceil(d, 64)
         s = max(1, min(_ceil(4096, tiles), 64, T // 16))

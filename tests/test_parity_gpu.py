@@ -65,6 +65,10 @@ SMALL = {
     # 256 x 256 tiles over experts of ~256 rows: many last row blocks hold a
     # few rows, whose idle waves and activation DMAs are skipped
     "big_ragged": CFG["deepseek_v3"].with_(name="big_ragged", T=2048, d=512, h=512, E=64),
+    # 32 experts of ~275 rows: an expert's last row block runs as one taller
+    # tile of up to 288 rows; few tiles, so the taller tiles are split along K
+    "big_taller_split": CFG["deepseek_v3"].with_(name="big_taller_split", T=1100, d=512,
+                                                  h=256, E=32),
     # experts of ~150 rows: persistent 256 x 128 tiles, two row blocks per expert
     "mid_rows_multi": CFG["mixtral_prefill"].with_(name="mid_rows_multi", T=600, d=512, h=1536),
     # 64 experts under a capacity of 80 rows: persistent 256 x 128 tiles, a

@@ -595,17 +595,17 @@ int launch_ring(const uint16_t* x, const int32_t* sorted_token, const int32_t* o
   BigWork* list2 = list1 + g1;
   const dim3 gr(kTailSlots * kReduceSlices);
   hipLaunchKernelGGL((big_plan<kBigBM, true>), dim3(ceil_div(g1 + g2, kMaxE)), dim3(kMaxE), 0, s,
-                     offsets, E, h / kBigBN, d / kRS, g1, d / kBigBN, h / kRS, g2, hdr, list1, list2,
-                     sorted_token, (int32_t*)nullptr);
+                     offsets, E, big_xr(E), h / kBigBN, d / kRS, g1, d / kBigBN, h / kRS, g2, hdr,
+                     list1, list2, sorted_token, (int32_t*)nullptr);
   hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, true, kEpiSilu>), dim3(g1), dim3(kRingWaves * 64),
                      0, s, x, sorted_token, list1, w1, b1, H, part, h, d, (size_t)h * d, 0,
                      (const uint16_t*)nullptr, zout);
-  hipLaunchKernelGGL((big_tail_reduce<kBigBM, kEpiSilu>), gr, dim3(256), 0, s, hdr, list1, b1, part,
+  hipLaunchKernelGGL((big_tail_reduce<kBigRowsMax, kEpiSilu>), gr, dim3(256), 0, s, hdr, list1, b1, part,
                      H, h, (const uint16_t*)nullptr, zout);
   hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, false, kEpiBias>), dim3(g2), dim3(kRingWaves * 64),
                      0, s, H, sorted_token, list2, w2, b2, y, part, d, h, (size_t)d * h, 0,
                      (const uint16_t*)nullptr, (uint16_t*)nullptr);
-  hipLaunchKernelGGL((big_tail_reduce<kBigBM, kEpiBias>), gr, dim3(256), 0, s, hdr + 1, list2, b2,
+  hipLaunchKernelGGL((big_tail_reduce<kBigRowsMax, kEpiBias>), gr, dim3(256), 0, s, hdr + 1, list2, b2,
                      part, y, d, (const uint16_t*)nullptr, (uint16_t*)nullptr);
   return launch_status();
 }
@@ -629,7 +629,7 @@ int launch_pring(const uint16_t* x, const int32_t* sorted_token, const int32_t* 
     return MOE_ERR_WORKSPACE;
   const dim3 gr(kTailSlots * kReduceSlices);
   hipLaunchKernelGGL((big_plan<BM, false>), dim3(ceil_div(g1 + g2 + ntok, kMaxE)), dim3(kMaxE), 0,
-                     s, offsets, E, h / kBigBN, d / kRS, g1, d / kBigBN, h / kRS, g2, hdr, list1,
+                     s, offsets, E, 0, h / kBigBN, d / kRS, g1, d / kBigBN, h / kRS, g2, hdr, list1,
                      list2, sorted_token, tok);
   hipLaunchKernelGGL((gemm_bf16_pring<BM, true, true>), dim3(kTailSlots), dim3(512), 0, s, x, tok,
                      hdr, list1, w1, b1, H, part, h, d, zout);

@@ -481,8 +481,9 @@ int ffn_backward_bf16(const uint16_t* x, int T, int d, int h, int E, int k,
   const uint16_t* none = nullptr;
   const dim3 gr(kTailSlots * kReduceSlices), rb(kRingWaves * 64);
 
+  // the data-gradient products (K-major weights) run plain 256-row tiles
   hipLaunchKernelGGL((big_plan<kBigBM, true>), dim3(ceil_div(g1 + g2, kMaxE)), dim3(kMaxE), 0, s,
-                     offsets, E, mh, d / kRS, g1, md, h / kRS, g2, hdr, list1, list2, sorted_token,
+                     offsets, E, 0, mh, d / kRS, g1, md, h / kRS, g2, hdr, list1, list2, sorted_token,
                      (int32_t*)nullptr);
   hipLaunchKernelGGL(wgrad_plan, dim3(ceil_div(nw2, 256)), dim3(256), 0, s, offsets, E, d / kWgBM, mh,
                      wl2);
@@ -492,17 +493,24 @@ int ffn_backward_bf16(const uint16_t* x, int T, int d, int h, int E, int k,
     hipLaunchKernelGGL(gather_rows, dim3(ceil_div(rows, 4)), dim3(256), 0, s, x, sorted_token,
                        offsets, E, d, xp);
   if (!zin) {
-    // Z = W1[e] x + b1 (the forward's first product without the activation)
+    // Z = W1[e] x + b1 (the forward's first product without the activation),
+    // on the forward's tiles (taller last tiles included), so that it equals
+    // the Z a training forward keeps bit for bit
+    BigHdr* hdr_r = (BigHdr*)(base + L.zr);
+    BigWork* list_r = (BigWork*)(base + L.zr + 256);
+    hipLaunchKernelGGL((big_plan<kBigBM, true>), dim3(ceil_div(g1, kMaxE)), dim3(kMaxE), 0,
+                       s, offsets, E, big_xr(E), mh, d / kRS, g1, md, h / kRS, 0, hdr_r, list_r,
+                       (BigWork*)nullptr, sorted_token, (int32_t*)nullptr);
     hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, true, kEpiBias>), dim3(g1), rb, 0, s, x,
-                       sorted_token, list1, w1, b1, Zw, part, h, d, (size_t)h * d, 0, none, nz);
-    hipLaunchKernelGGL((big_tail_reduce<kBigBM, kEpiBias>), gr, dim3(256), 0, s, hdr, list1, b1,
-                       part, Zw, h, none, nz);
+                       sorted_token, list_r, w1, b1, Zw, part, h, d, (size_t)h * d, 0, none, nz);
+    hipLaunchKernelGGL((big_tail_reduce<kBigRowsMax, kEpiBias>), gr, dim3(256), 0, s, hdr_r,
+                       list_r, b1, part, Zw, h, none, nz);
   }
   // dZ = (dY W2[e]) * SiLU'(Z): W2[e] is [d][h], K-major for this product
   hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, false, kEpiDSilu, true>), dim3(g1), rb, 0, s, dy,
                      (const int32_t*)nullptr, list1, w2, none, dZ, part, h, d, (size_t)h * d, 0,
                      Z, nz);
-  hipLaunchKernelGGL((big_tail_reduce<kBigBM, kEpiDSilu>), gr, dim3(256), 0, s, hdr, list1, none,
+  hipLaunchKernelGGL((big_tail_reduce<kBigRowsMax, kEpiDSilu>), gr, dim3(256), 0, s, hdr, list1, none,
                      part, dZ, h, Z, nz);
   // H: the forward's, or SiLU of the recomputed Z (in place, Z is no longer read)
   const uint16_t* H = hin;
@@ -519,7 +527,7 @@ int ffn_backward_bf16(const uint16_t* x, int T, int d, int h, int E, int k,
   hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, false, kEpiBias, true>), dim3(g2), rb, 0, s,
                      (const uint16_t*)dZ, (const int32_t*)nullptr, list2, w1, none, dxp, part, d, h,
                      (size_t)d * h, 0, none, nz);
-  hipLaunchKernelGGL((big_tail_reduce<kBigBM, kEpiBias>), gr, dim3(256), 0, s, hdr + 1, list2, none,
+  hipLaunchKernelGGL((big_tail_reduce<kBigRowsMax, kEpiBias>), gr, dim3(256), 0, s, hdr + 1, list2, none,
                      part, dxp, d, none, nz);
   if (db2)
     hipLaunchKernelGGL(bias_grad_bf16, dim3(d / 128, E), dim3(256), 0, s, dy, offsets, d, db2);

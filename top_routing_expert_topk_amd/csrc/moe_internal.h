@@ -135,7 +135,13 @@ inline size_t ffn_plan_bytes(int T, int d, int h, int E, int k) {
   return align_up(tmap > ring ? tmap : ring, 256);
 }
 inline size_t ffn_hidden_bytes(int T, int h, int k) { return align_up((size_t)T * k * h * 4, 256); }
-inline size_t ffn_partial_bytes() { return (size_t)kTailSlots * 256 * 256 * sizeof(float); }
+// A DMA-ring tile holds up to 256 + 32 permuted rows (an expert's last row
+// block takes up to 32 more rows rather than leaving them to a nearly empty
+// tile); its fp32 partial is [288][256].
+constexpr int kBigRowsMax = 288;
+inline size_t ffn_partial_bytes() {
+  return (size_t)kTailSlots * kBigRowsMax * 256 * sizeof(float);
+}
 inline size_t ffn_ws(int T, int d, int h, int E, int k) {
   return ffn_plan_bytes(T, d, h, E, k) + ffn_hidden_bytes(T, h, k) + ffn_partial_bytes();
 }
@@ -156,10 +162,11 @@ inline size_t router_bwd_ws(int T, int d, int E) {
 
 // FFN backward: [plan of the forward-shaped GEMMs (ffn_plan_bytes)]
 //   [weight-gradient work lists: 2 x E x (d/128)(h/256) entries]
+//   [header + work list of the Z recompute (the forward's taller last tiles)]
 //   [Z: T*k*h x 4 B] [dZ: T*k*h x 4 B] [tail partials]
 //   [gathered input rows: T*k*d bf16]
 struct FfnBwdLayout {
-  size_t wl, z, dz, part, xp, total;
+  size_t wl, zr, z, dz, part, xp, total;
 };
 inline FfnBwdLayout ffn_bwd_layout(int T, int d, int h, int E, int k) {
   FfnBwdLayout L;
@@ -167,6 +174,8 @@ inline FfnBwdLayout ffn_bwd_layout(int T, int d, int h, int E, int k) {
   size_t o = ffn_plan_bytes(T, d, h, E, k);
   L.wl = o;
   o += align_up((size_t)4 * E * (d / kBigBNTile) * (h / kBigBNTile) * kWorkBytes, 256);
+  L.zr = o;
+  o += align_up(256 + (size_t)ffn_big_grid(rows, E, h, kBigBNTile) * kWorkBytes, 256);
   L.z = o;
   o += align_up(rows * h * 4, 256);
   L.dz = o;

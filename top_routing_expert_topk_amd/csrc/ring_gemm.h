@@ -42,6 +42,15 @@ namespace {
 // bank groups. Lane l of a DMA instruction writes chunk slot l%8 of row l/8,
 // so it fetches chunk (l%8) ^ swizzle(row).
 constexpr int kBigBM = 256;          // permuted rows per tile
+constexpr int kBigXR = kBigRowsMax - kBigBM;  // more rows an expert's last tile may take
+// Taller last tiles are planned for layers of at least 32 experts. There each
+// XCD's contiguous range of tiles spans several experts, and an expert's
+// taller tiles replace tiles that would stream a whole weight panel for a few
+// rows. With fewer experts an XCD's range is one or two experts, so all taller
+// tiles of one expert (which keep one K step in flight instead of one and a
+// half) land on the same XCD, and its CUs finish last.
+constexpr int kBigXRMinExperts = 32;
+inline int big_xr(int E) { return E >= kBigXRMinExperts ? kBigXR : 0; }
 constexpr int kBigBN = kBigBNTile;   // weight rows (output features) per tile
 constexpr int kRS = 64;              // K columns per step
 constexpr int kRBlk = 128 * kRS;     // bf16 elements per block (16 KB)
@@ -178,7 +187,10 @@ __device__ __forceinline__ int find_le(const int* ts, int E, int v) {
 }
 
 // Work lists of both GEMMs of the FFN (N = nt * kBigBN features, nk K steps,
-// BM permuted rows per tile). Tile order: expert-major; inside an expert,
+// BM permuted rows per tile; with xr > 0 an expert's last row block takes up
+// to BM + xr rows, so an expert of BM + r rows, r <= xr, runs as one tile
+// instead of a full one plus one of r rows that would stream the same
+// weights for almost no work). Tile order: expert-major; inside an expert,
 // groups of kGroupN weight-row tiles, inside a group the expert's row blocks.
 // REMAP: entry b is the work of hardware block b, whole tiles dealt to the
 // XCDs in contiguous ranges of that order (block b runs on XCD b % 8), so each
@@ -186,7 +198,7 @@ __device__ __forceinline__ int find_le(const int* ts, int E, int v) {
 // in that order (whole tiles, then the K ranges of the tail tiles) and the
 // persistent kernel deals them out itself.
 template <int BM, bool REMAP>
-__global__ __launch_bounds__(512) void big_plan(const int32_t* __restrict__ offsets, int E,
+__global__ __launch_bounds__(512) void big_plan(const int32_t* __restrict__ offsets, int E, int xr,
                                                 int nt1, int nk1, int g1, int nt2, int nk2,
                                                 int g2, BigHdr* __restrict__ hdr,
                                                 BigWork* __restrict__ list1,
@@ -197,7 +209,12 @@ __global__ __launch_bounds__(512) void big_plan(const int32_t* __restrict__ offs
   __shared__ int ts[kMaxE + 1];
   const int x = threadIdx.x;  // blockDim == kMaxE
   int cur = 0;
-  sc[0][x] = x < E ? (offsets[x + 1] - offsets[x] + BM - 1) / BM : 0;
+  if (x < E) {
+    const int c = offsets[x + 1] - offsets[x];
+    sc[0][x] = c <= 0 ? 0 : max(1, (c - xr + BM - 1) / BM);
+  } else {
+    sc[0][x] = 0;
+  }
   __syncthreads();
   for (int off = 1; off < kMaxE; off <<= 1) {
     const int v = sc[cur][x] + (x >= off ? sc[cur][x - off] : 0);
@@ -213,7 +230,7 @@ __global__ __launch_bounds__(512) void big_plan(const int32_t* __restrict__ offs
   if (i >= g1 + g2) {
     // token table: entry ms * BM + r = the token of row r of row block ms,
     // rows past the block's last one repeating it
-    if (!tok_tab) return;
+    if (xr > 0 || !tok_tab) return;
     const int j = i - g1 - g2, ms = j / BM, r = j % BM;
     if (ms >= ts[E]) return;
     const int e = find_le(ts, E, ms);
@@ -261,7 +278,7 @@ __global__ __launch_bounds__(512) void big_plan(const int32_t* __restrict__ offs
     const int mi = l2 / gs, ni = g * kGroupN + l2 % gs;
     w.e = e;
     w.row0 = offsets[e] + mi * BM;
-    w.rows = min(BM, offsets[e + 1] - w.row0);
+    w.rows = mi == mt - 1 ? offsets[e + 1] - w.row0 : BM;
     w.n0 = ni * kBigBN;
     w.kbeg = p * nk / split;
     w.kend = (p + 1) * nk / split;
@@ -272,8 +289,10 @@ __global__ __launch_bounds__(512) void big_plan(const int32_t* __restrict__ offs
 }
 
 // Epilogue of a 256 x 256 tile, each of NW waves holding 128 x (32 TM) of it
-// as 4 x TM 32x32 MFMA accumulators. A split tail tile stores its fp32 partial
-// [256 rows][256 features] for big_tail_reduce; a whole tile adds the bias,
+// as 4 x TM 32x32 MFMA accumulators; a taller last tile (rows > 256) adds
+// rows 256..287, wave (wn, wm) holding features 128 wn + 32 wm .. +31 of them
+// in accx. A split tail tile stores its fp32 partial [288 rows][256
+// features] for big_tail_reduce; a whole tile adds the bias,
 // applies SiLU if asked, rounds to bf16 into LDS (ot, the idle ring), and
 // leaves with 16-byte stores of whole rows: 32 lanes write one 512-byte row.
 // LDS rows are padded by 16 bytes so the 32 rows a wave writes at one feature
@@ -283,7 +302,8 @@ __global__ __launch_bounds__(512) void big_plan(const int32_t* __restrict__ offs
 // row m: e * ores + row0 + m. kEpiSilu with zout: the pre-activation
 // acc + bias also leaves, to zout, in a first pass through the same staging.
 template <int NW, int TM, int EPI>
-__device__ __forceinline__ void big_store(f32x16 (&acc)[4][TM], uint16_t* ot, size_t ot_bytes,
+__device__ __forceinline__ void big_store(f32x16 (&acc)[4][TM], const f32x16& accx,
+                                          uint16_t* ot, size_t ot_bytes,
                                           const BigWork& wk, const uint16_t* __restrict__ bias,
                                           uint16_t* __restrict__ out, float* __restrict__ part,
                                           int N, int ores, const uint16_t* __restrict__ zin,
@@ -291,8 +311,11 @@ __device__ __forceinline__ void big_store(f32x16 (&acc)[4][TM], uint16_t* ot, si
                                           int tid) {
   constexpr int BM = kBigBM, BN = kBigBN, TN = 4, WTN = 128, WTM = 32 * TM;
   const int ch = lane >> 5;
+  const bool ext = wk.rows > BM;
+  const int mx = BM + (lane & 31);  // the extra tile's row, and its features:
+  auto nlx = [&](int q) { return wn * WTN + wm * 32 + 8 * q + 4 * ch; };
   if (wk.unit >= 0) {
-    float* pp = part + (size_t)wk.unit * (BM * BN);
+    float* pp = part + (size_t)wk.unit * (kBigRowsMax * BN);
 #pragma unroll
     for (int i = 0; i < TN; ++i)
 #pragma unroll
@@ -305,8 +328,23 @@ __device__ __forceinline__ void big_store(f32x16 (&acc)[4][TM], uint16_t* ot, si
               f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
         }
       }
+    if (ext)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *(f32x4*)(pp + mx * BN + nlx(q)) =
+            f32x4{accx[4 * q], accx[4 * q + 1], accx[4 * q + 2], accx[4 * q + 3]};
     return;
   }
+  auto bias4 = [&](int nl, float* bv) __attribute__((always_inline)) {
+    bv[0] = bv[1] = bv[2] = bv[3] = 0.0f;
+    if (bias) {
+      const u32x2 bb = *(const u32x2*)(bias + (size_t)wk.e * N + wk.n0 + nl);
+      bv[0] = bf16lo(bb[0]);
+      bv[1] = bf16hi(bb[0]);
+      bv[2] = bf16lo(bb[1]);
+      bv[3] = bf16hi(bb[1]);
+    }
+  };
   constexpr int OSTR = BN + 8;  // LDS row stride in bf16 elements
   constexpr int CPR = BN / 8;   // 16-byte chunks per row
   (void)ot_bytes;  // callers static_assert BM * OSTR * 2 <= ot_bytes
@@ -335,14 +373,27 @@ __device__ __forceinline__ void big_store(f32x16 (&acc)[4][TM], uint16_t* ot, si
         }
       }
     }
+    if (ext)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float bv[4];
+        bias4(nlx(q), bv);
+        u32x2 o;
+        o[0] = pack_bf16x2(accx[4 * q] + bv[0], accx[4 * q + 1] + bv[1]);
+        o[1] = pack_bf16x2(accx[4 * q + 2] + bv[2], accx[4 * q + 3] + bv[3]);
+        *(u32x2*)(ot + mx * OSTR + nlx(q)) = o;
+      }
     __syncthreads();
-#pragma unroll 4
-    for (int c = tid; c < BM * CPR; c += NW * 64) {
+    auto zrow = [&](int c) __attribute__((always_inline)) {
       const int m = c / CPR, cc = c % CPR;
       if (m < wk.rows)
         *(u32x4*)(zout + (size_t)(wk.row0 + m) * N + wk.n0 + cc * 8) =
             *(const u32x4*)(ot + m * OSTR + cc * 8);
-    }
+    };
+#pragma unroll 4
+    for (int c = tid; c < BM * CPR; c += NW * 64) zrow(c);
+    if (ext)
+      for (int c = BM * CPR + tid; c < kBigRowsMax * CPR; c += NW * 64) zrow(c);
     __syncthreads();
   }
 #pragma unroll
@@ -374,9 +425,23 @@ __device__ __forceinline__ void big_store(f32x16 (&acc)[4][TM], uint16_t* ot, si
       }
     }
   }
+  if (ext)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float bv[4], v[4];
+      bias4(nlx(q), bv);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        v[u] = accx[4 * q + u] + bv[u];
+        if (EPI == kEpiSilu) v[u] = silu_bf16(v[u]);
+      }
+      u32x2 o;
+      o[0] = pack_bf16x2(v[0], v[1]);
+      o[1] = pack_bf16x2(v[2], v[3]);
+      *(u32x2*)(ot + mx * OSTR + nlx(q)) = o;
+    }
   __syncthreads();
-#pragma unroll 4
-  for (int c = tid; c < BM * CPR; c += NW * 64) {
+  auto orow = [&](int c) __attribute__((always_inline)) {
     const int m = c / CPR, cc = c % CPR;
     if (m < wk.rows) {
       u32x4 o = *(const u32x4*)(ot + m * OSTR + cc * 8);
@@ -389,7 +454,11 @@ __device__ __forceinline__ void big_store(f32x16 (&acc)[4][TM], uint16_t* ot, si
       }
       *(u32x4*)(out + ((size_t)wk.e * ores + wk.row0 + m) * N + wk.n0 + cc * 8) = o;
     }
-  }
+  };
+#pragma unroll 4
+  for (int c = tid; c < BM * CPR; c += NW * 64) orow(c);
+  if (ext)
+    for (int c = BM * CPR + tid; c < kBigRowsMax * CPR; c += NW * 64) orow(c);
 }
 
 // out[row][n] = epilogue(sum_k act[src(row)][k] w[e][n][k]): act rows and
@@ -422,7 +491,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
   constexpr int IPB = 16 / NW;        // DMA instructions per wave per 16 KB block
   static_assert(NW == 4 || NW == 8, "waves");
   __shared__ __align__(1024) uint16_t ring[kRSlots * kRBlk];
-  static_assert((size_t)BM * (BN + 8) * 2 <= sizeof(ring), "output tile must fit the ring");
+  static_assert((size_t)kBigRowsMax * (BN + 8) * 2 <= sizeof(ring), "output tile must fit the ring");
 
   const BigWork wk = work[blockIdx.x];
   if (wk.e < 0) return;
@@ -496,6 +565,116 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
     for (int j = 0; j < TM; ++j) acc[i][j] = f32x16{};
 
   const int ns = wk.kend - kbeg;
+  if constexpr (!WT) {
+    if (rows > BM) {
+      // A taller last tile: rows 256 .. rows-1 (at most 32) ride along in
+      // the same weight stream. The ring becomes two step buffers of four
+      // parts (weights 0-127, 128-255: 16 KB each; rows 0-127: 16 KB; rows
+      // 128-287: 20 KB, 160 LDS rows), i.e. 136 KB, so a step is in flight
+      // while one is computed; part p of a step always lands in the same
+      // place, which lets the parts differ in size. Each wave adds one 32x32
+      // MFMA tile: the extra rows x its weight slice 128 wn + 32 wm .. +31,
+      // whose A fragment it already holds (FA[wm], selected with masks: a
+      // select chain on a uniform index becomes a scratch-memory load).
+      constexpr int kPW = 128 * kRS;              // elements of a 128-row part
+      constexpr int kP3 = (128 + kBigXR) * kRS;   // elements of the tall part
+      constexpr int kBuf = 3 * kPW + kP3;
+      constexpr int kN3 = (128 + kBigXR) / 8;     // DMA instructions of the tall part
+      static_assert(2 * kBuf * 2 <= (int)sizeof(ring), "two step buffers must fit");
+      static_assert(NW == 8 && kN3 <= 3 * NW, "tall-part DMA mapping");
+      uint32_t b3[3];  // this lane's rows of the tall part (clamped to the tile)
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const int pr = 128 + (i * NW + wave) * 8 + (lane >> 3);
+        const int rr = row0 + (pr < rows ? pr : rows - 1);
+        const uint32_t tok = GATHER ? (uint32_t)sorted_token[rr] : (uint32_t)rr;
+        b3[i] = tok * (uint32_t)K + c0;
+      }
+      // this wave's DMA instructions per step: 2 IPB (weights) + IPB (rows
+      // 0-127) + its share of the kN3 instructions of the tall part
+      const int n3 = (wave < kN3 - 2 * NW) ? 3 : 2;
+      auto issue_step = [&](int step) __attribute__((always_inline)) {
+        const int koff = (kbeg + step) * kRS;
+        uint16_t* buf = ring + (step & 1) * kBuf;
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int i = 0; i < IPB; ++i)
+            dma16(wbase + (size_t)(q * 128 + i * NW * 8) * K + koff,
+                  buf + q * kPW + (i * NW + wave) * 8 * kRS);
+#pragma unroll
+        for (int i = 0; i < IPB; ++i)
+          dma16(act + boff[0][i] + koff, buf + 2 * kPW + (i * NW + wave) * 8 * kRS);
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+          if (i < n3) dma16(act + b3[i] + koff, buf + 3 * kPW + (i * NW + wave) * 8 * kRS);
+      };
+      const uint32_t pm0 = wm == 0 ? ~0u : 0u, pm1 = wm == 1 ? ~0u : 0u;
+      const uint32_t pm2 = wm == 2 ? ~0u : 0u, pm3 = wm == 3 ? ~0u : 0u;
+      auto pick = [&](const bf16x8 (&F)[4]) __attribute__((always_inline)) {
+        const u32x4 a0 = __builtin_bit_cast(u32x4, F[0]), a1 = __builtin_bit_cast(u32x4, F[1]);
+        const u32x4 a2 = __builtin_bit_cast(u32x4, F[2]), a3 = __builtin_bit_cast(u32x4, F[3]);
+        return __builtin_bit_cast(bf16x8, (a0 & pm0) | (a1 & pm1) | (a2 & pm2) | (a3 & pm3));
+      };
+      const int ch = lane >> 5;
+      // this wave's row fragments: rows wm*64 + 32 j + lane%32, in part 2 or 3
+      const int bpart = (wm * WTM) >= 128 ? 3 : 2, brow = (wm * WTM) & 127;
+      bf16x8 fa0[4], fb0[2], fx0, fa1[4], fb1[2], fx1;
+      f32x16 accx = f32x16{};
+#define MOE_XRD(step, sub, FA, FB, FX)                                                     \
+      do {                                                                                 \
+        const uint16_t* bb_ = ring + ((step) & 1) * kBuf;                                  \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                    \
+          const int r = i * 32 + (lane & 31);                                              \
+          FA[i] = *(const bf16x8*)(bb_ + wn * kPW + r * kRS + swz128(r, 2 * (sub) + ch) * 8); \
+        }                                                                                  \
+        _Pragma("unroll") for (int jj = 0; jj < 2; ++jj) {                                 \
+          const int r = brow + jj * 32 + (lane & 31);                                      \
+          FB[jj] = *(const bf16x8*)(bb_ + bpart * kPW + r * kRS + swz128(r, 2 * (sub) + ch) * 8); \
+        }                                                                                  \
+        {                                                                                  \
+          const int r = 128 + (lane & 31);                                                 \
+          FX = *(const bf16x8*)(bb_ + 3 * kPW + r * kRS + swz128(r, 2 * (sub) + ch) * 8);  \
+        }                                                                                  \
+      } while (0)
+#define MOE_XMM(FA, FB, FX)                                                                \
+      do {                                                                                 \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i)                                      \
+        _Pragma("unroll") for (int jj = 0; jj < 2; ++jj)                                   \
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[i], FB[jj], acc[i][jj], 0, 0, 0); \
+        accx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pick(FA), FX, accx, 0, 0, 0);      \
+      } while (0)
+      issue_step(0);
+      if (ns > 1) issue_step(1);
+      // step 0 landed: step 1 may be in flight
+      if (ns > 1) wait_vmcnt_le<3 * IPB>(n3); else wait_vmcnt<0>();
+      lds_barrier();
+      MOE_XRD(0, 0, fa0, fb0, fx0);
+      for (int j = 0; j < ns; ++j) {
+        MOE_XRD(j, 1, fa1, fb1, fx1);
+        MOE_XMM(fa0, fb0, fx0);
+        MOE_XRD(j, 2, fa0, fb0, fx0);
+        MOE_XMM(fa1, fb1, fx1);
+        MOE_XRD(j, 3, fa1, fb1, fx1);
+        MOE_XMM(fa0, fb0, fx0);
+        if (j + 1 < ns) {
+          // step j+1 landed, and this wave's reads of step j are done before
+          // its buffer takes step j+2
+          wait_vmcnt<0>();
+          wait_lgkmcnt0();
+          lds_barrier();
+          if (j + 2 < ns) issue_step(j + 2);
+          MOE_XRD(j + 1, 0, fa0, fb0, fx0);
+        }
+        MOE_XMM(fa1, fb1, fx1);
+      }
+#undef MOE_XRD
+#undef MOE_XMM
+      big_store<NW, TM, EPI>(acc, accx, ring, sizeof(ring), wk, bias, out, part, N, ores, zin,
+                             zout, wn, wm, lane, tid);
+      return;
+    }
+  }
   // blocks 0..9: steps 0 and 1, and the weight half of step 2
 #pragma unroll
   for (int st = 0; st < 2; ++st)
@@ -604,7 +783,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
 #undef MOE_RD
 #undef MOE_MM
 
-  big_store<NW, TM, EPI>(acc, ring, sizeof(ring), wk, bias, out, part, N, ores, zin, zout, wn, wm,
+  const f32x16 accx = f32x16{};  // no extra rows on this path
+  big_store<NW, TM, EPI>(acc, accx, ring, sizeof(ring), wk, bias, out, part, N, ores, zin, zout, wn, wm,
                          lane, tid);
 }
 

@@ -481,9 +481,9 @@ int ffn_backward_bf16(const uint16_t* x, int T, int d, int h, int E, int k,
   const uint16_t* none = nullptr;
   const dim3 gr(kTailSlots * kReduceSlices), rb(kRingWaves * 64);
 
-  // the data-gradient products (K-major weights) run plain 256-row tiles
+  // the data-gradient products (K-major weights) run on the forward's tiles
   hipLaunchKernelGGL((big_plan<kBigBM, true>), dim3(ceil_div(g1 + g2, kMaxE)), dim3(kMaxE), 0, s,
-                     offsets, E, 0, mh, d / kRS, g1, md, h / kRS, g2, hdr, list1, list2, sorted_token,
+                     offsets, E, big_xr(E), mh, d / kRS, g1, md, h / kRS, g2, hdr, list1, list2, sorted_token,
                      (int32_t*)nullptr);
   hipLaunchKernelGGL(wgrad_plan, dim3(ceil_div(nw2, 256)), dim3(256), 0, s, offsets, E, d / kWgBM, mh,
                      wl2);

@@ -565,115 +565,119 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
     for (int j = 0; j < TM; ++j) acc[i][j] = f32x16{};
 
   const int ns = wk.kend - kbeg;
-  if constexpr (!WT) {
-    if (rows > BM) {
-      // A taller last tile: rows 256 .. rows-1 (at most 32) ride along in
-      // the same weight stream. The ring becomes two step buffers of four
-      // parts (weights 0-127, 128-255: 16 KB each; rows 0-127: 16 KB; rows
-      // 128-287: 20 KB, 160 LDS rows), i.e. 136 KB, so a step is in flight
-      // while one is computed; part p of a step always lands in the same
-      // place, which lets the parts differ in size. Each wave adds one 32x32
-      // MFMA tile: the extra rows x its weight slice 128 wn + 32 wm .. +31,
-      // whose A fragment it already holds (FA[wm], selected with masks: a
-      // select chain on a uniform index becomes a scratch-memory load).
-      constexpr int kPW = 128 * kRS;              // elements of a 128-row part
-      constexpr int kP3 = (128 + kBigXR) * kRS;   // elements of the tall part
-      constexpr int kBuf = 3 * kPW + kP3;
-      constexpr int kN3 = (128 + kBigXR) / 8;     // DMA instructions of the tall part
-      static_assert(2 * kBuf * 2 <= (int)sizeof(ring), "two step buffers must fit");
-      static_assert(NW == 8 && kN3 <= 3 * NW, "tall-part DMA mapping");
-      uint32_t b3[3];  // this lane's rows of the tall part (clamped to the tile)
+  if (rows > BM) {
+    // A taller last tile: rows 256 .. rows-1 (at most 32) ride along in the
+    // same weight stream. The ring becomes two step buffers of four parts
+    // (weights 0-127, 128-255: 16 KB each; rows 0-127: 16 KB; rows 128-287:
+    // 20 KB, 160 LDS rows), i.e. 136 KB, so a step is in flight while one is
+    // computed; part p of a step always lands in the same place, which lets
+    // the parts differ in size. Each wave adds one 32x32 MFMA tile: the extra
+    // rows x its weight slice 128 wn + 32 wm .. +31, whose A fragment is one
+    // more LDS read (two transpose reads for K-major weights).
+    constexpr int kPW = 128 * kRS;              // elements of a 128-row part
+    constexpr int kP3 = (128 + kBigXR) * kRS;   // elements of the tall part
+    constexpr int kBuf = 3 * kPW + kP3;
+    constexpr int kN3 = (128 + kBigXR) / 8;     // DMA instructions of the tall part
+    static_assert(2 * kBuf * 2 <= (int)sizeof(ring), "two step buffers must fit");
+    static_assert(NW == 8 && kN3 <= 3 * NW, "tall-part DMA mapping");
+    uint32_t b3[3];  // this lane's rows of the tall part (clamped to the tile)
 #pragma unroll
-      for (int i = 0; i < 3; ++i) {
-        const int pr = 128 + (i * NW + wave) * 8 + (lane >> 3);
-        const int rr = row0 + (pr < rows ? pr : rows - 1);
-        const uint32_t tok = GATHER ? (uint32_t)sorted_token[rr] : (uint32_t)rr;
-        b3[i] = tok * (uint32_t)K + c0;
-      }
-      // this wave's DMA instructions per step: 2 IPB (weights) + IPB (rows
-      // 0-127) + its share of the kN3 instructions of the tall part
-      const int n3 = (wave < kN3 - 2 * NW) ? 3 : 2;
-      auto issue_step = [&](int step) __attribute__((always_inline)) {
-        const int koff = (kbeg + step) * kRS;
-        uint16_t* buf = ring + (step & 1) * kBuf;
+    for (int i = 0; i < 3; ++i) {
+      const int pr = 128 + (i * NW + wave) * 8 + (lane >> 3);
+      const int rr = row0 + (pr < rows ? pr : rows - 1);
+      const uint32_t tok = GATHER ? (uint32_t)sorted_token[rr] : (uint32_t)rr;
+      b3[i] = tok * (uint32_t)K + c0;
+    }
+    // this wave's DMA instructions per step: 2 IPB (weights) + IPB (rows
+    // 0-127) + its share of the kN3 instructions of the tall part
+    const int n3 = (wave < kN3 - 2 * NW) ? 3 : 2;
+    auto issue_step = [&](int step) __attribute__((always_inline)) {
+      const int koff = (kbeg + step) * kRS;
+      uint16_t* buf = ring + (step & 1) * kBuf;
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
-#pragma unroll
-          for (int i = 0; i < IPB; ++i)
-            dma16(wbase + (size_t)(q * 128 + i * NW * 8) * K + koff,
-                  buf + q * kPW + (i * NW + wave) * 8 * kRS);
+      for (int q = 0; q < 2; ++q)
 #pragma unroll
         for (int i = 0; i < IPB; ++i)
-          dma16(act + boff[0][i] + koff, buf + 2 * kPW + (i * NW + wave) * 8 * kRS);
+          dma16(WT ? wbase + (size_t)(koff + (i * NW + wave) * 4) * N + q * 128
+                   : wbase + (size_t)(q * 128 + i * NW * 8) * K + koff,
+                buf + q * kPW + (i * NW + wave) * 8 * kRS);
 #pragma unroll
-        for (int i = 0; i < 3; ++i)
-          if (i < n3) dma16(act + b3[i] + koff, buf + 3 * kPW + (i * NW + wave) * 8 * kRS);
-      };
-      const uint32_t pm0 = wm == 0 ? ~0u : 0u, pm1 = wm == 1 ? ~0u : 0u;
-      const uint32_t pm2 = wm == 2 ? ~0u : 0u, pm3 = wm == 3 ? ~0u : 0u;
-      auto pick = [&](const bf16x8 (&F)[4]) __attribute__((always_inline)) {
-        const u32x4 a0 = __builtin_bit_cast(u32x4, F[0]), a1 = __builtin_bit_cast(u32x4, F[1]);
-        const u32x4 a2 = __builtin_bit_cast(u32x4, F[2]), a3 = __builtin_bit_cast(u32x4, F[3]);
-        return __builtin_bit_cast(bf16x8, (a0 & pm0) | (a1 & pm1) | (a2 & pm2) | (a3 & pm3));
-      };
-      const int ch = lane >> 5;
-      // this wave's row fragments: rows wm*64 + 32 j + lane%32, in part 2 or 3
-      const int bpart = (wm * WTM) >= 128 ? 3 : 2, brow = (wm * WTM) & 127;
-      bf16x8 fa0[4], fb0[2], fx0, fa1[4], fb1[2], fx1;
-      f32x16 accx = f32x16{};
+      for (int i = 0; i < IPB; ++i)
+        dma16(act + boff[0][i] + koff, buf + 2 * kPW + (i * NW + wave) * 8 * kRS);
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+        if (i < n3) dma16(act + b3[i] + koff, buf + 3 * kPW + (i * NW + wave) * 8 * kRS);
+    };
+    const int ch = lane >> 5;
+    // this wave's row fragments: rows wm*64 + 32 j + lane%32, in part 2 or 3
+    const int bpart = (wm * WTM) >= 128 ? 3 : 2, brow = (wm * WTM) & 127;
+    // FX[0]: rows 256 + lane%32 (B); FX[1]: weight rows 32 wm + lane%32 of
+    // this wave's half (A)
+    bf16x8 fa0[4], fb0[2], fx0[2], fa1[4], fb1[2], fx1[2];
+    f32x16 accx = f32x16{};
 #define MOE_XRD(step, sub, FA, FB, FX)                                                     \
-      do {                                                                                 \
-        const uint16_t* bb_ = ring + ((step) & 1) * kBuf;                                  \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                    \
+    do {                                                                                   \
+      const uint16_t* bb_ = ring + ((step) & 1) * kBuf;                                    \
+      const uint16_t* wb_ = bb_ + wn * kPW;                                                \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                      \
+        if constexpr (WT) {                                                                \
+          FA[i] = tr_frag(wb_, (sub), i, lane);                                            \
+        } else {                                                                           \
           const int r = i * 32 + (lane & 31);                                              \
-          FA[i] = *(const bf16x8*)(bb_ + wn * kPW + r * kRS + swz128(r, 2 * (sub) + ch) * 8); \
+          FA[i] = *(const bf16x8*)(wb_ + r * kRS + swz128(r, 2 * (sub) + ch) * 8);         \
         }                                                                                  \
-        _Pragma("unroll") for (int jj = 0; jj < 2; ++jj) {                                 \
-          const int r = brow + jj * 32 + (lane & 31);                                      \
-          FB[jj] = *(const bf16x8*)(bb_ + bpart * kPW + r * kRS + swz128(r, 2 * (sub) + ch) * 8); \
-        }                                                                                  \
-        {                                                                                  \
-          const int r = 128 + (lane & 31);                                                 \
-          FX = *(const bf16x8*)(bb_ + 3 * kPW + r * kRS + swz128(r, 2 * (sub) + ch) * 8);  \
-        }                                                                                  \
-      } while (0)
+      }                                                                                    \
+      _Pragma("unroll") for (int jj = 0; jj < 2; ++jj) {                                   \
+        const int r = brow + jj * 32 + (lane & 31);                                        \
+        FB[jj] = *(const bf16x8*)(bb_ + bpart * kPW + r * kRS + swz128(r, 2 * (sub) + ch) * 8); \
+      }                                                                                    \
+      {                                                                                    \
+        const int r = 128 + (lane & 31);                                                   \
+        FX[0] = *(const bf16x8*)(bb_ + 3 * kPW + r * kRS + swz128(r, 2 * (sub) + ch) * 8); \
+      }                                                                                    \
+      if constexpr (WT) {                                                                  \
+        FX[1] = tr_frag(wb_, (sub), wm, lane);                                             \
+      } else {                                                                             \
+        const int r = wm * 32 + (lane & 31);                                               \
+        FX[1] = *(const bf16x8*)(wb_ + r * kRS + swz128(r, 2 * (sub) + ch) * 8);           \
+      }                                                                                    \
+    } while (0)
 #define MOE_XMM(FA, FB, FX)                                                                \
-      do {                                                                                 \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i)                                      \
-        _Pragma("unroll") for (int jj = 0; jj < 2; ++jj)                                   \
-          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[i], FB[jj], acc[i][jj], 0, 0, 0); \
-        accx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pick(FA), FX, accx, 0, 0, 0);      \
-      } while (0)
-      issue_step(0);
-      if (ns > 1) issue_step(1);
-      // step 0 landed: step 1 may be in flight
-      if (ns > 1) wait_vmcnt_le<3 * IPB>(n3); else wait_vmcnt<0>();
-      lds_barrier();
-      MOE_XRD(0, 0, fa0, fb0, fx0);
-      for (int j = 0; j < ns; ++j) {
-        MOE_XRD(j, 1, fa1, fb1, fx1);
-        MOE_XMM(fa0, fb0, fx0);
-        MOE_XRD(j, 2, fa0, fb0, fx0);
-        MOE_XMM(fa1, fb1, fx1);
-        MOE_XRD(j, 3, fa1, fb1, fx1);
-        MOE_XMM(fa0, fb0, fx0);
-        if (j + 1 < ns) {
-          // step j+1 landed, and this wave's reads of step j are done before
-          // its buffer takes step j+2
-          wait_vmcnt<0>();
-          wait_lgkmcnt0();
-          lds_barrier();
-          if (j + 2 < ns) issue_step(j + 2);
-          MOE_XRD(j + 1, 0, fa0, fb0, fx0);
-        }
-        MOE_XMM(fa1, fb1, fx1);
+    do {                                                                                   \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                        \
+      _Pragma("unroll") for (int jj = 0; jj < 2; ++jj)                                     \
+        acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[i], FB[jj], acc[i][jj], 0, 0, 0); \
+      accx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FX[1], FX[0], accx, 0, 0, 0);         \
+    } while (0)
+    issue_step(0);
+    if (ns > 1) issue_step(1);
+    // step 0 landed: step 1 may be in flight
+    if (ns > 1) wait_vmcnt_le<3 * IPB>(n3); else wait_vmcnt<0>();
+    lds_barrier();
+    MOE_XRD(0, 0, fa0, fb0, fx0);
+    for (int j = 0; j < ns; ++j) {
+      MOE_XRD(j, 1, fa1, fb1, fx1);
+      MOE_XMM(fa0, fb0, fx0);
+      MOE_XRD(j, 2, fa0, fb0, fx0);
+      MOE_XMM(fa1, fb1, fx1);
+      MOE_XRD(j, 3, fa1, fb1, fx1);
+      MOE_XMM(fa0, fb0, fx0);
+      if (j + 1 < ns) {
+        // step j+1 landed, and this wave's reads of step j are done before
+        // its buffer takes step j+2
+        wait_vmcnt<0>();
+        wait_lgkmcnt0();
+        lds_barrier();
+        if (j + 2 < ns) issue_step(j + 2);
+        MOE_XRD(j + 1, 0, fa0, fb0, fx0);
       }
+      MOE_XMM(fa1, fb1, fx1);
+    }
 #undef MOE_XRD
 #undef MOE_XMM
-      big_store<NW, TM, EPI>(acc, accx, ring, sizeof(ring), wk, bias, out, part, N, ores, zin,
-                             zout, wn, wm, lane, tid);
-      return;
-    }
+    big_store<NW, TM, EPI>(acc, accx, ring, sizeof(ring), wk, bias, out, part, N, ores, zin,
+                           zout, wn, wm, lane, tid);
+    return;
   }
   // blocks 0..9: steps 0 and 1, and the weight half of step 2
 #pragma unroll

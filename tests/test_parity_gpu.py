@@ -83,6 +83,34 @@ def test_reduced_shape_every_element(name):
     _run_and_check(SMALL[name])
 
 
+def test_taller_tiles_are_planned():
+    """The big_taller_split shape does reach the taller-tile path: the first
+    product's work list (FFN workspace from byte 256, 32-byte entries e, row0,
+    rows, n0, kbeg, kend, unit, ms) holds tiles of 257..288 rows, among them
+    K ranges of split tiles, and covers every permuted row of every expert
+    exactly once per output panel."""
+    cfg = SMALL["big_taller_split"]
+    inp = mi.make_inputs(cfg, "cuda")
+    b = run_gpu(cfg, inp)
+    R, E = int(b.offsets[-1]), cfg.E
+    nt = cfg.h // 256
+    n_ent = -(-((-(-R // 256) + min(R, E)) * nt + 256) // 8) * 8  # entries of the list
+    ent = b.ws_ffn[256:256 + 32 * n_ent].view(torch.int32).reshape(-1, 8).cpu().numpy()
+    ent = ent[ent[:, 0] >= 0]
+    assert ent[:, 2].max() > 256 and ent[:, 2].max() <= 288
+    assert ((ent[:, 2] > 256) & (ent[:, 6] >= 0)).any()
+    off = b.offsets.cpu().numpy()
+    whole = ent[(ent[:, 6] < 0) | (ent[:, 4] == 0)]  # one entry per tile
+    for e in range(E):
+        for n0 in range(0, cfg.h, 256):
+            t = whole[(whole[:, 0] == e) & (whole[:, 3] == n0)]
+            if off[e + 1] == off[e]:
+                assert len(t) == 0
+                continue
+            covered = np.sort(np.concatenate([np.arange(r0, r0 + n) for r0, n in t[:, 1:3]]))
+            assert np.array_equal(covered, np.arange(off[e], off[e + 1])), (e, n0)
+
+
 # ------------------------------------------------------------ edge cases ----
 def test_single_token():
     _run_and_check(CFG["mixtral_prefill"].with_(T=1, d=256, h=512), label="single_token")

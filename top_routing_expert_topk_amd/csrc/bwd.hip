@@ -651,30 +651,54 @@ __global__ __launch_bounds__(256) void wgate_mfma(const uint16_t* __restrict__ x
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = f32x16{};
+  // A chunk's global loads are issued a chunk ahead, into registers, so
+  // their latency hides behind the previous chunk's MFMAs.
+  u32x4 xr[4];
+  float dv[4][8];
+  auto load_chunk = [&](int t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = tid + 256 * i, r = q >> 4, c = q & 15;
+      xr[i] = *(const u32x4*)(x + (size_t)min(t + r, te - 1) * d + c0 + c * 8);
+    }
+    const int r = tid >> 2, qd = tid & 3, tr = t + r;
+    const bool vec = tr < te && e0 + 128 <= E && (E & 3) == 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int eb = e0 + qd * 32 + q * 8;
+      if (vec) {
+        const f32x4 a = *(const f32x4*)(dl + (size_t)tr * E + eb);
+        const f32x4 b = *(const f32x4*)(dl + (size_t)tr * E + eb + 4);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          dv[q][u] = a[u];
+          dv[q][4 + u] = b[u];
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          dv[q][u] = (tr < te && eb + u < E) ? dl[(size_t)tr * E + eb + u] : 0.0f;
+      }
+    }
+  };
+  if (tb < te) load_chunk(tb);
   for (int t = tb; t < te; t += 64) {
     __syncthreads();  // the previous chunk's reads are done
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int q = tid + 256 * i, r = q >> 4, c = q & 15;
-      const u32x4 v = *(const u32x4*)(x + (size_t)min(t + r, te - 1) * d + c0 + c * 8);
-      *(u32x4*)(sx + r * 128 + ((c ^ (4 * (r & 3))) << 3)) = v;
+      *(u32x4*)(sx + r * 128 + ((c ^ (4 * (r & 3))) << 3)) = xr[i];
     }
     {
-      const int r = tid >> 2, qd = tid & 3, tr = t + r;
+      const int r = tid >> 2, qd = tid & 3;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        float v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int e = e0 + qd * 32 + q * 8 + u;
-          v[u] = (tr < te && e < E) ? dl[(size_t)tr * E + e] : 0.0f;
-        }
         u32x4 hi, lo;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const uint32_t ph = pack_bf16x2(v[2 * u], v[2 * u + 1]);
+          const uint32_t ph = pack_bf16x2(dv[q][2 * u], dv[q][2 * u + 1]);
           hi[u] = ph;
-          lo[u] = pack_bf16x2(v[2 * u] - bf16lo(ph), v[2 * u + 1] - bf16hi(ph));
+          lo[u] = pack_bf16x2(dv[q][2 * u] - bf16lo(ph), dv[q][2 * u + 1] - bf16hi(ph));
         }
         const int pos = r * 128 + (((qd * 4 + q) ^ (4 * (r & 3))) << 3);
         *(u32x4*)(sdl[0] + pos) = hi;
@@ -682,6 +706,7 @@ __global__ __launch_bounds__(256) void wgate_mfma(const uint16_t* __restrict__ x
       }
     }
     __syncthreads();
+    if (t + 64 < te) load_chunk(t + 64);
     const int nsub = min(4, (te - t + 15) / 16);
     for (int sub = 0; sub < nsub; ++sub) {
       bf16x8 b[2];

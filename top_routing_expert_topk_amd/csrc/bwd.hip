@@ -438,9 +438,34 @@ __global__ __launch_bounds__(256) void gather_bwd_mfma(const uint16_t* __restric
     }
   }
 
-  // 2. router term
+  // 2. router term; a chunk's global loads are issued a chunk ahead, into
+  // registers, so their latency hides behind the previous chunk's MFMAs
   f32x16 acc[2] = {f32x16{}, f32x16{}};
   if (dlogits) {
+    u32x4 wr[4];
+    float dv[16];
+    auto load_chunk = [&](int e0) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q = tid + 256 * i, r = q >> 4, c = q & 15;
+        wr[i] = *(const u32x4*)(wg + (size_t)min(e0 + r, E - 1) * d + c0 + c * 8);
+      }
+      const int r = tid >> 2, qd = tid & 3, t = t0 + r;
+      const int eb = e0 + qd * 16;
+      if (t < Tn && eb + 16 <= E && (E & 3) == 0) {
+#pragma unroll
+        for (int u4 = 0; u4 < 4; ++u4) {
+          const f32x4 a = *(const f32x4*)(dlogits + (size_t)t * E + eb + 4 * u4);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) dv[4 * u4 + u] = a[u];
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          dv[u] = (t < Tn && eb + u < E) ? dlogits[(size_t)t * E + eb + u] : 0.0f;
+      }
+    };
+    load_chunk(0);
     for (int e0 = 0; e0 < E; e0 += 64) {
       __syncthreads();  // the previous chunk's reads are done
       // W_g rows e0 .. e0 + 63 (clamped), columns c0 .. c0 + 127: 16-byte
@@ -448,25 +473,18 @@ __global__ __launch_bounds__(256) void gather_bwd_mfma(const uint16_t* __restric
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int q = tid + 256 * i, r = q >> 4, c = q & 15;
-        const u32x4 v = *(const u32x4*)(wg + (size_t)min(e0 + r, E - 1) * d + c0 + c * 8);
-        *(u32x4*)(sm.ops.wgs + r * 128 + ((c ^ (4 * (r & 3))) << 3)) = v;
+        *(u32x4*)(sm.ops.wgs + r * 128 + ((c ^ (4 * (r & 3))) << 3)) = wr[i];
       }
       // dlogits rows t0 .. t0 + 63, experts e0 .. e0 + 63: thread (row tid / 4,
       // experts 16 (tid % 4) .. +15) -> hi and lo chunks 2 (tid % 4), +1
       {
-        const int r = tid >> 2, qd = tid & 3, t = t0 + r;
-        float v[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const int e = e0 + qd * 16 + u;
-          v[u] = (t < Tn && e < E) ? dlogits[(size_t)t * E + e] : 0.0f;
-        }
+        const int r = tid >> 2, qd = tid & 3;
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           u32x4 hi, lo;
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            const float a = v[h2 * 8 + 2 * u], b = v[h2 * 8 + 2 * u + 1];
+            const float a = dv[h2 * 8 + 2 * u], b = dv[h2 * 8 + 2 * u + 1];
             const uint32_t ph = pack_bf16x2(a, b);
             hi[u] = ph;
             lo[u] = pack_bf16x2(a - bf16lo(ph), b - bf16hi(ph));
@@ -477,6 +495,7 @@ __global__ __launch_bounds__(256) void gather_bwd_mfma(const uint16_t* __restric
         }
       }
       __syncthreads();
+      if (e0 + 64 < E) load_chunk(e0 + 64);
       const int nsub = min(4, (E - e0 + 15) / 16);
       for (int sub = 0; sub < nsub; ++sub) {
         const bf16x8 b = tr_frag(sm.ops.wgs, sub, wave, lane);
@@ -522,6 +541,18 @@ __global__ __launch_bounds__(256) void gather_bwd_mfma(const uint16_t* __restric
     }
     const int n = nlist[tt];
     int j = 0;
+    for (; j + 8 <= n; j += 8) {  // eight rows in flight, added in slot order
+      u32x4 rv[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) rv[q] = *(const u32x4*)(dxp + (size_t)list[tt][j + q] * d + c);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          a[2 * u] += bf16lo(rv[q][u]);
+          a[2 * u + 1] += bf16hi(rv[q][u]);
+        }
+    }
     for (; j + 4 <= n; j += 4) {  // four rows in flight, added in slot order
       u32x4 rv[4];
 #pragma unroll

@@ -81,7 +81,7 @@ inline RouterPlan router_plan(int T, int d, int E) {
   p.tt = tt;  // 256, 128 or 64 for E <= 512
   p.ntt = ceil_div(T > 0 ? T : 1, tt);
   p.nch = ceil_div(d, 32);
-  int s = 512 / p.ntt;
+  int s = 256 / p.ntt;  // about one block per CU: more splits cost more partial traffic
   if (s > p.nch) s = p.nch;
   if (s < 1) s = 1;
   p.split = s;

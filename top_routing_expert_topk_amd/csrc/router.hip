@@ -131,7 +131,11 @@ __device__ __forceinline__ void write_prob_partial(const float (&pacc)[8], int E
 __device__ __forceinline__ void dma16(const void* g, void* lds_base) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
-__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 // 16 consecutive 64-byte rows at one chunk land in 16 distinct bank groups.
 __device__ __forceinline__ int rswz(int r, int c) { return c ^ ((r >> 2) & 3); }
@@ -141,7 +145,17 @@ __device__ __forceinline__ int rswz(int r, int c) { return c ^ ((r >> 2) & 3); }
 // 64 bytes each, chunk c of row r at slot c ^ ((r >> 2) & 3); each DMA
 // instruction fills 16 rows, lane l writing slot l%4 of row l/4. Wave w owns
 // token tiles w, w+4, ... and every expert tile, so a token fragment is read
-// once per chunk and reused across all expert tiles.
+// once per chunk and reused across all expert tiles. A ring of NS stages
+// (as many as fit in 80 KB, so two blocks share a CU) keeps NS - 1 chunks
+// in flight: a chunk is a few MFMAs per wave, far shorter than a load.
+template <int MTW, int NTE>
+struct LogitsCfg {
+  static constexpr int ROWS = 64 * MTW + 16 * NTE;
+  static constexpr int STAGE = ROWS * RKS;  // bf16 elements
+  static constexpr int NS0 = 81920 / (STAGE * 2);
+  static constexpr int NS = NS0 < 2 ? 2 : NS0 > 4 ? 4 : NS0;
+  static constexpr size_t LDS = (size_t)NS * STAGE * 2;
+};
 // v_mfma_f32_16x16x32_bf16: A = 16 tokens x 32 k, B = 32 k x 16 experts; lane
 // l supplies row l%16, k-octet l/16 and receives D[4*(l/16)+v][l%16].
 template <int MTW, int NTE>
@@ -151,7 +165,9 @@ __global__ __launch_bounds__(256) void router_logits_bf16(
   constexpr int TT = 64 * MTW, EP = 16 * NTE;
   constexpr int ROWS = TT + EP;
   constexpr int STAGE = ROWS * RKS;
+  constexpr int NS = LogitsCfg<MTW, NTE>::NS;
   constexpr int NI = ROWS / 16;  // DMA instructions per stage (multiple of 4)
+  constexpr int IPC = NI / 4;    // of them per wave
   extern __shared__ __align__(1024) uint16_t rs[];
   const int tile = blockIdx.x / split, p = blockIdx.x % split;
   const int t0 = tile * TT;
@@ -185,14 +201,21 @@ __global__ __launch_bounds__(256) void router_logits_bf16(
     for (int n = 0; n < NTE; ++n) acc[j][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int ch = lane >> 4;
-  if (c0 < c1) issue(0, c0);
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i)
+    if (c0 + i < c1) issue(i, c0 + i);
   for (int c = c0; c < c1; ++c) {
-    const int buf = (c - c0) & 1;
-    // this wave's DMA of chunk c has landed; after the barrier every wave's
-    // has, and every wave is done reading the other buffer
-    wait_vmcnt0();
+    const int buf = (c - c0) % NS;
+    // this wave's DMA of chunk c has landed (the up to NS - 2 later chunks
+    // issued may not have); after the barrier every wave's has, and every
+    // wave is done reading the stage of chunk c - 1, which takes chunk
+    // c + NS - 1
+    const int later = min(c1 - 1 - c, NS - 2);
+    if (NS > 3 && later >= 2) wait_vm<(NS > 3 ? 2 : 0) * IPC>();
+    else if (NS > 2 && later >= 1) wait_vm<(NS > 2 ? 1 : 0) * IPC>();
+    else wait_vm<0>();
     lds_barrier();
-    if (c + 1 < c1) issue(buf ^ 1, c + 1);
+    if (c + NS - 1 < c1) issue((c - c0 + NS - 1) % NS, c + NS - 1);
     const uint16_t* sx = rs + buf * STAGE;
     const uint16_t* sw = sx + TT * RKS;
     bf16x8 a[MTW];
@@ -327,7 +350,7 @@ __global__ void fill_zero_f32(float* __restrict__ p, int n) {
 template <int MTW, int NTE>
 bool launch_logits(const RouterPlan& pl, const void* x, const void* w, int T, int d, int E,
                    float* part, hipStream_t s) {
-  const size_t lds = (size_t)2 * (64 * MTW + 16 * NTE) * RKS * 2;
+  const size_t lds = LogitsCfg<MTW, NTE>::LDS;
   if (lds > 65536 &&
       hipFuncSetAttribute((const void*)router_logits_bf16<MTW, NTE>,
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)

@@ -655,13 +655,18 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
     if (ns > 1) wait_vmcnt_le<3 * IPB>(n3); else wait_vmcnt<0>();
     lds_barrier();
     MOE_XRD(0, 0, fa0, fb0, fx0);
+    // LDS reads paired with the 9 MFMAs of a sub-step by the scheduling hint
+    constexpr int kXR = WT ? 9 : 8;
     for (int j = 0; j < ns; ++j) {
       MOE_XRD(j, 1, fa1, fb1, fx1);
       MOE_XMM(fa0, fb0, fx0);
+      interleave_mfma_reads<9, kXR>();
       MOE_XRD(j, 2, fa0, fb0, fx0);
       MOE_XMM(fa1, fb1, fx1);
+      interleave_mfma_reads<9, kXR>();
       MOE_XRD(j, 3, fa1, fb1, fx1);
       MOE_XMM(fa0, fb0, fx0);
+      interleave_mfma_reads<9, kXR>();
       if (j + 1 < ns) {
         // step j+1 landed, and this wave's reads of step j are done before
         // its buffer takes step j+2
@@ -672,6 +677,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
         MOE_XRD(j + 1, 0, fa0, fb0, fx0);
       }
       MOE_XMM(fa1, fb1, fx1);
+      interleave_mfma_reads<9, kXR>();
     }
 #undef MOE_XRD
 #undef MOE_XMM

@@ -49,8 +49,9 @@ OFFLOAD_BATCHES = 16        # distinct token batches the offload workload cycles
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20,
+                    help="untimed steps first: on a fresh process the first heavy calls run up to 30%% slower and settle after about ten")
     ap.add_argument("--config", default="mixtral_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true",

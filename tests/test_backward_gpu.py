@@ -49,6 +49,8 @@ CASES = {
     # tiles, so they are split along K
     "taller_tiles": mi.CONFIGS["deepseek_v3"].with_(name="taller_tiles", T=1100, d=512, h=256,
                                                     E=32),
+    # the same with top-2 of 32 at d = 256, h = 768 (~281 rows per expert)
+    "taller_top2": BASE.with_(name="taller_top2", T=4500, d=256, h=768, E=32),
     # top-16 of 40 (the router's largest k): as many kept slots per token as
     # the gather lists in LDS, two of the combine's passes of eight, and 40
     # experts ending in a partial 16-expert MFMA step of the router products

@@ -69,6 +69,12 @@ SMALL = {
     # tile of up to 288 rows; few tiles, so the taller tiles are split along K
     "big_taller_split": CFG["deepseek_v3"].with_(name="big_taller_split", T=1100, d=512,
                                                   h=256, E=32),
+    # taller last tiles at other widths and expert counts: 48 experts of ~267
+    # rows (d = 768, h = 512), and top-2 of 32 with ~281 rows per expert
+    "big_taller_e48": CFG["deepseek_v3"].with_(name="big_taller_e48", T=1600, d=768, h=512,
+                                                E=48),
+    "big_taller_top2": CFG["mixtral_prefill"].with_(name="big_taller_top2", T=4500, d=256,
+                                                     h=768, E=32),
     # experts of ~150 rows: persistent 256 x 128 tiles, two row blocks per expert
     "mid_rows_multi": CFG["mixtral_prefill"].with_(name="mid_rows_multi", T=600, d=512, h=1536),
     # 64 experts under a capacity of 80 rows: persistent 256 x 128 tiles, a

@@ -1,0 +1,34 @@
+"""bench.py on the host: the one-GPU contract and the traffic record lookup
+(no GPU needed)."""
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr or "--gpus 1" in r.stderr
+    assert r.stdout.strip() == ""  # no JSON line
+
+
+def test_traffic_is_used_only_for_the_current_kernel_source(tmp_path):
+    h = bench.ffn_source_hash()
+    assert len(h) == 16 and h == bench.ffn_source_hash()
+    rec = {"mixtral_prefill": {"ffn_source": h, "fetch_bytes": 3.0e9, "write_bytes": 1.0e9}}
+    p = tmp_path / "traffic.json"
+    p.write_text(json.dumps(rec))
+    assert bench.measured_traffic(str(p), "mixtral_prefill") == 4.0e9
+    assert bench.measured_traffic(str(p), "deepseek_v3") is None
+    rec["mixtral_prefill"]["ffn_source"] = "0" * 16
+    p.write_text(json.dumps(rec))
+    assert bench.measured_traffic(str(p), "mixtral_prefill") is None
+    assert bench.measured_traffic(str(tmp_path / "missing.json"), "mixtral_prefill") is None
+

@@ -92,7 +92,11 @@ def check_layer(cfg, inp, b, tokens=None, e2e_tokens=None, label=""):
     gap = srt[:, k - 1] - srt[:, k] if k < E else np.full(e2e.size, np.inf)
     clear = gap > GAP
     e_idx, _, _ = orc.route(lg_o, k, cfg.renorm)
-    assert np.array_equal(gi[e2e][clear], e_idx[clear]), f"{label}: end-to-end selection"
+    # the contract is which experts are selected: the order inside the top-k
+    # may flip between fp32 and double logits (same-logits mode above checks
+    # the order bit for bit)
+    assert np.array_equal(np.sort(gi[e2e][clear], axis=1), np.sort(e_idx[clear], axis=1)), \
+        f"{label}: end-to-end selection"
     # -- outputs on the checked tokens
     toks = sample_tokens(T, None) if tokens is None else tokens
     res = orc.moe_forward(x_h, wg_h, None, None, None, None, k, cfg.renorm, cfg.capacity,

@@ -108,3 +108,66 @@ def test_backward_mutant_is_caught(name, tmp_path):
                         os.path.join(ROOT, "tests", "test_oracle_backward.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
+
+
+# Slips in the error yardsticks that set the GPU bounds (the magnitudes of
+# backward.py and the abs_terms of oracle.py), caught by the per-element
+# definitions of tests/test_oracle_scales.py. An inflated yardstick would
+# widen a GPU bound without failing any gradient or output pin.
+SCALE_MUTANTS = {
+    "scale_dw1_inflated": ('        m["dw1"][e] = adz.T @ aX[tok]',
+                           '        m["dw1"][e] = 16.0 * (adz.T @ aX[tok])'),
+    "scale_gate_dropped": ("        ady = np.abs(gflat[slots])[:, None] * aO[tok]",
+                           "        ady = aO[tok]"),
+    "scale_z_term_dropped": ('        adz = (ady @ np.abs(W2[e])) * (np.abs(silu_grad(z)) + np.abs(z) / 8.0)\n'
+                             '        m["dw1"][e]',
+                             '        adz = (ady @ np.abs(W2[e])) * np.abs(silu_grad(z))\n'
+                             '        m["dw1"][e]'),
+    "scale_router_centring_sign": ("(ag * (m_dg + inner)).ravel()", "(ag * (m_dg - inner)).ravel()"),
+    "scale_aux_dropped": ("        m_dl = m_dl + p * (dpa + (p * dpa).sum(axis=1, keepdims=True))",
+                          "        m_dl = m_dl"),
+    "ec_scale_dw1_inflated": ('            mag["dw1"][e] = adz.T @ np.abs(X[tok])',
+                              '            mag["dw1"][e] = 16.0 * (adz.T @ np.abs(X[tok]))'),
+    "ec_scale_gate_dropped": ("            ady = np.abs(dy)", "            ady = np.abs(dO[tok])"),
+    "ec_scale_softmax_dropped": ('        mdl = p * (mag["dgate"] + (p * mag["dgate"]).sum(axis=1, keepdims=True))',
+                                 '        mdl = mag["dgate"]'),
+}
+ORC_PY = os.path.join(ROOT, "oracle", "oracle.py")
+ABS_TERMS_MUTANTS = {
+    "abs_terms_gate_dropped": ("abs_terms[pos[mine]] += gate[mine, e][:, None] * np.abs(y)",
+                               "abs_terms[pos[mine]] += np.abs(y)"),
+    "abs_terms_inflated": ("abs_terms[pos[mine]] += gate[mine, e][:, None] * np.abs(y)",
+                           "abs_terms[pos[mine]] += 16.0 * gate[mine, e][:, None] * np.abs(y)"),
+    "abs_terms_signed": ("abs_terms[pos[mine]] += gate[mine, e][:, None] * np.abs(y)",
+                         "abs_terms[pos[mine]] += gate[mine, e][:, None] * y"),
+}
+
+
+def _run_scale_pins(env):
+    return subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                           os.path.join(ROOT, "tests", "test_oracle_scales.py")],
+                          cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+
+
+@pytest.mark.parametrize("name", sorted(SCALE_MUTANTS))
+def test_scale_mutant_is_caught(name, tmp_path):
+    old, new = SCALE_MUTANTS[name]
+    src = open(BWD_SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    mut = tmp_path / "backward_mut.py"
+    mut.write_text(src.replace(old, new))
+    r = _run_scale_pins(dict(os.environ, MOE_ORACLE_BWD=str(mut), OMP_NUM_THREADS="2"))
+    assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
+
+
+@pytest.mark.parametrize("name", sorted(ABS_TERMS_MUTANTS))
+def test_abs_terms_mutant_is_caught(name, tmp_path):
+    old, new = ABS_TERMS_MUTANTS[name]
+    src = open(ORC_PY).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    mut = tmp_path / "oracle_mut.py"
+    mut.write_text(src.replace(old, new))
+    lib = os.path.join(ROOT, "oracle", "libmoe_oracle.so")
+    r = _run_scale_pins(dict(os.environ, MOE_ORACLE_PY=str(mut), MOE_ORACLE_LIB=lib,
+                             OMP_NUM_THREADS="2"))
+    assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"

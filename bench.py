@@ -7,8 +7,12 @@ steps, then K timed steps bracketed by device synchronisation. Per-call
 durations come from HIP events recorded on the same stream around every
 call of every timed step.
 
-The default workload is the Mixtral-shaped prefill layer (T=4096, d=4096,
-expert hidden 14336, 8 experts, top-2, bf16). Prints one JSON line.
+The default workload is the DeepSeek-V3-shaped routed-expert layer (T=8192,
+d=7168, expert hidden 2048, 256 experts, top-8, bf16): the largest of the
+workloads that fits one GPU. Prints one JSON line, with the dominant call
+(the grouped FFN) against both rooflines (dense bf16 MFMA at the published
+2.5 PFLOP/s and at 2.3 PFLOP/s, HBM at 8 TB/s), the binding one named in
+"bound", and the shader clock sampled during the timed steps.
 
 --backward times a training step instead: the forward (keeping the logits,
 pre-activations and hidden rows) followed by the backward calls (combine, router, grouped FFN, gather,
@@ -30,6 +34,7 @@ import numpy as np
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_BF16_ALT_TFLOPS = 2300.0  # the dense bf16 figure the workload statement quotes
 METRIC = "routed tokens/sec per MoE layer fwd (bf16, 1 GPU) + % of MFMA/HBM roofline"
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CALLS = ("router", "permute", "ffn", "combine", "aux")
@@ -52,7 +57,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20,
                     help="untimed steps first: on a fresh process the first heavy calls run up to 30%% slower and settle after about ten")
-    ap.add_argument("--config", default="mixtral_prefill")
+    ap.add_argument("--config", default="deepseek_v3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="time forward + backward (a training step) instead of the forward")
@@ -60,6 +65,11 @@ def parse():
                     help="JSON with HBM bytes per dominant-call launch from rocprofv3 counters")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a device-to-device copy of BYTES bytes (counter calibration)")
+    ap.add_argument("--summarize-counters", default="", metavar="DIR",
+                    help="only turn the rocprofv3 FETCH_SIZE / WRITE_SIZE runs under DIR (subfolders "
+                         "pmc_FETCH_SIZE, pmc_WRITE_SIZE, pmc_copy_FETCH_SIZE, pmc_copy_WRITE_SIZE) "
+                         "into the --traffic record of --config, scaled by the copy calibration "
+                         "(--copy-calibration BYTES gives its size)")
     return ap.parse_args()
 
 
@@ -82,6 +92,55 @@ def measured_traffic(path, workload):
     return rec["fetch_bytes"] + rec["write_bytes"]
 
 
+# kernels of one moe_grouped_ffn call, by name prefix
+FFN_KERNELS = ("big_plan", "gemm_bf16_ring", "gemm_bf16_pring", "big_tail_reduce", "gemm_bf16<",
+               "build_tile_map", "decode_bf16", "gemm_f32")
+
+
+def _counter_means(folder, counter):
+    """Mean value of `counter` per dispatch, per kernel name, from the rocprofv3
+    counter-collection CSV files under folder."""
+    import csv
+    import glob
+    vals = {}
+    for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        for row in csv.DictReader(open(f)):
+            if row.get("Counter_Name") != counter:
+                continue
+            name = row["Kernel_Name"]
+            for pre in ("void ", "moe::(anonymous namespace)::", "moe::"):
+                name = name.replace(pre, "")
+            vals.setdefault(name.split("(")[0], []).append(float(row["Counter_Value"]))
+    return {k: float(np.mean(v)) for k, v in vals.items()}
+
+
+def summarize_counters(folder, workload, copy_bytes, out_path):
+    """Writes the traffic record of one workload: the FFN call's HBM-side
+    bytes per call (FETCH_SIZE + WRITE_SIZE, KiB per dispatch, summed over
+    the call's kernels), each counter divided by what it reads for a plain
+    device copy of copy_bytes bytes (FETCH_SIZE counts about twice the bytes
+    a copy reads)."""
+    factor = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        cal = _counter_means(os.path.join(folder, f"pmc_copy_{c}"), c)
+        copy_kib = max(cal.values())  # the copy kernel dominates its run
+        factor[c] = copy_kib * 1024.0 / copy_bytes
+    per_kernel, tot = {}, {"FETCH_SIZE": 0.0, "WRITE_SIZE": 0.0}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        for name, kib in _counter_means(os.path.join(folder, f"pmc_{c}"), c).items():
+            b = kib * 1024.0 / factor[c]
+            per_kernel.setdefault(name, {})["fetch_bytes" if c == "FETCH_SIZE" else "write_bytes"] = b
+            if name.startswith(FFN_KERNELS):
+                tot[c] += b
+    rec = json.load(open(out_path)) if os.path.exists(out_path) else {}
+    rec[workload] = {"ffn_source": ffn_source_hash(), "fetch_bytes": tot["FETCH_SIZE"],
+                     "write_bytes": tot["WRITE_SIZE"], "fetch_factor": factor["FETCH_SIZE"],
+                     "write_factor": factor["WRITE_SIZE"], "per_kernel": per_kernel}
+    json.dump(rec, open(out_path, "w"), indent=1)
+    print(json.dumps({"workload": workload, **{k: v for k, v in rec[workload].items()
+                                                if k != "per_kernel"}}), flush=True)
+
+
 def copy_calibration(nbytes, steps):
     import torch
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
@@ -91,6 +150,49 @@ def copy_calibration(nbytes, steps):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": nbytes, "steps": steps}), flush=True)
+
+
+class ClockSampler:
+    """Samples the GPU's current graphics (shader) clock through amdsmi in a
+    background thread while the timed steps run; no figure where amdsmi is
+    absent or refused."""
+
+    def __init__(self, period_s=0.01):
+        import threading
+        self.period, self.samples, self.err = period_s, [], None
+        self._stop = threading.Event()
+        self._th = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            try:
+                h = amdsmi.amdsmi_get_processor_handles()[0]
+                while not self._stop.is_set():
+                    info = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
+                    self.samples.append(float(info["clk"]))
+                    self._stop.wait(self.period)
+            finally:
+                amdsmi.amdsmi_shut_down()
+        except Exception as exc:  # no amdsmi or no permission: report none
+            self.err = repr(exc)[:200]
+
+    def __enter__(self):
+        self._th.start()
+        return self
+
+    def __exit__(self, *a):
+        self._stop.set()
+        self._th.join(timeout=5)
+
+    def summary(self):
+        if not self.samples:
+            return {"mhz": None, "note": self.err or "no samples"}
+        v = np.array(self.samples)
+        return {"mhz": float(np.median(v)), "mean_mhz": float(v.mean()), "min_mhz": float(v.min()),
+                "max_mhz": float(v.max()), "samples": int(v.size),
+                "source": "amdsmi GFX clock every 10 ms during the timed steps (median)"}
 
 
 def cpu_model():
@@ -208,14 +310,15 @@ def bench_offload(args, cfg, inp, dev):
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     loads, touched = [], []
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(args.warmup, args.warmup + args.steps):
-        loads.append(step(i))
-        touched.append(int((bufs.counts.cpu() > 0).sum()))
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with ClockSampler() as clk:
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(args.warmup, args.warmup + args.steps):
+            loads.append(step(i))
+            touched.append(int((bufs.counts.cpu() > 0).sum()))
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     ms_step = e0.elapsed_time(e1) / args.steps
     loaded = float(np.mean(loads))
     pcie_bytes = loaded * expert_bytes
@@ -236,6 +339,7 @@ def bench_offload(args, cfg, inp, dev):
                     "pcie_peak_GBps": PCIE_GBS},
         "wall_ms_per_step": wall * 1e3 / args.steps,
         "device": torch.cuda.get_device_name(dev),
+        "sclk": clk.summary(),
     }
     print(json.dumps(out), flush=True)
 
@@ -337,11 +441,12 @@ def bench_backward(args, cfg, inp, dev):
     calls = ("forward",) + BWD_CALLS
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
               for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with ClockSampler() as clk:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(events[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     ms = {c: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in events]))
           for j, c in enumerate(calls)}
     ms_step = events[0][0].elapsed_time(events[-1][len(calls)]) / args.steps
@@ -383,6 +488,7 @@ def bench_backward(args, cfg, inp, dev):
         "ms_per_call": ms,
         "wall_ms_per_step": wall * 1e3 / args.steps,
         "device": torch.cuda.get_device_name(dev),
+        "sclk": clk.summary(),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_backward(cfg, inp, dout, BWD_CPU_SAMPLE.get(cfg.name, 64))
@@ -396,6 +502,10 @@ def main():
               "(no expert or data parallelism across GPUs); run it with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.config, args.copy_calibration or (1 << 30),
+                           args.traffic)
+        return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, args.steps)
         return
@@ -474,11 +584,12 @@ def main():
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
               for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with ClockSampler() as clk:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(events[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     nc = len(calls)
     per_call = {c: [] for c in calls}
     for ev in events:
@@ -512,6 +623,18 @@ def main():
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic
+    if cfg.dtype == "bf16":
+        # both rooflines of the call: time at 100% of each peak, and the
+        # fraction reached of each (the binding one is the longer time)
+        tflops = ffn_flop / t_ffn / 1e12
+        roof["both"] = {
+            "mfma_ms_at_peak": ffn_flop / (PEAK_BF16_TFLOPS * 1e12) * 1e3,
+            "hbm_ms_at_peak": expert_bytes / (PEAK_HBM_GBS * 1e9) * 1e3,
+            "mfma_frac": tflops / PEAK_BF16_TFLOPS,
+            "mfma_frac_at_2300": tflops / PEAK_BF16_ALT_TFLOPS,
+            "hbm_frac": expert_bytes / t_ffn / 1e9 / PEAK_HBM_GBS,
+            "ffn_ms": ms["ffn"],
+        }
     roof["kernel"] = "moe_grouped_ffn (expert GEMM1+SiLU and GEMM2, both grouped MFMA launches)"
     roof["per_launch"] = {"flop": ffn_flop, "expert_weight_bytes": expert_bytes, "rows": R,
                           "touched_experts": touched}
@@ -530,6 +653,7 @@ def main():
         "ms_per_call": ms,
         "wall_ms_per_step": wall * 1e3 / args.steps,
         "device": torch.cuda.get_device_name(dev),
+        "sclk": clk.summary(),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, CPU_SAMPLE.get(cfg.name, 64))

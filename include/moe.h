@@ -117,6 +117,23 @@ int moe_permute(const int32_t *topk_idx, int T, int k, int E, int capacity, int3
                 size_t ws_bytes, moe_stream_t stream);
 
 /*
+ * moe_permute without a workspace, for callers that cannot allocate (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): same arguments and outputs as moe_permute. Its per-chunk
+ * histograms live in a static device array of the library (4 MiB on each GPU
+ * it runs on, held until the process ends), so T*k may be at most
+ * MOE_PERMUTE_NOALLOC_MAX_ASSIGN (status MOE_ERR_UNSUPPORTED beyond). Every
+ * call on one GPU uses that GPU's one array: calls that overlap on one GPU
+ * (two streams, or two host threads) race and must be ordered by the caller.
+ * The first call on a device looks up the array's address there (no
+ * allocation); nothing in the array needs clearing between calls.
+ */
+#define MOE_PERMUTE_NOALLOC_MAX_ASSIGN (1L << 20)
+int moe_permute_noalloc(const int32_t *topk_idx, int T, int k, int E, int capacity,
+                        int32_t *counts, int32_t *offsets, int32_t *dest_row,
+                        int32_t *sorted_token, moe_stream_t stream);
+
+/*
  * Grouped expert FFN over the permuted rows   [Routing page, Expert;
  * Trilemma page 3.3, one grouped FFN per expert]:
  *   for each expert e and row r in [offsets[e], offsets[e+1]):

@@ -99,6 +99,19 @@ def test_permute_rejects_bad_arguments():
     assert L.moe_permute(BAD, 10, 2, 8, -1, BAD, BAD, BAD, BAD, BAD, 4, None) == 4
 
 
+def test_noalloc_permute_rejects_bad_arguments_and_sizes_beyond_its_array():
+    L = N.lib()
+    assert L.moe_permute_noalloc(BAD, -1, 2, 8, -1, BAD, BAD, BAD, BAD, None) == 1
+    assert L.moe_permute_noalloc(BAD, 10, 9, 8, -1, BAD, BAD, BAD, BAD, None) == 1
+    assert L.moe_permute_noalloc(BAD, 10, 2, 513, -1, BAD, BAD, BAD, BAD, None) == 2
+    assert L.moe_permute_noalloc(BAD, 10, 2, 8, -1, None, BAD, BAD, BAD, None) == 1
+    # MOE_PERMUTE_NOALLOC_MAX_ASSIGN = 2^20 assignments, refused beyond
+    header = open(N.HEADER).read()
+    assert "#define MOE_PERMUTE_NOALLOC_MAX_ASSIGN (1L << 20)" in header
+    assert L.moe_permute_noalloc(BAD, (1 << 17) + 1, 8, 512, -1, BAD, BAD, BAD, BAD, None) == 2
+    assert L.moe_permute_noalloc(BAD, 1 << 19, 4, 512, -1, BAD, BAD, BAD, BAD, None) == 2
+
+
 def test_ffn_rejects_bad_arguments():
     L = N.lib()
 

@@ -18,6 +18,8 @@
 //               chunk comes from wave ballots (lanes with the same expert),
 //               prefix over earlier waves and earlier rounds, so the order is
 //               stable in f; then dest_row / sorted_token.
+#include <mutex>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -143,25 +145,13 @@ __global__ __launch_bounds__(NTH) void permute_scatter(
   }
 }
 
-}  // namespace
-}  // namespace moe
-
-using namespace moe;
-
-extern "C" int moe_permute(const int32_t* topk_idx, int T, int k, int E, int capacity,
-                           int32_t* counts, int32_t* offsets, int32_t* dest_row,
-                           int32_t* sorted_token, void* ws, size_t ws_bytes,
-                           moe_stream_t stream) {
-  if (T < 0 || k < 1 || E < 1 || k > E) return MOE_ERR_INVALID;
-  if (E > kMaxE) return MOE_ERR_UNSUPPORTED;
-  if (!counts || !offsets) return MOE_ERR_INVALID;
+// The three kernels over a caller's workspace (per-chunk histograms and
+// bases, 2 E nb int32, every entry written before it is read).
+int permute_run(const int32_t* topk_idx, int T, int k, int E, int capacity, int32_t* counts,
+                int32_t* offsets, int32_t* dest_row, int32_t* sorted_token, int32_t* blk_hist,
+                hipStream_t s) {
   const long n = (long)T * k;
-  if (n > 0x7FFFFFFFL) return MOE_ERR_UNSUPPORTED;
-  if (n > 0 && (!topk_idx || !dest_row || !sorted_token)) return MOE_ERR_INVALID;
   const int nb = permute_blocks(n);
-  if (nb > 0 && (!ws || ws_bytes < permute_ws(T, k, E))) return MOE_ERR_WORKSPACE;
-  hipStream_t s = (hipStream_t)stream;
-  int32_t* blk_hist = (int32_t*)ws;
   int32_t* blk_base = blk_hist + (size_t)E * nb;
   if (nb > 0) hipLaunchKernelGGL(permute_hist, dim3(nb), dim3(NTH), 0, s, topk_idx, n, E, nb, blk_hist);
   // with n == 0 the scan still writes zero counts and offsets (nb == 0)
@@ -171,4 +161,79 @@ extern "C" int moe_permute(const int32_t* topk_idx, int T, int k, int E, int cap
     hipLaunchKernelGGL(permute_scatter, dim3(nb), dim3(NTH), 0, s, topk_idx, n, k, E, nb, blk_base,
                        offsets, dest_row, sorted_token);
   return launch_status();
+}
+
+int permute_check(const int32_t* topk_idx, int T, int k, int E, int32_t* counts,
+                  int32_t* offsets, int32_t* dest_row, int32_t* sorted_token) {
+  if (T < 0 || k < 1 || E < 1 || k > E) return MOE_ERR_INVALID;
+  if (E > kMaxE) return MOE_ERR_UNSUPPORTED;
+  if (!counts || !offsets) return MOE_ERR_INVALID;
+  const long n = (long)T * k;
+  if (n > 0x7FFFFFFFL) return MOE_ERR_UNSUPPORTED;
+  if (n > 0 && (!topk_idx || !dest_row || !sorted_token)) return MOE_ERR_INVALID;
+  return MOE_OK;
+}
+
+// The allocation-free variant's histograms: a file-scope device array, one
+// copy per GPU, sized for MOE_PERMUTE_NOALLOC_MAX_ASSIGN assignments at the
+// largest E. Host code never passes the array's name to a kernel (in host
+// code it is a stand-in, not a device address): each device's address is
+// looked up once, with that device current, and kept.
+constexpr long kNoallocAssign = MOE_PERMUTE_NOALLOC_MAX_ASSIGN;
+constexpr size_t kNoallocInts = (size_t)2 * kMaxE * (kNoallocAssign / kPermuteChunk);
+static_assert(kNoallocAssign % kPermuteChunk == 0, "whole chunks");
+__device__ __align__(256) int32_t scratch[kNoallocInts];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch[kMaxDevices] = {};
+
+// This device's copy of scratch, or nullptr if it cannot be found.
+int32_t* scratch_on(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !p) return nullptr;
+    g_scratch[dev] = (int32_t*)p;
+  }
+  return g_scratch[dev];
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int moe_permute(const int32_t* topk_idx, int T, int k, int E, int capacity,
+                           int32_t* counts, int32_t* offsets, int32_t* dest_row,
+                           int32_t* sorted_token, void* ws, size_t ws_bytes,
+                           moe_stream_t stream) {
+  const int st = permute_check(topk_idx, T, k, E, counts, offsets, dest_row, sorted_token);
+  if (st != MOE_OK) return st;
+  const int nb = permute_blocks((long)T * k);
+  if (nb > 0 && (!ws || ws_bytes < permute_ws(T, k, E))) return MOE_ERR_WORKSPACE;
+  return permute_run(topk_idx, T, k, E, capacity, counts, offsets, dest_row, sorted_token,
+                     (int32_t*)ws, (hipStream_t)stream);
+}
+
+extern "C" int moe_permute_noalloc(const int32_t* topk_idx, int T, int k, int E, int capacity,
+                                   int32_t* counts, int32_t* offsets, int32_t* dest_row,
+                                   int32_t* sorted_token, moe_stream_t stream) {
+  const int st = permute_check(topk_idx, T, k, E, counts, offsets, dest_row, sorted_token);
+  if (st != MOE_OK) return st;
+  if ((long)T * k > kNoallocAssign) return MOE_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  int dev = -1;
+  if (s ? hipStreamGetDevice(s, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess)
+    return MOE_ERR_LAUNCH;
+  int32_t* hist = scratch_on(dev);
+  if (!hist) return MOE_ERR_LAUNCH;
+  return permute_run(topk_idx, T, k, E, capacity, counts, offsets, dest_row, sorted_token, hist,
+                     s);
 }

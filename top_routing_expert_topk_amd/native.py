@@ -50,6 +50,7 @@ def lib():
         L.moe_workspace_size.restype = Z
         L.moe_router_topk.argtypes = [P, I, I, I, P, P, I, I, I, P, P, P, P, P, Z, P]
         L.moe_permute.argtypes = [P, I, I, I, I, P, P, P, P, P, Z, P]
+        L.moe_permute_noalloc.argtypes = [P, I, I, I, I, P, P, P, P, P]
         L.moe_grouped_ffn.argtypes = [P, I, I, I, I, I, I, P, P, P, P, P, P, P, P, Z, P]
         L.moe_combine.argtypes = [P, I, P, P, I, I, I, P, P, I, P]
         L.moe_aux_loss.argtypes = [P, P, I, I, P, P, P, P]
@@ -70,7 +71,8 @@ def lib():
                                             P]
         L.moe_gather_backward.argtypes = [P, I, P, I, I, I, P, P, P, I, P, P]
         L.moe_router_weight_backward.argtypes = [P, I, I, I, I, P, P, P, P, Z, P]
-        for f in ("moe_router_topk", "moe_permute", "moe_grouped_ffn", "moe_combine",
+        for f in ("moe_router_topk", "moe_permute", "moe_permute_noalloc", "moe_grouped_ffn",
+                  "moe_combine",
                   "moe_aux_loss", "moe_expert_choice", "moe_cache_init", "moe_cache_step",
                   "moe_cache_slot_of", "moe_grouped_ffn_cached", "moe_combine_backward",
                   "moe_router_backward", "moe_grouped_ffn_backward", "moe_gather_backward",
@@ -145,6 +147,13 @@ def moe_permute(topk_idx, T, k, E, capacity, counts, offsets, dest_row, sorted_t
     _check("moe_permute", lib().moe_permute(
         _p(topk_idx), T, k, E, int(capacity), _p(counts), _p(offsets), _p(dest_row),
         _p(sorted_token), _p(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_permute_noalloc(topk_idx, T, k, E, capacity, counts, offsets, dest_row, sorted_token,
+                        stream=None):
+    _check("moe_permute_noalloc", lib().moe_permute_noalloc(
+        _p(topk_idx), T, k, E, int(capacity), _p(counts), _p(offsets), _p(dest_row),
+        _p(sorted_token), _stream(stream)))
 
 
 def moe_grouped_ffn(x, T, d, h, E, k, offsets, sorted_token, w1, b1, w2, b2, y_perm, ws,

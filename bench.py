@@ -550,7 +550,7 @@ def main():
                           inp["b1"], inp["w2"], inp["b2"], b.y_perm, b.ws_ffn, stream)
         if ev is not None:
             ev[3].record(stream)
-        N.moe_combine(b.y_perm, b.dest_row, b.gate, T, E, d, resid, b.out, stream)
+        N.moe_combine(b.y_perm, x.dtype, b.dest_row, b.gate, T, E, d, resid, b.out, stream)
         if ev is not None:
             ev[4].record(stream)
 
@@ -572,7 +572,7 @@ def main():
                           inp["w2"], inp["b2"], b.y_perm, b.ws_ffn, stream)
         if ev is not None:
             ev[3].record(stream)
-        N.moe_combine(b.y_perm, b.dest_row, b.topk_gate, T, k, d, resid, b.out, stream)
+        N.moe_combine(b.y_perm, x.dtype, b.dest_row, b.topk_gate, T, k, d, resid, b.out, stream)
         if ev is not None:
             ev[4].record(stream)
         N.moe_aux_loss(b.prob_sum, b.counts, T, E, b.f, b.P, b.loss, stream)

@@ -29,8 +29,9 @@
  *     validated on the host before anything is launched; on a non-zero status
  *     nothing was enqueued, except for MOE_ERR_LAUNCH.
  *   - dtype is MOE_F32 or MOE_BF16 and applies to x, the weights, the expert
- *     biases, y_perm, residual and out. Logits, gates, probability sums, f, P
- *     and the loss are always fp32; indices and offsets are int32.
+ *     biases and residual; out is fp32 or, for bf16 layers, optionally bf16.
+ *     The expert outputs y_perm, logits, gates, probability sums, f, P and
+ *     the loss are always fp32; indices and offsets are int32.
  *   - Inputs must be finite: NaN or Inf in x or the weights is outside the
  *     contract.
  *   - Results are deterministic: every sum has a fixed order and no kernel
@@ -140,9 +141,10 @@ int moe_permute_noalloc(const int32_t *topk_idx, int T, int k, int E, int capaci
  *     H[r]      = SiLU(W1[e] . x[sorted_token[r]] + b1[e]),  SiLU(z) = z/(1+e^-z)
  *     y_perm[r] = W2[e] . H[r] + b2[e]
  * x [T][d]; w1 [E][h][d]; b1 [E][h] or NULL; w2 [E][d][h]; b2 [E][d] or
- * NULL; y_perm [T*k][d] (rows 0..R-1 written, R = offsets[E] read on the
- * device). fp32 accumulation; with MOE_BF16, H and y_perm are rounded to
- * bf16. offsets and sorted_token come from moe_permute with the same T, k, E,
+ * NULL; y_perm [T*k][d] fp32 for both dtypes (rows 0..R-1 written, R =
+ * offsets[E] read on the device). fp32 accumulation; with MOE_BF16, H is
+ * rounded to bf16 (the second product's operand) and y_perm keeps the fp32
+ * accumulation, so no rounding sits between it and the combine. offsets and sorted_token come from moe_permute with the same T, k, E,
  * or from moe_expert_choice with k = ceil(E * min(C, T) / T) (any k with
  * R <= T*k). The kernel choice depends only on T*k (no device-to-host read).
  * bf16 needs d and h to be multiples of 64. Workspace holds H:
@@ -160,8 +162,8 @@ int moe_grouped_ffn(const void *x, int dtype, int T, int d, int h, int E, int k,
  *   out[t] = (residual ? residual[t] : 0)
  *            + sum_{j=0..k-1, dest_row[t,j] >= 0} topk_gate[t,j] * y_perm[dest_row[t,j]]
  * summed in fp32 in ascending j, then stored as out_dtype. A token with every
- * slot dropped gets residual[t] (or 0). y_perm [T*k][d] and residual [T][d]
- * (or NULL) are `dtype`; dest_row [T][k]; topk_gate [T][k] fp32; out [T][d]
+ * slot dropped gets residual[t] (or 0). y_perm [T*k][d] is fp32 (as
+ * moe_grouped_ffn writes it) and residual [T][d] (or NULL) is `dtype`; dest_row [T][k]; topk_gate [T][k] fp32; out [T][d]
  * is `out_dtype`: MOE_F32 (always allowed; keeps the fp32 sum unrounded) or
  * MOE_BF16 (only with dtype MOE_BF16). 1 <= k <= 512: with the slots of
  * moe_expert_choice (k = E) a token sums its choosing experts in ascending
@@ -237,7 +239,7 @@ int moe_cache_slot_of(const void *state, int32_t *slot_of, int32_t *phase_of);
  * computed (run phase 0 while the misses are copied, then phase 1 after
  * the copy stream's work). bf16 only, decode-size batches (T*k <= 4*E and
  * <= 1024, the weight-streaming path): status 2 otherwise. Same workspace
- * as moe_grouped_ffn.
+ * as moe_grouped_ffn; y_perm fp32 as there.
  */
 int moe_grouped_ffn_cached(const void *x, int dtype, int T, int d, int h, int E, int k,
                            const int32_t *offsets, const int32_t *sorted_token,
@@ -275,7 +277,8 @@ int moe_aux_loss(const float *prob_sum, const int32_t *counts, int T, int E, flo
  * Combine backward: for every kept slot (t, j) (r = dest_row[t*k+j] >= 0)
  *   dy_perm[r] = topk_gate[t,j] * dout[t]          (dtype, [T*k][d] rows)
  *   dgate[t,j] = sum_i dout[t,i] * y_perm[r,i]     (fp32, fixed-order sum)
- * and dgate = 0 for dropped slots. y_perm: the forward's expert outputs.
+ * and dgate = 0 for dropped slots. y_perm: the forward's expert outputs,
+ * fp32 [T*k][d] for both dtypes; dout [T][d] is `dtype`.
  * k <= 512 (Expert Choice layouts included).
  */
 int moe_combine_backward(const void *y_perm, int dtype, const int32_t *dest_row,

@@ -237,6 +237,24 @@ def _scales(X, Wg, W1, B1, W2, dO, lg, idx, gate, dest, st, offsets, slot_of_row
         np.add.at(m_dx, tok, adz @ np.abs(W1[e]))
         m_dg[slots] = (aO[tok] * np.abs(y_rows[r0:r1])).sum(axis=1)
     m_dg = m_dg.reshape(T, k)
+    m_dl = _router_scales(lg, idx, gate, m_dg, renorm, counts, daux)
+    m_dx += m_dl @ np.abs(Wg)
+    m.update(dx=m_dx, dw_gate=m_dl.T @ aX, dgate_bias=m_dl.sum(axis=0) if has_gate_bias else None,
+             dgate=m_dg, dlogits=m_dl)
+    if not has_b2:
+        m["db2"] = None
+    if B1 is None:
+        m["db1"] = None
+    return m
+
+
+def _router_scales(lg, idx, gate, m_dg, renorm, counts, daux):
+    """Magnitude of dlogits [T, E] from the magnitude m_dg [T, k] of the
+    gate gradients: the gate and aux-loss backward of ``gate_grad`` and
+    ``aux_grad`` run on absolute values (the centring term added, not
+    subtracted)."""
+    T, E = lg.shape
+    k = idx.shape[1]
     ag = np.abs(gate)
     rows = np.repeat(np.arange(T), k)
     m_dl = np.zeros((T, E))
@@ -252,14 +270,52 @@ def _scales(X, Wg, W1, B1, W2, dO, lg, idx, gate, dest, st, offsets, slot_of_row
         p = softmax(lg)
         dpa = np.broadcast_to(abs(daux) * E * counts.astype(np.float64) / (float(T) * T), (T, E))
         m_dl = m_dl + p * (dpa + (p * dpa).sum(axis=1, keepdims=True))
-    m_dx += m_dl @ np.abs(Wg)
-    m.update(dx=m_dx, dw_gate=m_dl.T @ aX, dgate_bias=m_dl.sum(axis=0) if has_gate_bias else None,
-             dgate=m_dg, dlogits=m_dl)
-    if not has_b2:
-        m["db2"] = None
-    if B1 is None:
-        m["db1"] = None
-    return m
+    return m_dl
+
+
+def router_backward_all(x, w_gate, fetch, k: int, renorm: bool, capacity: int, dout,
+                        daux: float, lg, gate_bias=None):
+    """The router's gradients over every token, for layers too large for
+    ``moe_backward``: dgate [T, k], dlogits [T, E], dW_g [E, d] and db_g [E]
+    (None without a router bias), each a (value, magnitude) pair with the
+    magnitude as in ``_scales``.
+
+    The gate gradient of a kept slot (t, j) is <dout[t], y>, y the forward
+    output of token t in its j-th expert; y comes from the forward oracle's
+    ``expert_rows``, one expert at a time over all of its rows (fetch(e) ->
+    (w1e, b1e, w2e, b2e) gives the expert's weights). The rest is
+    ``gate_grad`` and ``aux_grad`` on all T rows, then logits = x W_g^T + b_g
+    backwards.
+    """
+    X = widen(x)
+    dO = widen(dout)
+    T = X.shape[0]
+    E = np.asarray(w_gate).shape[0]
+    lg = np.asarray(lg, dtype=np.float64)
+    idx, gate, _ = fwd.route(lg, k, renorm)
+    counts, offsets, dest, st = fwd.permute(idx, E, capacity)
+    R = int(offsets[E])
+    slot_of_row = np.empty(R, np.int64)
+    kept = np.nonzero(dest >= 0)[0]
+    slot_of_row[dest[kept]] = kept
+    dgate = np.zeros(T * k)
+    m_dg = np.zeros(T * k)
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        tok = st[r0:r1]
+        y = fwd.expert_rows(x, tok, *fetch(e))
+        dgate[slot_of_row[r0:r1]] = (dO[tok] * y).sum(axis=1)
+        m_dg[slot_of_row[r0:r1]] = (np.abs(dO[tok]) * np.abs(y)).sum(axis=1)
+    dgate, m_dg = dgate.reshape(T, k), m_dg.reshape(T, k)
+    dl = gate_grad(lg, idx, gate, dgate, renorm)
+    if daux:
+        dl = dl + aux_grad(lg, counts, daux)
+    m_dl = _router_scales(lg, idx, gate, m_dg, renorm, counts, daux)
+    return dict(dgate=(dgate, m_dg), dlogits=(dl, m_dl), dw_gate=(dl.T @ X, m_dl.T @ np.abs(X)),
+                dgate_bias=None if gate_bias is None else (dl.sum(axis=0), m_dl.sum(axis=0)),
+                counts=counts, offsets=offsets, idx=idx)
 
 
 def moe_backward_sampled(x, w_gate, fetch, k: int, renorm: bool, capacity: int, dout, daux: float,

@@ -279,7 +279,6 @@ def moe_forward_ec(x, w_gate, w1, b1, w2, b2, C: int, gate_bias=None, residual: 
         out = xr[tokens].copy()
     else:
         out = np.zeros((tokens.size, d), np.float64)
-    abs_terms = np.zeros((tokens.size, d), np.float64)  # sum_e gate * |y_e|, an error scale
     for e in range(E):  # ascending expert order for every token
         rows = sorted_token[offsets[e]:offsets[e + 1]]
         mine = rows[pos[rows] >= 0]
@@ -293,9 +292,8 @@ def moe_forward_ec(x, w_gate, w1, b1, w2, b2, C: int, gate_bias=None, residual: 
             b2e = None if b2 is None else b2[e]
         y = expert_rows(x, mine, w1e, b1e, w2e, b2e)
         out[pos[mine]] += gate[mine, e][:, None] * y
-        abs_terms[pos[mine]] += gate[mine, e][:, None] * np.abs(y)
     return dict(logits=lg, p=p, score=sel, offsets=offsets, sorted_token=sorted_token,
-                dest_row=dest, gate=gate, out=out, abs_terms=abs_terms, tokens=tokens)
+                dest_row=dest, gate=gate, out=out, tokens=tokens)
 
 
 def _bf16_to_f64(a) -> np.ndarray:

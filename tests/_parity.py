@@ -7,7 +7,12 @@ double-precision logits must pick the same experts on every token whose
 k-th / (k+1)-th logit gap exceeds 1e-3. Outputs are compared element by
 element on the checked tokens: max |err| <= 1e-5 * RMS (fp32 layers) or
 2e-2 * RMS (bf16 layers), RMS taken over the oracle outputs of the checked
-tokens. Gates: 1e-6 (fp32) / 1e-5 (bf16) absolute. Aux: f and loss within
+tokens; out is fp32 (the product contract for bf16 layers too). A second
+run of the same layer that stores out in bf16 must hold exactly the first
+run's fp32 out rounded to nearest even; its error against the oracle is
+reported next to the floor any bf16 storage has (the oracle's output rounded
+once), which at 10^7 - 10^8 elements reaches most of the 2e-2 * RMS bar by
+itself. Gates: 1e-6 (fp32) / 1e-5 (bf16) absolute. Aux: f and loss within
 1e-5 relative, P exact.
 """
 import numpy as np
@@ -53,8 +58,12 @@ def expert_fetcher(inp):
     return fetch
 
 
-def check_layer(cfg, inp, b, tokens=None, e2e_tokens=None, label=""):
-    """Every comparison of one layer run; returns a dict of the measured errors."""
+def check_layer(cfg, inp, b, tokens=None, e2e_tokens=None, label="", b_bf16=None):
+    """Every comparison of one layer run; returns a dict of the measured errors.
+
+    ``b_bf16``: optional second run of the same layer with a bf16 ``out``;
+    its routing must equal the first run's and its out be the first run's
+    fp32 out rounded to bf16."""
     tol = TOL[cfg.dtype]
     T, E, k = cfg.T, cfg.E, cfg.k
     lg = _np(b.logits)
@@ -107,6 +116,20 @@ def check_layer(cfg, inp, b, tokens=None, e2e_tokens=None, label=""):
     rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
     out_err = float(np.abs(got - ref).max()) if ref.size else 0.0
     assert out_err <= tol["out"] * rms, f"{label}: out max err {out_err} vs {tol['out']}*RMS {rms}"
-    return dict(gate_err=gate_err, f_err=f_err, logit_err=logit_err, out_err=out_err, rms=rms,
-                out_rel=out_err / rms if rms else 0.0, rows=R, drops=int((dest < 0).sum()),
-                unclear=int((~clear).sum()), checked_tokens=int(toks.size))
+    r = dict(gate_err=gate_err, f_err=f_err, logit_err=logit_err, out_err=out_err, rms=rms,
+             out_rel=out_err / rms if rms else 0.0, rows=R, drops=int((dest < 0).sum()),
+             unclear=int((~clear).sum()), checked_tokens=int(toks.size))
+    if b_bf16 is not None:
+        # bf16 storage of out: the same fp32 sums, rounded to nearest even
+        assert b_bf16.out.dtype == torch.bfloat16
+        assert np.array_equal(_np(b_bf16.topk_idx), gi), f"{label}: bf16-output run routed apart"
+        assert torch.equal(b_bf16.out, b.out.to(torch.bfloat16)), \
+            f"{label}: bf16 out is not the fp32 out rounded"
+        # reported, not asserted: against the plain bar, and the floor that
+        # any bf16 storage of out has (the oracle's output rounded once)
+        got16 = _out64(b_bf16.out)[toks]
+        exact16 = torch.from_numpy(ref).to(torch.bfloat16).double().numpy()
+        if rms:
+            r["bf16_out_rel"] = float(np.abs(got16 - ref).max()) / rms
+            r["bf16_rounding_floor_rel"] = float(np.abs(exact16 - ref).max()) / rms
+    return r

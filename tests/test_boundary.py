@@ -163,8 +163,9 @@ def test_expert_choice_rejects_bad_arguments():
 def test_binding_refuses_host_tensors():
     import torch
     x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    y = torch.zeros(4, 64, dtype=torch.float32)
     with pytest.raises(ValueError):
-        N.moe_combine(x, x, x, 4, 1, 64, None, x)
+        N.moe_combine(y, x.dtype, x, x, 4, 1, 64, None, x)
 
 
 def test_backward_workspace_sizes():

@@ -6,13 +6,9 @@ so offsets, sorted_token, dest_row and gates must be bit-exact. The GPU's
 scores must match the oracle's double softmax of the same logits within
 1e-6, and the oracle's double scores must choose the same tokens for every
 expert whose C-th / (C+1)-th score gap exceeds 1e-6. Outputs are compared
-element by element on the checked tokens: |err| <= 1e-5 * RMS (fp32 layers);
-for bf16 layers |err| <= 2e-2 * RMS + 2^-7 * sum_e gate * |y_e| at that
-element. The second term is the bf16 rounding of H and Y (2^-9 relative
-each, with room for the fp32 sum order): an Expert Choice token without a
-residual can sum a few large-output experts with small gates, so one
-rounded term can exceed 2e-2 of the output RMS (E = 512, C = 3: a CPU
-emulation of the same roundings reaches 2.8% of the RMS).
+element by element on every token: max |err| <= 1e-5 * RMS (fp32 layers) or
+2e-2 * RMS (bf16 layers), the bar of the token-choice layers (the expert
+outputs reach the combine in fp32; H is the only rounded intermediate).
 """
 import numpy as np
 import pytest
@@ -82,11 +78,10 @@ def check_ec(cfg, inp, b, C, tokens=None, label=""):
     rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
     err = np.abs(got - ref)
     out_err = float(err.max()) if ref.size else 0.0
-    bound = tol["out"] * rms + (2.0 ** -7 * res["abs_terms"] if cfg.dtype == "bf16" else 0.0)
-    worst = float((err - bound).max()) if ref.size else 0.0
-    assert worst <= 0, f"{label}: out err {out_err} exceeds its bound by {worst} (RMS {rms})"
+    assert out_err <= tol["out"] * rms, f"{label}: out err {out_err} vs {tol['out']}*RMS {rms}"
     return dict(score_err=score_err, out_err=out_err, rms=rms, unclear=unclear,
-                rows=E * Cc, uncovered=int(((dest >= 0).sum(axis=1) == 0).sum()))
+                rows=E * Cc, uncovered=int(((dest >= 0).sum(axis=1) == 0).sum()),
+                bar_ratio=out_err / (tol["out"] * rms) if rms else 0.0)
 
 
 def _run(cfg, C=None, nsample=None, mutate=None, label=None):
@@ -103,10 +98,12 @@ def _run(cfg, C=None, nsample=None, mutate=None, label=None):
     return inp, b, r
 
 
+@pytest.mark.timeout(600)
 def test_full_switch_shaped_workload():
-    """Switch-shaped layer with the Zipf-skewed router: every expert takes
-    exactly 80 tokens although token choice would drop ~60% of assignments."""
-    _, b, r = _run(EC, nsample=256)
+    """Switch-shaped layer with the Zipf-skewed router, every token: every
+    expert takes exactly 80 tokens although token choice would drop ~60% of
+    assignments."""
+    _, b, r = _run(EC)
     assert r["rows"] == EC.E * EC.capacity
 
 

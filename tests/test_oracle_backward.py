@@ -278,6 +278,33 @@ def test_sampled_backward_matches_the_whole_one():
             np.testing.assert_allclose(sm["db2"][e][0], full["db2"][e], rtol=1e-12, atol=1e-13)
 
 
+def test_router_backward_over_every_token_matches_the_whole_one():
+    """router_backward_all, which takes each expert's outputs from the forward
+    oracle's expert_rows, gives moe_backward's dgate, dlogits, dW_g and db_g
+    and their magnitudes, in both gate modes, with drops, a router bias and
+    the aux term."""
+    for renorm, k, cap, gb, daux in ((True, 2, 9, False, 0.7), (False, 1, 6, True, 0.7),
+                                     (True, 3, -1, True, 0.0), (False, 2, 0, False, 0.3)):
+        p, dout = _layer(95 + k, 30, 8, 12, 5, gb)
+        lg = orc.logits(p["x"], p["w_gate"], p.get("gate_bias"))
+        full = bwd.moe_backward(p["x"], p["w_gate"], p["w1"], p["b1"], p["w2"], p["b2"], k,
+                                renorm, cap, dout, daux, gate_bias=p.get("gate_bias"), lg=lg,
+                                want_scale=True)
+        fetch = lambda e: (p["w1"][e], p["b1"][e], p["w2"][e], p["b2"][e])  # noqa: E731
+        rb = bwd.router_backward_all(p["x"], p["w_gate"], fetch, k, renorm, cap, dout, daux, lg,
+                                     gate_bias=p.get("gate_bias"))
+        sc = full["scale"]
+        names = ("dgate", "dlogits", "dw_gate") + (("dgate_bias",) if gb else ())
+        for name in names:
+            v, m = rb[name]
+            np.testing.assert_allclose(v, full[name], rtol=1e-10, atol=1e-12, err_msg=name)
+            np.testing.assert_allclose(m, sc[name], rtol=1e-10, atol=1e-12, err_msg=name)
+        if not gb:
+            assert rb["dgate_bias"] is None
+        if cap == 0:
+            assert not np.any(rb["dgate"][0])
+
+
 # ------------------------------------------------------------ Expert Choice --
 
 def _ec_loss(p, dout, C, res):

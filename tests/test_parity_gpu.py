@@ -1,9 +1,9 @@
 """GPU parity: the HIP path through the C-ABI against the CPU oracle.
 
 Full-size workloads are checked on every routing / permutation / aux output
-and on a seeded sample of tokens' outputs; reduced shapes that still span
-several tiles and a ragged tail are checked on every output element; the
-edge cases cover ties, capacity 0, k = E, E = 1, a single hot expert, the
+and on every token's output (out in fp32; a bf16 out must be the fp32 out
+rounded); reduced shapes that still span several tiles and a ragged tail are
+checked on every output element; the edge cases cover ties, capacity 0, k = E, E = 1, a single hot expert, the
 largest E and k, T = 0, missing biases and run-to-run determinism.
 """
 import numpy as np
@@ -18,30 +18,33 @@ pytestmark = pytest.mark.gpu
 CFG = mi.CONFIGS
 
 
-def _run_and_check(cfg, nsample=None, e2e=None, mutate=None, label=None):
+def _run_and_check(cfg, nsample=None, e2e=None, mutate=None, label=None, bf16_out=False):
     print(f"[parity] {label or cfg.name}: T={cfg.T} d={cfg.d} h={cfg.h} E={cfg.E} k={cfg.k} "
           f"cap={cfg.capacity} {cfg.dtype}", flush=True)
     inp = mi.make_inputs(cfg, "cuda")
     if mutate:
         mutate(inp)
     b = run_gpu(cfg, inp)
+    b16 = run_gpu(cfg, inp, out_dtype=torch.bfloat16) if bf16_out else None
     toks = sample_tokens(cfg.T, nsample, seed=cfg.cfg_id)
     e2e_t = sample_tokens(cfg.T, e2e, seed=cfg.cfg_id + 100)
-    r = check_layer(cfg, inp, b, tokens=toks, e2e_tokens=e2e_t, label=label or cfg.name)
+    r = check_layer(cfg, inp, b, tokens=toks, e2e_tokens=e2e_t, label=label or cfg.name,
+                    b_bf16=b16)
     print(f"[parity] {label or cfg.name}: {r}", flush=True)
     return inp, b, r
 
 
 # ------------------------------------------------------- full workloads ----
-@pytest.mark.parametrize("name,nsample,e2e", [
-    ("tiny_fp32", None, None),
-    ("mixtral_prefill", 24, 1024),
-    ("switch_top1_cap", 256, None),
-    ("decode", None, None),
-    ("deepseek_v3", 24, 1024),
-])
-def test_full_workload(name, nsample, e2e):
-    _run_and_check(CFG[name], nsample, e2e)
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["tiny_fp32", "mixtral_prefill", "switch_top1_cap", "decode",
+                                  "deepseek_v3"])
+def test_full_workload(name):
+    """Every token of the full layer, logits chosen end to end included; the
+    bf16 layers run a second time with out stored in bf16, which must be the
+    fp32 out rounded (its distance to the oracle is reported). The oracle visits each expert once for all its rows
+    (about a minute for the 8192 x 8 DeepSeek-shaped layer on 16 threads)."""
+    cfg = CFG[name]
+    _run_and_check(cfg, bf16_out=cfg.dtype == "bf16")
 
 
 # ------------------------------------------- reduced shapes, every element ----
@@ -195,24 +198,12 @@ def test_empty_batch():
     assert torch.all(ps == 0) and torch.all(counts == 0) and torch.all(offsets == 0)
 
 
-def test_bf16_output_within_rounding_bound():
-    """out stored as bf16: the 2e-2 * RMS bound plus the final rounding's own bound,
-    half an ulp of bf16 (2^-8 relative) of the exact value."""
-    import numpy as np
-    from _parity import expert_fetcher
-    from oracle import oracle as orc
-    cfg = SMALL["mixtral_small"]
-    inp = mi.make_inputs(cfg, "cuda")
-    b = run_gpu(cfg, inp, out_dtype=torch.bfloat16)
-    assert b.out.dtype == torch.bfloat16
-    lg = b.logits.cpu().numpy()
-    res = orc.moe_forward(mi.to_host_array(inp["x"]), mi.to_host_array(inp["w_gate"]), None, None,
-                          None, None, cfg.k, cfg.renorm, cfg.capacity, lg=lg,
-                          expert_weights=expert_fetcher(inp))
-    ref = res["out"]
-    got = b.out.float().cpu().numpy().astype(np.float64)
-    rms = float(np.sqrt(np.mean(ref ** 2)))
-    assert np.all(np.abs(got - ref) <= 2e-2 * rms + 2.0 ** -8 * np.abs(ref))
+@pytest.mark.parametrize("name", ["mixtral_small", "switch_small", "deepseek_small",
+                                  "bn64_small", "big_ragged", "mid_rows_capacity"])
+def test_bf16_output_is_the_rounded_fp32_output(name):
+    """out stored as bf16 on reduced shapes: every element is the fp32-output
+    run's value rounded to nearest even (the fp32 run meets the bar)."""
+    _run_and_check(SMALL[name], label=f"{name}_bf16_out", bf16_out=True)
 
 
 @pytest.mark.parametrize("E,k", [(8, 2), (100, 3), (130, 1), (200, 4), (300, 2), (400, 6),
@@ -221,3 +212,22 @@ def test_router_expert_counts(E, k):
     """Every expert-tile shape of the bf16 router (E padded to 64, 128, ..., 512)."""
     cfg = CFG["deepseek_v3"].with_(T=300, d=320, h=64, E=E, k=k)
     _run_and_check(cfg, label=f"router_E{E}_k{k}")
+
+
+@pytest.mark.parametrize("T,E,k,d,bias", [(4100, 256, 8, 448, False), (2048, 512, 16, 256, True),
+                                          (4096, 256, 1, 320, True), (8192, 256, 8, 7168, False)])
+def test_router_at_scale(T, E, k, d, bias):
+    """The bf16 router at thousands of tokens and 256 or 512 experts: a ragged
+    last token tile, the largest k, a router bias, and the DeepSeek-shaped
+    width. Logits, every token's selection (same logits: bit-exact; end to
+    end: where the gap is clear), gates, the permutation and the aux
+    statistics against the oracle; the FFN outputs of these shapes are not
+    what is tested here."""
+    cfg = CFG["deepseek_v3"].with_(name=f"router_T{T}_E{E}", T=T, d=d, h=256, E=E, k=k,
+                                   zipf_gate_bias=bias)
+    print(f"[parity] {cfg.name}: T={T} d={d} E={E} k={k} bias={bias}", flush=True)
+    inp = mi.make_inputs(cfg, "cuda")
+    b = run_gpu(cfg, inp)
+    r = check_layer(cfg, inp, b, tokens=np.zeros(0, np.int32),
+                    e2e_tokens=sample_tokens(T, 2048, seed=7))
+    print(f"[parity] {cfg.name}: {r}", flush=True)

@@ -108,9 +108,10 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
 // for the dropped ones, so a layer with many slots per token (Expert Choice:
 // one per expert, most of them empty) pays one coalesced read of its dest
 // row instead of a dependent read per slot. vec: d % 8 == 0 (8 elements per
-// thread per pass).
+// thread per pass). y (the forward's expert outputs) is fp32; dout and dy
+// are the layer's dtype T.
 template <typename T>
-__global__ __launch_bounds__(256) void combine_bwd(const T* __restrict__ y,
+__global__ __launch_bounds__(256) void combine_bwd(const float* __restrict__ y,
                                                    const int32_t* __restrict__ dest,
                                                    const float* __restrict__ gate, int k, int d,
                                                    const T* __restrict__ dout, T* __restrict__ dy,
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(256) void combine_bwd(const T* __restrict__ y,
         float a[8], b[8][8];
         load8<T>(go + c, a);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) load8<T>(y + (size_t)krow[q + u] * d + c, b[u]);
+        for (int u = 0; u < 8; ++u) load8<float>(y + (size_t)krow[q + u] * d + c, b[u]);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           float o[8];
@@ -187,14 +188,14 @@ __global__ __launch_bounds__(256) void combine_bwd(const T* __restrict__ y,
   for (; q < nk; ++q) {  // one slot per pass
     const int j = kept[q], r = krow[q];
     const float g = gate[(size_t)t * k + j];
-    const T* yr = y + (size_t)r * d;
+    const float* yr = y + (size_t)r * d;
     T* dr = dy + (size_t)r * d;
     float dot = 0.0f;
     if (vec) {
       for (int c = tid * 8; c < d; c += 256 * 8) {
         float a[8], b[8], o[8];
         load8<T>(go + c, a);
-        load8<T>(yr + c, b);
+        load8<float>(yr + c, b);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           dot = fmaf(a[u], b[u], dot);
@@ -205,7 +206,7 @@ __global__ __launch_bounds__(256) void combine_bwd(const T* __restrict__ y,
     } else {
       for (int c = tid; c < d; c += 256) {
         const float a = ld1<T>(go + c);
-        dot = fmaf(a, ld1<T>(yr + c), dot);
+        dot = fmaf(a, yr[c], dot);
         st1<T>(dr + c, g * a);
       }
     }
@@ -819,7 +820,7 @@ extern "C" int moe_combine_backward(const void* y_perm, int dtype, const int32_t
   hipStream_t s = (hipStream_t)stream;
   const bool vec = (d % 8) == 0;
   if (dtype == MOE_BF16)
-    hipLaunchKernelGGL(combine_bwd<uint16_t>, dim3(T), dim3(256), 0, s, (const uint16_t*)y_perm,
+    hipLaunchKernelGGL(combine_bwd<uint16_t>, dim3(T), dim3(256), 0, s, (const float*)y_perm,
                        dest_row, topk_gate, k, d, (const uint16_t*)dout, (uint16_t*)dy_perm, dgate,
                        vec);
   else

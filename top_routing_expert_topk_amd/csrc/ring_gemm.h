@@ -110,10 +110,13 @@ __device__ __forceinline__ void interleave_mfma_reads() {
 }
 
 // Epilogues of a tile: out = acc + bias, SiLU(acc + bias), or acc * SiLU'(z)
-// with z read from a second [rows][N] array (the backward of the activation).
+// with z read from a second [rows][N] array (the backward of the activation),
+// all three stored as bf16; kEpiBiasF32 stores acc + bias in fp32 (the
+// expert outputs Y of the forward, which the combine sums unrounded).
 constexpr int kEpiBias = 0;
 constexpr int kEpiSilu = 1;
 constexpr int kEpiDSilu = 2;
+constexpr int kEpiBiasF32 = 3;
 
 // MFMA operand fragment of a K-major weight block in LDS (64 k-rows x 128
 // features, 256-byte rows, chunk c of row k at c ^ 4 (k % 4)): lane l gets
@@ -305,7 +308,7 @@ template <int NW, int TM, int EPI>
 __device__ __forceinline__ void big_store(f32x16 (&acc)[4][TM], const f32x16& accx,
                                           uint16_t* ot, size_t ot_bytes,
                                           const BigWork& wk, const uint16_t* __restrict__ bias,
-                                          uint16_t* __restrict__ out, float* __restrict__ part,
+                                          void* __restrict__ outv, float* __restrict__ part,
                                           int N, int ores, const uint16_t* __restrict__ zin,
                                           uint16_t* __restrict__ zout, int wn, int wm, int lane,
                                           int tid) {
@@ -345,6 +348,39 @@ __device__ __forceinline__ void big_store(f32x16 (&acc)[4][TM], const f32x16& ac
       bv[3] = bf16hi(bb[1]);
     }
   };
+  if constexpr (EPI == kEpiBiasF32) {
+    // fp32 rows straight from the accumulators, like the partials: each
+    // store puts 32 bytes into each of 32 rows, and the four q passes fill
+    // 128 contiguous bytes of every row
+    float* out = (float*)outv;
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int nl = wn * WTN + i * 32 + 8 * q + 4 * ch;
+        float bv[4];
+        bias4(nl, bv);
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+          const int m = wm * WTM + j * 32 + (lane & 31);
+          if (m < wk.rows)
+            *(f32x4*)(out + ((size_t)wk.e * ores + wk.row0 + m) * N + wk.n0 + nl) =
+                f32x4{acc[i][j][4 * q] + bv[0], acc[i][j][4 * q + 1] + bv[1],
+                      acc[i][j][4 * q + 2] + bv[2], acc[i][j][4 * q + 3] + bv[3]};
+        }
+      }
+    if (ext && mx < wk.rows)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float bv[4];
+        bias4(nlx(q), bv);
+        *(f32x4*)(out + ((size_t)wk.e * ores + wk.row0 + mx) * N + wk.n0 + nlx(q)) =
+            f32x4{accx[4 * q] + bv[0], accx[4 * q + 1] + bv[1], accx[4 * q + 2] + bv[2],
+                  accx[4 * q + 3] + bv[3]};
+      }
+    return;
+  }
+  uint16_t* out = (uint16_t*)outv;
   constexpr int OSTR = BN + 8;  // LDS row stride in bf16 elements
   constexpr int CPR = BN / 8;   // 16-byte chunks per row
   (void)ot_bytes;  // callers static_assert BM * OSTR * 2 <= ot_bytes
@@ -482,7 +518,7 @@ template <int NW, bool GATHER, int EPI, bool WT = false>
 __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ sorted_token,
     const BigWork* __restrict__ work, const uint16_t* __restrict__ w,
-    const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, float* __restrict__ part, int N,
+    const uint16_t* __restrict__ bias, void* __restrict__ out, float* __restrict__ part, int N,
     int K, size_t wes, int ores, const uint16_t* __restrict__ zin, uint16_t* __restrict__ zout) {
   constexpr int BM = kBigBM, BN = kBigBN;
   constexpr int WM = NW / 2;          // waves along the permuted rows (2 along the weight rows)
@@ -808,7 +844,7 @@ __global__ __launch_bounds__(256) void big_tail_reduce(const BigHdr* __restrict_
                                                        const BigWork* __restrict__ work,
                                                        const uint16_t* __restrict__ bias,
                                                        const float* __restrict__ part,
-                                                       uint16_t* __restrict__ out, int N,
+                                                       void* __restrict__ out, int N,
                                                        const uint16_t* __restrict__ zin,
                                                        uint16_t* __restrict__ zout) {
   const BigHdr sp = *hdr;
@@ -833,6 +869,12 @@ __global__ __launch_bounds__(256) void big_tail_reduce(const BigHdr* __restrict_
       v[0] += lo[0]; v[1] += lo[1]; v[2] += lo[2]; v[3] += lo[3];
       v[4] += hi[0]; v[5] += hi[1]; v[6] += hi[2]; v[7] += hi[3];
     }
+    if constexpr (EPI == kEpiBiasF32) {
+      float* o = (float*)out + (size_t)(tile.row0 + m) * N + tile.n0 + nl;
+      *(f32x4*)o = f32x4{v[0] + bv[0], v[1] + bv[1], v[2] + bv[2], v[3] + bv[3]};
+      *(f32x4*)(o + 4) = f32x4{v[4] + bv[4], v[5] + bv[5], v[6] + bv[6], v[7] + bv[7]};
+      continue;
+    }
     u32x4 o, z, pre;
     if (EPI == kEpiDSilu) z = *(const u32x4*)(zin + (size_t)(tile.row0 + m) * N + tile.n0 + nl);
 #pragma unroll
@@ -848,7 +890,7 @@ __global__ __launch_bounds__(256) void big_tail_reduce(const BigHdr* __restrict_
       }
       o[q] = pack_bf16x2(a, c);
     }
-    *(u32x4*)(out + (size_t)(tile.row0 + m) * N + tile.n0 + nl) = o;
+    *(u32x4*)((uint16_t*)out + (size_t)(tile.row0 + m) * N + tile.n0 + nl) = o;
     if (EPI == kEpiSilu && zout) *(u32x4*)(zout + (size_t)(tile.row0 + m) * N + tile.n0 + nl) = pre;
   }
 }

@@ -41,7 +41,7 @@ class MoEBuffers:
         self.offsets = torch.empty((E + 1,), dtype=i32, device=dev)
         self.dest_row = torch.empty((T * k,), dtype=i32, device=dev)
         self.sorted_token = torch.empty((T * k,), dtype=i32, device=dev)
-        self.y_perm = torch.empty((T * k, d), dtype=self.dtype, device=dev)
+        self.y_perm = torch.empty((T * k, d), dtype=f32, device=dev)  # fp32 expert outputs
         self.out = torch.empty((T, d), dtype=self.out_dtype, device=dev)
         self.f = torch.empty((E,), dtype=f32, device=dev)
         self.P = torch.empty((E,), dtype=f32, device=dev)
@@ -82,8 +82,8 @@ def moe_layer_forward(x, w_gate, gate_bias, w1, b1, w2, b2, k, renorm=True, capa
     else:
         N.moe_grouped_ffn(x, T, d, h, E, k, b.offsets, b.sorted_token, w1, b1, w2, b2, b.y_perm,
                           b.ws_ffn, stream)
-    N.moe_combine(b.y_perm, b.dest_row, b.topk_gate, T, k, d, x if residual else None, b.out,
-                  stream)
+    N.moe_combine(b.y_perm, x.dtype, b.dest_row, b.topk_gate, T, k, d, x if residual else None,
+                  b.out, stream)
     N.moe_aux_loss(b.prob_sum, b.counts, T, E, b.f, b.P, b.loss, stream)
     return b
 
@@ -122,7 +122,7 @@ class ECBuffers:
         self.sorted_token = torch.empty((max(E * self.Cc, 1),), dtype=i32, device=dev)
         self.dest_row = torch.empty((T, E), dtype=i32, device=dev)
         self.gate = torch.empty((T, E), dtype=f32, device=dev)
-        self.y_perm = torch.empty((T * self.k_ffn, d), dtype=self.dtype, device=dev)
+        self.y_perm = torch.empty((T * self.k_ffn, d), dtype=f32, device=dev)
         self.out = torch.empty((T, d), dtype=self.out_dtype, device=dev)
         self.z_perm = self.h_perm = None
         if self.train:
@@ -158,7 +158,8 @@ def moe_layer_forward_ec(x, w_gate, gate_bias, w1, b1, w2, b2, C, residual=False
     else:
         N.moe_grouped_ffn(x, T, d, h, E, b.k_ffn, b.offsets, b.sorted_token, w1, b1, w2, b2,
                           b.y_perm, b.ws_ffn, stream)
-    N.moe_combine(b.y_perm, b.dest_row, b.gate, T, E, d, x if residual else None, b.out, stream)
+    N.moe_combine(b.y_perm, x.dtype, b.dest_row, b.gate, T, E, d, x if residual else None, b.out,
+                  stream)
     return b
 
 
@@ -233,7 +234,8 @@ def moe_layer_forward_cached(x, w_gate, gate_bias, cache: ExpertCache, k, renorm
             s.wait_event(ready)
         N.moe_grouped_ffn_cached(x, T, d, h, E, k, b.offsets, b.sorted_token, cache.slot_of,
                                  cache.phase_of, phase, w1s, b1s, w2s, b2s, b.y_perm, b.ws_ffn, s)
-    N.moe_combine(b.y_perm, b.dest_row, b.topk_gate, T, k, d, x if residual else None, b.out, s)
+    N.moe_combine(b.y_perm, x.dtype, b.dest_row, b.topk_gate, T, k, d, x if residual else None,
+                  b.out, s)
     N.moe_aux_loss(b.prob_sum, b.counts, T, E, b.f, b.P, b.loss, s)
     return b
 

@@ -163,9 +163,11 @@ def moe_grouped_ffn(x, T, d, h, E, k, offsets, sorted_token, w1, b1, w2, b2, y_p
         _p(b2), _p(y_perm), _p(ws), _nbytes(ws), _stream(stream)))
 
 
-def moe_combine(y_perm, dest_row, topk_gate, T, k, d, residual, out, stream=None):
+def moe_combine(y_perm, dtype, dest_row, topk_gate, T, k, d, residual, out, stream=None):
+    """y_perm: fp32 expert outputs; dtype: the layer's torch dtype (that of
+    x and of residual)."""
     _check("moe_combine", lib().moe_combine(
-        _p(y_perm), _dt(y_perm), _p(dest_row), _p(topk_gate), T, k, d, _p(residual), _p(out),
+        _p(y_perm), _DTYPE[dtype], _p(dest_row), _p(topk_gate), T, k, d, _p(residual), _p(out),
         _dt(out), _stream(stream)))
 
 
@@ -244,7 +246,7 @@ def moe_grouped_ffn_cached(x, T, d, h, E, k, offsets, sorted_token, slot_of, pha
 def moe_combine_backward(y_perm, dest_row, topk_gate, T, k, d, dout, dy_perm, dgate,
                          stream=None):
     _check("moe_combine_backward", lib().moe_combine_backward(
-        _p(y_perm), _dt(y_perm), _p(dest_row), _p(topk_gate), T, k, d, _p(dout), _p(dy_perm),
+        _p(y_perm), _dt(dout), _p(dest_row), _p(topk_gate), T, k, d, _p(dout), _p(dy_perm),
         _p(dgate), _stream(stream)))
 
 

@@ -153,11 +153,12 @@ def copy_calibration(nbytes, steps):
 
 
 class ClockSampler:
-    """Samples the GPU's current graphics (shader) clock through amdsmi in a
-    background thread while the timed steps run; no figure where amdsmi is
-    absent or refused."""
+    """Samples amdsmi's GPU metrics table in a background thread: the current
+    shader clock of every XCD (current_gfxclks). The firmware refreshes that
+    table about once a second, so a sample only describes the load if the
+    table was refreshed while the load ran; see clock_window."""
 
-    def __init__(self, period_s=0.01):
+    def __init__(self, period_s=0.02):
         import threading
         self.period, self.samples, self.err = period_s, [], None
         self._stop = threading.Event()
@@ -170,8 +171,12 @@ class ClockSampler:
             try:
                 h = amdsmi.amdsmi_get_processor_handles()[0]
                 while not self._stop.is_set():
-                    info = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
-                    self.samples.append(float(info["clk"]))
+                    m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                    xcd = [float(v) for v in (m.get("current_gfxclks") or [])
+                           if isinstance(v, (int, float)) and 0 < v < 65535]
+                    if xcd:
+                        self.samples.append((time.perf_counter(), m.get("system_clock_counter"),
+                                             float(np.mean(xcd)), min(xcd), max(xcd)))
                     self._stop.wait(self.period)
             finally:
                 amdsmi.amdsmi_shut_down()
@@ -186,13 +191,40 @@ class ClockSampler:
         self._stop.set()
         self._th.join(timeout=5)
 
-    def summary(self):
-        if not self.samples:
-            return {"mhz": None, "note": self.err or "no samples"}
-        v = np.array(self.samples)
-        return {"mhz": float(np.median(v)), "mean_mhz": float(v.mean()), "min_mhz": float(v.min()),
-                "max_mhz": float(v.max()), "samples": int(v.size),
-                "source": "amdsmi GFX clock every 10 ms during the timed steps (median)"}
+    def summary(self, t_load):
+        """Table refreshes first seen at least 0.25 s after the load began."""
+        seen, upd = set(), []
+        for t, cnt, mean, lo, hi in self.samples:
+            if cnt in seen:
+                continue
+            seen.add(cnt)
+            if t >= t_load + 0.25:
+                upd.append((mean, lo, hi))
+        if not upd:
+            return {"mhz": None, "note": self.err or "no table refresh during the load"}
+        v = np.array(upd)
+        return {"mhz": float(np.median(v[:, 0])), "mean_mhz": float(v[:, 0].mean()),
+                "min_xcd_mhz": float(v[:, 1].min()), "max_xcd_mhz": float(v[:, 2].max()),
+                "refreshes": int(len(upd)),
+                "source": "amdsmi gpu_metrics current_gfxclks (mean of the 8 XCDs, table "
+                          "refreshed ~1/s) while the same step runs for 3 s after the timed "
+                          "steps; median over the refreshes"}
+
+
+def clock_window(step, seconds=3.0):
+    """Runs step() back to back for `seconds` (untimed, after the timed
+    region) and returns the shader clock the metrics table reported meanwhile."""
+    import torch
+    with ClockSampler() as clk:
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < seconds:
+            step()
+            n += 1
+            if n % 8 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+    return clk.summary(t0)
 
 
 def cpu_model():
@@ -310,15 +342,16 @@ def bench_offload(args, cfg, inp, dev):
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     loads, touched = [], []
-    with ClockSampler() as clk:
-        t0 = time.perf_counter()
-        e0.record(stream)
-        for i in range(args.warmup, args.warmup + args.steps):
-            loads.append(step(i))
-            touched.append(int((bufs.counts.cpu() > 0).sum()))
-        e1.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.warmup, args.warmup + args.steps):
+        loads.append(step(i))
+        touched.append(int((bufs.counts.cpu() > 0).sum()))
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ctr = iter(range(args.warmup + args.steps, 1 << 30))
+    sclk = clock_window(lambda: step(next(ctr)))
     ms_step = e0.elapsed_time(e1) / args.steps
     loaded = float(np.mean(loads))
     pcie_bytes = loaded * expert_bytes
@@ -339,7 +372,7 @@ def bench_offload(args, cfg, inp, dev):
                     "pcie_peak_GBps": PCIE_GBS},
         "wall_ms_per_step": wall * 1e3 / args.steps,
         "device": torch.cuda.get_device_name(dev),
-        "sclk": clk.summary(),
+        "sclk": sclk,
     }
     print(json.dumps(out), flush=True)
 
@@ -441,12 +474,12 @@ def bench_backward(args, cfg, inp, dev):
     calls = ("forward",) + BWD_CALLS
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
               for _ in range(args.steps)]
-    with ClockSampler() as clk:
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            step(events[i])
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    sclk = clock_window(step)
     ms = {c: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in events]))
           for j, c in enumerate(calls)}
     ms_step = events[0][0].elapsed_time(events[-1][len(calls)]) / args.steps
@@ -488,7 +521,7 @@ def bench_backward(args, cfg, inp, dev):
         "ms_per_call": ms,
         "wall_ms_per_step": wall * 1e3 / args.steps,
         "device": torch.cuda.get_device_name(dev),
-        "sclk": clk.summary(),
+        "sclk": sclk,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_backward(cfg, inp, dout, BWD_CPU_SAMPLE.get(cfg.name, 64))
@@ -584,12 +617,12 @@ def main():
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
               for _ in range(args.steps)]
-    with ClockSampler() as clk:
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            step(events[i])
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    sclk = clock_window(step)
     nc = len(calls)
     per_call = {c: [] for c in calls}
     for ev in events:
@@ -653,7 +686,7 @@ def main():
         "ms_per_call": ms,
         "wall_ms_per_step": wall * 1e3 / args.steps,
         "device": torch.cuda.get_device_name(dev),
-        "sclk": clk.summary(),
+        "sclk": sclk,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, CPU_SAMPLE.get(cfg.name, 64))

@@ -74,8 +74,33 @@ const char *moe_status_string(int status);
 int moe_version(void);
 
 /*
+ * Host-side check of the permutation arrays   [Routing page, counting sort
+ * of the MoELayer dispatch; capacity section for the drops]. All pointers
+ * are HOST pointers; any of the three arrays may be NULL:
+ *   offsets [E+1]: offsets[0] = 0, non-decreasing, R = offsets[E] <= T*k;
+ *   sorted_token [R] (needs offsets): every entry in [0, T);
+ *   dest_row [T*k]: every entry -1 or in [0, R) (R = T*k without offsets);
+ *   with all three: each row 0..R-1 is the row of exactly one slot i
+ *   (dest_row[i] = r) and sorted_token[r] = i / k, the slot's token.
+ * The token-choice layout has k slots per token; the Expert Choice layout
+ * has E (k = E). Returns MOE_OK or MOE_ERR_INVALID; reads nothing else,
+ * writes nothing. A library built with MOE_HOST_BOUNDS_CHECK runs these
+ * checks on the device arrays (copied to the host after synchronising the
+ * stream) at the top of moe_grouped_ffn, moe_grouped_ffn_train,
+ * moe_grouped_ffn_cached, moe_combine, moe_combine_backward,
+ * moe_grouped_ffn_backward and moe_gather_backward, and returns
+ * MOE_ERR_INVALID instead of launching on bad arrays.
+ */
+int moe_check_permutation(const int32_t *offsets, int E, const int32_t *sorted_token,
+                          const int32_t *dest_row, int T, int k);
+
+/* 1 in a library built with MOE_HOST_BOUNDS_CHECK (the debug build), else 0. */
+int moe_debug_checks(void);
+
+/*
  * Workspace bytes that call `op` needs for these sizes (dtype-independent
- * upper bound; d, h unused by some ops). Returns 0 for a bad op or size.
+ * upper bound; d, h unused by some ops). Returns 0 for a bad op or size,
+ * E > 512 included.
  */
 size_t moe_workspace_size(int op, int T, int d, int h, int E, int k);
 

@@ -32,3 +32,21 @@ def test_traffic_is_used_only_for_the_current_kernel_source(tmp_path):
     assert bench.measured_traffic(str(p), "mixtral_prefill") is None
     assert bench.measured_traffic(str(tmp_path / "missing.json"), "mixtral_prefill") is None
 
+
+
+def test_clock_summary_keeps_table_refreshes_seen_during_the_load():
+    """The metrics table refreshes about once a second: repeated reads of one
+    refresh count once, and refreshes first seen before the load (plus a
+    quarter second) are left out."""
+    import bench
+    c = bench.ClockSampler()
+    t0 = 100.0
+    # (time, table counter, mean, min, max of the XCD clocks)
+    c.samples = [(99.9, 1, 95.0, 90.0, 100.0), (100.1, 1, 95.0, 90.0, 100.0),
+                 (100.2, 2, 1500.0, 1490.0, 1510.0), (100.5, 3, 1900.0, 1800.0, 2000.0),
+                 (100.6, 3, 1900.0, 1800.0, 2000.0), (101.5, 4, 2000.0, 1950.0, 2050.0)]
+    s = c.summary(t0)
+    assert s["refreshes"] == 2 and s["mhz"] == 1950.0
+    assert s["min_xcd_mhz"] == 1800.0 and s["max_xcd_mhz"] == 2050.0
+    c.samples = c.samples[:2]
+    assert c.summary(t0)["mhz"] is None

@@ -38,6 +38,12 @@ def test_workspace_sizes():
     assert ffn >= 4096 * 2 * 14336 * 2
     assert N.moe_workspace_size(7, 10, 10, 10, 4, 2) == 0
     assert N.moe_workspace_size(N.MOE_OP_FFN, 10, 0, 10, 4, 2) == 0
+    # more experts than any call takes (the host-sanitized build found the
+    # router's plan dividing by a zero-row token tile there)
+    for op in range(5):
+        assert N.moe_workspace_size(op, 0, 64, 128, 513, 2) == 0
+        assert N.moe_workspace_size(op, 100, 64, 128, 513, 2) == 0
+        assert N.moe_workspace_size(op, 100, 64, 128, 512, 2) > 0
 
 
 def _ceil(a, b):

@@ -818,6 +818,7 @@ extern "C" int moe_combine_backward(const void* y_perm, int dtype, const int32_t
   if (T == 0) return MOE_OK;
   if (!y_perm || !dest_row || !topk_gate || !dout || !dy_perm || !dgate) return MOE_ERR_INVALID;
   hipStream_t s = (hipStream_t)stream;
+  MOE_DEBUG_CHECK(s, nullptr, 1, nullptr, dest_row, T, k);
   const bool vec = (d % 8) == 0;
   if (dtype == MOE_BF16)
     hipLaunchKernelGGL(combine_bwd<uint16_t>, dim3(T), dim3(256), 0, s, (const float*)y_perm,
@@ -856,6 +857,7 @@ extern "C" int moe_gather_backward(const void* dx_perm, int dtype, const int32_t
   if (T == 0) return MOE_OK;
   if (!dx_perm || !dest_row || !dx || (dlogits && !w_gate)) return MOE_ERR_INVALID;
   hipStream_t s = (hipStream_t)stream;
+  MOE_DEBUG_CHECK(s, nullptr, 1, nullptr, dest_row, T, k);
   if (dtype == MOE_BF16 && (d % kGmCols) == 0) {
     hipLaunchKernelGGL(gather_bwd_mfma, dim3(ceil_div(T, kGmTok), d / kGmCols), dim3(256), 0, s,
                        (const uint16_t*)dx_perm, dest_row, T, k, d,

@@ -185,6 +185,7 @@ extern "C" int moe_combine(const void* y_perm, int dtype, const int32_t* dest_ro
   if (T == 0) return MOE_OK;
   if (!y_perm || !dest_row || !topk_gate || !out) return MOE_ERR_INVALID;
   hipStream_t s = (hipStream_t)stream;
+  MOE_DEBUG_CHECK(s, nullptr, 1, nullptr, dest_row, T, k);
   const int nb = ceil_div(T, kCombineWaves);
   if (dtype == MOE_BF16 && k > kMaxK) {
     if (out_dtype == MOE_BF16)

@@ -768,6 +768,7 @@ extern "C" int moe_grouped_ffn(const void* x, int dtype, int T, int d, int h, in
   const int st = ffn_check(x, dtype, T, d, h, E, k, offsets, sorted_token, w1, w2, y_perm, ws,
                            ws_bytes);
   if (st != MOE_OK || (long)T * k == 0) return st;
+  MOE_DEBUG_CHECK((hipStream_t)stream, offsets, E, sorted_token, nullptr, T, k);
   void* H = (unsigned char*)ws + ffn_plan_bytes(T, d, h, E, k);
   return grouped_ffn(x, dtype, T, d, h, E, k, offsets, sorted_token, w1, b1, w2, b2, y_perm, ws,
                      H, nullptr, (hipStream_t)stream);
@@ -782,6 +783,7 @@ extern "C" int moe_grouped_ffn_train(const void* x, int dtype, int T, int d, int
                            ws_bytes);
   if (st != MOE_OK || (long)T * k == 0) return st;
   if (!z_perm || !h_perm) return MOE_ERR_INVALID;
+  MOE_DEBUG_CHECK((hipStream_t)stream, offsets, E, sorted_token, nullptr, T, k);
   return grouped_ffn(x, dtype, T, d, h, E, k, offsets, sorted_token, w1, b1, w2, b2, y_perm, ws,
                      h_perm, z_perm, (hipStream_t)stream);
 }
@@ -802,6 +804,7 @@ extern "C" int moe_grouped_ffn_cached(const void* x, int dtype, int T, int d, in
   if (!x || !offsets || !sorted_token || !slot_of || !phase_of || !w1 || !w2 || !y_perm)
     return MOE_ERR_INVALID;
   if (!ws || ws_bytes < ffn_ws(T, d, h, E, k)) return MOE_ERR_WORKSPACE;
+  MOE_DEBUG_CHECK((hipStream_t)stream, offsets, E, sorted_token, nullptr, T, k);
   void* H = (unsigned char*)ws + ffn_plan_bytes(T, d, h, E, k);
   return launch_decode((const uint16_t*)x, sorted_token, offsets, (const uint16_t*)w1,
                        (const uint16_t*)b1, (const uint16_t*)w2, (const uint16_t*)b2,

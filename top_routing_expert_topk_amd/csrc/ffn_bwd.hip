@@ -559,6 +559,7 @@ extern "C" int moe_grouped_ffn_backward(const void* x, int dtype, int T, int d, 
   if ((z_perm == nullptr) != (h_perm == nullptr)) return MOE_ERR_INVALID;
   if (!ws || ws_bytes < ffn_bwd_layout(T, d, h, E, k).total) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
+  MOE_DEBUG_CHECK(s, offsets, E, rows > 0 ? sorted_token : nullptr, nullptr, T, k);
   if (dtype == MOE_F32)
     return ffn_backward_f32((const float*)x, T, d, h, E, k, offsets, sorted_token,
                             (const float*)w1, (const float*)b1, (const float*)w2,

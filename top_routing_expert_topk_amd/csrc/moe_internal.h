@@ -56,6 +56,24 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 
 // ---- host helpers ----------------------------------------------------------
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Debug builds (MOE_HOST_BOUNDS_CHECK): copy the permutation arrays a call
+// is about to index with to the host (synchronising `s`) and check them with
+// moe_check_permutation; any of the device pointers may be NULL. Returns
+// the status the entry point gives back (MOE_ERR_INVALID for bad arrays).
+int debug_check(hipStream_t s, const int32_t* offsets, int E, const int32_t* sorted_token,
+                const int32_t* dest_row, int T, int k);
+#ifdef MOE_HOST_BOUNDS_CHECK
+#define MOE_DEBUG_CHECK(...)                  \
+  do {                                        \
+    const int st_ = moe::debug_check(__VA_ARGS__); \
+    if (st_ != MOE_OK) return st_;            \
+  } while (0)
+#else
+#define MOE_DEBUG_CHECK(...) \
+  do {                       \
+  } while (0)
+#endif
 inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 
 inline int launch_status() {

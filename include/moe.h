@@ -30,8 +30,9 @@
  *     nothing was enqueued, except for MOE_ERR_LAUNCH.
  *   - dtype is MOE_F32 or MOE_BF16 and applies to x, the weights, the expert
  *     biases and residual; out is fp32 or, for bf16 layers, optionally bf16.
- *     The expert outputs y_perm, logits, gates, probability sums, f, P and
- *     the loss are always fp32; indices and offsets are int32.
+ *     The expert outputs y_perm are fp32 (fp32 layers) or block fixed point
+ *     (bf16 layers; see moe_expert_output_bytes). Logits, gates, probability
+ *     sums, f, P and the loss are always fp32; indices and offsets are int32.
  *   - Inputs must be finite: NaN or Inf in x or the weights is outside the
  *     contract.
  *   - Results are deterministic: every sum has a fixed order and no kernel
@@ -96,6 +97,21 @@ int moe_check_permutation(const int32_t *offsets, int E, const int32_t *sorted_t
 
 /* 1 in a library built with MOE_HOST_BOUNDS_CHECK (the debug build), else 0. */
 int moe_debug_checks(void);
+
+/*
+ * Bytes of `rows` rows of y_perm, the expert outputs of moe_grouped_ffn that
+ * moe_combine and moe_combine_backward read. MOE_F32: rows * d * 4 (fp32).
+ * MOE_BF16: rows * MOE_YQ_ROW_BYTES(d), a block fixed point: each row holds d
+ * int16 mantissas (2d bytes), then one int8 exponent per block of 8
+ * consecutive features (d/8 bytes, padded to a multiple of 16). Feature c of
+ * a row is mantissa[c] * 2^(exponent[c/8] - 14); a block whose largest
+ * magnitude m has 2^e <= m < 2^(e+1) is stored with exponent e (-127 for a
+ * block below the fp32 normal range), so each value is within 2^-15 m of
+ * the fp32 accumulation (2^-14 m where a mantissa clamps at +-32767). 0 for
+ * a bad dtype, rows < 0, d < 1, or d % 8 != 0 with MOE_BF16.
+ */
+#define MOE_YQ_ROW_BYTES(d) (2 * (size_t)(d) + ((((size_t)(d) / 8) + 15) & ~(size_t)15))
+size_t moe_expert_output_bytes(int dtype, int rows, int d);
 
 /*
  * Workspace bytes that call `op` needs for these sizes (dtype-independent
@@ -166,10 +182,12 @@ int moe_permute_noalloc(const int32_t *topk_idx, int T, int k, int E, int capaci
  *     H[r]      = SiLU(W1[e] . x[sorted_token[r]] + b1[e]),  SiLU(z) = z/(1+e^-z)
  *     y_perm[r] = W2[e] . H[r] + b2[e]
  * x [T][d]; w1 [E][h][d]; b1 [E][h] or NULL; w2 [E][d][h]; b2 [E][d] or
- * NULL; y_perm [T*k][d] fp32 for both dtypes (rows 0..R-1 written, R =
- * offsets[E] read on the device). fp32 accumulation; with MOE_BF16, H is
- * rounded to bf16 (the second product's operand) and y_perm keeps the fp32
- * accumulation, so no rounding sits between it and the combine. offsets and sorted_token come from moe_permute with the same T, k, E,
+ * NULL; y_perm: T*k rows of moe_expert_output_bytes(dtype, 1, d) bytes (rows
+ * 0..R-1 written, R = offsets[E] read on the device). fp32 accumulation;
+ * with MOE_BF16, H is rounded to bf16 (the second product's operand) and
+ * y_perm holds the accumulation in block fixed point (within 2^-15 of the
+ * largest of every 8 consecutive features; see moe_expert_output_bytes),
+ * far finer than a bf16 rounding of each value. offsets and sorted_token come from moe_permute with the same T, k, E,
  * or from moe_expert_choice with k = ceil(E * min(C, T) / T) (any k with
  * R <= T*k). The kernel choice depends only on T*k (no device-to-host read).
  * bf16 needs d and h to be multiples of 64. Workspace holds H:
@@ -187,8 +205,9 @@ int moe_grouped_ffn(const void *x, int dtype, int T, int d, int h, int E, int k,
  *   out[t] = (residual ? residual[t] : 0)
  *            + sum_{j=0..k-1, dest_row[t,j] >= 0} topk_gate[t,j] * y_perm[dest_row[t,j]]
  * summed in fp32 in ascending j, then stored as out_dtype. A token with every
- * slot dropped gets residual[t] (or 0). y_perm [T*k][d] is fp32 (as
- * moe_grouped_ffn writes it) and residual [T][d] (or NULL) is `dtype`; dest_row [T][k]; topk_gate [T][k] fp32; out [T][d]
+ * slot dropped gets residual[t] (or 0). y_perm: T*k rows as moe_grouped_ffn
+ * writes them (fp32, or block fixed point for MOE_BF16, decoded exactly);
+ * residual [T][d] (or NULL) is `dtype`; dest_row [T][k]; topk_gate [T][k] fp32; out [T][d]
  * is `out_dtype`: MOE_F32 (always allowed; keeps the fp32 sum unrounded) or
  * MOE_BF16 (only with dtype MOE_BF16). 1 <= k <= 512: with the slots of
  * moe_expert_choice (k = E) a token sums its choosing experts in ascending
@@ -264,7 +283,7 @@ int moe_cache_slot_of(const void *state, int32_t *slot_of, int32_t *phase_of);
  * computed (run phase 0 while the misses are copied, then phase 1 after
  * the copy stream's work). bf16 only, decode-size batches (T*k <= 4*E and
  * <= 1024, the weight-streaming path): status 2 otherwise. Same workspace
- * as moe_grouped_ffn; y_perm fp32 as there.
+ * as moe_grouped_ffn; y_perm as there.
  */
 int moe_grouped_ffn_cached(const void *x, int dtype, int T, int d, int h, int E, int k,
                            const int32_t *offsets, const int32_t *sorted_token,
@@ -302,8 +321,9 @@ int moe_aux_loss(const float *prob_sum, const int32_t *counts, int T, int E, flo
  * Combine backward: for every kept slot (t, j) (r = dest_row[t*k+j] >= 0)
  *   dy_perm[r] = topk_gate[t,j] * dout[t]          (dtype, [T*k][d] rows)
  *   dgate[t,j] = sum_i dout[t,i] * y_perm[r,i]     (fp32, fixed-order sum)
- * and dgate = 0 for dropped slots. y_perm: the forward's expert outputs,
- * fp32 [T*k][d] for both dtypes; dout [T][d] is `dtype`.
+ * and dgate = 0 for dropped slots. y_perm: the forward's expert outputs, T*k
+ * rows as moe_grouped_ffn writes them (MOE_BF16 needs d % 8 == 0); dout
+ * [T][d] is `dtype`.
  * k <= 512 (Expert Choice layouts included).
  */
 int moe_combine_backward(const void *y_perm, int dtype, const int32_t *dest_row,

@@ -133,3 +133,14 @@ def check_layer(cfg, inp, b, tokens=None, e2e_tokens=None, label="", b_bf16=None
             r["bf16_out_rel"] = float(np.abs(got16 - ref).max()) / rms
             r["bf16_rounding_floor_rel"] = float(np.abs(exact16 - ref).max()) / rms
     return r
+
+
+def decode_expert_outputs(y, d):
+    """The block fixed point of a bf16 layer's y_perm (uint8 [rows][row
+    bytes]): returns (values [rows][d] float64, mantissas int16 [rows][d],
+    exponents int [rows][d/8]), value = mantissa * 2^(exponent - 14)."""
+    a = y.detach().cpu().numpy()
+    mant = np.ascontiguousarray(a[:, :2 * d]).view("<i2")
+    ex = a[:, 2 * d:2 * d + d // 8].view(np.int8).astype(np.int64)
+    vals = mant.astype(np.float64) * np.exp2(np.repeat(ex, 8, axis=1) - 14)
+    return vals, mant, ex

@@ -79,7 +79,7 @@ def test_debug_build_refuses_corrupted_permutations(debug_lib):
     x = xs[:T]
     b = run_gpu(cfg, dict(inp, x=x))
     R = int(b.offsets[-1])
-    ys = torch.zeros((T * k + spare, d), dtype=torch.float32, device="cuda")
+    ys = N.expert_output_buffer(torch.bfloat16, T * k + spare, d, "cuda")
     y = ys[:T * k]
 
     def ffn(offsets, sorted_token):

@@ -120,6 +120,43 @@ def test_taller_tiles_are_planned():
             assert np.array_equal(covered, np.arange(off[e], off[e + 1])), (e, n0)
 
 
+@pytest.mark.parametrize("name", ["big_full_tail", "big_taller_split", "mid_rows_capacity",
+                                  "bn64_small", "decode_small"])
+def test_expert_outputs_are_block_fixed_point(name):
+    """y_perm of a bf16 layer on the 256 x 256 ring (whole and split tiles),
+    taller tiles, the persistent ring, 64-wide tiles and the streaming path:
+    every block of 8 features of a written row is normalised (its largest
+    mantissa in [2^14, 2^15), or all zero with exponent -127), and the decoded
+    rows match the oracle's expert outputs (each expert over its rows, double
+    precision) within 2e-2 of their RMS, as the layer outputs do."""
+    from _parity import decode_expert_outputs, expert_fetcher
+    from oracle import oracle as orc
+    cfg = SMALL[name]
+    inp = mi.make_inputs(cfg, "cuda")
+    b = run_gpu(cfg, inp)
+    d = cfg.d
+    assert b.y_perm.dtype == torch.uint8
+    assert b.y_perm.shape[1] == 2 * d + (-(-(d // 8) // 16)) * 16
+    off = b.offsets.cpu().numpy()
+    R = int(off[-1])
+    vals, mant, ex = decode_expert_outputs(b.y_perm[:R], d)
+    top = np.abs(mant.astype(np.int64)).reshape(R, d // 8, 8).max(axis=2)
+    zero = ex == -127
+    assert np.all(top[zero] == 0)
+    assert np.all((top[~zero] >= 1 << 14) & (top[~zero] <= 32767))
+    st = b.sorted_token.cpu().numpy()
+    fetch = expert_fetcher(inp)
+    x_h = mi.to_host_array(inp["x"])
+    ref = np.zeros((R, d))
+    for e in range(cfg.E):
+        if off[e + 1] > off[e]:
+            ref[off[e]:off[e + 1]] = orc.expert_rows(x_h, st[off[e]:off[e + 1]], *fetch(e))
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    err = float(np.abs(vals - ref).max())
+    print(f"[yq] {name}: rows {R} max err {err:.3g} = {err / rms:.4f} RMS", flush=True)
+    assert err <= 2e-2 * rms
+
+
 # ------------------------------------------------------------ edge cases ----
 def test_single_token():
     _run_and_check(CFG["mixtral_prefill"].with_(T=1, d=256, h=512), label="single_token")

@@ -19,6 +19,14 @@ extern "C" const char* moe_status_string(int status) {
 
 extern "C" int moe_version(void) { return 100; }
 
+extern "C" size_t moe_expert_output_bytes(int dtype, int rows, int d) {
+  if (rows < 0 || d < 1) return 0;
+  if (dtype == MOE_F32) return (size_t)rows * d * sizeof(float);
+  if (dtype != MOE_BF16 || (d % kYBlock) != 0) return 0;
+  static_assert(MOE_YQ_ROW_BYTES(64) == 2 * 64 + 16, "row bytes");
+  return (size_t)rows * yq_row_bytes(d);
+}
+
 extern "C" size_t moe_workspace_size(int op, int T, int d, int h, int E, int k) {
   // no call of this build takes more than kMaxE experts (the router's token
   // tile would round down to zero rows past it)

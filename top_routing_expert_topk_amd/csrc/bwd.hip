@@ -108,10 +108,11 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
 // for the dropped ones, so a layer with many slots per token (Expert Choice:
 // one per expert, most of them empty) pays one coalesced read of its dest
 // row instead of a dependent read per slot. vec: d % 8 == 0 (8 elements per
-// thread per pass). y (the forward's expert outputs) is fp32; dout and dy
-// are the layer's dtype T.
+// thread per pass). y holds the forward's expert outputs: fp32 rows for an
+// fp32 layer, the grouped FFN's block fixed point for a bf16 one (T =
+// uint16_t, d % 8 == 0); dout and dy are the layer's dtype T.
 template <typename T>
-__global__ __launch_bounds__(256) void combine_bwd(const float* __restrict__ y,
+__global__ __launch_bounds__(256) void combine_bwd(const void* __restrict__ y,
                                                    const int32_t* __restrict__ dest,
                                                    const float* __restrict__ gate, int k, int d,
                                                    const T* __restrict__ dout, T* __restrict__ dy,
@@ -123,6 +124,12 @@ __global__ __launch_bounds__(256) void combine_bwd(const float* __restrict__ y,
   __shared__ int nkept;
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const T* go = dout + (size_t)t * d;
+  constexpr bool kYQ = std::is_same<T, uint16_t>::value;
+  const size_t yrb = kYQ ? yq_row_bytes(d) : (size_t)d * sizeof(float);
+  auto yload8 = [&](long r, int c, float* v) __attribute__((always_inline)) {
+    if constexpr (kYQ) yq_load8((const unsigned char*)y, yrb, d, r, c, v);
+    else load8<float>((const float*)y + (size_t)r * d + c, v);
+  };
   int base = 0;
   for (int j0 = 0; j0 < k; j0 += 256) {
     const int j = j0 + tid;
@@ -161,7 +168,7 @@ __global__ __launch_bounds__(256) void combine_bwd(const float* __restrict__ y,
         float a[8], b[8][8];
         load8<T>(go + c, a);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) load8<float>(y + (size_t)krow[q + u] * d + c, b[u]);
+        for (int u = 0; u < 8; ++u) yload8(krow[q + u], c, b[u]);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           float o[8];
@@ -188,14 +195,13 @@ __global__ __launch_bounds__(256) void combine_bwd(const float* __restrict__ y,
   for (; q < nk; ++q) {  // one slot per pass
     const int j = kept[q], r = krow[q];
     const float g = gate[(size_t)t * k + j];
-    const float* yr = y + (size_t)r * d;
     T* dr = dy + (size_t)r * d;
     float dot = 0.0f;
     if (vec) {
       for (int c = tid * 8; c < d; c += 256 * 8) {
         float a[8], b[8], o[8];
         load8<T>(go + c, a);
-        load8<float>(yr + c, b);
+        yload8(r, c, b);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           dot = fmaf(a[u], b[u], dot);
@@ -206,7 +212,7 @@ __global__ __launch_bounds__(256) void combine_bwd(const float* __restrict__ y,
     } else {
       for (int c = tid; c < d; c += 256) {
         const float a = ld1<T>(go + c);
-        dot = fmaf(a, yr[c], dot);
+        if constexpr (!kYQ) dot = fmaf(a, ((const float*)y)[(size_t)r * d + c], dot);
         st1<T>(dr + c, g * a);
       }
     }
@@ -815,17 +821,18 @@ extern "C" int moe_combine_backward(const void* y_perm, int dtype, const int32_t
   if (T < 0 || k < 1 || d < 1) return MOE_ERR_INVALID;
   if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_INVALID;
   if (k > kMaxE) return MOE_ERR_UNSUPPORTED;
+  if (dtype == MOE_BF16 && (d % 8) != 0) return MOE_ERR_UNSUPPORTED;  // whole blocks of 8
   if (T == 0) return MOE_OK;
   if (!y_perm || !dest_row || !topk_gate || !dout || !dy_perm || !dgate) return MOE_ERR_INVALID;
   hipStream_t s = (hipStream_t)stream;
   MOE_DEBUG_CHECK(s, nullptr, 1, nullptr, dest_row, T, k);
   const bool vec = (d % 8) == 0;
   if (dtype == MOE_BF16)
-    hipLaunchKernelGGL(combine_bwd<uint16_t>, dim3(T), dim3(256), 0, s, (const float*)y_perm,
+    hipLaunchKernelGGL(combine_bwd<uint16_t>, dim3(T), dim3(256), 0, s, y_perm,
                        dest_row, topk_gate, k, d, (const uint16_t*)dout, (uint16_t*)dy_perm, dgate,
                        vec);
   else
-    hipLaunchKernelGGL(combine_bwd<float>, dim3(T), dim3(256), 0, s, (const float*)y_perm, dest_row,
+    hipLaunchKernelGGL(combine_bwd<float>, dim3(T), dim3(256), 0, s, y_perm, dest_row,
                        topk_gate, k, d, (const float*)dout, (float*)dy_perm, dgate, vec);
   return launch_status();
 }

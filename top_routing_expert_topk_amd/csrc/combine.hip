@@ -8,8 +8,10 @@
 // The "weighted scatter" is done as a per-token gather: each output element
 // is owned by one lane, which sums its k terms in fp32 in ascending j, so
 // the result is deterministic and needs no atomics. The expert outputs
-// y_perm are fp32 for both layer dtypes (the grouped FFN's accumulations,
-// unrounded); a bf16 layer's residual is bf16. Expert Choice gives a
+// y_perm of a bf16 layer are in the block fixed point the grouped FFN writes
+// (moe_internal.h: int16 mantissas, one exponent per 8 features of a row,
+// rows of yq_row_bytes(d) bytes) and are decoded exactly to fp32 here; an
+// fp32 layer's are fp32. A bf16 layer's residual is bf16. Expert Choice gives a
 // token one slot per expert (k = E, dest_row -1 where the expert did not
 // take it); the same sum then runs over its choosing experts in order.
 //
@@ -38,23 +40,24 @@ __device__ __forceinline__ void store8<float>(float* p, const float* v) {
   *(f32x4*)(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
 }
 
-__device__ __forceinline__ void fma8(float g, const float* __restrict__ p, float* acc) {
-  const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+// acc[0..7] += g * features c..c+7 of expert-output row r
+__device__ __forceinline__ void fma8(float g, const unsigned char* __restrict__ y, size_t rb, int d,
+                                     long r, int c, float* acc) {
+  float v[8];
+  yq_load8(y, rb, d, r, c, v);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    acc[q] = fmaf(g, a[q], acc[q]);
-    acc[4 + q] = fmaf(g, b[q], acc[4 + q]);
-  }
+  for (int q = 0; q < 8; ++q) acc[q] = fmaf(g, v[q], acc[q]);
 }
 
 template <typename OutT>
 __global__ __launch_bounds__(256) void combine_bf16(
-    const float* __restrict__ y, const int32_t* __restrict__ dest,
+    const unsigned char* __restrict__ y, const int32_t* __restrict__ dest,
     const float* __restrict__ gate, int T, int k, int d, const uint16_t* __restrict__ resid,
     OutT* __restrict__ out) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * kCombineWaves + (threadIdx.x >> 6);
   if (t >= T) return;
+  const size_t rb = yq_row_bytes(d);
   int dj[kMaxK];
   float gj[kMaxK];
 #pragma unroll
@@ -81,7 +84,7 @@ __global__ __launch_bounds__(256) void combine_bf16(
     }
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j)
-      if (j < k && dj[j] >= 0) fma8(gj[j], y + (size_t)dj[j] * d + c, acc);
+      if (j < k && dj[j] >= 0) fma8(gj[j], y, rb, d, dj[j], c, acc);
     store8<OutT>(out + (size_t)t * d + c, acc);
   }
 }
@@ -91,12 +94,13 @@ __global__ __launch_bounds__(256) void combine_bf16(
 // ones and adds them in ascending slot order.
 template <typename OutT>
 __global__ __launch_bounds__(256) void combine_bf16_many(
-    const float* __restrict__ y, const int32_t* __restrict__ dest,
+    const unsigned char* __restrict__ y, const int32_t* __restrict__ dest,
     const float* __restrict__ gate, int T, int k, int d, const uint16_t* __restrict__ resid,
     OutT* __restrict__ out) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * kCombineWaves + (threadIdx.x >> 6);
   if (t >= T) return;
+  const size_t rb = yq_row_bytes(d);
   for (int c0 = 0; c0 < d; c0 += 64 * 8) {
     const int c = c0 + lane * 8;
     const bool mine = c < d;
@@ -122,7 +126,7 @@ __global__ __launch_bounds__(256) void combine_bf16_many(
         live &= live - 1;
         const int r = __builtin_amdgcn_readlane(dj, b);
         const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gj), b));
-        if (mine) fma8(g, y + (size_t)r * d + c, acc);
+        if (mine) fma8(g, y, rb, d, r, c, acc);
       }
     }
     if (mine) store8<OutT>(out + (size_t)t * d + c, acc);
@@ -190,17 +194,19 @@ extern "C" int moe_combine(const void* y_perm, int dtype, const int32_t* dest_ro
   if (dtype == MOE_BF16 && k > kMaxK) {
     if (out_dtype == MOE_BF16)
       hipLaunchKernelGGL(combine_bf16_many<uint16_t>, dim3(nb), dim3(256), 0, s,
-                         (const float*)y_perm, dest_row, topk_gate, T, k, d,
+                         (const unsigned char*)y_perm, dest_row, topk_gate, T, k, d,
                          (const uint16_t*)residual, (uint16_t*)out);
     else
       hipLaunchKernelGGL(combine_bf16_many<float>, dim3(nb), dim3(256), 0, s,
-                         (const float*)y_perm, dest_row, topk_gate, T, k, d,
+                         (const unsigned char*)y_perm, dest_row, topk_gate, T, k, d,
                          (const uint16_t*)residual, (float*)out);
   } else if (dtype == MOE_BF16 && out_dtype == MOE_BF16)
-    hipLaunchKernelGGL(combine_bf16<uint16_t>, dim3(nb), dim3(256), 0, s, (const float*)y_perm,
+    hipLaunchKernelGGL(combine_bf16<uint16_t>, dim3(nb), dim3(256), 0, s,
+                       (const unsigned char*)y_perm,
                        dest_row, topk_gate, T, k, d, (const uint16_t*)residual, (uint16_t*)out);
   else if (dtype == MOE_BF16)
-    hipLaunchKernelGGL(combine_bf16<float>, dim3(nb), dim3(256), 0, s, (const float*)y_perm,
+    hipLaunchKernelGGL(combine_bf16<float>, dim3(nb), dim3(256), 0, s,
+                       (const unsigned char*)y_perm,
                        dest_row, topk_gate, T, k, d, (const uint16_t*)residual, (float*)out);
   else
     hipLaunchKernelGGL(combine_f32, dim3(nb), dim3(256), 0, s, (const float*)y_perm, dest_row,

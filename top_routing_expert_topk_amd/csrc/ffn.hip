@@ -25,8 +25,9 @@
 //   gemm_f32        FMA tiles for fp32 layers
 // In every kernel the gather of x rows is fused into the activation load and
 // bias (+SiLU) into the epilogue. H leaves in bf16 (the second product's
-// MFMA operand); Y leaves in fp32 (F32OUT), so the combine sums the fp32
-// accumulations without a rounding in between.
+// MFMA operand); Y leaves in the block fixed point of moe_internal.h (YQ: 8
+// features of a row share a power-of-two exponent, int16 mantissas), whose
+// error is a 2^-15 fraction of each block's largest value.
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -51,7 +52,7 @@ constexpr int KC = 64;  // bf16 K elements per LDS stage (128 bytes per row)
 // LDS rows are 64 bf16 (8 chunks of 16 B); chunk c of row r sits at
 // c ^ ((r >> 1) & 7), so the 16 lanes of one ds_read_b128 pass, reading 16
 // rows at one chunk, spread over all 16 bank groups of 16 bytes.
-template <int BN, int BM, bool GATHER, bool SILU, bool F32OUT = false>
+template <int BN, int BM, bool GATHER, bool SILU, bool YQ = false>
 __global__ __launch_bounds__(256) void gemm_bf16(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ sorted_token,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_start,
@@ -156,6 +157,25 @@ __global__ __launch_bounds__(256) void gemm_bf16(
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
       const int m = wm * (BM / 2) + j * 16 + (lane & 15);
+      if constexpr (YQ) {
+        // lanes l and l ^ 16 hold features 0-3 and 4-7 of one block of a row
+        float v[4], mx = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[q] = acc[i][j][q] + bv[q];
+          mx = fmaxf(mx, fabsf(v[q]));
+        }
+        const int ex = yq_exponent(fmaxf(mx, __shfl_xor(mx, 16, 64)));
+        if (m < rows) {
+          unsigned char* row = (unsigned char*)out + (size_t)(row0 + m) * yq_row_bytes(N);
+          u32x2 o;
+          o[0] = ((uint32_t)yq_encode(v[0], ex) & 0xFFFFu) | ((uint32_t)yq_encode(v[1], ex) << 16);
+          o[1] = ((uint32_t)yq_encode(v[2], ex) & 0xFFFFu) | ((uint32_t)yq_encode(v[3], ex) << 16);
+          *(u32x2*)(row + (size_t)2 * n) = o;
+          if (((lane >> 4) & 1) == 0) row[(size_t)2 * N + n / kYBlock] = (unsigned char)(signed char)ex;
+        }
+        continue;
+      }
       if (m < rows) {
         float v[4];
 #pragma unroll
@@ -169,14 +189,10 @@ __global__ __launch_bounds__(256) void gemm_bf16(
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           if (SILU) v[q] = silu_bf16(v[q]);
-        if constexpr (F32OUT) {
-          *(f32x4*)((float*)out + (size_t)(row0 + m) * N + n) = f32x4{v[0], v[1], v[2], v[3]};
-        } else {
-          u32x2 o;
-          o[0] = pack_bf16x2(v[0], v[1]);
-          o[1] = pack_bf16x2(v[2], v[3]);
-          *(u32x2*)((uint16_t*)out + (size_t)(row0 + m) * N + n) = o;
-        }
+        u32x2 o;
+        o[0] = pack_bf16x2(v[0], v[1]);
+        o[1] = pack_bf16x2(v[2], v[3]);
+        *(u32x2*)((uint16_t*)out + (size_t)(row0 + m) * N + n) = o;
       }
     }
   }
@@ -212,7 +228,7 @@ struct PRing {
   static constexpr int NBQ = BM / 128;          // permuted-row blocks per step
 };
 
-template <int BM, bool GATHER, bool SILU, bool F32OUT = false>
+template <int BM, bool GATHER, bool SILU, bool YQ = false>
 __global__ __launch_bounds__(512) void gemm_bf16_pring(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ tok_tab,
     const BigHdr* __restrict__ hdr, const BigWork* __restrict__ units,
@@ -428,16 +444,26 @@ __global__ __launch_bounds__(512) void gemm_bf16_pring(
 #pragma unroll
               for (int t = 0; t < 4; ++t)
                 if (SILU) v[t] = silu_bf16(v[t]);
-              if (m < uc.rows) {
-                if constexpr (F32OUT) {
-                  *(f32x4*)((float*)out + (size_t)(uc.row0 + m) * N + uc.n0 + nl) =
-                      f32x4{v[0], v[1], v[2], v[3]};
-                } else {
+              if constexpr (YQ) {
+                // lanes l and l ^ 32 hold features nb..nb+3 and nb+4..nb+7
+                float mx = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+                const int ex = yq_exponent(fmaxf(mx, __shfl_xor(mx, 32, 64)));
+                if (m < uc.rows) {
+                  unsigned char* row = (unsigned char*)out + (size_t)(uc.row0 + m) * yq_row_bytes(N);
                   u32x2 o;
-                  o[0] = pack_bf16x2(v[0], v[1]);
-                  o[1] = pack_bf16x2(v[2], v[3]);
-                  *(u32x2*)((uint16_t*)out + (size_t)(uc.row0 + m) * N + uc.n0 + nl) = o;
+                  o[0] = ((uint32_t)yq_encode(v[0], ex) & 0xFFFFu) |
+                         ((uint32_t)yq_encode(v[1], ex) << 16);
+                  o[1] = ((uint32_t)yq_encode(v[2], ex) & 0xFFFFu) |
+                         ((uint32_t)yq_encode(v[3], ex) << 16);
+                  *(u32x2*)(row + (size_t)2 * (uc.n0 + nl)) = o;
+                  if (ch == 0)
+                    row[(size_t)2 * N + (uc.n0 + nb) / kYBlock] = (unsigned char)(signed char)ex;
                 }
+              } else if (m < uc.rows) {
+                u32x2 o;
+                o[0] = pack_bf16x2(v[0], v[1]);
+                o[1] = pack_bf16x2(v[2], v[3]);
+                *(u32x2*)((uint16_t*)out + (size_t)(uc.row0 + m) * N + uc.n0 + nl) = o;
               }
             }
           }
@@ -484,14 +510,18 @@ __device__ __forceinline__ float wave_sum(float v) {
 // With an expert cache (slot_of != NULL) expert e's weights sit in device slot
 // slot_of[e] of the weight arrays, and only experts with phase_of[e] == phase
 // run, so a launch can cover the resident experts while others are copied in.
-template <bool GATHER, bool SILU, typename OutT>
+// YQ: the outputs leave in the block fixed point (the second product); a
+// block of 8 features is the 4 of wave w and the 4 of wave w ^ 1, whose
+// largest magnitudes meet in LDS. Otherwise bf16 (H).
+template <bool GATHER, bool SILU, bool YQ>
 __global__ __launch_bounds__(256) void decode_bf16(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ sorted_token,
     const int32_t* __restrict__ offsets, const uint16_t* __restrict__ w,
-    const uint16_t* __restrict__ bias, OutT* __restrict__ out, int E, int N, int K,
+    const uint16_t* __restrict__ bias, void* __restrict__ out, int E, int N, int K,
     const int32_t* __restrict__ slot_of, const int32_t* __restrict__ phase_of, int phase,
     uint16_t* __restrict__ zout) {
   extern __shared__ __align__(16) uint16_t sx[];  // [DG][K]
+  __shared__ float smax[4][DG];                   // YQ: each wave's block half maxima
   const int e = blockIdx.y;
   const int r0 = offsets[e];
   const int cnt = offsets[e + 1] - r0;
@@ -511,6 +541,8 @@ __global__ __launch_bounds__(256) void decode_bf16(
       *(u32x4*)(sx + g * K + kc * 8) = *(const u32x4*)(act + src * K + kc * 8);
     }
     __syncthreads();
+    float yv[DRPW][DG] = {};  // YQ: this wave's outputs, encoded once all 4 are known
+#pragma unroll
     for (int rp = 0; rp < DRPW; rp += 2) {
       const int n = nw + rp;
       float acc[2][DG];
@@ -556,12 +588,37 @@ __global__ __launch_bounds__(256) void decode_bf16(
             if (SILU && zout && lane == 0 && na < N)
               zout[(size_t)(r0 + g0 + g) * N + na] = (uint16_t)f32_to_bf16(v);
             if (SILU) v = silu_bf16(v);
-            if (lane == 0 && na < N) {
-              if constexpr (std::is_same<OutT, float>::value)
-                out[(size_t)(r0 + g0 + g) * N + na] = v;
-              else
-                out[(size_t)(r0 + g0 + g) * N + na] = (uint16_t)f32_to_bf16(v);
-            }
+            if constexpr (YQ) yv[rp + a][g] = v;
+            else if (lane == 0 && na < N)
+              ((uint16_t*)out)[(size_t)(r0 + g0 + g) * N + na] = (uint16_t)f32_to_bf16(v);
+          }
+        }
+      }
+    }
+    if constexpr (YQ) {
+      // N is a multiple of 16 here, so all 4 features of every wave exist
+#pragma unroll
+      for (int g = 0; g < DG; ++g) {
+        float mx = 0.0f;
+#pragma unroll
+        for (int f = 0; f < DRPW; ++f) mx = fmaxf(mx, fabsf(yv[f][g]));
+        if (lane == 0) smax[wave][g] = mx;
+      }
+      __syncthreads();
+      if (lane == 0) {
+        const size_t rb = yq_row_bytes(N);
+#pragma unroll
+        for (int g = 0; g < DG; ++g) {
+          if (g < ng) {
+            const int ex = yq_exponent(fmaxf(smax[wave][g], smax[wave ^ 1][g]));
+            unsigned char* row = (unsigned char*)out + (size_t)(r0 + g0 + g) * rb;
+            u32x2 o;
+            o[0] = ((uint32_t)yq_encode(yv[0][g], ex) & 0xFFFFu) |
+                   ((uint32_t)yq_encode(yv[1][g], ex) << 16);
+            o[1] = ((uint32_t)yq_encode(yv[2][g], ex) & 0xFFFFu) |
+                   ((uint32_t)yq_encode(yv[3][g], ex) << 16);
+            *(u32x2*)(row + (size_t)2 * nw) = o;
+            if ((wave & 1) == 0) row[(size_t)2 * N + nw / kYBlock] = (unsigned char)(signed char)ex;
           }
         }
       }
@@ -575,7 +632,7 @@ constexpr int kBM = 128;
 template <int BN>
 int launch_gemms_bf16(const uint16_t* x, const int32_t* sorted_token, const int32_t* offsets,
                       const int32_t* tile_start, const uint16_t* w1, const uint16_t* b1,
-                      const uint16_t* w2, const uint16_t* b2, uint16_t* H, float* y, int E,
+                      const uint16_t* w2, const uint16_t* b2, uint16_t* H, unsigned char* y, int E,
                       int d, int h, int mslots, uint16_t* zout, hipStream_t s) {
   hipLaunchKernelGGL((gemm_bf16<BN, kBM, true, true>), dim3(mslots * (h / BN)), dim3(256), 0, s, x,
                      sorted_token, offsets, tile_start, w1, b1, H, E, h, d, mslots, zout);
@@ -603,7 +660,7 @@ bool use_ring128(long rows, int E, int T, int d, int h) {
 
 int launch_ring(const uint16_t* x, const int32_t* sorted_token, const int32_t* offsets, void* plan,
                 const uint16_t* w1, const uint16_t* b1, const uint16_t* w2, const uint16_t* b2,
-                uint16_t* H, float* y, float* part, uint16_t* zout, int E, int d, int h,
+                uint16_t* H, unsigned char* y, float* part, uint16_t* zout, int E, int d, int h,
                 long rows, hipStream_t s) {
   const int g1 = ffn_big_grid(rows, E, h, kBigBM), g2 = ffn_big_grid(rows, E, d, kBigBM);
   BigHdr* hdr = (BigHdr*)plan;
@@ -618,10 +675,10 @@ int launch_ring(const uint16_t* x, const int32_t* sorted_token, const int32_t* o
                      (const uint16_t*)nullptr, zout);
   hipLaunchKernelGGL((big_tail_reduce<kBigRowsMax, kEpiSilu>), gr, dim3(256), 0, s, hdr, list1, b1, part,
                      H, h, (const uint16_t*)nullptr, zout);
-  hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, false, kEpiBiasF32>), dim3(g2),
+  hipLaunchKernelGGL((gemm_bf16_ring<kRingWaves, false, kEpiBiasQ>), dim3(g2),
                      dim3(kRingWaves * 64), 0, s, H, sorted_token, list2, w2, b2, y, part, d, h,
                      (size_t)d * h, 0, (const uint16_t*)nullptr, (uint16_t*)nullptr);
-  hipLaunchKernelGGL((big_tail_reduce<kBigRowsMax, kEpiBiasF32>), gr, dim3(256), 0, s, hdr + 1,
+  hipLaunchKernelGGL((big_tail_reduce<kBigRowsMax, kEpiBiasQ>), gr, dim3(256), 0, s, hdr + 1,
                      list2, b2, part, y, d, (const uint16_t*)nullptr, (uint16_t*)nullptr);
   return launch_status();
 }
@@ -630,7 +687,7 @@ int launch_ring(const uint16_t* x, const int32_t* sorted_token, const int32_t* o
 template <int BM>
 int launch_pring(const uint16_t* x, const int32_t* sorted_token, const int32_t* offsets,
                  void* plan, const uint16_t* w1, const uint16_t* b1, const uint16_t* w2,
-                 const uint16_t* b2, uint16_t* H, float* y, float* part, uint16_t* zout, int E,
+                 const uint16_t* b2, uint16_t* H, unsigned char* y, float* part, uint16_t* zout, int E,
                  int d, int h, int T, int k, long rows, hipStream_t s) {
   const int g1 = ffn_big_grid(rows, E, h, BM), g2 = ffn_big_grid(rows, E, d, BM);
   BigHdr* hdr = (BigHdr*)plan;
@@ -654,7 +711,7 @@ int launch_pring(const uint16_t* x, const int32_t* sorted_token, const int32_t* 
   hipLaunchKernelGGL((gemm_bf16_pring<BM, false, false, true>), dim3(kTailSlots), dim3(512), 0, s,
                      H, (const int32_t*)nullptr, hdr + 1, list2, w2, b2, y, part, d, h,
                      (uint16_t*)nullptr);
-  hipLaunchKernelGGL((big_tail_reduce<BM, kEpiBiasF32>), gr, dim3(256), 0, s, hdr + 1, list2, b2,
+  hipLaunchKernelGGL((big_tail_reduce<BM, kEpiBiasQ>), gr, dim3(256), 0, s, hdr + 1, list2, b2,
                      part, y, d, (const uint16_t*)nullptr, (uint16_t*)nullptr);
   return launch_status();
 }
@@ -662,21 +719,21 @@ int launch_pring(const uint16_t* x, const int32_t* sorted_token, const int32_t* 
 // Both FFN GEMMs through the weight-streaming kernel (H in the workspace).
 int launch_decode(const uint16_t* x, const int32_t* sorted_token, const int32_t* offsets,
                   const uint16_t* w1, const uint16_t* b1, const uint16_t* w2, const uint16_t* b2,
-                  uint16_t* H, float* y, int E, int d, int h, const int32_t* slot_of,
+                  uint16_t* H, unsigned char* y, int E, int d, int h, const int32_t* slot_of,
                   const int32_t* phase_of, int phase, uint16_t* zout, hipStream_t s) {
   const size_t lds1 = (size_t)DG * d * 2, lds2 = (size_t)DG * h * 2;
   if (lds1 > 160 * 1024 || lds2 > 160 * 1024) return MOE_ERR_UNSUPPORTED;
   if (lds1 > 65536 &&
-      hipFuncSetAttribute((const void*)decode_bf16<true, true, uint16_t>,
+      hipFuncSetAttribute((const void*)decode_bf16<true, true, false>,
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1) != hipSuccess)
     return MOE_ERR_LAUNCH;
   if (lds2 > 65536 &&
-      hipFuncSetAttribute((const void*)decode_bf16<false, false, float>,
+      hipFuncSetAttribute((const void*)decode_bf16<false, false, true>,
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2) != hipSuccess)
     return MOE_ERR_LAUNCH;
-  hipLaunchKernelGGL((decode_bf16<true, true, uint16_t>), dim3(ceil_div(h, DRPB), E), dim3(256), lds1, s, x,
+  hipLaunchKernelGGL((decode_bf16<true, true, false>), dim3(ceil_div(h, DRPB), E), dim3(256), lds1, s, x,
                      sorted_token, offsets, w1, b1, H, E, h, d, slot_of, phase_of, phase, zout);
-  hipLaunchKernelGGL((decode_bf16<false, false, float>), dim3(ceil_div(d, DRPB), E), dim3(256), lds2, s,
+  hipLaunchKernelGGL((decode_bf16<false, false, true>), dim3(ceil_div(d, DRPB), E), dim3(256), lds2, s,
                      (const uint16_t*)H, sorted_token, offsets, w2, b2, y, E, d, h, slot_of,
                      phase_of, phase, (uint16_t*)nullptr);
   return launch_status();
@@ -721,26 +778,26 @@ int grouped_ffn(const void* x, int dtype, int T, int d, int h, int E, int k,
   if (use_decode(rows, E)) {
     return launch_decode(xb, sorted_token, offsets, (const uint16_t*)w1, (const uint16_t*)b1,
                          (const uint16_t*)w2, (const uint16_t*)b2, (uint16_t*)H,
-                         (float*)y_perm, E, d, h, nullptr, nullptr, 0, zb, s);
+                         (unsigned char*)y_perm, E, d, h, nullptr, nullptr, 0, zb, s);
   }
 
   if (use_ring(rows, E, T, d, h))
     return launch_ring(xb, sorted_token, offsets, ws, (const uint16_t*)w1, (const uint16_t*)b1,
-                       (const uint16_t*)w2, (const uint16_t*)b2, (uint16_t*)H, (float*)y_perm,
+                       (const uint16_t*)w2, (const uint16_t*)b2, (uint16_t*)H, (unsigned char*)y_perm,
                        part, zb, E, d, h, rows, s);
   if (use_ring128(rows, E, T, d, h))
     return launch_pring<128>(xb, sorted_token, offsets, ws, (const uint16_t*)w1,
                              (const uint16_t*)b1, (const uint16_t*)w2, (const uint16_t*)b2,
-                             (uint16_t*)H, (float*)y_perm, part, zb, E, d, h, T, k, rows, s);
+                             (uint16_t*)H, (unsigned char*)y_perm, part, zb, E, d, h, T, k, rows, s);
   const int mslots = ceil_div(rows, kBM) + nonempty;
   hipLaunchKernelGGL(build_tile_map, dim3(1), dim3(512), 0, s, offsets, E, kBM, tile_start);
   if ((d % 128) == 0 && (h % 128) == 0)
     return launch_gemms_bf16<128>(xb, sorted_token, offsets, tile_start, (const uint16_t*)w1,
                                   (const uint16_t*)b1, (const uint16_t*)w2, (const uint16_t*)b2,
-                                  (uint16_t*)H, (float*)y_perm, E, d, h, mslots, zb, s);
+                                  (uint16_t*)H, (unsigned char*)y_perm, E, d, h, mslots, zb, s);
   return launch_gemms_bf16<64>(xb, sorted_token, offsets, tile_start, (const uint16_t*)w1,
                                (const uint16_t*)b1, (const uint16_t*)w2, (const uint16_t*)b2,
-                               (uint16_t*)H, (float*)y_perm, E, d, h, mslots, zb, s);
+                               (uint16_t*)H, (unsigned char*)y_perm, E, d, h, mslots, zb, s);
 }
 
 int ffn_check(const void* x, int dtype, int T, int d, int h, int E, int k,
@@ -808,6 +865,6 @@ extern "C" int moe_grouped_ffn_cached(const void* x, int dtype, int T, int d, in
   void* H = (unsigned char*)ws + ffn_plan_bytes(T, d, h, E, k);
   return launch_decode((const uint16_t*)x, sorted_token, offsets, (const uint16_t*)w1,
                        (const uint16_t*)b1, (const uint16_t*)w2, (const uint16_t*)b2,
-                       (uint16_t*)H, (float*)y_perm, E, d, h, slot_of, phase_of, phase,
+                       (uint16_t*)H, (unsigned char*)y_perm, E, d, h, slot_of, phase_of, phase,
                        (uint16_t*)nullptr, (hipStream_t)stream);
 }

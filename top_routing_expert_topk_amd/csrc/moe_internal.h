@@ -50,6 +50,65 @@ __device__ __forceinline__ float silu_grad(float z) {
   return s * (1.0f + z * (1.0f - s));
 }
 
+// ---- expert outputs of bf16 layers (block fixed point) ----------------------
+// Row r of y_perm takes moe_yq_row_bytes(d) bytes: d int16 mantissas, then
+// one int8 exponent per block of 8 consecutive features (padded to 16
+// bytes). A block with largest magnitude m, 2^e <= m < 2^(e+1), stores each
+// value as round(v 2^(14-e)) (|.| <= 32767) with exponent e, and reads back
+// exactly q 2^(e-14): the error is at most 2^(e-15) <= m 2^-15 (2^-14 m for a
+// value clamped at the top), against 2^-9 |v| for a bf16 value, in 2.125
+// bytes per element instead of fp32's 4. Blocks below the normal range use
+// e = -127.
+constexpr int kYBlock = 8;
+__host__ __device__ inline size_t yq_row_bytes(int d) { return MOE_YQ_ROW_BYTES(d); }
+__device__ __forceinline__ int yq_exponent(float maxabs) {
+  if (!(maxabs >= 1.17549435e-38f)) return -127;  // zero, or below the normal range
+  return (int)((__float_as_uint(maxabs) >> 23) & 0xFFu) - 127;
+}
+__device__ __forceinline__ int yq_encode(float v, int e) {
+  const float s = __builtin_rintf(__builtin_ldexpf(v, 14 - e));
+  return (int)fminf(fmaxf(s, -32767.0f), 32767.0f);
+}
+__device__ __forceinline__ float yq_decode(int q, int e) {
+  return __builtin_ldexpf((float)q, e - 14);
+}
+// Eight features of one row: mantissas as 16 bytes and the block exponent.
+__device__ __forceinline__ void yq_encode8(const float* v, u32x4& mant, int& e) {
+  float m = 0.0f;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) m = fmaxf(m, fabsf(v[u]));
+  e = yq_exponent(m);
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    mant[u] = ((uint32_t)yq_encode(v[2 * u], e) & 0xFFFFu) |
+              ((uint32_t)yq_encode(v[2 * u + 1], e) << 16);
+}
+__device__ __forceinline__ void yq_decode8(const u32x4 mant, int e, float* v) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    v[2 * u] = yq_decode((int)(int16_t)(mant[u] & 0xFFFFu), e);
+    v[2 * u + 1] = yq_decode((int)(int16_t)(mant[u] >> 16), e);
+  }
+}
+// Features c..c+7 (c a multiple of 8) of row r of a y_perm with rows of
+// `rb` bytes.
+__device__ __forceinline__ void yq_load8(const unsigned char* __restrict__ y, size_t rb, int d,
+                                         long r, int c, float* v) {
+  const unsigned char* row = y + (size_t)r * rb;
+  const u32x4 mant = *(const u32x4*)(row + (size_t)2 * c);
+  const int e = (int)(signed char)row[(size_t)2 * d + c / kYBlock];
+  yq_decode8(mant, e, v);
+}
+__device__ __forceinline__ void yq_store8(unsigned char* __restrict__ y, size_t rb, int d, long r,
+                                          int c, const float* v) {
+  unsigned char* row = y + (size_t)r * rb;
+  u32x4 mant;
+  int e;
+  yq_encode8(v, mant, e);
+  *(u32x4*)(row + (size_t)2 * c) = mant;
+  row[(size_t)2 * d + c / kYBlock] = (unsigned char)(signed char)e;
+}
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
   return (1ull << __lane_id()) - 1ull;
 }

@@ -111,12 +111,13 @@ __device__ __forceinline__ void interleave_mfma_reads() {
 
 // Epilogues of a tile: out = acc + bias, SiLU(acc + bias), or acc * SiLU'(z)
 // with z read from a second [rows][N] array (the backward of the activation),
-// all three stored as bf16; kEpiBiasF32 stores acc + bias in fp32 (the
-// expert outputs Y of the forward, which the combine sums unrounded).
+// all three stored as bf16; kEpiBiasQ stores acc + bias in the block fixed
+// point of moe_internal.h (the expert outputs Y of the forward: 2^-15 of the
+// largest of every 8 consecutive features instead of bf16's 2^-9 of each).
 constexpr int kEpiBias = 0;
 constexpr int kEpiSilu = 1;
 constexpr int kEpiDSilu = 2;
-constexpr int kEpiBiasF32 = 3;
+constexpr int kEpiBiasQ = 3;
 
 // MFMA operand fragment of a K-major weight block in LDS (64 k-rows x 128
 // features, 256-byte rows, chunk c of row k at c ^ 4 (k % 4)): lane l gets
@@ -348,36 +349,58 @@ __device__ __forceinline__ void big_store(f32x16 (&acc)[4][TM], const f32x16& ac
       bv[3] = bf16hi(bb[1]);
     }
   };
-  if constexpr (EPI == kEpiBiasF32) {
-    // fp32 rows straight from the accumulators, like the partials: each
-    // store puts 32 bytes into each of 32 rows, and the four q passes fill
-    // 128 contiguous bytes of every row
-    float* out = (float*)outv;
+  if constexpr (EPI == kEpiBiasQ) {
+    // rows leave through LDS (the idle ring) in two halves of 128 features:
+    // the waves of weight-row half wn stage half wn in fp32 (rows padded by
+    // 16 bytes, so the 32 rows a wave writes at one feature offset spread
+    // over the banks), then 16 lanes encode a row's 16 blocks of 8 features
+    // and store its 256 bytes of mantissas and 16 exponent bytes
+    unsigned char* out = (unsigned char*)outv;
+    const size_t rb = yq_row_bytes(N);
+    float* st = (float*)ot;
+    constexpr int FSTR = 128 + 4;  // LDS row stride in floats
+    lds_barrier();                 // every wave is done reading the ring
+#pragma unroll 1
+    for (int hh = 0; hh < 2; ++hh) {
+      if (wn == hh) {
 #pragma unroll
-    for (int i = 0; i < TN; ++i)
+        for (int i = 0; i < TN; ++i)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int nl = wn * WTN + i * 32 + 8 * q + 4 * ch;
-        float bv[4];
-        bias4(nl, bv);
+          for (int q = 0; q < 4; ++q) {
+            const int nl = i * 32 + 8 * q + 4 * ch;  // feature within the half
+            float bv[4];
+            bias4(wn * WTN + nl, bv);
 #pragma unroll
-        for (int j = 0; j < TM; ++j) {
-          const int m = wm * WTM + j * 32 + (lane & 31);
-          if (m < wk.rows)
-            *(f32x4*)(out + ((size_t)wk.e * ores + wk.row0 + m) * N + wk.n0 + nl) =
-                f32x4{acc[i][j][4 * q] + bv[0], acc[i][j][4 * q + 1] + bv[1],
-                      acc[i][j][4 * q + 2] + bv[2], acc[i][j][4 * q + 3] + bv[3]};
-        }
+            for (int j = 0; j < TM; ++j) {
+              const int m = wm * WTM + j * 32 + (lane & 31);
+              *(f32x4*)(st + m * FSTR + nl) =
+                  f32x4{acc[i][j][4 * q] + bv[0], acc[i][j][4 * q + 1] + bv[1],
+                        acc[i][j][4 * q + 2] + bv[2], acc[i][j][4 * q + 3] + bv[3]};
+            }
+          }
+        if (ext)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int nl = nlx(q) - wn * WTN;
+            float bv[4];
+            bias4(nlx(q), bv);
+            *(f32x4*)(st + mx * FSTR + nl) =
+                f32x4{accx[4 * q] + bv[0], accx[4 * q + 1] + bv[1], accx[4 * q + 2] + bv[2],
+                      accx[4 * q + 3] + bv[3]};
+          }
       }
-    if (ext && mx < wk.rows)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float bv[4];
-        bias4(nlx(q), bv);
-        *(f32x4*)(out + ((size_t)wk.e * ores + wk.row0 + mx) * N + wk.n0 + nlx(q)) =
-            f32x4{accx[4 * q] + bv[0], accx[4 * q + 1] + bv[1], accx[4 * q + 2] + bv[2],
-                  accx[4 * q + 3] + bv[3]};
+      __syncthreads();
+      const int bl = tid & 15;  // this thread's block of 8 features in the half
+      const long r0 = (long)wk.e * ores + wk.row0;
+#pragma unroll 2
+      for (int m = tid >> 4; m < wk.rows; m += NW * 4) {
+        const f32x4 a = *(const f32x4*)(st + m * FSTR + bl * 8);
+        const f32x4 b = *(const f32x4*)(st + m * FSTR + bl * 8 + 4);
+        const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        yq_store8(out, rb, N, r0 + m, wk.n0 + hh * WTN + bl * 8, v);
       }
+      __syncthreads();
+    }
     return;
   }
   uint16_t* out = (uint16_t*)outv;
@@ -528,6 +551,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_ring(
   static_assert(NW == 4 || NW == 8, "waves");
   __shared__ __align__(1024) uint16_t ring[kRSlots * kRBlk];
   static_assert((size_t)kBigRowsMax * (BN + 8) * 2 <= sizeof(ring), "output tile must fit the ring");
+  static_assert((size_t)kBigRowsMax * (BN / 2 + 4) * 4 <= sizeof(ring),
+                "half an output tile in fp32 must fit the ring");
 
   const BigWork wk = work[blockIdx.x];
   if (wk.e < 0) return;
@@ -869,10 +894,11 @@ __global__ __launch_bounds__(256) void big_tail_reduce(const BigHdr* __restrict_
       v[0] += lo[0]; v[1] += lo[1]; v[2] += lo[2]; v[3] += lo[3];
       v[4] += hi[0]; v[5] += hi[1]; v[6] += hi[2]; v[7] += hi[3];
     }
-    if constexpr (EPI == kEpiBiasF32) {
-      float* o = (float*)out + (size_t)(tile.row0 + m) * N + tile.n0 + nl;
-      *(f32x4*)o = f32x4{v[0] + bv[0], v[1] + bv[1], v[2] + bv[2], v[3] + bv[3]};
-      *(f32x4*)(o + 4) = f32x4{v[4] + bv[4], v[5] + bv[5], v[6] + bv[6], v[7] + bv[7]};
+    if constexpr (EPI == kEpiBiasQ) {
+      float y8[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) y8[u] = v[u] + bv[u];
+      yq_store8((unsigned char*)out, yq_row_bytes(N), N, tile.row0 + m, tile.n0 + nl, y8);
       continue;
     }
     u32x4 o, z, pre;

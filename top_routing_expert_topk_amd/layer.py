@@ -41,7 +41,7 @@ class MoEBuffers:
         self.offsets = torch.empty((E + 1,), dtype=i32, device=dev)
         self.dest_row = torch.empty((T * k,), dtype=i32, device=dev)
         self.sorted_token = torch.empty((T * k,), dtype=i32, device=dev)
-        self.y_perm = torch.empty((T * k, d), dtype=f32, device=dev)  # fp32 expert outputs
+        self.y_perm = N.expert_output_buffer(self.dtype, T * k, d, dev)
         self.out = torch.empty((T, d), dtype=self.out_dtype, device=dev)
         self.f = torch.empty((E,), dtype=f32, device=dev)
         self.P = torch.empty((E,), dtype=f32, device=dev)
@@ -122,7 +122,7 @@ class ECBuffers:
         self.sorted_token = torch.empty((max(E * self.Cc, 1),), dtype=i32, device=dev)
         self.dest_row = torch.empty((T, E), dtype=i32, device=dev)
         self.gate = torch.empty((T, E), dtype=f32, device=dev)
-        self.y_perm = torch.empty((T * self.k_ffn, d), dtype=f32, device=dev)
+        self.y_perm = N.expert_output_buffer(self.dtype, T * self.k_ffn, d, dev)
         self.out = torch.empty((T, d), dtype=self.out_dtype, device=dev)
         self.z_perm = self.h_perm = None
         if self.train:

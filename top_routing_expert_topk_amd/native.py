@@ -66,6 +66,8 @@ def load(path):
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_version.argtypes = []
     L.moe_version.restype = I
+    L.moe_expert_output_bytes.argtypes = [I, I, I]
+    L.moe_expert_output_bytes.restype = Z
     L.moe_workspace_size.argtypes = [I, I, I, I, I, I]
     L.moe_workspace_size.restype = Z
     L.moe_router_topk.argtypes = [P, I, I, I, P, P, I, I, I, P, P, P, P, P, Z, P]
@@ -117,6 +119,22 @@ def version() -> int:
 
 def moe_workspace_size(op: int, T: int, d: int, h: int, E: int, k: int) -> int:
     return int(lib().moe_workspace_size(op, T, d, h, E, k))
+
+
+def moe_expert_output_bytes(dtype, rows: int, d: int) -> int:
+    """Bytes of `rows` rows of y_perm for a layer of torch dtype `dtype`."""
+    return int(lib().moe_expert_output_bytes(_DTYPE[dtype], rows, d))
+
+
+def expert_output_buffer(dtype, rows: int, d: int, device):
+    """A y_perm buffer: fp32 [rows][d] for fp32 layers; for bf16 layers
+    [rows][row bytes] uint8 holding the block fixed point."""
+    if dtype == torch.float32:
+        return torch.empty((rows, d), dtype=torch.float32, device=device)
+    rb = moe_expert_output_bytes(dtype, 1, d)
+    if rb == 0:
+        raise ValueError(f"no expert-output layout for {dtype} with d = {d}")
+    return torch.empty((rows, rb), dtype=torch.uint8, device=device)
 
 
 def moe_check_permutation(offsets, E, sorted_token, dest_row, T, k) -> int:

@@ -59,6 +59,9 @@ def parse():
                     help="untimed steps first: on a fresh process the first heavy calls run up to 30%% slower and settle after about ten")
     ap.add_argument("--config", default="deepseek_v3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the 3 s run after the timed steps that reads the shader clock "
+                         "(for counter runs, where every dispatch is serialised)")
     ap.add_argument("--backward", action="store_true",
                     help="time forward + backward (a training step) instead of the forward")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -118,8 +121,8 @@ def summarize_counters(folder, workload, copy_bytes, out_path):
     """Writes the traffic record of one workload: the FFN call's HBM-side
     bytes per call (FETCH_SIZE + WRITE_SIZE, KiB per dispatch, summed over
     the call's kernels), each counter divided by what it reads for a plain
-    device copy of copy_bytes bytes (FETCH_SIZE counts about twice the bytes
-    a copy reads)."""
+    device copy of copy_bytes bytes (FETCH_SIZE reads about half the bytes
+    a copy reads, WRITE_SIZE all it writes)."""
     factor = {}
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         cal = _counter_means(os.path.join(folder, f"pmc_copy_{c}"), c)
@@ -211,10 +214,16 @@ class ClockSampler:
                           "steps; median over the refreshes"}
 
 
-def clock_window(step, seconds=3.0):
+CLOCK_SECONDS = 3.0
+
+
+def clock_window(step, seconds=None):
     """Runs step() back to back for `seconds` (untimed, after the timed
     region) and returns the shader clock the metrics table reported meanwhile."""
     import torch
+    seconds = CLOCK_SECONDS if seconds is None else seconds
+    if seconds <= 0:
+        return {"mhz": None, "note": "not measured (--no-clock)"}
     with ClockSampler() as clk:
         t0 = time.perf_counter()
         n = 0
@@ -542,6 +551,9 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, args.steps)
         return
+    global CLOCK_SECONDS
+    if args.no_clock:
+        CLOCK_SECONDS = 0.0
     import torch
     import moe_inputs as mi
     import top_routing_expert_topk_amd as moe

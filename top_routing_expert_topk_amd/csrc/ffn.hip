@@ -511,8 +511,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 // slot_of[e] of the weight arrays, and only experts with phase_of[e] == phase
 // run, so a launch can cover the resident experts while others are copied in.
 // YQ: the outputs leave in the block fixed point (the second product); a
-// block of 8 features is the 4 of wave w and the 4 of wave w ^ 1, whose
-// largest magnitudes meet in LDS. Otherwise bf16 (H).
+// block of 8 features is the 4 of wave w and the 4 of wave w ^ 1, so the
+// waves leave their sums in LDS and lane 0 of each encodes its 4 against the
+// largest magnitude of the 8. Otherwise bf16 (H).
 template <bool GATHER, bool SILU, bool YQ>
 __global__ __launch_bounds__(256) void decode_bf16(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ sorted_token,
@@ -521,7 +522,7 @@ __global__ __launch_bounds__(256) void decode_bf16(
     const int32_t* __restrict__ slot_of, const int32_t* __restrict__ phase_of, int phase,
     uint16_t* __restrict__ zout) {
   extern __shared__ __align__(16) uint16_t sx[];  // [DG][K]
-  __shared__ float smax[4][DG];                   // YQ: each wave's block half maxima
+  __shared__ float sy[4][DRPW][DG];               // YQ: every wave's outputs of the pass
   const int e = blockIdx.y;
   const int r0 = offsets[e];
   const int cnt = offsets[e + 1] - r0;
@@ -541,8 +542,9 @@ __global__ __launch_bounds__(256) void decode_bf16(
       *(u32x4*)(sx + g * K + kc * 8) = *(const u32x4*)(act + src * K + kc * 8);
     }
     __syncthreads();
-    float yv[DRPW][DG] = {};  // YQ: this wave's outputs, encoded once all 4 are known
-#pragma unroll
+    // not unrolled: two passes' weight loads in flight at once would cost a
+    // wave per SIMD of occupancy, which this HBM-bound loop needs more
+#pragma unroll 1
     for (int rp = 0; rp < DRPW; rp += 2) {
       const int n = nw + rp;
       float acc[2][DG];
@@ -588,8 +590,9 @@ __global__ __launch_bounds__(256) void decode_bf16(
             if (SILU && zout && lane == 0 && na < N)
               zout[(size_t)(r0 + g0 + g) * N + na] = (uint16_t)f32_to_bf16(v);
             if (SILU) v = silu_bf16(v);
-            if constexpr (YQ) yv[rp + a][g] = v;
-            else if (lane == 0 && na < N)
+            if constexpr (YQ) {
+              if (lane == 0) sy[wave][rp + a][g] = v;
+            } else if (lane == 0 && na < N)
               ((uint16_t*)out)[(size_t)(r0 + g0 + g) * N + na] = (uint16_t)f32_to_bf16(v);
           }
         }
@@ -597,26 +600,23 @@ __global__ __launch_bounds__(256) void decode_bf16(
     }
     if constexpr (YQ) {
       // N is a multiple of 16 here, so all 4 features of every wave exist
-#pragma unroll
-      for (int g = 0; g < DG; ++g) {
-        float mx = 0.0f;
-#pragma unroll
-        for (int f = 0; f < DRPW; ++f) mx = fmaxf(mx, fabsf(yv[f][g]));
-        if (lane == 0) smax[wave][g] = mx;
-      }
       __syncthreads();
       if (lane == 0) {
         const size_t rb = yq_row_bytes(N);
 #pragma unroll
         for (int g = 0; g < DG; ++g) {
           if (g < ng) {
-            const int ex = yq_exponent(fmaxf(smax[wave][g], smax[wave ^ 1][g]));
+            float mx = 0.0f;
+#pragma unroll
+            for (int f = 0; f < DRPW; ++f)
+              mx = fmaxf(mx, fmaxf(fabsf(sy[wave][f][g]), fabsf(sy[wave ^ 1][f][g])));
+            const int ex = yq_exponent(mx);
             unsigned char* row = (unsigned char*)out + (size_t)(r0 + g0 + g) * rb;
             u32x2 o;
-            o[0] = ((uint32_t)yq_encode(yv[0][g], ex) & 0xFFFFu) |
-                   ((uint32_t)yq_encode(yv[1][g], ex) << 16);
-            o[1] = ((uint32_t)yq_encode(yv[2][g], ex) & 0xFFFFu) |
-                   ((uint32_t)yq_encode(yv[3][g], ex) << 16);
+            o[0] = ((uint32_t)yq_encode(sy[wave][0][g], ex) & 0xFFFFu) |
+                   ((uint32_t)yq_encode(sy[wave][1][g], ex) << 16);
+            o[1] = ((uint32_t)yq_encode(sy[wave][2][g], ex) & 0xFFFFu) |
+                   ((uint32_t)yq_encode(sy[wave][3][g], ex) << 16);
             *(u32x2*)(row + (size_t)2 * nw) = o;
             if ((wave & 1) == 0) row[(size_t)2 * N + nw / kYBlock] = (unsigned char)(signed char)ex;
           }
@@ -722,7 +722,8 @@ int launch_decode(const uint16_t* x, const int32_t* sorted_token, const int32_t*
                   uint16_t* H, unsigned char* y, int E, int d, int h, const int32_t* slot_of,
                   const int32_t* phase_of, int phase, uint16_t* zout, hipStream_t s) {
   const size_t lds1 = (size_t)DG * d * 2, lds2 = (size_t)DG * h * 2;
-  if (lds1 > 160 * 1024 || lds2 > 160 * 1024) return MOE_ERR_UNSUPPORTED;
+  const size_t lds_static = sizeof(float) * 4 * DRPW * DG;  // the kernel's sy
+  if (lds1 + lds_static > 160 * 1024 || lds2 + lds_static > 160 * 1024) return MOE_ERR_UNSUPPORTED;
   if (lds1 > 65536 &&
       hipFuncSetAttribute((const void*)decode_bf16<true, true, false>,
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1) != hipSuccess)

@@ -49,26 +49,38 @@ __device__ __forceinline__ void fma8(float g, const unsigned char* __restrict__ 
   for (int q = 0; q < 8; ++q) acc[q] = fmaf(g, v[q], acc[q]);
 }
 
-template <typename OutT>
+// KK slots per token (k rounded up to 1, 2, 4, 8 or 16). A token's slot rows
+// are wave-uniform, so their bases sit in scalar registers and every row's
+// load of a column chunk is issued before the first is used (the loads carry
+// no branch). A dropped slot, or one past k, reads the token's first live
+// row with gate 0: it adds a zero, which changes no sum except a -0 to +0.
+template <int KK, typename OutT>
 __global__ __launch_bounds__(256) void combine_bf16(
     const unsigned char* __restrict__ y, const int32_t* __restrict__ dest,
     const float* __restrict__ gate, int T, int k, int d, const uint16_t* __restrict__ resid,
     OutT* __restrict__ out) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * kCombineWaves + (threadIdx.x >> 6);
+  const int t = blockIdx.x * kCombineWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (t >= T) return;
   const size_t rb = yq_row_bytes(d);
-  int dj[kMaxK];
-  float gj[kMaxK];
+  int dj[KK];
+  float gj[KK];
+  int first = -1;
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    if (j < k) {
-      dj[j] = dest[(size_t)t * k + j];
-      gj[j] = gate[(size_t)t * k + j];
-    }
+  for (int j = 0; j < KK; ++j) {
+    dj[j] = j < k ? __builtin_amdgcn_readfirstlane(dest[(size_t)t * k + j]) : -1;
+    gj[j] = j < k ? __int_as_float(__builtin_amdgcn_readfirstlane(
+                        __float_as_int(gate[(size_t)t * k + j])))
+                  : 0.0f;
+    if (first < 0 && dj[j] >= 0) first = dj[j];
   }
-  // two column chunks per pass, so 2 (k + 1) row loads are in flight per lane
-#pragma unroll 2
+  const bool any = first >= 0;
+  const unsigned char* rowp[KK];
+#pragma unroll
+  for (int j = 0; j < KK; ++j) {
+    if (dj[j] < 0) gj[j] = 0.0f;
+    rowp[j] = y + (size_t)(dj[j] >= 0 ? dj[j] : (any ? first : 0)) * rb;
+  }
   for (int c = lane * 8; c < d; c += 64 * 8) {
     float acc[8];
     if (resid) {
@@ -82,9 +94,22 @@ __global__ __launch_bounds__(256) void combine_bf16(
 #pragma unroll
       for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
     }
+    if (any) {
+      u32x4 mant[KK];
+      int ex[KK];
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j)
-      if (j < k && dj[j] >= 0) fma8(gj[j], y, rb, d, dj[j], c, acc);
+      for (int j = 0; j < KK; ++j) {
+        mant[j] = *(const u32x4*)(rowp[j] + (uint32_t)(2 * c));
+        ex[j] = (int)(signed char)rowp[j][(uint32_t)(2 * d + c / kYBlock)];
+      }
+#pragma unroll
+      for (int j = 0; j < KK; ++j) {
+        float v[8];
+        yq_decode8(mant[j], ex[j], v);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = fmaf(gj[j], v[q], acc[q]);
+      }
+    }
     store8<OutT>(out + (size_t)t * d + c, acc);
   }
 }
@@ -172,6 +197,24 @@ __global__ __launch_bounds__(512) void aux_kernel(const float* __restrict__ prob
   if (e == 0) *loss = (float)((double)E * s[0]);
 }
 
+template <int KK, typename OutT>
+void launch_kk(int nb, hipStream_t s, const unsigned char* y, const int32_t* dest,
+               const float* gate, int T, int k, int d, const uint16_t* resid, OutT* out) {
+  hipLaunchKernelGGL((combine_bf16<KK, OutT>), dim3(nb), dim3(256), 0, s, y, dest, gate,
+                     T, k, d, resid, out);
+}
+template <typename OutT>
+bool launch_combine(int k, int nb, hipStream_t s, const unsigned char* y, const int32_t* dest,
+                    const float* gate, int T, int d, const uint16_t* resid, OutT* out) {
+  if (k == 1) launch_kk<1>(nb, s, y, dest, gate, T, k, d, resid, out);
+  else if (k == 2) launch_kk<2>(nb, s, y, dest, gate, T, k, d, resid, out);
+  else if (k <= 4) launch_kk<4>(nb, s, y, dest, gate, T, k, d, resid, out);
+  else if (k <= 8) launch_kk<8>(nb, s, y, dest, gate, T, k, d, resid, out);
+  else if (k <= kMaxK) launch_kk<kMaxK>(nb, s, y, dest, gate, T, k, d, resid, out);
+  else return false;
+  return true;
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -200,17 +243,19 @@ extern "C" int moe_combine(const void* y_perm, int dtype, const int32_t* dest_ro
       hipLaunchKernelGGL(combine_bf16_many<float>, dim3(nb), dim3(256), 0, s,
                          (const unsigned char*)y_perm, dest_row, topk_gate, T, k, d,
                          (const uint16_t*)residual, (float*)out);
-  } else if (dtype == MOE_BF16 && out_dtype == MOE_BF16)
-    hipLaunchKernelGGL(combine_bf16<uint16_t>, dim3(nb), dim3(256), 0, s,
-                       (const unsigned char*)y_perm,
-                       dest_row, topk_gate, T, k, d, (const uint16_t*)residual, (uint16_t*)out);
-  else if (dtype == MOE_BF16)
-    hipLaunchKernelGGL(combine_bf16<float>, dim3(nb), dim3(256), 0, s,
-                       (const unsigned char*)y_perm,
-                       dest_row, topk_gate, T, k, d, (const uint16_t*)residual, (float*)out);
-  else
+  } else if (dtype == MOE_BF16) {
+    const unsigned char* yq = (const unsigned char*)y_perm;
+    const uint16_t* res = (const uint16_t*)residual;
+    if (out_dtype == MOE_BF16) {
+      if (!launch_combine<uint16_t>(k, nb, s, yq, dest_row, topk_gate, T, d, res, (uint16_t*)out))
+        return MOE_ERR_UNSUPPORTED;
+    } else if (!launch_combine<float>(k, nb, s, yq, dest_row, topk_gate, T, d, res, (float*)out)) {
+      return MOE_ERR_UNSUPPORTED;
+    }
+  } else {
     hipLaunchKernelGGL(combine_f32, dim3(nb), dim3(256), 0, s, (const float*)y_perm, dest_row,
                        topk_gate, T, k, d, (const float*)residual, (float*)out);
+  }
   return launch_status();
 }
 

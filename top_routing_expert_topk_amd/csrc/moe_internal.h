@@ -141,12 +141,13 @@ inline int launch_status() {
 
 // Workspace layouts; each op's size function is the single source of truth
 // for both moe_workspace_size() and the call that consumes the workspace.
-constexpr int kRouterTokens = 4;  // tokens per selection block (one per wave)
+constexpr int kRouterTokens = 4;  // fewest tokens per selection block (sizes the partials)
 constexpr int kPermuteChunk = 1024;  // assignments per permute block
 
 // bf16 router logits: blocks of tt tokens x ep (E padded to 64) experts, each
 // over one of `split` ranges of the 32-wide K chunks; fp32 partial logits
 // [split][T][E] are summed in order by the selection kernel.
+constexpr int kRouterMinChunks = 8;
 struct RouterPlan {
   int ep, tt, ntt, nch, split;
 };
@@ -158,8 +159,10 @@ inline RouterPlan router_plan(int T, int d, int E) {
   p.tt = tt;  // 256, 128 or 64 for E <= 512
   p.ntt = ceil_div(T > 0 ? T : 1, tt);
   p.nch = ceil_div(d, 32);
-  int s = 256 / p.ntt;  // about one block per CU: more splits cost more partial traffic
-  if (s > p.nch) s = p.nch;
+  // about one block per CU, but each K range at least kRouterMinChunks chunks:
+  // a shorter one costs more partial-logit traffic than it saves
+  int s = 256 / p.ntt;
+  if (s > p.nch / kRouterMinChunks) s = p.nch / kRouterMinChunks;
   if (s < 1) s = 1;
   p.split = s;
   return p;

@@ -15,19 +15,23 @@
 //                       a long K (d = 7168) spreads over every CU; operands
 //                       reach LDS by direct global->LDS DMA, double-buffered;
 //                       each block writes fp32 partial logits [split][T][E].
-//   router_select       one wave per token: partial logits summed in split
-//                       order (+ bias), then softmax / top-k / gates.
-// fp32 layers (small) use one fused kernel with FMA dot products.
+//   router_select       S lanes per token (8 experts each): partial logits
+//                       summed in split order (+ bias), each lane's top-k
+//                       merged across the S lanes, softmax, gates and the
+//                       block's probability column sums.
+// fp32 layers (small) compute the logits by FMA dot products
+// (router_logits_f32) and run the same selection over them.
 // router_reduce sums the per-block probability partials in a fixed order.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int RT = kRouterTokens;  // tokens per selection block
-constexpr int kWaves = 4;
-constexpr int RT32 = 32;  // tokens per fp32 fused block (a multiple of RT)
-constexpr int RKS = 32;  // K columns per LDS stage (64-byte rows)
+constexpr int RT32 = 32;            // tokens per fp32 logits block
+constexpr int kF32Chunk = 32;       // K columns staged per step (fp32 logits)
+constexpr int kF32Row = kF32Chunk + 1;  // their LDS row stride (no bank conflicts)
+constexpr int RKS = 32;             // K columns per LDS stage (64-byte rows)
+constexpr int kSelectPerLane = 8;   // experts per lane in the selection
 
 // Total order for selection: larger value first, then lower expert index.
 // +0 and -0 map to the same key.
@@ -38,93 +42,6 @@ __device__ __forceinline__ uint32_t ordered_bits(float v) {
 __device__ __forceinline__ float from_ordered_bits(uint32_t o) {
   uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
   return __uint_as_float(u);
-}
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint64_t o = __shfl_xor(v, off, 64);
-    v = o > v ? o : v;
-  }
-  return v;
-}
-__device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
-// One token, one wave. Lane l holds v[i] = logit of expert l + 64 i (i < 8).
-// Writes the k selected experts (descending, lower index first on ties) and
-// their gates, and adds this token's softmax probabilities to pacc.
-__device__ __forceinline__ void select_token(const float (&v)[8], int E, int k, int renorm,
-                                             int lane, int32_t* __restrict__ idx_row,
-                                             float* __restrict__ gate_row, float (&pacc)[8]) {
-  const int EPL = (E + 63) >> 6;
-  uint32_t taken = 0;
-  float selv[kMaxK];
-  int sele[kMaxK];
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    if (j < k) {
-      uint64_t best = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int e = lane + 64 * i;
-        if (i < EPL && e < E && !((taken >> i) & 1u)) {
-          const uint64_t key =
-              ((uint64_t)ordered_bits(v[i]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
-          best = key > best ? key : best;
-        }
-      }
-      best = wave_max_u64(best);
-      const int ej = (int)(0xFFFFFFFFu - (uint32_t)best);
-      if ((ej & 63) == lane) taken |= 1u << (ej >> 6);
-      sele[j] = ej;
-      selv[j] = from_ordered_bits((uint32_t)(best >> 32));
-    }
-  }
-  const float m = selv[0];
-  float ex[8], zl = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int e = lane + 64 * i;
-    ex[i] = (i < EPL && e < E) ? expf(v[i] - m) : 0.0f;
-    zl += ex[i];
-  }
-  const float z = wave_sum_f32(zl);
-  float zs = 0.0f;
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j)
-    if (j < k) zs += expf(selv[j] - m);
-  const float denom = renorm ? zs : z;
-  if (lane == 0) {
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      if (j < k) {
-        idx_row[j] = sele[j];
-        gate_row[j] = expf(selv[j] - m) / denom;
-      }
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) pacc[i] += ex[i] / z;
-}
-
-// Per-block probability partials: the four waves' sums added in wave order.
-__device__ __forceinline__ void write_prob_partial(const float (&pacc)[8], int E, float* part,
-                                                   float* __restrict__ out) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int EPL = (E + 63) >> 6;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int e = lane + 64 * i;
-    if (i < EPL && e < E) part[wave * E + e] = pacc[i];
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256)
-    out[(size_t)blockIdx.x * E + e] =
-        ((part[e] + part[E + e]) + part[2 * E + e]) + part[3 * E + e];
 }
 
 // ---------------------------------------------------- bf16 partial logits --
@@ -247,83 +164,236 @@ __global__ __launch_bounds__(256) void router_logits_bf16(
     }
 }
 
+// Insert key into top[0..KK) (descending), dropping the smallest.
+template <int KK>
+__device__ __forceinline__ void topk_insert(uint64_t (&top)[KK], uint64_t key) {
+#pragma unroll
+  for (int j = 0; j < KK; ++j) {
+    const uint64_t hi = top[j] > key ? top[j] : key;
+    key = top[j] > key ? key : top[j];
+    top[j] = hi;
+  }
+}
+// top (descending) becomes the KK largest of top and o (both descending):
+// the larger of top[j] and o[KK-1-j] are those KK and form a bitonic
+// sequence, which half-cleaners of width KK/2 .. 1 sort.
+template <int KK>
+__device__ __forceinline__ void topk_merge(uint64_t (&top)[KK], const uint64_t (&o)[KK]) {
+#pragma unroll
+  for (int j = 0; j < KK; ++j) top[j] = top[j] > o[KK - 1 - j] ? top[j] : o[KK - 1 - j];
+#pragma unroll
+  for (int h = KK / 2; h >= 1; h >>= 1)
+#pragma unroll
+    for (int j = 0; j < KK; ++j)
+      if ((j & h) == 0) {
+        const uint64_t a = top[j], b = top[j + h];
+        top[j] = a > b ? a : b;
+        top[j + h] = a > b ? b : a;
+      }
+}
+
+// Selection over the partial logits: S lanes per token (a power of two),
+// each holding NPL = 8 of its experts (consecutive ones, e = sg * 8 + i, when
+// rows split into 16-byte pieces; else e = sg + S * i), so a block of 4 waves
+// takes 256 / S tokens. A lane sums its experts' partials in split order
+// (+ bias), keeps its KK largest keys (logit, then lower index first), and
+// the S lanes merge their lists by xor butterflies, after which every lane
+// of the token holds the token's top KK. The softmax denominator is the
+// xor-butterfly sum of the lanes' sums (the same bits on every lane), and
+// the block's probability column sums run over its tokens in order.
+template <int S, int KK>
 __global__ __launch_bounds__(256) void router_select(
     const float* __restrict__ part, int split, const float* __restrict__ gbias, int T, int E,
     int k, int renorm, float* __restrict__ logits_out, int32_t* __restrict__ idx_out,
     float* __restrict__ gate_out, float* __restrict__ probpart) {
-  __shared__ float wpart[kWaves * kMaxE];
+  constexpr int NPL = kSelectPerLane;
+  constexpr int TPW = 64 / S, TB = 4 * TPW;  // tokens per wave, per block
+  __shared__ float sp[TB * S * NPL];         // [TB][E] logits, then probabilities (E <= S * NPL)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int EPL = (E + 63) >> 6;
-  float pacc[8];
+  const int tl = wave * TPW + lane / S, sg = lane % S;
+  const int t = blockIdx.x * TB + tl;
+  const bool valid = t < T;
+  const bool vec = (NPL % 4) == 0 && (E % 4) == 0;
+  auto expert = [&](int i) { return vec ? sg * NPL + i : sg + S * i; };
+  float v[NPL];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) pacc[i] = 0.0f;
-  const int t = blockIdx.x * RT + wave;
-  if (t < T) {
-    float v[8];
+  for (int i = 0; i < NPL; ++i) v[i] = 0.0f;
+  if (valid) {
+    const size_t plane = (size_t)T * E;
+    const float* src = part + (size_t)t * E;
+    // PB planes per batch, so that about 16 loads per lane are in flight
+    if (vec) {
+      constexpr int NQ = NPL / 4 > 0 ? NPL / 4 : 1, PB = 16 / NQ > 0 ? 16 / NQ : 1;
+      for (int p0 = 0; p0 < split; p0 += PB) {
+        f32x4 a[PB][NQ];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int e = lane + 64 * i;
-      float s = 0.0f;
-      if (i < EPL && e < E) {
-        // partials in split order; loads issued 8 at a time
-        const float* src = part + (size_t)t * E + e;
-        const size_t stride = (size_t)T * E;
-        int p = 0;
-        for (; p + 8 <= split; p += 8) {
-          float q[8];
+        for (int u = 0; u < PB; ++u)
 #pragma unroll
-          for (int u = 0; u < 8; ++u) q[u] = src[(size_t)(p + u) * stride];
+          for (int q = 0; q < NQ; ++q)
+            if (p0 + u < split && sg * NPL + 4 * q < E)
+              a[u][q] = *(const f32x4*)(src + (size_t)(p0 + u) * plane + sg * NPL + 4 * q);
 #pragma unroll
-          for (int u = 0; u < 8; ++u) s += q[u];
-        }
-        for (; p < split; ++p) s += src[(size_t)p * stride];
-        if (gbias) s += gbias[e];
-        if (logits_out) logits_out[(size_t)t * E + e] = s;
+        for (int u = 0; u < PB; ++u)
+#pragma unroll
+          for (int q = 0; q < NQ; ++q)
+            if (p0 + u < split && sg * NPL + 4 * q < E)
+#pragma unroll
+              for (int w = 0; w < 4; ++w) v[4 * q + w] += a[u][q][w];
       }
-      v[i] = s;
+    } else {
+      constexpr int PB = 16 / NPL > 0 ? 16 / NPL : 1;
+      for (int p0 = 0; p0 < split; p0 += PB) {
+        float a[PB][NPL];
+#pragma unroll
+        for (int u = 0; u < PB; ++u)
+#pragma unroll
+          for (int i = 0; i < NPL; ++i)
+            if (p0 + u < split && expert(i) < E) a[u][i] = src[(size_t)(p0 + u) * plane + expert(i)];
+#pragma unroll
+        for (int u = 0; u < PB; ++u)
+#pragma unroll
+          for (int i = 0; i < NPL; ++i)
+            if (p0 + u < split && expert(i) < E) v[i] += a[u][i];
+      }
     }
-    select_token(v, E, k, renorm, lane, idx_out + (size_t)t * k, gate_out + (size_t)t * k, pacc);
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int e = expert(i);
+      if (e < E) {
+        if (gbias) v[i] += gbias[e];
+        if (logits_out) logits_out[(size_t)t * E + e] = v[i];
+      }
+    }
   }
-  write_prob_partial(pacc, E, wpart, probpart);
-}
-
-// ----------------------------------------------------------- fp32 fused --
-// RT tokens per block: logits by FMA dot products into LDS, then selection.
-__global__ __launch_bounds__(256) void router_f32(
-    const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ gbias,
-    int T, int d, int E, int k, int renorm, float* __restrict__ logits_out,
-    int32_t* __restrict__ idx_out, float* __restrict__ gate_out, float* __restrict__ probpart) {
-  extern __shared__ float lg[];  // [RT32][E] then [kWaves][E]
-  const int t0 = blockIdx.x * RT32;
-  for (int pi = threadIdx.x; pi < RT32 * E; pi += 256) {
-    const int tl = pi / E, e = pi % E, t = t0 + tl;
-    float s = 0.0f;
-    if (t < T) {
-      const float* xr = x + (size_t)t * d;
-      const float* wr = w + (size_t)e * d;
-      for (int i = 0; i < d; ++i) s = fmaf(xr[i], wr[i], s);
+  auto key = [](float x, int e) {
+    return ((uint64_t)ordered_bits(x) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+  };
+  uint64_t top[KK];
+#pragma unroll
+  for (int j = 0; j < KK; ++j) top[j] = 0;
+  if constexpr (KK <= 2) {
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int e = expert(i);
+      topk_insert(top, (valid && e < E) ? key(v[i], e) : 0ull);
     }
-    lg[pi] = s + (gbias ? gbias[e] : 0.0f);
+  } else {
+    // With k <= S, a logit below the smallest of the S lanes' largest has at
+    // least S larger ones, so only logits at or above it are inserted; they
+    // are read back from LDS in a loop that runs as often as the lane with
+    // the most of them needs.
+    float lm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int e = expert(i);
+      if (e < E) {
+        lm = fmaxf(lm, v[i]);
+        sp[tl * E + e] = v[i];
+      }
+    }
+    float tau = lm;
+#pragma unroll
+    for (int off = 1; off < S; off <<= 1) tau = fminf(tau, __shfl_xor(tau, off, 64));
+    if (k > S) tau = -INFINITY;
+    uint32_t cand = 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      if (valid && expert(i) < E && v[i] >= tau) cand |= 1u << i;
+    while (cand) {
+      const int i = __builtin_ctz(cand);
+      cand &= cand - 1;
+      const int e = expert(i);
+      topk_insert(top, key(sp[tl * E + e], e));
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < S; off <<= 1) {
+    uint64_t o[KK];
+#pragma unroll
+    for (int j = 0; j < KK; ++j) o[j] = __shfl_xor(top[j], off, 64);
+    topk_merge(top, o);
+  }
+  const float m = from_ordered_bits((uint32_t)(top[0] >> 32));
+  float ex[NPL], zl = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    ex[i] = (valid && expert(i) < E) ? expf(v[i] - m) : 0.0f;
+    zl += ex[i];
+  }
+  float z = zl;
+#pragma unroll
+  for (int off = 1; off < S; off <<= 1) z += __shfl_xor(z, off, 64);
+  if (valid && sg == 0) {
+    float selv[KK], zs = 0.0f;
+#pragma unroll
+    for (int j = 0; j < KK; ++j) {
+      selv[j] = from_ordered_bits((uint32_t)(top[j] >> 32));
+      if (j < k) zs += expf(selv[j] - m);
+    }
+    const float denom = renorm ? zs : z;
+#pragma unroll
+    for (int j = 0; j < KK; ++j) {
+      if (j < k) {
+        idx_out[(size_t)t * k + j] = (int)(0xFFFFFFFFu - (uint32_t)top[j]);
+        gate_out[(size_t)t * k + j] = expf(selv[j] - m) / denom;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int e = expert(i);
+    if (e < E) sp[tl * E + e] = valid ? ex[i] / z : 0.0f;
   }
   __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int EPL = (E + 63) >> 6;
-  float pacc[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) pacc[i] = 0.0f;
-  for (int tl = wave; tl < RT32; tl += kWaves) {
-    const int t = t0 + tl;
-    if (t >= T) break;
-    float v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int e = lane + 64 * i;
-      v[i] = (i < EPL && e < E) ? lg[tl * E + e] : 0.0f;
-      if (logits_out && i < EPL && e < E) logits_out[(size_t)t * E + e] = v[i];
-    }
-    select_token(v, E, k, renorm, lane, idx_out + (size_t)t * k, gate_out + (size_t)t * k, pacc);
+  for (int e = threadIdx.x; e < E; e += 256) {
+    float s = 0.0f;
+    for (int r = 0; r < TB; ++r) s += sp[r * E + e];
+    probpart[(size_t)blockIdx.x * E + e] = s;
   }
-  write_prob_partial(pacc, E, lg + RT32 * E, probpart);
+}
+
+// ------------------------------------------------------------ fp32 logits --
+// RT32 tokens x E experts per block by FMA dot products, each over
+// i = 0 .. d-1 in order, a chunk of columns at a time from rows staged in LDS
+// by coalesced loads; the logits (without bias) go to part [T][E], which the
+// selection then reads as a single K range.
+__global__ __launch_bounds__(256) void router_logits_f32(
+    const float* __restrict__ x, const float* __restrict__ w, int T, int d, int E,
+    float* __restrict__ part) {
+  // [RT32][E] sums, then RT32 token rows and E expert rows of a chunk
+  extern __shared__ float lg[];
+  float* xs = lg + RT32 * E;
+  float* ws = xs + RT32 * kF32Row;
+  const int t0 = blockIdx.x * RT32;
+  for (int pi = threadIdx.x; pi < RT32 * E; pi += 256) lg[pi] = 0.0f;
+  for (int c0 = 0; c0 < d; c0 += kF32Chunk) {
+    const int nc = min(kF32Chunk, d - c0);
+    __syncthreads();  // the previous chunk's reads are done
+    for (int q = threadIdx.x; q < (RT32 + E) * kF32Chunk; q += 256) {
+      const int r = q / kF32Chunk, c = q % kF32Chunk;
+      float val = 0.0f;
+      if (c < nc) {
+        if (r < RT32) {
+          if (t0 + r < T) val = x[(size_t)(t0 + r) * d + c0 + c];
+        } else {
+          val = w[(size_t)(r - RT32) * d + c0 + c];
+        }
+      }
+      (r < RT32 ? xs + r * kF32Row : ws + (r - RT32) * kF32Row)[c] = val;
+    }
+    __syncthreads();
+    for (int pi = threadIdx.x; pi < RT32 * E; pi += 256) {
+      const int tl = pi / E, e = pi % E;
+      const float* xr = xs + tl * kF32Row;
+      const float* wr = ws + e * kF32Row;
+      float s = lg[pi];
+      for (int i = 0; i < nc; ++i) s = fmaf(xr[i], wr[i], s);
+      lg[pi] = s;
+    }
+  }
+  __syncthreads();
+  for (int pi = threadIdx.x; pi < RT32 * E; pi += 256)
+    if (t0 + pi / E < T) part[(size_t)t0 * E + pi] = lg[pi];
 }
 
 // prob_sum[e] = sum over blocks of probpart[b][e]: fixed-order tree in double.
@@ -358,6 +428,54 @@ bool launch_logits(const RouterPlan& pl, const void* x, const void* w, int T, in
   hipLaunchKernelGGL((router_logits_bf16<MTW, NTE>), dim3(pl.ntt * pl.split), dim3(256), lds, s,
                      (const uint16_t*)x, (const uint16_t*)w, T, d, E, pl.nch, pl.split, part);
   return true;
+}
+
+// Lanes per token for E experts: the power of two S with S * kSelectPerLane
+// >= E (so 64 / S tokens per wave, 4 waves per block).
+inline int select_lanes(int E) {
+  int s = 1;
+  while (s * kSelectPerLane < E) s <<= 1;
+  return s;
+}
+inline int select_tokens(int E) { return 4 * (64 / select_lanes(E)); }
+
+template <int S>
+bool launch_select_k(int k, int nb, hipStream_t s, const float* part, int split, const float* gbias,
+                     int T, int E, int renorm, float* logits_out, int32_t* idx, float* gate,
+                     float* probpart) {
+#define MOE_SEL(KK)                                                                            \
+  hipLaunchKernelGGL((router_select<S, KK>), dim3(nb), dim3(256), 0, s, part, split, gbias, T, E, \
+                     k, renorm, logits_out, idx, gate, probpart)
+  if (k == 1) MOE_SEL(1);
+  else if (k == 2) MOE_SEL(2);
+  else if (k <= 4) MOE_SEL(4);
+  else if (k <= 8) MOE_SEL(8);
+  else if (k <= 16) MOE_SEL(16);
+  else return false;
+#undef MOE_SEL
+  return true;
+}
+
+bool launch_select(int k, hipStream_t s, const float* part, int split, const float* gbias, int T,
+                   int E, int renorm, float* logits_out, int32_t* idx, float* gate,
+                   float* probpart) {
+  const int nb = ceil_div(T, select_tokens(E));
+  switch (select_lanes(E)) {
+#define MOE_S(S)                                                                             \
+  case S:                                                                                    \
+    return launch_select_k<S>(k, nb, s, part, split, gbias, T, E, renorm, logits_out, idx, \
+                              gate, probpart);
+    MOE_S(1)
+    MOE_S(2)
+    MOE_S(4)
+    MOE_S(8)
+    MOE_S(16)
+    MOE_S(32)
+    MOE_S(64)
+#undef MOE_S
+    default:
+      return false;
+  }
 }
 
 bool dispatch_logits(const RouterPlan& pl, const void* x, const void* w, int T, int d, int E,
@@ -402,25 +520,27 @@ extern "C" int moe_router_topk(const void* x, int dtype, int T, int d, const voi
   }
   if (!x || !w_gate || !topk_idx || !topk_gate) return MOE_ERR_INVALID;
   if (!ws || ws_bytes < router_ws(T, d, E)) return MOE_ERR_WORKSPACE;
-  int nb = router_blocks(T);
   float* logit_part = (float*)ws;
   float* probpart = (float*)((unsigned char*)ws + router_partial_bytes(T, d, E));
   if (dtype == MOE_BF16) {
     const RouterPlan pl = router_plan(T, d, E);
     if (!dispatch_logits(pl, x, w_gate, T, d, E, logit_part, s)) return MOE_ERR_LAUNCH;
-    hipLaunchKernelGGL(router_select, dim3(nb), dim3(256), 0, s, logit_part, pl.split, gate_bias,
-                       T, E, k, renorm, logits_out, topk_idx, topk_gate, probpart);
-  } else {
-    const size_t lds = (size_t)(RT32 + kWaves) * E * sizeof(float);
-    if (lds > 65536 &&
-        hipFuncSetAttribute((const void*)router_f32, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)lds) != hipSuccess)
+    if (!launch_select(k, s, logit_part, pl.split, gate_bias, T, E, renorm, logits_out, topk_idx,
+                       topk_gate, probpart))
       return MOE_ERR_LAUNCH;
-    nb = ceil_div(T, RT32);
-    hipLaunchKernelGGL(router_f32, dim3(nb), dim3(256), lds, s, (const float*)x,
-                       (const float*)w_gate, gate_bias, T, d, E, k, renorm, logits_out, topk_idx,
-                       topk_gate, probpart);
+  } else {
+    const size_t lds = ((size_t)RT32 * E + (size_t)(RT32 + E) * kF32Row) * sizeof(float);
+    if (lds > 65536 &&
+        hipFuncSetAttribute((const void*)router_logits_f32,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return MOE_ERR_LAUNCH;
+    hipLaunchKernelGGL(router_logits_f32, dim3(ceil_div(T, RT32)), dim3(256), lds, s,
+                       (const float*)x, (const float*)w_gate, T, d, E, logit_part);
+    if (!launch_select(k, s, logit_part, 1, gate_bias, T, E, renorm, logits_out, topk_idx,
+                       topk_gate, probpart))
+      return MOE_ERR_LAUNCH;
   }
+  const int nb = ceil_div(T, select_tokens(E));
   if (prob_sum)
     hipLaunchKernelGGL(router_reduce, dim3(E), dim3(256), 0, s, probpart, nb, E, prob_sum);
   return launch_status();

@@ -10,11 +10,13 @@
 // the probabilities) so that no tie is created by rounding in exp.
 //
 // bf16 layers run two kernels:
-//   router_logits_bf16  a skinny MFMA GEMM split over (token tile, K range)
+//   router_logits_wide  a skinny MFMA GEMM split over (token tile, K range)
 //                       blocks so that even a handful of tokens (decode) or
 //                       a long K (d = 7168) spreads over every CU; operands
-//                       reach LDS by direct global->LDS DMA, double-buffered;
-//                       each block writes fp32 partial logits [split][T][E].
+//                       reach LDS by direct global->LDS DMA through a ring of
+//                       stages; each block writes fp32 partial logits
+//                       [split][T][E]. router_logits_bf16 is the same product
+//                       on 16x16x32 tiles for d not a multiple of 64.
 //   router_select       S lanes per token (8 experts each): partial logits
 //                       summed in split order (+ bias), each lane's top-k
 //                       merged across the S lanes, softmax, gates and the
@@ -352,6 +354,122 @@ __global__ __launch_bounds__(256) void router_select(
   }
 }
 
+// ------------------------------------------- bf16 logits, 32x32x16 tiles --
+// The same split-K product for d a multiple of 64, with 64-column stages
+// (128-byte LDS rows, chunk c of row r at c ^ ((r >> 1) & 7), which puts the
+// 16 rows a ds_read_b128 serves at once on distinct bank groups) and the
+// four waves in a 2 x 2 grid, each owning (TT/2) tokens x (EP/2) experts as
+// TM x TN v_mfma_f32_32x32x16_bf16 tiles: per 16 k a wave reads TM + TN
+// fragments for TM * TN MFMAs. Lane l supplies row l%32 and k-octet l/32 of
+// both operands (A = 32 experts, B = 32 tokens) and receives expert
+// 8*(v/4) + 4*(l/32) + v%4 of token l%32 in accumulator v.
+constexpr int RK2 = 64;  // K columns per stage
+__device__ __forceinline__ int swz8(int r, int c) { return c ^ ((r >> 1) & 7); }
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <int TM, int TN>
+struct WideCfg {
+  static constexpr int TT = 64 * TM, EP = 64 * TN, ROWS = TT + EP;
+  static constexpr int STAGE = ROWS * RK2;  // bf16 elements
+  static constexpr int NS0 = 163840 / (STAGE * 2);
+  static constexpr int NS = NS0 < 2 ? 2 : NS0 > 4 ? 4 : NS0;
+  static constexpr size_t LDS = (size_t)NS * STAGE * 2;
+};
+
+template <int TM, int TN>
+__global__ __launch_bounds__(256) void router_logits_wide(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int T, int d, int E, int nch,
+    int split, float* __restrict__ part) {
+  using C = WideCfg<TM, TN>;
+  constexpr int TT = C::TT, EP = C::EP, ROWS = C::ROWS, STAGE = C::STAGE, NS = C::NS;
+  constexpr int IPW = ROWS / 8 / 4;  // DMA instructions (8 rows each) per wave per stage
+  static_assert((ROWS / 8) % 4 == 0, "DMA instructions split over the four waves");
+  extern __shared__ __align__(1024) uint16_t rs[];
+  const int tile = blockIdx.x / split, p = blockIdx.x % split;
+  const int t0 = tile * TT;
+  const int c0 = p * nch / split, c1 = (p + 1) * nch / split;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const uint16_t* src[IPW];
+#pragma unroll
+  for (int q = 0; q < IPW; ++q) {
+    const int r = (q * 4 + wave) * 8 + (lane >> 3);
+    const uint16_t* base = r < TT ? x + (size_t)min(t0 + r, T - 1) * d
+                                  : w + (size_t)min(r - TT, E - 1) * d;
+    src[q] = base + swz8(r, lane & 7) * 8;
+  }
+  auto issue = [&](int buf, int c) {
+#pragma unroll
+    for (int q = 0; q < IPW; ++q)
+      dma16(src[q] + (size_t)c * RK2, &rs[buf * STAGE + (q * 4 + wave) * 8 * RK2]);
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+
+  const int ch = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i)
+    if (c0 + i < c1) issue(i, c0 + i);
+  for (int c = c0; c < c1; ++c) {
+    const int buf = (c - c0) % NS;
+    // as in router_logits_bf16: chunk c has landed for this wave, and after
+    // the barrier for every wave, whose reads of chunk c - 1 are done
+    const int later = min(c1 - 1 - c, NS - 2);
+    if (NS > 3 && later >= 2) wait_vm<(NS > 3 ? 2 : 0) * IPW>();
+    else if (NS > 2 && later >= 1) wait_vm<(NS > 2 ? 1 : 0) * IPW>();
+    else wait_vm<0>();
+    lds_barrier();
+    if (c + NS - 1 < c1) issue((c - c0 + NS - 1) % NS, c + NS - 1);
+    const uint16_t* st = rs + buf * STAGE;
+#pragma unroll
+    for (int s = 0; s < RK2 / 16; ++s) {
+      bf16x8 a[TN], b[TM];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int r = TT + wn * (EP / 2) + 32 * j + (lane & 31);
+        a[j] = *(const bf16x8*)(st + r * RK2 + swz8(r, 2 * s + ch) * 8);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm * (TT / 2) + 32 * i + (lane & 31);
+        b[i] = *(const bf16x8*)(st + r * RK2 + swz8(r, 2 * s + ch) * 8);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], b[i], acc[i][j], 0, 0, 0);
+    }
+  }
+  float* pp = part + (size_t)p * T * E;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int t = t0 + wm * (TT / 2) + 32 * i + (lane & 31);
+    if (t >= T) continue;
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int e = wn * (EP / 2) + 32 * j + 8 * g + 4 * ch;
+        float* dst = pp + (size_t)t * E + e;
+        if ((E & 3) == 0) {
+          if (e < E)
+            *(f32x4*)dst = f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                 acc[i][j][4 * g + 3]};
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (e + u < E) dst[u] = acc[i][j][4 * g + u];
+        }
+      }
+  }
+}
+
 // ------------------------------------------------------------ fp32 logits --
 // RT32 tokens x E experts per block by FMA dot products, each over
 // i = 0 .. d-1 in order, a chunk of columns at a time from rows staged in LDS
@@ -478,9 +596,35 @@ bool launch_select(int k, hipStream_t s, const float* part, int split, const flo
   }
 }
 
+template <int TM, int TN>
+bool launch_wide(const RouterPlan& pl, const void* x, const void* w, int T, int d, int E,
+                 float* part, hipStream_t s) {
+  const size_t lds = WideCfg<TM, TN>::LDS;
+  if (lds > 65536 &&
+      hipFuncSetAttribute((const void*)router_logits_wide<TM, TN>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+    return false;
+  hipLaunchKernelGGL((router_logits_wide<TM, TN>), dim3(pl.ntt * pl.split), dim3(256), lds, s,
+                     (const uint16_t*)x, (const uint16_t*)w, T, d, E, d / RK2, pl.split, part);
+  return true;
+}
+
 bool dispatch_logits(const RouterPlan& pl, const void* x, const void* w, int T, int d, int E,
                      float* part, hipStream_t s) {
   const int mtw = pl.tt / 64, nte = pl.ep / 16;
+  if (d % RK2 == 0 && pl.split <= d / RK2) {
+#define MOE_WIDE(A, B)                                                                 \
+  if (mtw == A && nte == 4 * B) return launch_wide<A, B>(pl, x, w, T, d, E, part, s);
+    MOE_WIDE(4, 1)
+    MOE_WIDE(4, 2)
+    MOE_WIDE(2, 3)
+    MOE_WIDE(2, 4)
+    MOE_WIDE(1, 5)
+    MOE_WIDE(1, 6)
+    MOE_WIDE(1, 7)
+    MOE_WIDE(1, 8)
+#undef MOE_WIDE
+  }
 #define MOE_CASE(A, B)                               \
   if (mtw == A && nte == B) return launch_logits<A, B>(pl, x, w, T, d, E, part, s);
   MOE_CASE(4, 4)

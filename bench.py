@@ -583,8 +583,8 @@ def main():
         b = bufs
         if ev is not None:
             ev[0].record(stream)
-        N.moe_router_topk(x, inp["w_gate"], inp["gate_bias"], E, 1, True, b.logits, b.topk_idx,
-                          b.topk_gate, None, b.ws_router, stream)
+        N.moe_router_topk(x, inp["w_gate"], inp["gate_bias"], E, 1, True, b.logits, None, None,
+                          None, b.ws_router, stream)
         if ev is not None:
             ev[1].record(stream)
         N.moe_expert_choice(b.logits, T, E, cfg.capacity, b.scores, b.offsets, b.sorted_token,

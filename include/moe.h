@@ -133,6 +133,9 @@ size_t moe_workspace_size(int op, int T, int d, int h, int E, int k);
  * x [T][d] dtype; w_gate [E][d] dtype; gate_bias [E] fp32 or NULL;
  * logits_out [T][E] fp32 or NULL; topk_idx [T][k] int32; topk_gate [T][k]
  * fp32; prob_sum [E] fp32 or NULL. 1 <= k <= E <= 512, k <= 16, T >= 0.
+ * With topk_idx, topk_gate and prob_sum all NULL only the logits are
+ * computed (logits_out is then required; Expert Choice routes from them);
+ * they are the same bits as in a full call.
  * Workspace: moe_workspace_size(MOE_OP_ROUTER, ...).
  */
 int moe_router_topk(const void *x, int dtype, int T, int d, const void *w_gate,

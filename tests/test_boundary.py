@@ -91,6 +91,10 @@ def test_router_rejects_bad_arguments():
     assert _router(d=60) == N.MOE_ERR_UNSUPPORTED
     assert _router(x=None) == N.MOE_ERR_INVALID
     assert _router(idx=None) == N.MOE_ERR_INVALID
+    assert _router(gate=None) == N.MOE_ERR_INVALID
+    # logits only (no idx, gate or prob_sum) needs logits_out
+    assert _router(idx=None, gate=None, ps=None, lg=None) == N.MOE_ERR_INVALID
+    assert _router(idx=None, gate=None, ps=BAD, lg=BAD) == N.MOE_ERR_INVALID
     assert _router(wsb=16) == N.MOE_ERR_WORKSPACE
     assert _router(ws=None) == N.MOE_ERR_WORKSPACE
 

@@ -268,3 +268,40 @@ def test_router_at_scale(T, E, k, d, bias):
     r = check_layer(cfg, inp, b, tokens=np.zeros(0, np.int32),
                     e2e_tokens=sample_tokens(T, 2048, seed=7))
     print(f"[parity] {cfg.name}: {r}", flush=True)
+
+
+@pytest.mark.parametrize("dtype,T,d,E,k,bias", [("bf16", 1000, 96, 100, 5, True),
+                                                ("bf16", 777, 320, 130, 2, False),
+                                                ("f32", 333, 72, 7, 3, True)])
+def test_router_alone_and_logits_only(dtype, T, d, E, k, bias):
+    """moe_router_topk on its own: a width that is not a multiple of 64 (the
+    16x16x32 logits kernel), one that is, and fp32 with E % 4 != 0. The
+    selection is bit-exact with the oracle's on the same logits and the
+    logits match the oracle's double ones; a call with no top-k, gate or
+    probability outputs writes the same logits bit for bit."""
+    from oracle import oracle as orc
+    from top_routing_expert_topk_amd import native as N
+    cfg = CFG["deepseek_v3"].with_(name="router_alone", T=T, d=d, h=64, E=E, k=k, dtype=dtype,
+                                   zipf_gate_bias=bias)
+    print(f"[parity] router alone: {dtype} T={T} d={d} E={E} k={k} bias={bias}", flush=True)
+    inp = mi.make_inputs(cfg, "cuda")
+    x, wg, gb = inp["x"], inp["w_gate"], inp["gate_bias"]
+    ws = torch.empty(N.moe_workspace_size(N.MOE_OP_ROUTER, T, d, 0, E, k), dtype=torch.uint8,
+                     device="cuda")
+    lg = torch.empty((T, E), device="cuda")
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    gate = torch.empty((T, k), device="cuda")
+    ps = torch.empty((E,), device="cuda")
+    N.moe_router_topk(x, wg, gb, E, k, True, lg, idx, gate, ps, ws)
+    lg2 = torch.full((T, E), float("nan"), device="cuda")
+    N.moe_router_topk(x, wg, gb, E, k, True, lg2, None, None, None, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(lg, lg2), "logits-only call"
+    lg_h = lg.cpu().numpy()
+    o_idx, o_gate, o_ps = orc.route(lg_h, k, True)
+    assert np.array_equal(idx.cpu().numpy(), o_idx), "top-k indices on the same logits"
+    assert np.abs(gate.cpu().numpy() - o_gate).max() <= 1e-5
+    assert np.allclose(ps.cpu().numpy(), o_ps, rtol=1e-5, atol=1e-6)
+    lg_o = orc.logits(mi.to_host_array(x), mi.to_host_array(wg), None if gb is None else gb.cpu().numpy())
+    tol = 1e-4 if dtype == "bf16" else 1e-5
+    assert np.abs(lg_h - lg_o).max() <= tol * max(1.0, float(np.abs(lg_o).max()))

@@ -514,6 +514,32 @@ __global__ __launch_bounds__(256) void router_logits_f32(
     if (t0 + pi / E < T) part[(size_t)t0 * E + pi] = lg[pi];
 }
 
+// Logits only: the partials summed in split order (+ bias), as the
+// selection sums them, four logits per thread when E % 4 == 0.
+__global__ __launch_bounds__(256) void router_sum(const float* __restrict__ part, int split,
+                                                  const float* __restrict__ gbias, int T, int E,
+                                                  float* __restrict__ logits_out) {
+  const size_t plane = (size_t)T * E;
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= plane) return;
+  if ((E & 3) == 0) {
+    f32x4 s = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int p = 0; p < split; ++p) s += *(const f32x4*)(part + (size_t)p * plane + i);
+    if (gbias) {
+      const int e = (int)(i % (size_t)E);
+      s += f32x4{gbias[e], gbias[e + 1], gbias[e + 2], gbias[e + 3]};
+    }
+    *(f32x4*)(logits_out + i) = s;
+  } else {
+    for (size_t j = i; j < i + 4 && j < plane; ++j) {
+      float s = 0.0f;
+      for (int p = 0; p < split; ++p) s += part[(size_t)p * plane + j];
+      if (gbias) s += gbias[j % (size_t)E];
+      logits_out[j] = s;
+    }
+  }
+}
+
 // prob_sum[e] = sum over blocks of probpart[b][e]: fixed-order tree in double.
 __global__ __launch_bounds__(256) void router_reduce(const float* __restrict__ probpart, int nb,
                                                       int E, float* __restrict__ prob_sum) {
@@ -662,13 +688,21 @@ extern "C" int moe_router_topk(const void* x, int dtype, int T, int d, const voi
     }
     return MOE_OK;
   }
-  if (!x || !w_gate || !topk_idx || !topk_gate) return MOE_ERR_INVALID;
+  // logits only: no selection, gates or probability sums asked for
+  const bool only_logits = !topk_idx && !topk_gate && !prob_sum;
+  if (!x || !w_gate) return MOE_ERR_INVALID;
+  if (only_logits ? !logits_out : (!topk_idx || !topk_gate)) return MOE_ERR_INVALID;
   if (!ws || ws_bytes < router_ws(T, d, E)) return MOE_ERR_WORKSPACE;
   float* logit_part = (float*)ws;
   float* probpart = (float*)((unsigned char*)ws + router_partial_bytes(T, d, E));
   if (dtype == MOE_BF16) {
     const RouterPlan pl = router_plan(T, d, E);
     if (!dispatch_logits(pl, x, w_gate, T, d, E, logit_part, s)) return MOE_ERR_LAUNCH;
+    if (only_logits) {
+      hipLaunchKernelGGL(router_sum, dim3((unsigned)ceil_div((long)T * E, 1024)), dim3(256), 0, s,
+                         logit_part, pl.split, gate_bias, T, E, logits_out);
+      return launch_status();
+    }
     if (!launch_select(k, s, logit_part, pl.split, gate_bias, T, E, renorm, logits_out, topk_idx,
                        topk_gate, probpart))
       return MOE_ERR_LAUNCH;
@@ -680,6 +714,11 @@ extern "C" int moe_router_topk(const void* x, int dtype, int T, int d, const voi
       return MOE_ERR_LAUNCH;
     hipLaunchKernelGGL(router_logits_f32, dim3(ceil_div(T, RT32)), dim3(256), lds, s,
                        (const float*)x, (const float*)w_gate, T, d, E, logit_part);
+    if (only_logits) {
+      hipLaunchKernelGGL(router_sum, dim3((unsigned)ceil_div((long)T * E, 1024)), dim3(256), 0, s,
+                         logit_part, 1, gate_bias, T, E, logits_out);
+      return launch_status();
+    }
     if (!launch_select(k, s, logit_part, 1, gate_bias, T, E, renorm, logits_out, topk_idx,
                        topk_gate, probpart))
       return MOE_ERR_LAUNCH;

@@ -115,8 +115,6 @@ class ECBuffers:
         self.Cc = max(0, min(self.C, T))
         self.k_ffn = ec_ffn_k(T, E, self.C)
         self.logits = torch.empty((T, E), dtype=f32, device=dev)
-        self.topk_idx = torch.empty((T, 1), dtype=i32, device=dev)
-        self.topk_gate = torch.empty((T, 1), dtype=f32, device=dev)
         self.scores = torch.empty((E, T), dtype=f32, device=dev)
         self.offsets = torch.empty((E + 1,), dtype=i32, device=dev)
         self.sorted_token = torch.empty((max(E * self.Cc, 1),), dtype=i32, device=dev)
@@ -148,7 +146,7 @@ def moe_layer_forward_ec(x, w_gate, gate_bias, w1, b1, w2, b2, C, residual=False
     if bufs is None:
         bufs = ECBuffers(T, d, h, E, C, x.dtype, x.device, out_dtype, train)
     b = bufs
-    N.moe_router_topk(x, w_gate, gate_bias, E, 1, True, b.logits, b.topk_idx, b.topk_gate, None,
+    N.moe_router_topk(x, w_gate, gate_bias, E, 1, True, b.logits, None, None, None,
                       b.ws_router, stream)
     N.moe_expert_choice(b.logits, T, E, C, b.scores, b.offsets, b.sorted_token, b.dest_row,
                         b.gate, stream)

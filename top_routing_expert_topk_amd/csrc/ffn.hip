@@ -560,8 +560,9 @@ __global__ __launch_bounds__(256) void decode_bf16(
         for (int u = 0; u < 8; ++u) {
           const int kk = kb + u * 512 + lane * 8;
           if (kk < K) {
-            wa[u] = *(const u32x4*)(w0 + kk);
-            wb[u] = *(const u32x4*)(w1 + kk);
+            // each weight is read once per call: non-temporal loads
+            wa[u] = __builtin_nontemporal_load((const u32x4*)(w0 + kk));
+            wb[u] = __builtin_nontemporal_load((const u32x4*)(w1 + kk));
           }
         }
 #pragma unroll

@@ -319,9 +319,16 @@ __global__ __launch_bounds__(512) void gemm_bf16_pring(
 #pragma unroll
     for (int i = 0; i < IPB; ++i) {
       const uint16_t* src;
-      if (q < 2) src = wb + (size_t)(q * 128 + i * 64) * K + koff;
-      else src = act + (q == 2 ? bo[0][i] : bo[NBQ - 1][i]) + koff;
-      dma16(src, dst + (i * NW + wave) * 8 * kRS);
+      // weights non-temporal: with at most a few row blocks per expert they
+      // are read about once, and the hint measured faster here (it slows
+      // the 256-row ring, whose tile order reuses weight panels from L2)
+      if (q < 2) {
+        src = wb + (size_t)(q * 128 + i * 64) * K + koff;
+        dma16_nt(src, dst + (i * NW + wave) * 8 * kRS);
+      } else {
+        src = act + (q == 2 ? bo[0][i] : bo[NBQ - 1][i]) + koff;
+        dma16(src, dst + (i * NW + wave) * 8 * kRS);
+      }
     }
   };
 

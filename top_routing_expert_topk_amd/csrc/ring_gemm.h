@@ -92,6 +92,10 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "me
 __device__ __forceinline__ void dma16(const void* g, void* lds_base) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
+// The same with the non-temporal cache policy, for data read once per call.
+__device__ __forceinline__ void dma16_nt(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 2);
+}
 
 __device__ __forceinline__ int swz128(int r, int c) { return c ^ ((r >> 1) & 7); }
 

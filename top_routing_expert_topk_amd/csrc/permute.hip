@@ -9,7 +9,8 @@
 // overflows is not stated there; here the first `capacity` in flat order
 // f = t*k + j are kept (first come, first served by token).
 //
-// Three kernels, all integer and exact:
+// Three kernels, all integer and exact (a few assignments take one block,
+// permute_small, through the same steps):
 //   1. hist:    one block per chunk of kPermuteChunk assignments; LDS
 //               histogram; counts per (expert, chunk).
 //   2. scan:    one block; per expert, exclusive prefix over chunks (block
@@ -145,12 +146,105 @@ __global__ __launch_bounds__(NTH) void permute_scatter(
   }
 }
 
+// Up to kSmallN assignments: the same three steps in one block of 1024
+// threads (histogram, kept counts and their scan, then rounds of 1024
+// assignments ranked as permute_scatter ranks them), one launch instead of
+// three and no workspace. (At 8192 assignments the one block takes as long
+// as the three kernels.)
+constexpr int kSmallN = 2048;
+constexpr int STH = 1024;
+__global__ __launch_bounds__(STH) void permute_small(const int32_t* __restrict__ idx, int n, int k,
+                                                     int E, int capacity,
+                                                     int32_t* __restrict__ counts,
+                                                     int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ dest_row,
+                                                     int32_t* __restrict__ sorted_token) {
+  __shared__ int hist[kMaxE];
+  __shared__ int run[kMaxE];
+  __shared__ int off[kMaxE + 1];
+  __shared__ int sc[2][kMaxE];
+  __shared__ int wcnt[STH / 64][kMaxE];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  for (int e = tid; e < kMaxE; e += STH) {
+    hist[e] = 0;
+    run[e] = 0;
+#pragma unroll
+    for (int w = 0; w < STH / 64; ++w) wcnt[w][e] = 0;
+  }
+  __syncthreads();
+  for (int f = tid; f < n; f += STH) atomicAdd(&hist[idx[f]], 1);
+  __syncthreads();
+  // kept per expert, inclusive scan over experts (threads 0 .. kMaxE-1)
+  int cur = 0;
+  if (tid < kMaxE) {
+    const int c = tid < E ? hist[tid] : 0;
+    if (tid < E) counts[tid] = c;
+    sc[0][tid] = (capacity >= 0 && c > capacity) ? capacity : c;
+  }
+  __syncthreads();
+  for (int o = 1; o < kMaxE; o <<= 1) {
+    if (tid < kMaxE) sc[cur ^ 1][tid] = sc[cur][tid] + (tid >= o ? sc[cur][tid - o] : 0);
+    cur ^= 1;
+    __syncthreads();
+  }
+  if (tid < E) {
+    off[tid + 1] = sc[cur][tid];
+    offsets[tid + 1] = sc[cur][tid];
+  }
+  if (tid == 0) {
+    off[0] = 0;
+    offsets[0] = 0;
+  }
+  int bits = 0;
+  while ((1 << bits) < E) ++bits;
+  __syncthreads();
+  for (int r0 = 0; r0 < n; r0 += STH) {
+    const int f = r0 + tid;
+    const bool valid = f < n;
+    const int e = valid ? idx[f] : 0;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < bits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(valid && bit);
+      peers &= bit ? m : ~m;
+    }
+    const int rank = __popcll(peers & lanemask_lt());
+    const int cnt = __popcll(peers);
+    const bool leader = valid && rank == 0;
+    if (leader) wcnt[wave][e] = cnt;
+    __syncthreads();
+    if (valid) {
+      int pos = run[e] + rank;
+      for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
+      const int kept = off[e + 1] - off[e];
+      int dst = -1;
+      if (pos < kept) {
+        dst = off[e] + pos;
+        sorted_token[dst] = f / k;
+      }
+      dest_row[f] = dst;
+    }
+    __syncthreads();
+    if (leader) {
+      atomicAdd(&run[e], cnt);
+      wcnt[wave][e] = 0;
+    }
+    __syncthreads();
+  }
+}
+
 // The three kernels over a caller's workspace (per-chunk histograms and
-// bases, 2 E nb int32, every entry written before it is read).
+// bases, 2 E nb int32, every entry written before it is read), or the
+// one-block kernel for a few assignments.
 int permute_run(const int32_t* topk_idx, int T, int k, int E, int capacity, int32_t* counts,
                 int32_t* offsets, int32_t* dest_row, int32_t* sorted_token, int32_t* blk_hist,
                 hipStream_t s) {
   const long n = (long)T * k;
+  if (n <= kSmallN) {
+    hipLaunchKernelGGL(permute_small, dim3(1), dim3(STH), 0, s, topk_idx, (int)n, k, E, capacity,
+                       counts, offsets, dest_row, sorted_token);
+    return launch_status();
+  }
   const int nb = permute_blocks(n);
   int32_t* blk_base = blk_hist + (size_t)E * nb;
   if (nb > 0) hipLaunchKernelGGL(permute_hist, dim3(nb), dim3(NTH), 0, s, topk_idx, n, E, nb, blk_hist);

@@ -665,7 +665,7 @@ __global__ __launch_bounds__(256) void wgate_partial(const T* __restrict__ x,
 
 // dW_g[e][c] = sum_s part[s][e][c] (s ascending); grid (ceil(E*d / 256)).
 // bf16 layers with d % 128 == 0: the same partial sums on the MFMA units.
-// Grid (ceil(E / 128), d / 128, S); four waves, each 64 experts x 64 columns
+// Grid ceil(E / 128) * (d / 128) * S; four waves, each 64 experts x 64 columns
 // of the block's 128 x 128 tile (2 x 2 32x32 MFMA tiles; lane = column,
 // registers = experts). Both operands contract over tokens, their leading
 // index, so each 64-token chunk is staged K-major ([64 tokens][128
@@ -679,7 +679,22 @@ __global__ __launch_bounds__(256) void wgate_mfma(const uint16_t* __restrict__ x
                                                   int E, int S, float* __restrict__ part) {
   __shared__ __align__(16) uint16_t sdl[2][64 * 128];
   __shared__ __align__(16) uint16_t sx[64 * 128];
-  const int e0 = blockIdx.x * 128, c0 = blockIdx.y * 128, s = blockIdx.z;
+  // Block -> (token range s, column tile, expert tile). With S a multiple of
+  // 8, range s runs on XCD s % 8 (blocks are dealt to the 8 XCDs in turn),
+  // all its tiles in a row with the expert tiles of a column adjacent, so
+  // its dlogits rows and x columns are fetched from HBM about once and
+  // re-read from that XCD's L2.
+  const int ne = (E + 127) / 128, per = ne * (d / 128);
+  int s, rem;
+  if ((S & 7) == 0) {
+    const int j = blockIdx.x >> 3;
+    s = (blockIdx.x & 7) + 8 * (j / per);
+    rem = j % per;
+  } else {
+    s = blockIdx.x / per;
+    rem = blockIdx.x % per;
+  }
+  const int e0 = (rem % ne) * 128, c0 = (rem / ne) * 128;
   const int tb = (int)((long)s * Tn / S), te = (int)((long)(s + 1) * Tn / S);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -778,15 +793,17 @@ __global__ __launch_bounds__(256) void wgate_mfma(const uint16_t* __restrict__ x
 
 // Token ranges of the MFMA form: about 1024 blocks, at most 64 ranges and
 // at least 64 tokens per range (never more ranges than router_bwd_splits,
-// whose workspace holds the partials).
+// whose workspace holds the partials); from 8 on a multiple of 8, one group
+// of ranges per XCD.
 inline int wgate_mfma_splits(int T, int d, int E) {
   const int tiles = ceil_div(E, 128) * (d / 128);
   int s = ceil_div(1024, tiles);
   if (s > 64) s = 64;
   if (s > T / 64) s = T / 64;
-  if (s < 1) s = 1;
   const int cap = router_bwd_splits(T, d, E);
-  return s < cap ? s : cap;
+  if (s > cap) s = cap;
+  if (s >= 8) s = s / 8 * 8;
+  return s < 1 ? 1 : s;
 }
 
 template <typename T>
@@ -908,7 +925,7 @@ extern "C" int moe_router_weight_backward(const void* x, int dtype, int T, int d
   float* part = (float*)ws;
   const dim3 g(ceil_div(E, kWgTile), ceil_div(d, kWgTile), S);
   if (mfma && T > 0)
-    hipLaunchKernelGGL(wgate_mfma, dim3(ceil_div(E, 128), d / 128, S), dim3(256), 0, s,
+    hipLaunchKernelGGL(wgate_mfma, dim3(ceil_div(E, 128) * (d / 128) * S), dim3(256), 0, s,
                        (const uint16_t*)x, dlogits, T, d, E, S, part);
   else if (dtype == MOE_BF16)
     hipLaunchKernelGGL(wgate_partial<uint16_t>, g, dim3(256), 0, s, (const uint16_t*)x, dlogits, T,

@@ -43,7 +43,7 @@ BWD_CALLS = ("combine_bwd", "router_bwd", "ffn_bwd", "gather_bwd", "router_weigh
 TRAIN_METRIC = "routed tokens/sec per MoE layer fwd+bwd (bf16, 1 GPU) + % of MFMA roofline"
 # tokens whose expert FFN the CPU baseline evaluates (routing always covers all T)
 CPU_SAMPLE = {"tiny_fp32": 256, "mixtral_prefill": 2048, "switch_top1_cap": 8192, "decode": 32,
-              "deepseek_v3": 512, "switch_expert_choice": 2048, "decode_offload": 32}
+              "deepseek_v3": 2048, "switch_expert_choice": 2048, "decode_offload": 32}
 # tokens of the sub-batch the backward CPU baseline differentiates
 BWD_CPU_SAMPLE = {"tiny_fp32": 256, "mixtral_prefill": 1024, "switch_top1_cap": 2048,
                   "deepseek_v3": 64, "switch_expert_choice": 2048}

@@ -149,8 +149,8 @@ __global__ __launch_bounds__(NTH) void permute_scatter(
 // Up to kSmallN assignments: the same three steps in one block of 1024
 // threads (histogram, kept counts and their scan, then rounds of 1024
 // assignments ranked as permute_scatter ranks them), one launch instead of
-// three and no workspace. (At 8192 assignments the one block takes as long
-// as the three kernels.)
+// three and no workspace; each thread loads its assignments once, up front.
+// (At 8192 assignments the one block is slower than the three kernels.)
 constexpr int kSmallN = 2048;
 constexpr int STH = 1024;
 __global__ __launch_bounds__(STH) void permute_small(const int32_t* __restrict__ idx, int n, int k,
@@ -171,8 +171,17 @@ __global__ __launch_bounds__(STH) void permute_small(const int32_t* __restrict__
 #pragma unroll
     for (int w = 0; w < STH / 64; ++w) wcnt[w][e] = 0;
   }
+  // every assignment this thread ranks, loaded once up front
+  int ev[kSmallN / STH];
+#pragma unroll
+  for (int r = 0; r < kSmallN / STH; ++r) {
+    const int f = r * STH + tid;
+    ev[r] = f < n ? idx[f] : 0;
+  }
   __syncthreads();
-  for (int f = tid; f < n; f += STH) atomicAdd(&hist[idx[f]], 1);
+#pragma unroll
+  for (int r = 0; r < kSmallN / STH; ++r)
+    if (r * STH + tid < n) atomicAdd(&hist[ev[r]], 1);
   __syncthreads();
   // kept per expert, inclusive scan over experts (threads 0 .. kMaxE-1)
   int cur = 0;
@@ -198,10 +207,13 @@ __global__ __launch_bounds__(STH) void permute_small(const int32_t* __restrict__
   int bits = 0;
   while ((1 << bits) < E) ++bits;
   __syncthreads();
-  for (int r0 = 0; r0 < n; r0 += STH) {
+#pragma unroll
+  for (int rr = 0; rr < kSmallN / STH; ++rr) {
+    const int r0 = rr * STH;
+    if (r0 >= n) break;
     const int f = r0 + tid;
     const bool valid = f < n;
-    const int e = valid ? idx[f] : 0;
+    const int e = ev[rr];
     uint64_t peers = __ballot(valid);
     for (int b = 0; b < bits; ++b) {
       const bool bit = (e >> b) & 1;

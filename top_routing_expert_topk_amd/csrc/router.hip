@@ -358,16 +358,18 @@ __global__ __launch_bounds__(256) void router_select(
 // The same split-K product for d a multiple of 64, with 64-column stages
 // (128-byte LDS rows, chunk c of row r at c ^ ((r >> 1) & 7), which puts the
 // 16 rows a ds_read_b128 serves at once on distinct bank groups) and the
-// four waves in a 2 x 2 grid, each owning (TT/2) tokens x (EP/2) experts as
-// TM x TN v_mfma_f32_32x32x16_bf16 tiles: per 16 k a wave reads TM + TN
-// fragments for TM * TN MFMAs. Lane l supplies row l%32 and k-octet l/32 of
+// waves in a 2 x NWN grid (NWN = 4, two waves per SIMD, when the expert
+// tiles split evenly; else 2), each owning (TT/2) tokens x (EP/NWN) experts
+// as TM x TNW v_mfma_f32_32x32x16_bf16 tiles: per 16 k a wave reads TM + TNW
+// fragments for TM * TNW MFMAs. Lane l supplies row l%32 and k-octet l/32 of
 // both operands (A = 32 experts, B = 32 tokens) and receives expert
 // 8*(v/4) + 4*(l/32) + v%4 of token l%32 in accumulator v.
 constexpr int RK2 = 64;  // K columns per stage
+constexpr int kWideNWN = 4;  // waves along the experts when a block has an even TN
 __device__ __forceinline__ int swz8(int r, int c) { return c ^ ((r >> 1) & 7); }
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-template <int TM, int TN>
+template <int TM, int TN, int NWN>
 struct WideCfg {
   static constexpr int TT = 64 * TM, EP = 64 * TN, ROWS = TT + EP;
   static constexpr int STAGE = ROWS * RK2;  // bf16 elements
@@ -376,25 +378,27 @@ struct WideCfg {
   static constexpr size_t LDS = (size_t)NS * STAGE * 2;
 };
 
-template <int TM, int TN>
-__global__ __launch_bounds__(256) void router_logits_wide(
+template <int TM, int TN, int NWN>
+__global__ __launch_bounds__(128 * NWN) void router_logits_wide(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int T, int d, int E, int nch,
     int split, float* __restrict__ part) {
-  using C = WideCfg<TM, TN>;
+  using C = WideCfg<TM, TN, NWN>;
   constexpr int TT = C::TT, EP = C::EP, ROWS = C::ROWS, STAGE = C::STAGE, NS = C::NS;
-  constexpr int IPW = ROWS / 8 / 4;  // DMA instructions (8 rows each) per wave per stage
-  static_assert((ROWS / 8) % 4 == 0, "DMA instructions split over the four waves");
+  constexpr int NW = 2 * NWN;         // waves: 2 along tokens x NWN along experts
+  constexpr int TNW = 2 * TN / NWN;   // expert tiles per wave
+  constexpr int IPW = ROWS / 8 / NW;  // DMA instructions (8 rows each) per wave per stage
+  static_assert((ROWS / 8) % NW == 0 && TNW >= 1, "wave layout");
   extern __shared__ __align__(1024) uint16_t rs[];
   const int tile = blockIdx.x / split, p = blockIdx.x % split;
   const int t0 = tile * TT;
   const int c0 = p * nch / split, c1 = (p + 1) * nch / split;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / NWN, wn = wave % NWN;
 
   const uint16_t* src[IPW];
 #pragma unroll
   for (int q = 0; q < IPW; ++q) {
-    const int r = (q * 4 + wave) * 8 + (lane >> 3);
+    const int r = (q * NW + wave) * 8 + (lane >> 3);
     const uint16_t* base = r < TT ? x + (size_t)min(t0 + r, T - 1) * d
                                   : w + (size_t)min(r - TT, E - 1) * d;
     src[q] = base + swz8(r, lane & 7) * 8;
@@ -402,14 +406,14 @@ __global__ __launch_bounds__(256) void router_logits_wide(
   auto issue = [&](int buf, int c) {
 #pragma unroll
     for (int q = 0; q < IPW; ++q)
-      dma16(src[q] + (size_t)c * RK2, &rs[buf * STAGE + (q * 4 + wave) * 8 * RK2]);
+      dma16(src[q] + (size_t)c * RK2, &rs[buf * STAGE + (q * NW + wave) * 8 * RK2]);
   };
 
-  f32x16 acc[TM][TN];
+  f32x16 acc[TM][TNW];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < TNW; ++j) acc[i][j] = f32x16{};
 
   const int ch = lane >> 5;
 #pragma unroll
@@ -428,10 +432,10 @@ __global__ __launch_bounds__(256) void router_logits_wide(
     const uint16_t* st = rs + buf * STAGE;
 #pragma unroll
     for (int s = 0; s < RK2 / 16; ++s) {
-      bf16x8 a[TN], b[TM];
+      bf16x8 a[TNW], b[TM];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int r = TT + wn * (EP / 2) + 32 * j + (lane & 31);
+      for (int j = 0; j < TNW; ++j) {
+        const int r = TT + wn * (EP / NWN) + 32 * j + (lane & 31);
         a[j] = *(const bf16x8*)(st + r * RK2 + swz8(r, 2 * s + ch) * 8);
       }
 #pragma unroll
@@ -442,7 +446,7 @@ __global__ __launch_bounds__(256) void router_logits_wide(
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+        for (int j = 0; j < TNW; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], b[i], acc[i][j], 0, 0, 0);
     }
   }
@@ -452,10 +456,10 @@ __global__ __launch_bounds__(256) void router_logits_wide(
     const int t = t0 + wm * (TT / 2) + 32 * i + (lane & 31);
     if (t >= T) continue;
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+    for (int j = 0; j < TNW; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int e = wn * (EP / 2) + 32 * j + 8 * g + 4 * ch;
+        const int e = wn * (EP / NWN) + 32 * j + 8 * g + 4 * ch;
         float* dst = pp + (size_t)t * E + e;
         if ((E & 3) == 0) {
           if (e < E)
@@ -625,12 +629,13 @@ bool launch_select(int k, hipStream_t s, const float* part, int split, const flo
 template <int TM, int TN>
 bool launch_wide(const RouterPlan& pl, const void* x, const void* w, int T, int d, int E,
                  float* part, hipStream_t s) {
-  const size_t lds = WideCfg<TM, TN>::LDS;
+  constexpr int NWN = (TN % 2 == 0) ? kWideNWN : 2;
+  const size_t lds = WideCfg<TM, TN, NWN>::LDS;
   if (lds > 65536 &&
-      hipFuncSetAttribute((const void*)router_logits_wide<TM, TN>,
+      hipFuncSetAttribute((const void*)router_logits_wide<TM, TN, NWN>,
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
     return false;
-  hipLaunchKernelGGL((router_logits_wide<TM, TN>), dim3(pl.ntt * pl.split), dim3(256), lds, s,
+  hipLaunchKernelGGL((router_logits_wide<TM, TN, NWN>), dim3(pl.ntt * pl.split), dim3(128 * NWN), lds, s,
                      (const uint16_t*)x, (const uint16_t*)w, T, d, E, d / RK2, pl.split, part);
   return true;
 }

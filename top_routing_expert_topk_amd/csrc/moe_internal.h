@@ -154,9 +154,13 @@ struct RouterPlan {
 inline RouterPlan router_plan(int T, int d, int E) {
   RouterPlan p;
   p.ep = (E + 63) / 64 * 64;
-  int tt = 32768 / p.ep / 64 * 64;
+  // token rows per tile: 128 x 256 for E = 256, where every token tile
+  // re-reads the 3.7 MB W_g; smaller tiles (less K splitting, fewer partial
+  // logits) for E <= 192
+  int tt = (p.ep >= 256 ? 32768 : 8192) / p.ep / 64 * 64;
   if (tt > 256) tt = 256;
-  p.tt = tt;  // 256, 128 or 64 for E <= 512
+  if (tt < 64) tt = 64;
+  p.tt = tt;  // 128 or 64
   p.ntt = ceil_div(T > 0 ? T : 1, tt);
   p.nch = ceil_div(d, 32);
   // about one block per CU, but each K range at least kRouterMinChunks chunks:

@@ -646,9 +646,9 @@ bool dispatch_logits(const RouterPlan& pl, const void* x, const void* w, int T, 
   if (d % RK2 == 0 && pl.split <= d / RK2) {
 #define MOE_WIDE(A, B)                                                                 \
   if (mtw == A && nte == 4 * B) return launch_wide<A, B>(pl, x, w, T, d, E, part, s);
-    MOE_WIDE(4, 1)
-    MOE_WIDE(4, 2)
-    MOE_WIDE(2, 3)
+    MOE_WIDE(2, 1)
+    MOE_WIDE(1, 2)
+    MOE_WIDE(1, 3)
     MOE_WIDE(2, 4)
     MOE_WIDE(1, 5)
     MOE_WIDE(1, 6)
@@ -658,9 +658,9 @@ bool dispatch_logits(const RouterPlan& pl, const void* x, const void* w, int T, 
   }
 #define MOE_CASE(A, B)                               \
   if (mtw == A && nte == B) return launch_logits<A, B>(pl, x, w, T, d, E, part, s);
-  MOE_CASE(4, 4)
-  MOE_CASE(4, 8)
-  MOE_CASE(2, 12)
+  MOE_CASE(2, 4)
+  MOE_CASE(1, 8)
+  MOE_CASE(1, 12)
   MOE_CASE(2, 16)
   MOE_CASE(1, 20)
   MOE_CASE(1, 24)

@@ -89,7 +89,7 @@ __global__ __launch_bounds__(256) void ec_scores(const float* __restrict__ logit
   }
 }
 
-constexpr int kSelThreads = 512;
+constexpr int kSelThreads = 1024;
 constexpr int kSelLds = 16384;  // columns up to this many tokens are staged in LDS
 
 // Inclusive prefix sum over the block (threads in order) of one int per

@@ -348,15 +348,29 @@ __device__ __forceinline__ void big_store(f32x16 (&acc)[4][TM], const f32x16& ac
             f32x4{accx[4 * q], accx[4 * q + 1], accx[4 * q + 2], accx[4 * q + 3]};
     return;
   }
-  auto bias4 = [&](int nl, float* bv) __attribute__((always_inline)) {
-    bv[0] = bv[1] = bv[2] = bv[3] = 0.0f;
-    if (bias) {
-      const u32x2 bb = *(const u32x2*)(bias + (size_t)wk.e * N + wk.n0 + nl);
-      bv[0] = bf16lo(bb[0]);
-      bv[1] = bf16hi(bb[0]);
-      bv[2] = bf16lo(bb[1]);
-      bv[3] = bf16hi(bb[1]);
+  // The tile's 256 biases go to LDS once, at the start of the epilogue
+  // (32 lanes, one 16-byte load each, behind the staging area): reading
+  // them from global memory where each piece is used cost one round trip
+  // per piece (and, after the first stores, a wait for those stores, which
+  // share the vector memory counter), about 4 us per half tile.
+  uint16_t* sbias = ot + ot_bytes / 2 - kBigBN;
+  static_assert((size_t)kBigRowsMax * (BN + 8) * 2 <= (size_t)kRSlots * kRBlk * 2 - kBigBN * 2 &&
+                    (size_t)kBigRowsMax * (BN / 2 + 4) * 4 <= (size_t)kRSlots * kRBlk * 2 - kBigBN * 2,
+                "the staged tile and the biases must not overlap");
+  auto load_bias = [&]() __attribute__((always_inline)) {
+    if (tid < kBigBN / 8) {
+      const u32x4 b = bias ? *(const u32x4*)(bias + (size_t)wk.e * N + wk.n0 + tid * 8)
+                           : u32x4{0u, 0u, 0u, 0u};
+      *(u32x4*)(sbias + tid * 8) = b;
     }
+    __syncthreads();
+  };
+  auto bias4 = [&](int nl, float* bv) __attribute__((always_inline)) {
+    const u32x2 bb = *(const u32x2*)(sbias + nl);
+    bv[0] = bf16lo(bb[0]);
+    bv[1] = bf16hi(bb[0]);
+    bv[2] = bf16lo(bb[1]);
+    bv[3] = bf16hi(bb[1]);
   };
   if constexpr (EPI == kEpiBiasQ) {
     // rows leave through LDS (the idle ring) in two halves of 128 features:
@@ -369,6 +383,7 @@ __device__ __forceinline__ void big_store(f32x16 (&acc)[4][TM], const f32x16& ac
     float* st = (float*)ot;
     constexpr int FSTR = 128 + 4;  // LDS row stride in floats
     lds_barrier();                 // every wave is done reading the ring
+    load_bias();
 #pragma unroll 1
     for (int hh = 0; hh < 2; ++hh) {
       if (wn == hh) {
@@ -378,7 +393,7 @@ __device__ __forceinline__ void big_store(f32x16 (&acc)[4][TM], const f32x16& ac
           for (int q = 0; q < 4; ++q) {
             const int nl = i * 32 + 8 * q + 4 * ch;  // feature within the half
             float bv[4];
-            bias4(wn * WTN + nl, bv);
+            bias4(wn * WTN + i * 32 + 8 * q + 4 * ch, bv);
 #pragma unroll
             for (int j = 0; j < TM; ++j) {
               const int m = wm * WTM + j * 32 + (lane & 31);
@@ -415,22 +430,16 @@ __device__ __forceinline__ void big_store(f32x16 (&acc)[4][TM], const f32x16& ac
   uint16_t* out = (uint16_t*)outv;
   constexpr int OSTR = BN + 8;  // LDS row stride in bf16 elements
   constexpr int CPR = BN / 8;   // 16-byte chunks per row
-  (void)ot_bytes;  // callers static_assert BM * OSTR * 2 <= ot_bytes
   lds_barrier();  // every wave is done reading the ring
+  load_bias();
   if (EPI == kEpiSilu && zout) {
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int nl = wn * WTN + i * 32 + 8 * q + 4 * ch;
-        float bv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (bias) {
-          const u32x2 bb = *(const u32x2*)(bias + (size_t)wk.e * N + wk.n0 + nl);
-          bv[0] = bf16lo(bb[0]);
-          bv[1] = bf16hi(bb[0]);
-          bv[2] = bf16lo(bb[1]);
-          bv[3] = bf16hi(bb[1]);
-        }
+        float bv[4];
+        bias4(wn * WTN + i * 32 + 8 * q + 4 * ch, bv);
 #pragma unroll
         for (int j = 0; j < TM; ++j) {
           const int m = wm * WTM + j * 32 + (lane & 31);
@@ -469,14 +478,8 @@ __device__ __forceinline__ void big_store(f32x16 (&acc)[4][TM], const f32x16& ac
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int nl = wn * WTN + i * 32 + 8 * q + 4 * ch;
-      float bv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (bias) {
-        const u32x2 bb = *(const u32x2*)(bias + (size_t)wk.e * N + wk.n0 + nl);
-        bv[0] = bf16lo(bb[0]);
-        bv[1] = bf16hi(bb[0]);
-        bv[2] = bf16lo(bb[1]);
-        bv[3] = bf16hi(bb[1]);
-      }
+      float bv[4];
+      bias4(wn * WTN + i * 32 + 8 * q + 4 * ch, bv);
 #pragma unroll
       for (int j = 0; j < TM; ++j) {
         const int m = wm * WTM + j * 32 + (lane & 31);

@@ -65,6 +65,9 @@ SMALL = {
                                                    E=4),
     # 256 x 256 tiles: whole rounds of tiles plus a split tail
     "big_full_tail": CFG["mixtral_prefill"].with_(name="big_full_tail", T=4096, d=512, h=2048),
+    # the same without expert biases (the whole tiles' epilogue stages zeros)
+    "big_full_tail_no_bias": CFG["mixtral_prefill"].with_(name="big_full_tail_no_bias", T=4096,
+                                                           d=512, h=2048, expert_bias=False),
     # 256 x 256 tiles over experts of ~256 rows: many last row blocks hold a
     # few rows, whose idle waves and activation DMAs are skipped
     "big_ragged": CFG["deepseek_v3"].with_(name="big_ragged", T=2048, d=512, h=512, E=64),

@@ -373,55 +373,62 @@ __device__ __forceinline__ void big_store(f32x16 (&acc)[4][TM], const f32x16& ac
     bv[3] = bf16hi(bb[1]);
   };
   if constexpr (EPI == kEpiBiasQ) {
-    // rows leave through LDS (the idle ring) in two halves of 128 features:
-    // the waves of weight-row half wn stage half wn in fp32 (rows padded by
-    // 16 bytes, so the 32 rows a wave writes at one feature offset spread
-    // over the banks), then 16 lanes add the bias, encode a row's 16 blocks
-    // of 8 features and store its 256 bytes of mantissas and 16 exponent
-    // bytes. The staging loop has no reads: with one (a bias read per run)
-    // each of its LDS waits also waited for the previous run's writes, and
-    // the staging of a half took about 2.6 us.
+    // rows leave through LDS (the idle ring) in passes of 128 rows x all 256
+    // features (then the up to 32 rows of a taller tile): the four waves that
+    // hold a pass's rows, one per SIMD, stage them in fp32 (rows padded by 16
+    // bytes, so the 32 rows a wave writes at one feature offset spread over
+    // the banks), then 32 lanes per row add the bias, encode its 32 blocks
+    // of 8 features and store its 512 bytes of mantissas and 32 exponent
+    // bytes. Staging by weight halves instead (the four waves of a half sit
+    // on two SIMDs) made each staging pass about 1 us longer. The staging
+    // loop has no reads: with one (a bias read per run) each of its LDS waits
+    // also waited for the previous run's writes.
     unsigned char* out = (unsigned char*)outv;
     const size_t rb = yq_row_bytes(N);
     float* st = (float*)ot;
-    constexpr int FSTR = 128 + 4;  // LDS row stride in floats
-    lds_barrier();                 // every wave is done reading the ring
+    constexpr int FSTR = BN + 4;  // LDS row stride in floats
+    static_assert(128 * FSTR * 4 <= (size_t)kRSlots * kRBlk * 2 - kBigBN * 2,
+                  "a staged pass and the biases must not overlap");
+    lds_barrier();  // every wave is done reading the ring
     load_bias();
+    const int bl = tid & 31;  // this thread's block of 8 features
+    const u32x4 bb = *(const u32x4*)(sbias + bl * 8);
+    const long r0 = (long)wk.e * ores + wk.row0;
+    const int npass = ext ? 3 : 2;
 #pragma unroll 1
-    for (int hh = 0; hh < 2; ++hh) {
-      if (wn == hh) {
+    for (int pp = 0; pp < npass; ++pp) {
+      if (pp < 2) {
+        if ((wm >> 1) == pp) {
 #pragma unroll
-        for (int i = 0; i < TN; ++i)
+          for (int i = 0; i < TN; ++i)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int nl = i * 32 + 8 * q + 4 * ch;  // feature within the half
+            for (int q = 0; q < 4; ++q) {
+              const int nl = wn * WTN + i * 32 + 8 * q + 4 * ch;
 #pragma unroll
-            for (int j = 0; j < TM; ++j) {
-              const int m = wm * WTM + j * 32 + (lane & 31);
-              *(f32x4*)(st + m * FSTR + nl) =
-                  f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                        acc[i][j][4 * q + 3]};
+              for (int j = 0; j < TM; ++j) {
+                const int m = (wm & 1) * WTM + j * 32 + (lane & 31);  // row within the pass
+                *(f32x4*)(st + m * FSTR + nl) =
+                    f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                          acc[i][j][4 * q + 3]};
+              }
             }
-          }
-        if (ext)
+        }
+      } else {
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            *(f32x4*)(st + mx * FSTR + nlx(q) - wn * WTN) =
-                f32x4{accx[4 * q], accx[4 * q + 1], accx[4 * q + 2], accx[4 * q + 3]};
+        for (int q = 0; q < 4; ++q)
+          *(f32x4*)(st + (lane & 31) * FSTR + nlx(q)) =
+              f32x4{accx[4 * q], accx[4 * q + 1], accx[4 * q + 2], accx[4 * q + 3]};
       }
       __syncthreads();
-      const int bl = tid & 15;  // this thread's block of 8 features in the half
-      const long r0 = (long)wk.e * ores + wk.row0;
-      const u32x4 bb = *(const u32x4*)(sbias + hh * WTN + bl * 8);
-      const float bv[8] = {bf16lo(bb[0]), bf16hi(bb[0]), bf16lo(bb[1]), bf16hi(bb[1]),
-                           bf16lo(bb[2]), bf16hi(bb[2]), bf16lo(bb[3]), bf16hi(bb[3])};
+      const int prow0 = pp * 128, prows = min(pp < 2 ? 128 : kBigXR, wk.rows - prow0);
 #pragma unroll 2
-      for (int m = tid >> 4; m < wk.rows; m += NW * 4) {
+      for (int m = tid >> 5; m < prows; m += NW * 2) {
         const f32x4 a = *(const f32x4*)(st + m * FSTR + bl * 8);
         const f32x4 b = *(const f32x4*)(st + m * FSTR + bl * 8 + 4);
-        const float v[8] = {a[0] + bv[0], a[1] + bv[1], a[2] + bv[2], a[3] + bv[3],
-                            b[0] + bv[4], b[1] + bv[5], b[2] + bv[6], b[3] + bv[7]};
-        yq_store8(out, rb, N, r0 + m, wk.n0 + hh * WTN + bl * 8, v);
+        const float v[8] = {a[0] + bf16lo(bb[0]), a[1] + bf16hi(bb[0]), a[2] + bf16lo(bb[1]),
+                            a[3] + bf16hi(bb[1]), b[0] + bf16lo(bb[2]), b[1] + bf16hi(bb[2]),
+                            b[2] + bf16lo(bb[3]), b[3] + bf16hi(bb[3])};
+        yq_store8(out, rb, N, r0 + prow0 + m, wk.n0 + bl * 8, v);
       }
       __syncthreads();
     }

@@ -314,6 +314,8 @@ __global__ __launch_bounds__(512) void big_plan(const int32_t* __restrict__ offs
 // (the product is taken of the bf16-rounded accumulator). Output row of tile
 // row m: e * ores + row0 + m. kEpiSilu with zout: the pre-activation
 // acc + bias also leaves, to zout, in a first pass through the same staging.
+// kEpiBiasQ (block fixed point) stages fp32 sums instead, in passes of 128
+// rows, and adds the bias as the rows leave (see there).
 template <int NW, int TM, int EPI>
 __device__ __forceinline__ void big_store(f32x16 (&acc)[4][TM], const f32x16& accx,
                                           uint16_t* ot, size_t ot_bytes,

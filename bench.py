@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--no-clock", action="store_true",
                     help="skip the 3 s run after the timed steps that reads the shader clock "
                          "(for counter runs, where every dispatch is serialised)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured in a HIP graph and replayed (a 'graph' "
+                         "object beside the eager line's figures)")
     ap.add_argument("--backward", action="store_true",
                     help="time forward + backward (a training step) instead of the forward")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -234,6 +237,30 @@ def clock_window(step, seconds=None):
                 torch.cuda.synchronize()
         torch.cuda.synchronize()
     return clk.summary(t0)
+
+
+def graph_replay(step, stream, steps, warmup, T):
+    """The same step captured once in a HIP graph on `stream` and replayed:
+    `steps` timed replays after `warmup` untimed ones, HIP events on the
+    stream around the whole timed region."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=stream):
+        step()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3), "replays": steps,
+            "note": "the five calls captured once in a HIP graph and replayed"}
 
 
 def cpu_model():
@@ -635,6 +662,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     sclk = clock_window(step)
+    graph = graph_replay(step, stream, args.steps, args.warmup, T) if args.graph else None
     nc = len(calls)
     per_call = {c: [] for c in calls}
     for ev in events:
@@ -700,6 +728,8 @@ def main():
         "device": torch.cuda.get_device_name(dev),
         "sclk": sclk,
     }
+    if graph is not None:
+        out["graph"] = graph
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, CPU_SAMPLE.get(cfg.name, 64))
     print(json.dumps(out), flush=True)

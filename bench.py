@@ -260,7 +260,7 @@ def graph_replay(step, stream, steps, warmup, T):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     return {"ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3), "replays": steps,
-            "note": "the five calls captured once in a HIP graph and replayed"}
+            "note": "the step's calls captured once in a HIP graph and replayed"}
 
 
 def cpu_model():
@@ -516,6 +516,7 @@ def bench_backward(args, cfg, inp, dev):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     sclk = clock_window(step)
+    graph = graph_replay(step, stream, args.steps, args.warmup, T) if args.graph else None
     ms = {c: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in events]))
           for j, c in enumerate(calls)}
     ms_step = events[0][0].elapsed_time(events[-1][len(calls)]) / args.steps
@@ -559,6 +560,8 @@ def bench_backward(args, cfg, inp, dev):
         "device": torch.cuda.get_device_name(dev),
         "sclk": sclk,
     }
+    if graph is not None:
+        out["graph"] = graph
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_backward(cfg, inp, dout, BWD_CPU_SAMPLE.get(cfg.name, 64))
     print(json.dumps(out), flush=True)

@@ -5,7 +5,8 @@ one step can be captured on a stream and replayed. Each replay must give the
 eager step's outputs bit for bit. Between replays the test poisons every
 output with eager fill kernels, synchronises, and also runs the eager step on
 the same buffers, so a replay that reused stale memory or skipped a kernel
-would show. Shapes cover the 256-row ring GEMM (whole and split tiles, and
+would show. The same holds for a training step (the forward keeping Z and
+H, then the five backward calls). Shapes cover the 256-row ring GEMM (whole and split tiles, and
 taller last tiles), the persistent 128-row GEMM with capacity drops and a
 residual, the decode weight-streaming kernel and an fp32 layer.
 """
@@ -55,9 +56,11 @@ def _snapshot(ts, R):
 
 
 def _equal(a, b):
-    if a.is_floating_point():
-        return torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a,
-                           b.view(torch.int32) if b.dtype == torch.float32 else b)
+    # bit patterns, so that NaN poison left behind would not compare equal
+    if a.dtype == torch.float32:
+        return torch.equal(a.view(torch.int32), b.view(torch.int32))
+    if a.dtype == torch.bfloat16:
+        return torch.equal(a.view(torch.int16), b.view(torch.int16))
     return torch.equal(a, b)
 
 
@@ -104,3 +107,68 @@ def test_graph_replay_equals_eager(name):
         for key, v in _snapshot(outs, R).items():
             assert _equal(v, ref[key]), f"{name}: eager step after replay {rep} differs in {key}"
     print(f"[graph] {name}: {REPLAYS} replays equal the eager step (R={R})", flush=True)
+
+
+# ------------------------------------------------------- training step ----
+TRAIN_CASES = {
+    "ring_taller": CASES["ring_taller"],
+    "switch_small": CFG["switch_top1_cap"].with_(name="switch_train_graph", T=1024, d=256,
+                                                  h=512, E=16, capacity=80),
+    "fp32": CASES["fp32"],
+}
+
+
+@pytest.mark.parametrize("name", sorted(TRAIN_CASES))
+def test_training_step_graph_replay_equals_eager(name):
+    """Forward keeping Z and H, then the five backward calls, captured once:
+    every replay gives the eager step's gradients bit for bit."""
+    cfg = TRAIN_CASES[name]
+    print(f"[graph-train] {name}: T={cfg.T} d={cfg.d} h={cfg.h} E={cfg.E} k={cfg.k} "
+          f"{cfg.dtype}", flush=True)
+    inp = mi.make_inputs(cfg, "cuda")
+    dout = mi.make_dout(cfg, "cuda")
+    dev = torch.device("cuda")
+    s = torch.cuda.Stream()  # default priority
+    fwd = moe.MoEBuffers(cfg.T, cfg.d, cfg.h, cfg.E, cfg.k, cfg.torch_dtype, dev,
+                         cfg.torch_dtype, train=True)
+    grads = moe.MoEGrads(cfg.T, cfg.d, cfg.h, cfg.E, cfg.k, cfg.torch_dtype, dev,
+                         inp["b1"] is not None, inp["b2"] is not None,
+                         inp["gate_bias"] is not None)
+    args = (inp["x"], inp["w_gate"], inp["gate_bias"], inp["w1"], inp["b1"], inp["w2"],
+            inp["b2"])
+
+    def step():
+        moe.moe_layer_forward(*args, cfg.k, cfg.renorm, cfg.capacity, cfg.residual, bufs=fwd,
+                              stream=s, train=True)
+        moe.moe_layer_backward(fwd, *args, dout, cfg.renorm, cfg.residual, 0.01, grads=grads,
+                               stream=s)
+
+    outs = {n: v for n, v in dict(dx=grads.dx, dw_gate=grads.dw_gate,
+                                  dgate_bias=grads.dgate_bias, dw1=grads.dw1, db1=grads.db1,
+                                  dw2=grads.dw2, db2=grads.db2, dgate=grads.dgate,
+                                  dlogits=grads.dlogits, out=fwd.out, loss=fwd.loss).items()
+            if v is not None}
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        _poison(outs)
+        step()
+    torch.cuda.synchronize()
+    ref = {n: v.clone() for n, v in outs.items()}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(REPLAYS):
+        with torch.cuda.stream(s):
+            _poison(outs)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for key, v in outs.items():
+            assert _equal(v, ref[key]), f"{name}: replay {rep} differs in {key}"
+        with torch.cuda.stream(s):
+            step()
+        torch.cuda.synchronize()
+        for key, v in outs.items():
+            assert _equal(v, ref[key]), f"{name}: eager step after replay {rep} differs in {key}"
+    print(f"[graph-train] {name}: {REPLAYS} replays equal the eager step", flush=True)

@@ -408,6 +408,13 @@ __global__ __launch_bounds__(128 * NWN) void router_logits_wide(
     for (int q = 0; q < IPW; ++q)
       dma16(src[q] + (size_t)c * RK2, &rs[buf * STAGE + (q * NW + wave) * 8 * RK2]);
   };
+  // part p of P of a stage's DMA instructions
+  auto issue_part = [&](int buf, int c, int p, int P) {
+#pragma unroll
+    for (int q = 0; q < IPW; ++q)
+      if (q * P / IPW == p)
+        dma16(src[q] + (size_t)c * RK2, &rs[buf * STAGE + (q * NW + wave) * 8 * RK2]);
+  };
 
   f32x16 acc[TM][TNW];
 #pragma unroll
@@ -428,10 +435,17 @@ __global__ __launch_bounds__(128 * NWN) void router_logits_wide(
     else if (NS > 2 && later >= 1) wait_vm<(NS > 2 ? 1 : 0) * IPW>();
     else wait_vm<0>();
     lds_barrier();
-    if (c + NS - 1 < c1) issue((c - c0 + NS - 1) % NS, c + NS - 1);
+    // the refill of chunk c - 1's buffer goes out in three parts, before each
+    // of the first three 16-column sub-steps, so no wave issues all of it
+    // behind the barrier before its first MFMA (router call 80 -> 77 us on
+    // the DeepSeek shape, 22 -> 21 us on the Switch shape, in an A/B on one
+    // box); all of it is issued before the next wait, whose counts hold
+    const bool refill = c + NS - 1 < c1;
+    const int rbuf = (c - c0 + NS - 1) % NS;
     const uint16_t* st = rs + buf * STAGE;
 #pragma unroll
     for (int s = 0; s < RK2 / 16; ++s) {
+      if (refill && s < 3) issue_part(rbuf, c + NS - 1, s, 3);
       bf16x8 a[TNW], b[TM];
 #pragma unroll
       for (int j = 0; j < TNW; ++j) {

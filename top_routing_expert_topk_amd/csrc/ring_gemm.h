@@ -391,6 +391,7 @@ __device__ __forceinline__ void big_store(f32x16 (&acc)[4][TM], const f32x16& ac
     constexpr int FSTR = BN + 4;  // LDS row stride in floats
     static_assert(128 * FSTR * 4 <= (size_t)kRSlots * kRBlk * 2 - kBigBN * 2,
                   "a staged pass and the biases must not overlap");
+    static_assert(NW == 8 && WTM == 64, "a pass is the rows of two 64-row wave groups");
     lds_barrier();  // every wave is done reading the ring
     load_bias();
     const int bl = tid & 31;  // this thread's block of 8 features

@@ -172,3 +172,57 @@ def test_training_step_graph_replay_equals_eager(name):
         for key, v in outs.items():
             assert _equal(v, ref[key]), f"{name}: eager step after replay {rep} differs in {key}"
     print(f"[graph-train] {name}: {REPLAYS} replays equal the eager step", flush=True)
+
+
+# ------------------------------------------------------- Expert Choice ----
+EC_CASES = {
+    "ec_switch_small": CFG["switch_expert_choice"].with_(name="ec_graph", T=1000, d=256, h=512,
+                                                         E=16, capacity=70),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EC_CASES))
+def test_expert_choice_graph_replay_equals_eager(name):
+    """The Expert Choice forward (router logits, selection per expert, grouped
+    FFN, combine) captured once: every replay equals the eager step."""
+    cfg = EC_CASES[name]
+    print(f"[graph-ec] {name}: T={cfg.T} d={cfg.d} h={cfg.h} E={cfg.E} C={cfg.capacity}",
+          flush=True)
+    inp = mi.make_inputs(cfg, "cuda")
+    s = torch.cuda.Stream()  # default priority
+    b = moe.ECBuffers(cfg.T, cfg.d, cfg.h, cfg.E, cfg.capacity, cfg.torch_dtype,
+                      torch.device("cuda"))
+
+    def step():
+        moe.moe_layer_forward_ec(inp["x"], inp["w_gate"], inp["gate_bias"], inp["w1"],
+                                 inp["b1"], inp["w2"], inp["b2"], cfg.capacity, cfg.residual,
+                                 bufs=b, stream=s)
+
+    outs = {"out": b.out, "logits": b.logits, "scores": b.scores, "offsets": b.offsets,
+            "sorted_token": b.sorted_token, "dest_row": b.dest_row, "gate": b.gate,
+            "y_perm": b.y_perm}
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        _poison(outs)
+        step()
+    torch.cuda.synchronize()
+    R = int(b.offsets[-1])
+    ref = _snapshot(outs, R)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(REPLAYS):
+        with torch.cuda.stream(s):
+            _poison(outs)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for key, v in _snapshot(outs, R).items():
+            assert _equal(v, ref[key]), f"{name}: replay {rep} differs in {key}"
+        with torch.cuda.stream(s):
+            step()
+        torch.cuda.synchronize()
+        for key, v in _snapshot(outs, R).items():
+            assert _equal(v, ref[key]), f"{name}: eager step after replay {rep} differs in {key}"
+    print(f"[graph-ec] {name}: {REPLAYS} replays equal the eager step (R={R})", flush=True)
